@@ -1,0 +1,110 @@
+// C ABI of the KDA hot path: argument validation, workspace carving and
+// kernel dispatch.  The operation each entry point performs is documented in
+// include/kda.h.  Nothing here allocates memory or synchronises the host,
+// except kda_chunk_fwd_check, which exists to do exactly that.
+#include "../../include/kda.h"
+#include "kda_internal.h"
+
+#include <limits.h>
+
+namespace {
+
+bool supported_d(int32_t d) { return d == 64 || d == 128; }
+
+bool aligned(const void* p, size_t bytes) { return (reinterpret_cast<uintptr_t>(p) % bytes) == 0; }
+
+kda_status check_common(int32_t H, int32_t dk, int32_t dv, kda_dtype dt, kda_gate gk) {
+    if (H <= 0) return KDA_ERR_INVALID_ARG;
+    if (dt != KDA_BF16 && dt != KDA_F32) return KDA_ERR_UNSUPPORTED;
+    if (gk != KDA_GATE_PER_CHANNEL && gk != KDA_GATE_PER_HEAD) return KDA_ERR_UNSUPPORTED;
+    if (!supported_d(dk) || !supported_d(dv)) return KDA_ERR_UNSUPPORTED;
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status status) {
+    switch (status) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG: null, misaligned or inconsistent argument";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: head dimension, dtype or gate mode not supported";
+        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing, misaligned or too small";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP: a HIP runtime call or kernel launch failed";
+        case KDA_ERR_BAD_SEQLENS: return "KDA_ERR_BAD_SEQLENS: device cu_seqlens rejected";
+    }
+    return "KDA_ERR_UNKNOWN";
+}
+
+int32_t kda_version(void) { return (1 << 16) | 0; }
+
+size_t kda_chunk_fwd_workspace_size(int64_t T_total, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                                    kda_dtype dt, kda_gate gk) {
+    if (check_common(H, d_k, d_v, dt, gk) != KDA_OK) return 0;
+    if (N <= 0 || T_total < 0 || T_total > INT32_MAX) return 0;
+    return kda::chunk_workspace_bytes(T_total, N, H, d_k, d_v, dt == KDA_BF16);
+}
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                         const float* S0, const int32_t* cu_seqlens, int32_t N, int64_t T_total, int32_t H,
+                         int32_t d_k, int32_t d_v, kda_dtype dt, kda_gate gk, void* o, float* S_T,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    const kda_status st = check_common(H, d_k, d_v, dt, gk);
+    if (st != KDA_OK) return st;
+    if (N <= 0 || T_total < 0 || T_total > INT32_MAX) return KDA_ERR_INVALID_ARG;
+    if (!cu_seqlens && T_total % N != 0) return KDA_ERR_INVALID_ARG;
+    if (T_total > 0) {
+        if (!q || !k || !v || !g || !beta || !o) return KDA_ERR_INVALID_ARG;
+        // q, k, v and a per-channel g are read two elements at a time
+        const size_t esz = dt == KDA_BF16 ? 2 : 4;
+        if (!aligned(q, 2 * esz) || !aligned(k, 2 * esz) || !aligned(v, 2 * esz) ||
+            !aligned(g, gk == KDA_GATE_PER_HEAD ? esz : 2 * esz) || !aligned(beta, esz) || !aligned(o, esz))
+            return KDA_ERR_INVALID_ARG;
+    }
+    if ((S0 && !aligned(S0, 4)) || (S_T && !aligned(S_T, 4)) || (cu_seqlens && !aligned(cu_seqlens, 4)))
+        return KDA_ERR_INVALID_ARG;
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERR_WORKSPACE;
+    const size_t need = kda::chunk_workspace_bytes(T_total, N, H, d_k, d_v, dt == KDA_BF16);
+    if (workspace_bytes < need) return KDA_ERR_WORKSPACE;
+
+    kda::ChunkArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.S0 = S0; a.cu_seqlens = cu_seqlens; a.o = o; a.S_T = S_T;
+    a.N = N; a.H = H; a.dk = d_k; a.dv = d_v; a.T = T_total;
+    a.max_chunks = kda::max_chunks_for(T_total, N);
+    a.bf16 = dt == KDA_BF16;
+    a.head_gate = gk == KDA_GATE_PER_HEAD;
+    const kda::ChunkWorkspace ws = kda::carve_chunk_workspace(workspace, T_total, N, H, d_k, d_v, a.bf16);
+    return kda::launch_chunk_fwd(a, ws, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_chunk_fwd_check(const void* workspace, hipStream_t stream) {
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERR_WORKSPACE;
+    if (hipStreamSynchronize(stream) != hipSuccess) return KDA_ERR_HIP;
+    kda::WsHeader h;
+    if (hipMemcpy(&h, workspace, sizeof h, hipMemcpyDeviceToHost) != hipSuccess) return KDA_ERR_HIP;
+    return h.bad_seqlens ? KDA_ERR_BAD_SEQLENS : KDA_OK;
+}
+
+kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                              float* S, int32_t N, int32_t H, int32_t d_k, int32_t d_v, kda_dtype dt, kda_gate gk,
+                              void* o, hipStream_t stream) {
+    const kda_status st = check_common(H, d_k, d_v, dt, gk);
+    if (st != KDA_OK) return st;
+    if (N < 0 || (int64_t)N * H > INT32_MAX) return KDA_ERR_INVALID_ARG;
+    if (N == 0) return KDA_OK;
+    if (!q || !k || !v || !g || !beta || !S || !o) return KDA_ERR_INVALID_ARG;
+    const size_t esz = dt == KDA_BF16 ? 2 : 4;
+    if (!aligned(q, esz) || !aligned(k, esz) || !aligned(v, esz) || !aligned(g, esz) || !aligned(beta, esz) ||
+        !aligned(o, esz) || !aligned(S, 16))
+        return KDA_ERR_INVALID_ARG;
+    kda::DecodeArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.S = S; a.o = o;
+    a.N = N; a.H = H; a.dk = d_k; a.dv = d_v;
+    a.bf16 = dt == KDA_BF16;
+    a.head_gate = gk == KDA_GATE_PER_HEAD;
+    return kda::launch_decode(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,688 @@
+// Chunkwise-parallel KDA forward on gfx950.
+//
+// "From GPT-2 to Kimi K3" (molayo1419.me), section on the parallelisation
+// trick: split each sequence into chunks of C tokens, treat the inside of a
+// chunk as masked attention, carry the state across chunks with one matrix
+// product, and use a Householder-type reparametrisation so that all deltas of
+// a chunk come out of one triangular solve.  "Kimi Linear architecture"
+// (ttj.ttj.kr), section "KDA: a memo that erases and rewrites": the transition
+// is diagonal plus a low-rank term built from the key itself, which is what
+// lets the decay be folded into the key operands below.
+//
+// Chunk algebra (start state S, chunk-local tokens t = 0..n-1, C = 64):
+//   b_t   = g_0 + ... + g_t              (per key channel, chunk-local)
+//   A_ti  = beta_t sum_c k_tc k_ic e^{b_tc - b_ic}           i < t
+//   T     = (I + A)^{-1}                 (unit lower triangular)
+//   W     = T diag(beta) (K * e^b),   U' = T diag(beta) V
+//   U     = U' - W S                     (the true per-token deltas)
+//   O     = (Q * e^b) S + P U,   P_ti = sum_c q_tc k_ic e^{b_tc - b_ic}, i <= t
+//   S    <- Diag(e^{b_last}) S + (K * e^{b_last - b})^T U
+// The decay e^{b_t - b_i} inside A and P is split per 16-token tile: for a
+// tile pair below the diagonal the reference rows lie between the two tiles,
+// so every factor is <= 1 and nothing can overflow; inside a diagonal tile
+// the reference is the tile's middle row, so a factor spans at most eight
+// tokens of decay.  W, Q e^b, K e^{b_last - b} and e^{b_last} only involve
+// factors <= 1.  Masks are applied by selection, never by multiplication.
+//
+// Kernels (one stream, in order):
+//   chunk_map_kernel   validate cu_seqlens, first chunk of every sequence
+//   intra_chunk_kernel one workgroup per (chunk, head): prefix sum of the
+//                      gate, decayed operands, A and P on MFMA, (I+A)^{-1} by
+//                      blocked forward substitution in LDS (fp32), W and U'
+//                      on MFMA; writes W, Q*e^b, (K*e^{b_last-b})^T, U', P,
+//                      e^{b_last} to the workspace
+//   chunk_walk_kernel  one workgroup per (sequence, head, 16-column slice of
+//                      d_v): walks the chunks in order with its fp32 slice of
+//                      S in registers; U = U' - W S, O = QG S + P U,
+//                      S <- Diag(Gn) S + KdT U, all on MFMA
+#include "kda_internal.h"
+
+namespace kda {
+
+// ----------------------------------------------------------------------------
+// Chunk map: copy (or synthesise) the sequence offsets, validate them, and
+// exclusive-scan the per-sequence chunk counts.
+__global__ __launch_bounds__(256) void chunk_map_kernel(const int32_t* __restrict__ cu_in, int32_t N,
+                                                        int64_t T, WsHeader* __restrict__ hdr,
+                                                        int32_t* __restrict__ cu,
+                                                        int32_t* __restrict__ chunk_off) {
+    __shared__ int bad;
+    __shared__ int carry;
+    __shared__ int scan[256];
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        bad = 0;
+        carry = 0;
+    }
+    __syncthreads();
+    const int64_t L = cu_in ? 0 : T / N;
+    for (int i = tid; i <= N; i += 256) {
+        const int64_t c = cu_in ? (int64_t)cu_in[i] : (int64_t)i * L;
+        const int64_t cn = (i < N) ? (cu_in ? (int64_t)cu_in[i + 1] : (int64_t)(i + 1) * L) : T;
+        cu[i] = (int32_t)c;
+        if ((i == 0 && c != 0) || (i == N && c != T) || c < 0 || c > T || cn < c) bad = 1;
+    }
+    __syncthreads();
+    const int isbad = bad;
+    for (int base = 0; base < N; base += 256) {
+        const int i = base + tid;
+        int cnt = 0;
+        if (i < N && !isbad) cnt = (cu[i + 1] - cu[i] + kChunk - 1) / kChunk;
+        scan[tid] = cnt;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {
+            const int x = tid >= off ? scan[tid - off] : 0;
+            __syncthreads();
+            scan[tid] += x;
+            __syncthreads();
+        }
+        if (i < N) chunk_off[i] = carry + scan[tid] - cnt;
+        __syncthreads();
+        if (tid == 255) carry += scan[255];
+        __syncthreads();
+    }
+    if (tid == 0) {
+        chunk_off[N] = carry;
+        hdr->total_chunks = isbad ? 0 : carry;
+        hdr->bad_seqlens = isbad;
+    }
+}
+
+// Largest n in [0, N) with chunk_off[n] <= cid (cid < chunk_off[N]).
+__device__ __forceinline__ int find_sequence(const int32_t* __restrict__ chunk_off, int N, int cid) {
+    int lo = 0, hi = N;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (chunk_off[mid] <= cid) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+// ----------------------------------------------------------------------------
+// Intra-chunk transform.
+template <typename E, int DK, int DV>
+struct IntraLayout {
+    static constexpr int C = kChunk;
+    static constexpr int PAD = 16 / (int)sizeof(E);
+    static constexpr int LDK = DK + PAD;  // [token][channel] row stride
+    static constexpr int LDT = C + PAD;   // [channel][token] row stride
+    static constexpr int LDA = C + 4;     // fp32 A / T row stride
+    static constexpr int NPART = 512 / DK;
+    static constexpr int RPT = C / NPART;
+    static constexpr int NPARTV = 512 / DV;
+    static constexpr int RPTV = C / NPARTV;
+    static constexpr int NBND = 12;       // b at rows 16i, 16i+8, 16i+15 of the four 16-row tiles
+    static constexpr int NCS = 10;        // column scales of the lower tile pairs (ti, tj <= ti)
+    // Region R1: [Kr | Qr | Kt] ([token][channel], E) while A and P are
+    // formed; afterwards [Kbt | Vt] ([channel][token], E) and the 3 x 16 x 16
+    // fp32 scratch of the off-diagonal inversion.
+    static constexpr size_t rhs_bytes = (size_t)(DK + DV) * LDT * sizeof(E);
+    static constexpr size_t r1_a = (size_t)3 * C * LDK * sizeof(E);
+    static constexpr size_t r1_b = (rhs_bytes + 15) / 16 * 16 + 3 * 256 * 4;
+    static constexpr size_t off_X = (rhs_bytes + 15) / 16 * 16;
+    static constexpr size_t off_A = ((r1_a > r1_b ? r1_a : r1_b) + 15) / 16 * 16;  // sA; sBnd before A
+    static constexpr size_t off_beta = off_A + (size_t)C * LDA * 4;
+    static constexpr size_t off_scale = off_beta + C * 4;  // sColScale, sRowScale; sPart before them
+    static constexpr size_t scale_bytes = (size_t)(NCS + 4) * DK * 4;
+    static constexpr size_t part_bytes = (size_t)NPART * DK * 4;
+    static constexpr size_t bytes = off_scale + (scale_bytes > part_bytes ? scale_bytes : part_bytes);
+    static_assert((size_t)NBND * DK * 4 <= (size_t)C * LDA * 4, "sBnd fits in sA");
+};
+
+template <typename E> __device__ __forceinline__ void load2(const E* p, float& a, float& b);
+template <> __device__ __forceinline__ void load2<bf16_t>(const bf16_t* p, float& a, float& b) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+    a = __uint_as_float(w << 16);
+    b = __uint_as_float(w & 0xffff0000u);
+}
+template <> __device__ __forceinline__ void load2<float>(const float* p, float& a, float& b) {
+    const float2 w = *reinterpret_cast<const float2*>(p);
+    a = w.x;
+    b = w.y;
+}
+template <typename E> __device__ __forceinline__ void store2(E* p, float a, float b);
+template <> __device__ __forceinline__ void store2<bf16_t>(bf16_t* p, float a, float b) {
+    *reinterpret_cast<uint32_t*>(p) = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+template <> __device__ __forceinline__ void store2<float>(float* p, float a, float b) {
+    *reinterpret_cast<float2*>(p) = make_float2(a, b);
+}
+
+// f[j] <- f[j] * s[j], j = 0..7 (s: 8 contiguous fp32 in LDS).
+__device__ __forceinline__ Frag<bf16_t> scale_frag(Frag<bf16_t> f, const float* s) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(s);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(s + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f.v[j] = f32_to_bf16(bf16_to_f32(f.v[j]) * a[j]);
+        f.v[j + 4] = f32_to_bf16(bf16_to_f32(f.v[j + 4]) * b[j]);
+    }
+    return f;
+}
+__device__ __forceinline__ Frag<float> scale_frag(Frag<float> f, const float* s) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(s);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(s + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f.v[j] *= a[j];
+        f.v[j + 4] *= b[j];
+    }
+    return f;
+}
+
+template <typename E, int DK, int DV, bool HG>
+__global__ __launch_bounds__(256) void intra_chunk_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v, const E* __restrict__ g,
+    const E* __restrict__ beta, const WsHeader* __restrict__ hdr, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ chunk_off, int32_t N, int32_t H, E* __restrict__ Wo, E* __restrict__ QGo,
+    E* __restrict__ KdTo, E* __restrict__ Upo, E* __restrict__ Po, float* __restrict__ Gno) {
+    using L = IntraLayout<E, DK, DV>;
+    constexpr int C = L::C, LDK = L::LDK, LDT = L::LDT, LDA = L::LDA;
+    constexpr int NPART = L::NPART, RPT = L::RPT, RPTV = L::RPTV;
+
+    extern __shared__ __align__(16) unsigned char smem[];
+    E* sKr = reinterpret_cast<E*>(smem);   // k_t e^{b_t - b_s(t)}, s(t) = first row of t's tile
+    E* sQr = sKr + C * LDK;                // q_t e^{b_t - b_s(t)}
+    E* sKt = sQr + C * LDK;                // k_i e^{b_e(i) - b_i}, e(i) = last row of i's tile
+    E* sKbt = reinterpret_cast<E*>(smem);  // reuses R1 once A and P are done
+    E* sVt = sKbt + DK * LDT;
+    float* sX = reinterpret_cast<float*>(smem + L::off_X);
+    float* sA = reinterpret_cast<float*>(smem + L::off_A);
+    float* sBnd = sA;  // [12][DK] tile-boundary prefix sums, dead before A is written
+    float* sBeta = reinterpret_cast<float*>(smem + L::off_beta);
+    float* sColScale = reinterpret_cast<float*>(smem + L::off_scale);  // [10][DK]
+    float* sRowScale = sColScale + L::NCS * DK;                          // [4][DK]
+    float* sPart = sColScale;  // [NPART][DK], dead before the scales are written
+
+    if (hdr->bad_seqlens) return;
+    const int cid = blockIdx.x;
+    if (cid >= hdr->total_chunks) return;
+    const int h = blockIdx.y;
+    const int n = find_sequence(chunk_off, N, cid);
+    const int64_t t0 = (int64_t)cu[n] + (int64_t)(cid - chunk_off[n]) * C;
+    const int len = (int)min((int64_t)C, (int64_t)cu[n + 1] - t0);
+    const int64_t ch = (int64_t)cid * H + h;  // chunk-head index into the workspace
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+
+    // ---- 1. chunk-local inclusive prefix sum of the log-gate ----------------
+    const int cp = tid % (DK / 2), part = tid / (DK / 2);
+    const int c0 = 2 * cp;
+    float bb[RPT][2];
+    {
+        float run0 = 0.f, run1 = 0.f;
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            const int row = part * RPT + r;
+            float g0 = 0.f, g1 = 0.f;
+            if (row < len) {
+                const int64_t tok = t0 + row;
+                if (HG) {
+                    g0 = g1 = Elt<E>::load(g + tok * H + h);
+                } else {
+                    load2<E>(g + (tok * H + h) * DK + c0, g0, g1);
+                }
+            }
+            run0 += g0;
+            run1 += g1;
+            bb[r][0] = run0;
+            bb[r][1] = run1;
+        }
+        sPart[part * DK + c0] = run0;
+        sPart[part * DK + c0 + 1] = run1;
+    }
+    if (tid < C) sBeta[tid] = (tid < len) ? Elt<E>::load(beta + (t0 + tid) * H + h) : 0.f;
+    __syncthreads();
+    {
+        float off0 = 0.f, off1 = 0.f;
+#pragma unroll
+        for (int p = 0; p < NPART - 1; ++p) {
+            if (p < part) {
+                off0 += sPart[p * DK + c0];
+                off1 += sPart[p * DK + c0 + 1];
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            bb[r][0] += off0;
+            bb[r][1] += off1;
+            const int row = part * RPT + r, tr = row & 15;
+            const int slot = (tr == 0) ? 0 : (tr == 8) ? 1 : (tr == 15) ? 2 : -1;
+            if (slot >= 0) {
+                sBnd[(3 * (row >> 4) + slot) * DK + c0] = bb[r][0];
+                sBnd[(3 * (row >> 4) + slot) * DK + c0 + 1] = bb[r][1];
+            }
+        }
+    }
+    __syncthreads();
+    const float last0 = sBnd[11 * DK + c0], last1 = sBnd[11 * DK + c0 + 1];
+
+    // ---- 2. decayed operands (every factor <= 1) and tile-pair scales -------
+    float kb[RPT][2];  // beta k e^b, kept for the W right-hand side
+    E kd0[RPT], kd1[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const int row = part * RPT + r;
+        const float* bs = sBnd + (3 * (row >> 4)) * DK;  // tile start
+        const float* be = bs + 2 * DK;                  // tile end
+        float k0 = 0.f, k1 = 0.f, q0 = 0.f, q1 = 0.f;
+        if (row < len) {
+            const int64_t off = ((t0 + row) * H + h) * DK + c0;
+            load2<E>(k + off, k0, k1);
+            load2<E>(q + off, q0, q1);
+        }
+        const float e0 = gate_exp<E>(bb[r][0] - bs[c0]), e1 = gate_exp<E>(bb[r][1] - bs[c0 + 1]);
+        const float f0 = gate_exp<E>(be[c0] - bb[r][0]), f1 = gate_exp<E>(be[c0 + 1] - bb[r][1]);
+        const float x0 = gate_exp<E>(bb[r][0]), x1 = gate_exp<E>(bb[r][1]);
+        const float d0 = gate_exp<E>(last0 - bb[r][0]), d1 = gate_exp<E>(last1 - bb[r][1]);
+        store2<E>(sKr + row * LDK + c0, k0 * e0, k1 * e1);
+        store2<E>(sQr + row * LDK + c0, q0 * e0, q1 * e1);
+        store2<E>(sKt + row * LDK + c0, k0 * f0, k1 * f1);
+        store2<E>(QGo + (ch * C + row) * DK + c0, q0 * x0, q1 * x1);
+        const float bt = sBeta[row];
+        kb[r][0] = bt * k0 * x0;
+        kb[r][1] = bt * k1 * x1;
+        kd0[r] = Elt<E>::from(k0 * d0);
+        kd1[r] = Elt<E>::from(k1 * d1);
+    }
+    {
+        E* p0 = KdTo + (ch * DK + c0) * C + part * RPT;
+        E* p1 = p0 + C;
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            p0[r] = kd0[r];
+            p1[r] = kd1[r];
+        }
+        if (part == 0) {
+            Gno[ch * DK + c0] = gate_exp<E>(last0);
+            Gno[ch * DK + c0 + 1] = gate_exp<E>(last1);
+        }
+    }
+    // Tile pair (ti, tj), tj < ti: e^{b_t - b_i} = [k-side e^{b_t - b_s(ti)}]
+    //   * e^{b_s(ti) - b_e(tj)} * [e^{b_e(tj) - b_i}], all three <= 1.
+    // Diagonal tile ti: reference m = 16 ti + 8: the row side takes
+    //   e^{b_s - b_m} and the column side e^{b_m - b_e}; each spans at most
+    //   eight tokens of decay.  The exponent is capped at 80 to stay finite.
+    for (int e = tid; e < 14 * DK; e += 256) {
+        const int v = e / DK, c = e % DK;
+        float x;
+        if (v < L::NCS) {
+            const int ti = (v >= 6) ? 3 : (v >= 3) ? 2 : (v >= 1) ? 1 : 0;
+            const int tj = v - ti * (ti + 1) / 2;
+            x = (tj < ti) ? sBnd[(3 * ti) * DK + c] - sBnd[(3 * tj + 2) * DK + c]
+                          : sBnd[(3 * ti + 1) * DK + c] - sBnd[(3 * ti + 2) * DK + c];
+            sColScale[v * DK + c] = gate_exp<E>(fminf(x, 80.f));
+        } else {
+            const int ti = v - L::NCS;
+            x = sBnd[(3 * ti) * DK + c] - sBnd[(3 * ti + 1) * DK + c];
+            sRowScale[ti * DK + c] = gate_exp<E>(fminf(x, 80.f));
+        }
+    }
+    __syncthreads();
+
+    // ---- 3. A = K K^T with decay (strictly lower, row-scaled by beta) -> LDS
+    //         (fp32);  P = Q K^T with decay (lower incl. diagonal) -> workspace
+    {
+        const int ti = wave;
+#pragma unroll
+        for (int tj = 0; tj < 4; ++tj) {
+            f32x4 accA = zero4(), accP = zero4();
+            if (tj <= ti) {
+                const float* cs = sColScale + (ti * (ti + 1) / 2 + tj) * DK;
+                const float* rs = sRowScale + ti * DK;
+#pragma unroll
+                for (int ks = 0; ks < DK / 32; ++ks) {
+                    const int cb = 32 * ks + 8 * lg;
+                    const Frag<E> fb = scale_frag(ld_frag(sKt + (16 * tj + lr) * LDK + cb), cs + cb);
+                    Frag<E> fa = ld_frag(sKr + (16 * ti + lr) * LDK + cb);
+                    Frag<E> fq = ld_frag(sQr + (16 * ti + lr) * LDK + cb);
+                    if (tj == ti) {
+                        fa = scale_frag(fa, rs + cb);
+                        fq = scale_frag(fq, rs + cb);
+                    }
+                    accA = mma(fa, fb, accA);
+                    accP = mma(fq, fb, accP);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * ti + 4 * lg + i, col = 16 * tj + lr;
+                sA[row * LDA + col] = (row > col) ? accA[i] * sBeta[row] : 0.f;
+                Po[(ch * C + row) * C + col] = Elt<E>::from((row >= col) ? accP[i] : 0.f);
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- 4. right-hand sides into the freed region; T = (I + A)^{-1} ---------
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        sKbt[c0 * LDT + part * RPT + r] = Elt<E>::from(kb[r][0]);
+        sKbt[(c0 + 1) * LDT + part * RPT + r] = Elt<E>::from(kb[r][1]);
+    }
+    {
+        const int jp = tid % (DV / 2), vpart = tid / (DV / 2);
+        const int j0 = 2 * jp;
+#pragma unroll
+        for (int r = 0; r < RPTV; ++r) {
+            const int row = vpart * RPTV + r;
+            float v0 = 0.f, v1 = 0.f;
+            if (row < len) load2<E>(v + ((t0 + row) * H + h) * DV + j0, v0, v1);
+            const float bt = sBeta[row];
+            sVt[j0 * LDT + row] = Elt<E>::from(bt * v0);
+            sVt[(j0 + 1) * LDT + row] = Elt<E>::from(bt * v1);
+        }
+    }
+    // (a) the four 16x16 diagonal blocks, one column per thread of wave 0
+    float x[16];
+    if (tid < 64) {
+        const int blk = tid >> 4, jc = tid & 15;
+        const float* Ab = sA + (16 * blk) * LDA + 16 * blk;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < t; ++i) acc -= Ab[t * LDA + i] * x[i];
+            x[t] = (t < jc) ? 0.f : ((t == jc) ? 1.f : acc);
+        }
+    }
+    __syncthreads();
+    if (tid < 64) {
+        const int blk = tid >> 4, jc = tid & 15;
+        float* Tb = sA + (16 * blk) * LDA + 16 * blk;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) Tb[t * LDA + jc] = x[t];
+    }
+    __syncthreads();
+    // (b) off-diagonal blocks, block row by block row:
+    //     T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj
+    {
+        const int rr = tid >> 4, cc = tid & 15;
+#pragma unroll
+        for (int bi = 1; bi < 4; ++bi) {
+            float xv[3];
+#pragma unroll
+            for (int bj = 0; bj < bi; ++bj) {
+                float acc = 0.f;
+#pragma unroll
+                for (int m = bj; m < bi; ++m) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        acc += sA[(16 * bi + rr) * LDA + 16 * m + e] * sA[(16 * m + e) * LDA + 16 * bj + cc];
+                }
+                xv[bj] = acc;
+            }
+#pragma unroll
+            for (int bj = 0; bj < bi; ++bj) sX[bj * 256 + rr * 16 + cc] = xv[bj];
+            __syncthreads();
+#pragma unroll
+            for (int bj = 0; bj < bi; ++bj) {
+                float acc = 0.f;
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    acc += sA[(16 * bi + rr) * LDA + 16 * bi + e] * sX[bj * 256 + e * 16 + cc];
+                sA[(16 * bi + rr) * LDA + 16 * bj + cc] = -acc;
+            }
+            __syncthreads();
+        }
+    }
+
+    // ---- 5. W = T (beta K e^b),  U' = T (beta V) ------------------------------
+    {
+        const int ti = wave;
+        const Frag<E> ft0 = ld_frag_from_f32<E>(sA + (16 * ti + lr) * LDA + 8 * lg);
+        const Frag<E> ft1 = ld_frag_from_f32<E>(sA + (16 * ti + lr) * LDA + 32 + 8 * lg);
+        const bool two = ti >= 2;  // rows 0..31 of T vanish beyond token 31
+#pragma unroll 4
+        for (int tn = 0; tn < DK / 16; ++tn) {
+            f32x4 acc = mma(ft0, ld_frag(sKbt + (16 * tn + lr) * LDT + 8 * lg), zero4());
+            if (two) acc = mma(ft1, ld_frag(sKbt + (16 * tn + lr) * LDT + 32 + 8 * lg), acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                Wo[(ch * C + 16 * ti + 4 * lg + i) * DK + 16 * tn + lr] = Elt<E>::from(acc[i]);
+        }
+#pragma unroll 4
+        for (int tn = 0; tn < DV / 16; ++tn) {
+            f32x4 acc = mma(ft0, ld_frag(sVt + (16 * tn + lr) * LDT + 8 * lg), zero4());
+            if (two) acc = mma(ft1, ld_frag(sVt + (16 * tn + lr) * LDT + 32 + 8 * lg), acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                Upo[(ch * C + 16 * ti + 4 * lg + i) * DV + 16 * tn + lr] = Elt<E>::from(acc[i]);
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// State walk + output.  Workgroup = (sequence n, head h, 16-column slice of
+// d_v); wave w owns token rows 16w..16w+15 of the chunk for U and O, and the
+// state rows (key channels) 16m.., m = w*MT .. w*MT+MT-1.
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__(256) void chunk_walk_kernel(
+    const WsHeader* __restrict__ hdr, const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
+    int32_t N, int32_t H, const E* __restrict__ Wi, const E* __restrict__ QGi, const E* __restrict__ KdTi,
+    const E* __restrict__ Upi, const E* __restrict__ Pi, const float* __restrict__ Gni,
+    const float* __restrict__ S0, float* __restrict__ S_T, E* __restrict__ o) {
+    constexpr int C = kChunk, DVS = 16, NS = DV / DVS;
+    constexpr int MT = DK / 64;  // state row tiles per wave
+    constexpr int KS = DK / 32;  // k-blocks over channels
+    constexpr int PAD = 16 / (int)sizeof(E);
+    constexpr int LDS_S = DK + PAD;
+    constexpr int LDS_U = C + PAD;
+    __shared__ __align__(16) E sSt[DVS * LDS_S];  // S slice, transposed: [col][channel]
+    __shared__ __align__(16) E sUt[DVS * LDS_U];  // U slice, transposed: [col][token]
+
+    if (hdr->bad_seqlens) return;
+    const int64_t NH = (int64_t)N * H;
+    const int64_t bid = blockIdx.x;
+    int64_t pair;
+    int slice;
+    if (NH % 8 == 0) {  // keep the NS slices of one (n, h) on one XCD (shared L2)
+        const int xcd = (int)(bid & 7);
+        const int64_t idx = bid >> 3;
+        pair = (idx / NS) * 8 + xcd;
+        slice = (int)(idx % NS);
+    } else {
+        pair = bid / NS;
+        slice = (int)(bid % NS);
+    }
+    const int n = (int)(pair / H), h = (int)(pair % H);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int col = slice * DVS + lr;
+
+    f32x4 Sreg[MT];
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * (w * MT + mm) + 4 * lg + i;
+            Sreg[mm][i] = S0 ? S0[(pair * DK + row) * DV + col] : 0.f;
+        }
+    auto put_state = [&]() {
+#pragma unroll
+        for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sSt[lr * LDS_S + 16 * (w * MT + mm) + 4 * lg + i] = Elt<E>::from(Sreg[mm][i]);
+    };
+    put_state();
+    __syncthreads();
+
+    const int cbeg = chunk_off[n], cend = chunk_off[n + 1];
+    const int64_t seq0 = cu[n], seqend = cu[n + 1];
+    for (int c = cbeg; c < cend; ++c) {
+        const int64_t ch = (int64_t)c * H + h;
+        const E* Wp = Wi + ch * C * DK;
+        const E* Qp = QGi + ch * C * DK;
+        const E* Kp = KdTi + ch * DK * C;
+        const E* Up = Upi + ch * C * DV;
+        const E* Pp = Pi + ch * C * C;
+        const float* Gp = Gni + ch * DK;
+
+        Frag<E> fW[KS], fQ[KS], fP[2], fK[MT][2];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            fW[ks] = ld_frag(Wp + (16 * w + lr) * DK + 32 * ks + 8 * lg);
+            fQ[ks] = ld_frag(Qp + (16 * w + lr) * DK + 32 * ks + 8 * lg);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) fP[kb] = ld_frag(Pp + (16 * w + lr) * C + 32 * kb + 8 * lg);
+#pragma unroll
+        for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                fK[mm][kb] = ld_frag(Kp + (16 * (w * MT + mm) + lr) * C + 32 * kb + 8 * lg);
+        float up[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) up[i] = Elt<E>::load(Up + (16 * w + 4 * lg + i) * DV + col);
+        f32x4 gn[MT];
+#pragma unroll
+        for (int mm = 0; mm < MT; ++mm) gn[mm] = *reinterpret_cast<const f32x4*>(Gp + 16 * (w * MT + mm) + 4 * lg);
+
+        // phase 1: U = U' - W S ;  O = QG S
+        f32x4 accW = zero4(), accQ = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const Frag<E> fs = ld_frag(sSt + lr * LDS_S + 32 * ks + 8 * lg);
+            accW = mma(fW[ks], fs, accW);
+            accQ = mma(fQ[ks], fs, accQ);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sUt[lr * LDS_U + 16 * w + 4 * lg + i] = Elt<E>::from(up[i] - accW[i]);
+        __syncthreads();
+
+        // phase 2: O += P U ;  S <- Diag(Gn) S + KdT U
+        const Frag<E> fu0 = ld_frag(sUt + lr * LDS_U + 8 * lg);
+        const Frag<E> fu1 = ld_frag(sUt + lr * LDS_U + 32 + 8 * lg);
+        f32x4 O = mma(fP[0], fu0, accQ);
+        if (w >= 2) O = mma(fP[1], fu1, O);
+#pragma unroll
+        for (int mm = 0; mm < MT; ++mm) {
+            f32x4 acc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = gn[mm][i] * Sreg[mm][i];
+            acc = mma(fK[mm][0], fu0, acc);
+            acc = mma(fK[mm][1], fu1, acc);
+            Sreg[mm] = acc;
+        }
+        const int64_t tok0 = seq0 + (int64_t)(c - cbeg) * C;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t tok = tok0 + 16 * w + 4 * lg + i;
+            if (tok < seqend) o[(tok * H + h) * DV + col] = Elt<E>::from(O[i]);
+        }
+        put_state();
+        __syncthreads();
+    }
+    if (S_T) {
+#pragma unroll
+        for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * (w * MT + mm) + 4 * lg + i;
+                S_T[(pair * DK + row) * DV + col] = Sreg[mm][i];
+            }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Host side.
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int64_t max_chunks_for(int64_t T, int32_t N) { return (T + kChunk - 1) / kChunk + N; }
+
+namespace {
+struct WsSizes {
+    size_t header, cu, chunk_off, W, QG, KdT, Up, P, Gn;
+};
+WsSizes ws_sizes(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, bool bf16) {
+    const size_t esz = bf16 ? 2 : 4;
+    const size_t mc = (size_t)max_chunks_for(T, N);
+    const size_t C = kChunk;
+    WsSizes s;
+    s.header = 256;
+    s.cu = align256((size_t)(N + 1) * 4);
+    s.chunk_off = align256((size_t)(N + 1) * 4);
+    s.W = align256(mc * H * C * dk * esz);
+    s.QG = s.W;
+    s.KdT = s.W;
+    s.Up = align256(mc * H * C * dv * esz);
+    s.P = align256(mc * H * C * C * esz);
+    s.Gn = align256(mc * H * dk * 4);
+    return s;
+}
+}  // namespace
+
+size_t chunk_workspace_bytes(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, bool bf16) {
+    const WsSizes s = ws_sizes(T, N, H, dk, dv, bf16);
+    return s.header + s.cu + s.chunk_off + s.W + s.QG + s.KdT + s.Up + s.P + s.Gn;
+}
+
+ChunkWorkspace carve_chunk_workspace(void* base, int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv,
+                                     bool bf16) {
+    const WsSizes s = ws_sizes(T, N, H, dk, dv, bf16);
+    char* p = static_cast<char*>(base);
+    ChunkWorkspace w;
+    w.header = reinterpret_cast<WsHeader*>(p); p += s.header;
+    w.cu = reinterpret_cast<int32_t*>(p); p += s.cu;
+    w.chunk_off = reinterpret_cast<int32_t*>(p); p += s.chunk_off;
+    w.W = p; p += s.W;
+    w.QG = p; p += s.QG;
+    w.KdT = p; p += s.KdT;
+    w.Up = p; p += s.Up;
+    w.P = p; p += s.P;
+    w.Gn = reinterpret_cast<float*>(p);
+    return w;
+}
+
+template <typename E, int DK, int DV, bool HG>
+static hipError_t launch_intra(const ChunkArgs& a, const ChunkWorkspace& ws, hipStream_t stream) {
+    using L = IntraLayout<E, DK, DV>;
+    auto kern = intra_chunk_kernel<E, DK, DV, HG>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)a.max_chunks, (unsigned)a.H), dim3(256), L::bytes, stream,
+                       (const E*)a.q, (const E*)a.k, (const E*)a.v, (const E*)a.g, (const E*)a.beta, ws.header,
+                       ws.cu, ws.chunk_off, a.N, a.H, (E*)ws.W, (E*)ws.QG, (E*)ws.KdT, (E*)ws.Up, (E*)ws.P,
+                       ws.Gn);
+    return hipGetLastError();
+}
+
+template <typename E, int DK, int DV>
+static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkWorkspace& ws, hipStream_t stream) {
+    hipError_t e = hipSuccess;
+    if (a.T > 0) {
+        e = a.head_gate ? launch_intra<E, DK, DV, true>(a, ws, stream) : launch_intra<E, DK, DV, false>(a, ws, stream);
+        if (e != hipSuccess) return e;
+    }
+    const int64_t blocks = (int64_t)a.N * a.H * (DV / 16);
+    hipLaunchKernelGGL((chunk_walk_kernel<E, DK, DV>), dim3((unsigned)blocks), dim3(256), 0, stream, ws.header,
+                       ws.cu, ws.chunk_off, a.N, a.H, (const E*)ws.W, (const E*)ws.QG, (const E*)ws.KdT,
+                       (const E*)ws.Up, (const E*)ws.P, (const float*)ws.Gn, a.S0, a.S_T, (E*)a.o);
+    return hipGetLastError();
+}
+
+template <typename E>
+static hipError_t launch_chunk_e(const ChunkArgs& a, const ChunkWorkspace& ws, hipStream_t s) {
+    if (a.dk == 64 && a.dv == 64) return launch_chunk_t<E, 64, 64>(a, ws, s);
+    if (a.dk == 64 && a.dv == 128) return launch_chunk_t<E, 64, 128>(a, ws, s);
+    if (a.dk == 128 && a.dv == 64) return launch_chunk_t<E, 128, 64>(a, ws, s);
+    return launch_chunk_t<E, 128, 128>(a, ws, s);
+}
+
+hipError_t launch_chunk_fwd(const ChunkArgs& a, const ChunkWorkspace& ws, hipStream_t stream) {
+    hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(256), 0, stream, a.cu_seqlens, a.N, a.T, ws.header, ws.cu,
+                       ws.chunk_off);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return a.bf16 ? launch_chunk_e<bf16_t>(a, ws, stream) : launch_chunk_e<float>(a, ws, stream);
+}
+
+}  // namespace kda

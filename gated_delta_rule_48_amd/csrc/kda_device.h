@@ -1,0 +1,112 @@
+// Internal device helpers for the KDA kernels (gfx950 / CDNA4).
+//
+// Element types: bf16 is carried as raw uint16_t bit patterns (widened to fp32
+// by a shift, narrowed with round-to-nearest-even); fp32 is plain float.
+//
+// Matrix-core fragments.  Every product in the chunked path is built from
+// 16x16 output tiles with a K-block of 32.  One K-block is one
+// v_mfma_f32_16x16x32_bf16 for bf16 operands, or eight
+// v_mfma_f32_16x16x4_f32 for fp32 operands.  Both use the same per-lane view,
+// with lane = 16*g + r (r = lane % 16, g = lane / 16):
+//   A fragment : A[r][8g + j],  j = 0..7   (row r of a 16 x 32 A block)
+//   B fragment : B[8g + j][r],  j = 0..7   (column r of a 32 x 16 B block)
+//   accumulator: C[4g + i][r],  i = 0..3
+// For fp32 the j-th single MFMA consumes element j of every lane, i.e. the
+// k-index 8g + j is fed to the 4-wide instruction's k-slot g; the sum over k
+// is the same.  A B fragment is therefore read exactly like an A fragment
+// from the TRANSPOSED matrix (8 contiguous elements of row r), which is how
+// every operand is laid out in LDS and in the workspace.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+typedef uint16_t bf16_t;  // raw bf16 bit pattern
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<bf16_t>(u >> 16);
+}
+
+template <typename E> struct Elt;
+template <> struct Elt<bf16_t> {
+    __device__ __forceinline__ static float load(const bf16_t* p) { return bf16_to_f32(*p); }
+    __device__ __forceinline__ static bf16_t from(float f) { return f32_to_bf16(f); }
+    __device__ __forceinline__ static float to(bf16_t h) { return bf16_to_f32(h); }
+};
+template <> struct Elt<float> {
+    __device__ __forceinline__ static float load(const float* p) { return *p; }
+    __device__ __forceinline__ static float from(float f) { return f; }
+    __device__ __forceinline__ static float to(float f) { return f; }
+};
+
+// One operand fragment: 8 elements per lane.
+template <typename E> struct Frag;
+template <> struct Frag<bf16_t> { u16x8 v; };
+template <> struct Frag<float> { f32x8 v; };
+
+__device__ __forceinline__ f32x4 mma(const Frag<bf16_t>& a, const Frag<bf16_t>& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.v),
+                                                   __builtin_bit_cast(bf16x8, b.v), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(const Frag<float>& a, const Frag<float>& b, f32x4 c) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], c, 0, 0, 0);
+    return c;
+}
+
+// Read 8 contiguous elements (one fragment) from p (16-byte aligned for bf16,
+// 32-byte for fp32).
+__device__ __forceinline__ Frag<bf16_t> ld_frag(const bf16_t* p) {
+    Frag<bf16_t> f;
+    f.v = *reinterpret_cast<const u16x8*>(p);
+    return f;
+}
+__device__ __forceinline__ Frag<float> ld_frag(const float* p) {
+    Frag<float> f;
+    const f32x4* q = reinterpret_cast<const f32x4*>(p);
+    f32x4 a = q[0], b = q[1];
+    f.v = f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return f;
+}
+// Read 8 contiguous fp32 values and narrow them to an E fragment.
+template <typename E> __device__ __forceinline__ Frag<E> ld_frag_from_f32(const float* p);
+template <> __device__ __forceinline__ Frag<float> ld_frag_from_f32<float>(const float* p) { return ld_frag(p); }
+template <> __device__ __forceinline__ Frag<bf16_t> ld_frag_from_f32<bf16_t>(const float* p) {
+    const f32x4* q = reinterpret_cast<const f32x4*>(p);
+    f32x4 a = q[0], b = q[1];
+    Frag<bf16_t> f;
+    f.v = u16x8{f32_to_bf16(a[0]), f32_to_bf16(a[1]), f32_to_bf16(a[2]), f32_to_bf16(a[3]),
+                f32_to_bf16(b[0]), f32_to_bf16(b[1]), f32_to_bf16(b[2]), f32_to_bf16(b[3])};
+    return f;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// exp(x) for the gate factors.  bf16 inputs use the hardware exp2 path; fp32
+// inputs use the correctly-rounded-ish library expf.
+template <typename E> __device__ __forceinline__ float gate_exp(float x);
+template <> __device__ __forceinline__ float gate_exp<bf16_t>(float x) { return __expf(x); }
+template <> __device__ __forceinline__ float gate_exp<float>(float x) { return expf(x); }
+
+// Workspace header written by the chunk-map kernel.
+struct WsHeader {
+    int32_t bad_seqlens;   // nonzero: cu_seqlens rejected, every later kernel exits
+    int32_t total_chunks;  // number of chunks over all sequences
+};
+
+}  // namespace kda

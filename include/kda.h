@@ -1,0 +1,167 @@
+/*
+ * kda.h - C ABI of the MI355X (gfx950) Kimi Delta Attention hot path.
+ *
+ * KDA is a linear-attention recurrence whose d_k x d_v state S is edited by
+ * the delta rule and forgotten channel by channel:
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t,            alpha_t = exp(g_t)
+ *
+ * Sources for the operation (pages, by title and section):
+ *  - "From GPT-2 to Kimi K3" (molayo1419.me): section "DeltaNet: memory you
+ *    can edit" (read the stored value, write back only the difference);
+ *    section "Gated DeltaNet: now it can forget" (decay first, then write;
+ *    alpha in [0,1]); section "KDA: Kimi's secret sauce" (alpha becomes a
+ *    vector, one forget rate per channel); section on the parallelisation
+ *    trick (chunks of C tokens; masked attention inside a chunk, the state and
+ *    one matmul between chunks; a Householder-type reparametrisation gives all
+ *    deltas of a chunk at once; C = 64 or 128 works best).
+ *  - "Kimi Linear architecture" (ttj.ttj.kr): section on linear attention
+ *    (chunkwise for training and prefill, a per-token state update for
+ *    generation); section "KDA: a memo that erases and rewrites" (per-channel
+ *    gate; diagonal-plus-low-rank transition whose low-rank term is tied to
+ *    the key).
+ *  - "Kimi Delta Attention ... 1M context" (molayo1419.me): paragraph on the
+ *    specialised DPLR transition.
+ * The write strength beta is not on the pages; it enters as in the transition
+ * written above (beta = 1 gives the pages' plain delta rule).
+ *
+ * Conventions for every entry point
+ *  - All tensor pointers are DEVICE pointers, row-major and densely packed.
+ *    Alignment: every pointer to its element size; in kda_chunk_fwd also
+ *    q, k, v and a per-channel g to two elements; in kda_recurrent_step S
+ *    to 16 bytes; the workspace to 256 bytes.  The caller allocates and owns every buffer, including
+ *    the workspace, and keeps it alive until the work on `stream` completes.
+ *    The library allocates nothing and keeps no per-call state.
+ *  - Calls are asynchronous on `stream` (0 = the null stream) and never
+ *    synchronise the host.
+ *  - Token tensors: q, k, g are [T, H, d_k]; v, o are [T, H, d_v]; beta is
+ *    [T, H].  With KDA_GATE_PER_HEAD, g is [T, H] (one log-gate per token and
+ *    head, broadcast over the key channels: the Gated DeltaNet special case).
+ *  - q, k, v, g, beta and o share the element type `dt`; state tensors are
+ *    always fp32, [N, H, d_k, d_v], row c = key channel c.
+ *  - No 1/sqrt(d) scale is applied and q, k are used as given (callers
+ *    L2-normalise them).  g must be finite and <= 0; other values are
+ *    computed without checks and the result is unspecified.  The chunked
+ *    path is exact (up to rounding) while the decay accumulated over any
+ *    eight consecutive tokens of a sequence stays above e^-80 (e.g. every
+ *    g >= -10); stronger decay stays finite but loses accuracy.
+ *  - Supported: d_k, d_v in {64, 128}; chunk size C = 64.
+ *  - Errors are returned, never thrown.  Argument checks run on the host
+ *    before anything is launched: KDA_ERR_INVALID_ARG (null pointer,
+ *    misalignment, negative or inconsistent sizes), KDA_ERR_UNSUPPORTED
+ *    (d_k or d_v outside {64,128}, unknown dtype or gate mode),
+ *    KDA_ERR_WORKSPACE (workspace null or smaller than required).  A failed
+ *    launch returns KDA_ERR_HIP.  Input values are not inspected.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *hipStream_t;
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = 1,
+    KDA_ERR_UNSUPPORTED = 2,
+    KDA_ERR_WORKSPACE = 3,
+    KDA_ERR_HIP = 4,
+    KDA_ERR_BAD_SEQLENS = 5
+} kda_status;
+
+typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
+
+typedef enum { KDA_GATE_PER_CHANNEL = 0, KDA_GATE_PER_HEAD = 1 } kda_gate;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *kda_status_string(kda_status status);
+
+/* Library version, (major << 16) | minor. */
+int32_t kda_version(void);
+
+/*
+ * Bytes of device workspace kda_chunk_fwd needs for these sizes (0 if the
+ * sizes are invalid or unsupported).  T_total counts all packed tokens and N
+ * the sequences.  The requirement depends only on the arguments.
+ */
+size_t kda_chunk_fwd_workspace_size(int64_t T_total, int32_t N, int32_t H,
+                                    int32_t d_k, int32_t d_v, kda_dtype dt,
+                                    kda_gate gk);
+
+/*
+ * Chunkwise-parallel KDA forward (prefill) over a packed batch.
+ *
+ * Operation: for every sequence n and head h, starting from S0[n,h] (zeros
+ * if S0 is NULL), run the recurrence above over the sequence's tokens in
+ * order; write o_t for every token and the final state into S_T[n,h].  It is
+ * evaluated in chunks of C = 64 tokens that restart at every sequence start
+ * (the last chunk of a sequence may be shorter): inside a chunk all deltas
+ * come from one unit-lower-triangular solve (the WY/UT form of the product of
+ * rank-one corrections), the state crosses chunk boundaries once per chunk.
+ *
+ *   q, k, v, g, beta  inputs as described above; T_total tokens
+ *   S0                fp32 [N, H, d_k, d_v] or NULL (= zeros)
+ *   cu_seqlens        int32 device array [N + 1] of sequence offsets
+ *                     (cu_seqlens[0] = 0, non-decreasing, cu_seqlens[N] =
+ *                     T_total; empty sequences allowed: S_T = S0), or NULL:
+ *                     N sequences of T_total / N tokens each (T_total % N
+ *                     must be 0).  Device offsets are validated on the
+ *                     device; if they are invalid no output is written and
+ *                     kda_chunk_fwd_check reports KDA_ERR_BAD_SEQLENS.
+ *   N, T_total, H     sequences (>= 1), packed tokens (>= 0), heads (>= 1)
+ *   o                 [T_total, H, d_v], element type dt (output)
+ *   S_T               fp32 [N, H, d_k, d_v] or NULL; may alias S0 exactly
+ *   workspace         device scratch of >= kda_chunk_fwd_workspace_size()
+ *                     bytes, 256-byte aligned; its contents on entry do not
+ *                     matter and are clobbered
+ *   stream            HIP stream the kernels are enqueued on
+ *
+ * Numerics: bf16 inputs are widened exactly; matrix products run on bf16
+ * MFMA with fp32 accumulation (fp32 MFMA for KDA_F32 inputs); the state is
+ * carried in fp32 and o is rounded once (round-to-nearest-even for bf16).
+ * Two calls with identical arguments give bit-identical results.
+ */
+kda_status kda_chunk_fwd(const void *q, const void *k, const void *v,
+                         const void *g, const void *beta, const float *S0,
+                         const int32_t *cu_seqlens, int32_t N, int64_t T_total,
+                         int32_t H, int32_t d_k, int32_t d_v, kda_dtype dt,
+                         kda_gate gk, void *o, float *S_T, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Wait for `stream` and report whether the last kda_chunk_fwd that used this
+ * workspace accepted its device cu_seqlens: KDA_OK, KDA_ERR_BAD_SEQLENS (the
+ * offsets were not 0 = c_0 <= ... <= c_N = T_total; nothing was written), or
+ * KDA_ERR_HIP if synchronisation fails.  Optional; it synchronises the host.
+ */
+kda_status kda_chunk_fwd_check(const void *workspace, hipStream_t stream);
+
+/*
+ * One recurrent (decode) step for N independent sequences, in place.
+ *
+ * Operation, per (n, h) with a = exp(g): r = S^T (a*k), s = S^T (a*q),
+ * u = beta (v - r), o = s + (q.k) u, S <- Diag(a) S + k u^T; equal to one
+ * token of the recurrence above.  S is read once and written once.
+ *
+ *   q, k, g   [N, H, d_k] (g is [N, H] with KDA_GATE_PER_HEAD), type dt
+ *   v         [N, H, d_v], type dt;  beta [N, H], type dt
+ *   S         fp32 [N, H, d_k, d_v], updated in place
+ *   o         [N, H, d_v], type dt (output)
+ */
+kda_status kda_recurrent_step(const void *q, const void *k, const void *v,
+                              const void *g, const void *beta, float *S,
+                              int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                              kda_dtype dt, kda_gate gk, void *o,
+                              hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

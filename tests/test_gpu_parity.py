@@ -1,0 +1,240 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Bar: max|gpu - oracle| / max|oracle| <= 1e-4 for fp32 inputs and <= 1e-2 for
+bf16 inputs with fp32 state, separately for o and S_T, on seeded inputs with
+the shapes and value distributions of the benchmark configurations.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from _kda_cases import TOL, chunk_case, dev_inputs, to_dev, to_np64
+
+pytestmark = pytest.mark.gpu
+
+kda = pytest.importorskip("gated_delta_rule_48_amd")
+
+
+def _announce(msg):
+    sys.stdout.write(f"\n[case] {msg}\n")
+    sys.stdout.flush()
+
+
+def _run_chunk(d, dtype, gate):
+    x = dev_inputs(d, dtype)
+    o, S_T = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], S0=x["S0"], cu_seqlens=x["cu_seqlens"],
+                           per_head_gate=(gate == "head"))
+    torch.cuda.synchronize()
+    return to_np64(o), to_np64(S_T)
+
+
+def _oracle_chunk(d, gate, **kw):
+    return oracle.recurrence(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=d["S0"], cu_seqlens=d["cu_seqlens"],
+                             per_head_gate=(gate == "head"), **kw)
+
+
+def _assert_close(name, got, ref, tol):
+    err = oracle.rel_err(got, ref)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    assert err <= tol, f"{name}: rel err {err:.3e} > {tol:.0e}"
+    return err
+
+
+# ------------------------------------------------------------- small cases
+SMALL = [
+    # (H, dk, dv, dtype, gate, lengths, s0_sigma)
+    (2, 64, 64, "f32", "channel", [256], 0.0),
+    (2, 64, 64, "f32", "channel", [1], 0.1),
+    (2, 64, 64, "f32", "channel", [63, 64, 65], 0.1),
+    (3, 128, 128, "f32", "channel", [130, 7], 0.1),
+    (2, 64, 128, "f32", "head", [100, 0, 37], 0.1),
+    (2, 128, 64, "f32", "channel", [191], 0.1),
+    (2, 64, 64, "bf16", "channel", [256], 0.0),
+    (2, 128, 128, "bf16", "channel", [300, 1, 64, 129], 0.1),
+    (2, 128, 128, "bf16", "head", [257, 0, 512], 0.1),
+    (4, 128, 64, "bf16", "channel", [333], 0.1),
+    (2, 64, 128, "bf16", "head", [65, 190], 0.1),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"H{c[0]}_dk{c[1]}_dv{c[2]}_{c[3]}_{c[4]}_L{'-'.join(map(str, c[5]))}")
+def test_chunk_small(case):
+    H, dk, dv, dtype, gate, lengths, s0 = case
+    _announce(f"chunk_small {case}")
+    d = chunk_case(H, dk, dv, dtype, gate, lengths, s0_sigma=s0, seed=sum(lengths) + dk)
+    o, S = _run_chunk(d, dtype, gate)
+    o_ref, S_ref = _oracle_chunk(d, gate)
+    _assert_close("o", o, o_ref, TOL[dtype])
+    _assert_close("S_T", S, S_ref, TOL[dtype])
+
+
+def test_chunk_strong_decay_tail():
+    """Gates drawn from N(+3, 1) (alpha near e^-3 per step) push the
+    chunk-local log-decay to about -200 over 64 tokens: exercises the range
+    guard of the decay factors."""
+    _announce("strong decay")
+    d = chunk_case(2, 128, 128, "bf16", "channel", [200], seed=5, gate_mu=3.0)
+    o, S = _run_chunk(d, "bf16", "channel")
+    o_ref, S_ref = _oracle_chunk(d, "channel")
+    _assert_close("o", o, o_ref, TOL["bf16"])
+    _assert_close("S_T", S, S_ref, TOL["bf16"])
+
+
+def test_chunk_no_decay_deltanet():
+    """g = 0 (plain DeltaNet with beta): the state carries over all chunks."""
+    _announce("no decay")
+    d = chunk_case(2, 64, 64, "f32", "channel", [300], seed=6)
+    d["g"] = np.zeros_like(d["g"])
+    o, S = _run_chunk(d, "f32", "channel")
+    o_ref, S_ref = _oracle_chunk(d, "channel")
+    _assert_close("o", o, o_ref, TOL["f32"])
+    _assert_close("S_T", S, S_ref, TOL["f32"])
+
+
+def test_chunk_deterministic_and_s0_none_equals_zeros():
+    _announce("determinism")
+    d = chunk_case(2, 128, 128, "bf16", "channel", [200, 77], seed=9)
+    x = dev_inputs(d, "bf16")
+    runs = []
+    for S0 in (None, torch.zeros(2, 2, 128, 128, device="cuda"), None):
+        o, S = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], S0=S0, cu_seqlens=x["cu_seqlens"])
+        torch.cuda.synchronize()
+        runs.append((o.clone(), S.clone()))
+    for o, S in runs[1:]:
+        assert torch.equal(o, runs[0][0]) and torch.equal(S, runs[0][1])
+
+
+def test_chunk_batched_equals_packed():
+    _announce("batched [B,T,H,d] == packed")
+    d = chunk_case(2, 64, 64, "bf16", "channel", [96, 96], seed=10)
+    x = dev_inputs(d, "bf16")
+    o1, S1 = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], S0=x["S0"], cu_seqlens=x["cu_seqlens"])
+    B = 2
+    r = lambda t: t.reshape(B, 96, *t.shape[1:])
+    o2, S2 = kda.chunk_fwd(r(x["q"]), r(x["k"]), r(x["v"]), r(x["g"]), r(x["beta"]), S0=x["S0"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1.reshape(B, 96, 2, 64), o2) and torch.equal(S1, S2)
+
+
+def test_chunk_state_alias_and_split():
+    """S_T may alias S0; two chained calls match the oracle of the whole."""
+    _announce("alias + split")
+    d = chunk_case(2, 128, 128, "bf16", "channel", [300], seed=12)
+    x = dev_inputs(d, "bf16")
+    S = x["S0"].clone()
+    outs = []
+    for s, e in ((0, 100), (100, 300)):
+        sl = lambda t: t[s:e].contiguous()
+        o, _ = kda.chunk_fwd(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]), sl(x["beta"]), S0=S, S_T=S)
+        outs.append(o)
+    torch.cuda.synchronize()
+    o_ref, S_ref = _oracle_chunk(d, "channel")
+    _assert_close("o", to_np64(torch.cat(outs)), o_ref, TOL["bf16"])
+    _assert_close("S_T", to_np64(S), S_ref, TOL["bf16"])
+
+
+def test_chunk_bad_seqlens_rejected_on_device():
+    _announce("bad cu_seqlens")
+    d = chunk_case(2, 64, 64, "bf16", "channel", [64, 64], seed=13)
+    x = dev_inputs(d, "bf16")
+    bad = torch.tensor([0, 100, 64], dtype=torch.int32, device="cuda")  # decreasing
+    o = torch.full((128, 2, 64), 7.0, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(kda.chunk_fwd_workspace_size(128, 2, 2, 64, 64), dtype=torch.uint8, device="cuda")
+    kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], cu_seqlens=bad, out=o, workspace=ws)
+    with pytest.raises(kda.KDAError) as ei:
+        kda.chunk_fwd_check(ws)
+    assert ei.value.code == 5
+    assert torch.all(o == 7.0)
+    kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], cu_seqlens=x["cu_seqlens"], out=o, workspace=ws)
+    kda.chunk_fwd_check(ws)
+
+
+def test_prefill_then_decode_matches_oracle():
+    _announce("prefill -> decode")
+    d = chunk_case(2, 128, 128, "bf16", "channel", [130], seed=14)
+    x = dev_inputs(d, "bf16")
+    T = 129
+    sl = lambda t: t[:T].contiguous()
+    _, S = kda.chunk_fwd(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]), sl(x["beta"]), S0=x["S0"])
+    tk = lambda t: t[T:T + 1].contiguous()
+    o = kda.recurrent_step(tk(x["q"]), tk(x["k"]), tk(x["v"]), tk(x["g"]), tk(x["beta"]), S)
+    torch.cuda.synchronize()
+    o_ref, S_ref = _oracle_chunk(d, "channel")
+    _assert_close("o", to_np64(o), o_ref[T:T + 1], TOL["bf16"])
+    _assert_close("S", to_np64(S), S_ref, TOL["bf16"])
+
+
+# ------------------------------------------------------------- decode
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("gate", ["channel", "head"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (64, 128), (128, 64)])
+def test_decode_small(dtype, gate, dk, dv):
+    _announce(f"decode small {dtype} {gate} {dk}x{dv}")
+    N, H, steps = 5, 3, 6
+    cfg = synth.DecodeConfig("t", N=N, H=H, dk=dk, dv=dv, steps=steps, dtype=dtype, gate=gate, gate_mu=0.0,
+                             s_sigma=0.1, seed=dk + dv)
+    rng = np.random.default_rng(cfg.seed)
+    S_np = synth.decode_state(cfg, rng)
+    S = torch.from_numpy(S_np).cuda()
+    S_ref = S_np.astype(np.float64)
+    cu = np.arange(N + 1)
+    for _ in range(steps):
+        tok = synth.decode_step_inputs(cfg, rng)
+        o = kda.recurrent_step(*(to_dev(tok[n], dtype) for n in ("q", "k", "v", "g", "beta")), S,
+                               per_head_gate=(gate == "head"))
+        o_ref, S_ref = oracle.recurrence(tok["q"], tok["k"], tok["v"], tok["g"], tok["beta"], S0=S_ref,
+                                         cu_seqlens=cu, per_head_gate=(gate == "head"))
+        _assert_close("o", to_np64(o), o_ref, TOL[dtype])
+    _assert_close("S", to_np64(S), S_ref, TOL[dtype])
+
+
+# ------------------------------------------------------- benchmark configs
+def test_config_tiny_f32():
+    """B=1, T=256, H=2, d=64, fp32, per-channel gate, S0 = 0."""
+    _announce("config kda_tiny_f32")
+    d = synth.chunk_inputs(synth.CONFIGS["kda_tiny_f32"])
+    o, S = _run_chunk(d, "f32", "channel")
+    o_ref, S_ref = _oracle_chunk(d, "channel")
+    print("tiny errs", _assert_close("o", o, o_ref, 1e-4), _assert_close("S_T", S, S_ref, 1e-4))
+
+
+def test_config_gdn_varlen_bf16():
+    """8 packed sequences (U{256..8192}), H=16, d=128, per-head gate, S0 ~ N(0, 0.1^2)."""
+    _announce("config gdn_varlen_bf16")
+    d = synth.chunk_inputs(synth.CONFIGS["gdn_varlen_bf16"])
+    o, S = _run_chunk(d, "bf16", "head")
+    o_ref, S_ref = _oracle_chunk(d, "head")
+    print("varlen errs", _assert_close("o", o, o_ref, 1e-2), _assert_close("S_T", S, S_ref, 1e-2))
+
+
+def test_config_32k_bf16():
+    """B=1, T=32768, H=32, d=128, per-channel gate from N(-1,1)."""
+    _announce("config kda_32k_bf16")
+    d = synth.chunk_inputs(synth.CONFIGS["kda_32k_bf16"])
+    o, S = _run_chunk(d, "bf16", "channel")
+    o_ref, S_ref = _oracle_chunk(d, "channel")
+    print("32k errs", _assert_close("o", o, o_ref, 1e-2), _assert_close("S_T", S, S_ref, 1e-2))
+
+
+def test_config_decode_256x32_64_steps():
+    """256 sequences x 32 heads, d=128, fp32 state, 64 consecutive steps."""
+    _announce("config decode_256x32")
+    cfg = synth.DECODE_CONFIGS["decode_256x32"]
+    rng = np.random.default_rng(cfg.seed)
+    S_np = synth.decode_state(cfg, rng)
+    S = torch.from_numpy(S_np).cuda()
+    S_ref = S_np.astype(np.float64)
+    cu = np.arange(cfg.N + 1)
+    worst = 0.0
+    for _ in range(cfg.steps):
+        tok = synth.decode_step_inputs(cfg, rng)
+        o = kda.recurrent_step(*(to_dev(tok[n], "bf16") for n in ("q", "k", "v", "g", "beta")), S)
+        o_ref, S_ref = oracle.recurrence(tok["q"], tok["k"], tok["v"], tok["g"], tok["beta"], S0=S_ref,
+                                         cu_seqlens=cu)
+        worst = max(worst, _assert_close("o", to_np64(o), o_ref, 1e-2))
+    print("decode errs", worst, _assert_close("S", to_np64(S), S_ref, 1e-2))
