@@ -1,0 +1,208 @@
+"""Benchmark of the KDA hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  * the chunked forward (prefill) over the 32K workload: B=1, T=32768, H=32,
+    d_k=d_v=128, C=64, bf16 inputs, fp32 state, per-channel gate
+    (kda_chunk_fwd: chunk map, intra-chunk, chunk walk), then
+  * one recurrent decode step over 256 sequences x 32 heads, d=128, fp32
+    state (kda_recurrent_step).
+Inputs are generated once (seeded, synth.CONFIGS / DECODE_CONFIGS) and are
+resident in HBM before the timed region.  `value` is prefill tokens/s over
+the chunked-forward time of the timed steps; `decode` reports the decode step
+in GB/s of its algorithmic bytes.  Each kernel is timed with HIP events
+recorded on the stream it runs on.  The oracle (fp64, host cores) is timed
+on a bounded prefix of the same workload as `cpu_baseline`.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA chunked fwd tokens/s (H=32,d=128,T=32K) + decode step GB/s; % of roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
+
+# Algorithmic figures (per head-token for the chunked path, d = 128, C = 64)
+PATH_MIN_BYTES_PER_HT = 1282           # bf16 q, k, v, g, o (5 x 2 x 128) + beta (2)
+PATH_FLOP_PER_HT = 139136              # 6 d^2 + (5C - 1) d
+INTRA_BYTES_PER_HT = 2186              # reads q,k,v,g,beta (1026); writes W,QG,KdT,U' (4 x 256), P (128), Gn (8)
+WALK_BYTES_PER_HT = 1416               # reads W,QG,KdT,U',P,Gn (1160); writes o (256)
+DECODE_BYTES_PER_STEP = 1084243968     # state read + write (2 x 536870912) + tokens in (8404992) + o (2097152)
+
+
+def _hip():
+    lib = ctypes.CDLL("libamdhip64.so")
+    lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    return lib
+
+
+class Events:
+    def __init__(self, hip, n):
+        self.hip = hip
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(e.value)
+
+    def record(self, i, stream):
+        if self.hip.hipEventRecord(ctypes.c_void_p(self.ev[i]), ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, i, j):
+        out = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(self.ev[i]), ctypes.c_void_p(self.ev[j])) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(out.value)
+
+
+def _to_dev(a, torch):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def cpu_baseline(d, prefix_tokens):
+    import oracle
+    oracle.build(force=False)
+    T = prefix_tokens
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    sl = lambda a: np.ascontiguousarray(a[:T])
+    t0 = time.perf_counter()
+    oracle.recurrence(sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["g"]), sl(d["beta"]), cu_seqlens=[0, T],
+                      threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {T} tokens of the 32K x 32-head prefill workload (all heads), fp64 sequential "
+                      f"recurrence, {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-prefix", type=int, default=8192)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the KDA hot path here is not sharded, got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_48_amd as kda
+    import synth
+
+    kda.load_library()
+    hip = _hip()
+    cfg = synth.CONFIGS["kda_32k_bf16"]
+    d = synth.chunk_inputs(cfg)
+    T, H, dk, dv = int(d["cu_seqlens"][-1]), cfg.H, cfg.dk, cfg.dv
+    x = {n: _to_dev(d[n], torch) for n in ("q", "k", "v", "g", "beta")}
+    o = torch.empty((T, H, dv), dtype=torch.bfloat16, device="cuda")
+    S_T = torch.empty((1, H, dk, dv), dtype=torch.float32, device="cuda")
+    ws = torch.empty(kda.chunk_fwd_workspace_size(T, 1, H, dk, dv), dtype=torch.uint8, device="cuda")
+
+    dcfg = synth.DECODE_CONFIGS["decode_256x32"]
+    rng = np.random.default_rng(dcfg.seed)
+    S_dec = torch.from_numpy(synth.decode_state(dcfg, rng)).cuda()
+    n_tok = min(args.steps + args.warmup, 8)
+    toks = []
+    for _ in range(n_tok):
+        t = synth.decode_step_inputs(dcfg, rng)
+        toks.append({n: _to_dev(t[n], torch) for n in ("q", "k", "v", "g", "beta")})
+    o_dec = torch.empty((dcfg.N, dcfg.H, dcfg.dv), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream().cuda_stream
+    K, W = args.steps, args.warmup
+    evs = [Events(hip, 6) for _ in range(K)]
+
+    def step(i, ev):
+        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], out=o, S_T=S_T, workspace=ws,
+                      events=None if ev is None else ev.ev[:4])
+        if ev is not None:
+            ev.record(4, stream)
+        tk = toks[i % n_tok]
+        kda.recurrent_step(tk["q"], tk["k"], tk["v"], tk["g"], tk["beta"], S_dec, out=o_dec)
+        if ev is not None:
+            ev.record(5, stream)
+
+    for i in range(W):
+        step(i, None)
+    dist = torch.distributed.is_available() and torch.distributed.is_initialized()
+    if dist:
+        torch.distributed.barrier()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(W + i, evs[i])
+    if dist:
+        torch.distributed.barrier()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / K
+
+    avg = lambda i, j: float(np.mean([e.ms(i, j) for e in evs]))
+    t_map, t_intra, t_walk = avg(0, 1), avg(1, 2), avg(2, 3)
+    t_fwd, t_dec = avg(0, 3), avg(4, 5)
+    ht = T * H
+    tokens_per_s = T / (t_fwd * 1e-3)
+
+    kern = {
+        "kda::intra_chunk_kernel": (t_intra, INTRA_BYTES_PER_HT * ht),
+        "kda::chunk_walk_kernel": (t_walk, WALK_BYTES_PER_HT * ht),
+        "kda::decode_step_kernel": (t_dec, DECODE_BYTES_PER_STEP),
+    }
+    dom = max(kern, key=lambda k: kern[k][0])
+    dom_ms, dom_bytes = kern[dom]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    dec_gbs = DECODE_BYTES_PER_STEP / (t_dec * 1e-3) / 1e9
+    path_gbs = PATH_MIN_BYTES_PER_HT * ht / (t_fwd * 1e-3) / 1e9
+    path_tflops = PATH_FLOP_PER_HT * ht / (t_fwd * 1e-3) / 1e12
+
+    res = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": wall_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "kda_32k_bf16 prefill: B=1, T=32768, H=32, d_k=d_v=128, C=64, per-channel gate, "
+                               "bf16 inputs, fp32 state; plus one decode step of decode_256x32: 256 sequences x "
+                               "32 heads, d=128, fp32 state",
+                   "global_batch": 1, "seq_len": T, "heads": H, "d_k": dk, "d_v": dv, "chunk": 64},
+        "prefill_ms": t_fwd,
+        "kernels_ms": {"chunk_map": t_map, "intra_chunk": t_intra, "chunk_walk": t_walk, "decode_step": t_dec},
+        "decode": {"us_per_step": t_dec * 1e3, "GB_per_s": dec_gbs, "frac_hbm_peak": dec_gbs / HBM_PEAK_GBS,
+                   "tokens_per_s": dcfg.N / (t_dec * 1e-3), "bytes_per_step": DECODE_BYTES_PER_STEP},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "path_roofline": {"what": "whole kda_chunk_fwd call vs the method's minimum bytes (1282 B/head-token) "
+                                  "and algorithmic FLOPs (139136 /head-token)",
+                          "GB_per_s": path_gbs, "frac_hbm_peak": path_gbs / HBM_PEAK_GBS,
+                          "TFLOP_per_s": path_tflops, "frac_bf16_mfma_peak": path_tflops / BF16_MFMA_PEAK_TFLOPS},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(d, args.cpu_prefix)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

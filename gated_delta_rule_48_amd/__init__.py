@@ -53,6 +53,8 @@ def load_library():
         lib.kda_chunk_fwd.restype = ctypes.c_int
         lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, ctypes.c_int,
                                       ctypes.c_int, vp, vp, vp, sz, vp]
+        lib.kda_chunk_fwd_instrumented.restype = ctypes.c_int
+        lib.kda_chunk_fwd_instrumented.argtypes = lib.kda_chunk_fwd.argtypes + [vp]
         lib.kda_chunk_fwd_check.restype = ctypes.c_int
         lib.kda_chunk_fwd_check.argtypes = [vp, vp]
         lib.kda_recurrent_step.restype = ctypes.c_int
@@ -110,7 +112,7 @@ def chunk_fwd_workspace_size(T_total, N, H, d_k, d_v, dtype=torch.bfloat16, per_
 
 
 def chunk_fwd(q, k, v, g, beta, *, S0=None, cu_seqlens=None, N=None, per_head_gate=False,
-              out=None, S_T=None, workspace=None, stream=None, output_final_state=True):
+              out=None, S_T=None, workspace=None, stream=None, output_final_state=True, events=None):
     """Chunked KDA forward (prefill).
 
     q, k: [T, H, dk] packed (with ``cu_seqlens`` int32 [N+1] on the device, or
@@ -119,7 +121,9 @@ def chunk_fwd(q, k, v, g, beta, *, S0=None, cu_seqlens=None, N=None, per_head_ga
     ``per_head_gate``; beta: [T, H] / [B, T, H].  q, k, v, g, beta share one
     dtype (bfloat16 or float32).  S0: fp32 [N, H, dk, dv] or None.
     Returns (o with q's dtype and v's leading shape, S_T fp32 [N, H, dk, dv]
-    or None).
+    or None).  ``events``: optional sequence of four raw hipEvent_t handles
+    (ints) recorded before the chunk-map, intra-chunk and walk kernels and
+    after the walk kernel (kda_chunk_fwd_instrumented).
     """
     batched = q.dim() == 4
     if batched:
@@ -164,9 +168,16 @@ def chunk_fwd(q, k, v, g, beta, *, S0=None, cu_seqlens=None, N=None, per_head_ga
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     _dev_contig("workspace", workspace)
-    _check(lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(cu_seqlens),
-                             N, T_total, H, dk, dv, dt, gk, _ptr(o), _ptr(S_T), _ptr(workspace),
-                             workspace.numel() * workspace.element_size(), _stream(stream)))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(cu_seqlens),
+            N, T_total, H, dk, dv, dt, gk, _ptr(o), _ptr(S_T), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    if events is None:
+        _check(lib.kda_chunk_fwd(*args))
+    else:
+        if len(events) != 4:
+            raise ValueError("events must hold four hipEvent_t handles")
+        arr = (ctypes.c_void_p * 4)(*[int(e) for e in events])
+        _check(lib.kda_chunk_fwd_instrumented(*args, arr))
     if batched:
         o = o.reshape(N, T_total // N, H, dv)
     return o, S_T

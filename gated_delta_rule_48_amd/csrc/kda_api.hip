@@ -46,10 +46,11 @@ size_t kda_chunk_fwd_workspace_size(int64_t T_total, int32_t N, int32_t H, int32
     return kda::chunk_workspace_bytes(T_total, N, H, d_k, d_v, dt == KDA_BF16);
 }
 
-kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
-                         const float* S0, const int32_t* cu_seqlens, int32_t N, int64_t T_total, int32_t H,
-                         int32_t d_k, int32_t d_v, kda_dtype dt, kda_gate gk, void* o, float* S_T,
-                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+namespace {
+kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                          const float* S0, const int32_t* cu_seqlens, int32_t N, int64_t T_total, int32_t H,
+                          int32_t d_k, int32_t d_v, kda_dtype dt, kda_gate gk, void* o, float* S_T,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* events) {
     const kda_status st = check_common(H, d_k, d_v, dt, gk);
     if (st != KDA_OK) return st;
     if (N <= 0 || T_total < 0 || T_total > INT32_MAX) return KDA_ERR_INVALID_ARG;
@@ -76,7 +77,26 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
     a.bf16 = dt == KDA_BF16;
     a.head_gate = gk == KDA_GATE_PER_HEAD;
     const kda::ChunkWorkspace ws = kda::carve_chunk_workspace(workspace, T_total, N, H, d_k, d_v, a.bf16);
-    return kda::launch_chunk_fwd(a, ws, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    return kda::launch_chunk_fwd(a, ws, stream, events) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+}  // namespace
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                         const float* S0, const int32_t* cu_seqlens, int32_t N, int64_t T_total, int32_t H,
+                         int32_t d_k, int32_t d_v, kda_dtype dt, kda_gate gk, void* o, float* S_T,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return chunk_fwd_impl(q, k, v, g, beta, S0, cu_seqlens, N, T_total, H, d_k, d_v, dt, gk, o, S_T, workspace,
+                          workspace_bytes, stream, nullptr);
+}
+
+kda_status kda_chunk_fwd_instrumented(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                      const float* S0, const int32_t* cu_seqlens, int32_t N, int64_t T_total,
+                                      int32_t H, int32_t d_k, int32_t d_v, kda_dtype dt, kda_gate gk, void* o,
+                                      float* S_T, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                      hipEvent_t* events) {
+    if (!events) return KDA_ERR_INVALID_ARG;
+    return chunk_fwd_impl(q, k, v, g, beta, S0, cu_seqlens, N, T_total, H, d_k, d_v, dt, gk, o, S_T, workspace,
+                          workspace_bytes, stream, events);
 }
 
 kda_status kda_chunk_fwd_check(const void* workspace, hipStream_t stream) {

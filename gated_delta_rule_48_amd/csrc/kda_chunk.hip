@@ -116,11 +116,18 @@ struct IntraLayout {
     // Region R1: [Kr | Qr | Kt] ([token][channel], E) while A and P are
     // formed; afterwards [Kbt | Vt] ([channel][token], E) and the 3 x 16 x 16
     // fp32 scratch of the off-diagonal inversion.
+    // Also in R1 after A and P: the P staging tile [C][C+PAD]; at the very end
+    // the W and U' staging tiles [C][DK+PAD], [C][DV+PAD] for coalesced stores.
+    static constexpr int LDP = C + PAD;
+    static constexpr int LDV = DV + PAD;
     static constexpr size_t rhs_bytes = (size_t)(DK + DV) * LDT * sizeof(E);
-    static constexpr size_t r1_a = (size_t)3 * C * LDK * sizeof(E);
-    static constexpr size_t r1_b = (rhs_bytes + 15) / 16 * 16 + 3 * 256 * 4;
     static constexpr size_t off_X = (rhs_bytes + 15) / 16 * 16;
-    static constexpr size_t off_A = ((r1_a > r1_b ? r1_a : r1_b) + 15) / 16 * 16;  // sA; sBnd before A
+    static constexpr size_t off_Pst = off_X + 3 * 256 * 4;
+    static constexpr size_t r1_a = (size_t)3 * C * LDK * sizeof(E);
+    static constexpr size_t r1_b = off_Pst + (size_t)C * LDP * sizeof(E);
+    static constexpr size_t r1_c = (size_t)C * (LDK + LDV) * sizeof(E);
+    static constexpr size_t r1_max = r1_a > r1_b ? (r1_a > r1_c ? r1_a : r1_c) : (r1_b > r1_c ? r1_b : r1_c);
+    static constexpr size_t off_A = (r1_max + 15) / 16 * 16;  // sA; sBnd before A
     static constexpr size_t off_beta = off_A + (size_t)C * LDA * 4;
     static constexpr size_t off_scale = off_beta + C * 4;  // sColScale, sRowScale; sPart before them
     static constexpr size_t scale_bytes = (size_t)(NCS + 4) * DK * 4;
@@ -142,21 +149,49 @@ template <> __device__ __forceinline__ void load2<float>(const float* p, float& 
 }
 template <typename E> __device__ __forceinline__ void store2(E* p, float a, float b);
 template <> __device__ __forceinline__ void store2<bf16_t>(bf16_t* p, float a, float b) {
-    *reinterpret_cast<uint32_t*>(p) = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+    *reinterpret_cast<uint32_t*>(p) = f32x2_to_bf16x2(a, b);
 }
 template <> __device__ __forceinline__ void store2<float>(float* p, float a, float b) {
     *reinterpret_cast<float2*>(p) = make_float2(a, b);
+}
+
+// Store N contiguous elements held in registers with 16-byte stores
+// (dst 16-byte aligned, N * sizeof(E) a multiple of 16).
+template <typename E, int N>
+__device__ __forceinline__ void store_run(E* dst, const E (&vals)[N]) {
+    constexpr int PER = 16 / (int)sizeof(E);
+    static_assert(N % PER == 0, "run length");
+#pragma unroll
+    for (int i = 0; i < N / PER; ++i) {
+        uint4 w;
+        __builtin_memcpy(&w, &vals[i * PER], 16);
+        *reinterpret_cast<uint4*>(dst + i * PER) = w;
+    }
+}
+
+// Copy a ROWS x COLS tile from LDS (row stride lds_ld elements) to a dense
+// global tile with 16-byte loads and stores spread over the 256 threads.
+template <typename E, int ROWS, int COLS>
+__device__ __forceinline__ void copy_tile_out(E* __restrict__ dst, const E* src, int lds_ld, int tid) {
+    constexpr int VPR = COLS * (int)sizeof(E) / 16;
+    constexpr int PER = 16 / (int)sizeof(E);
+#pragma unroll
+    for (int i = tid; i < ROWS * VPR; i += 256) {
+        const int r = i / VPR, c = (i % VPR) * PER;
+        *reinterpret_cast<uint4*>(dst + r * COLS + c) = *reinterpret_cast<const uint4*>(src + r * lds_ld + c);
+    }
 }
 
 // f[j] <- f[j] * s[j], j = 0..7 (s: 8 contiguous fp32 in LDS).
 __device__ __forceinline__ Frag<bf16_t> scale_frag(Frag<bf16_t> f, const float* s) {
     const f32x4 a = *reinterpret_cast<const f32x4*>(s);
     const f32x4 b = *reinterpret_cast<const f32x4*>(s + 4);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        f.v[j] = f32_to_bf16(bf16_to_f32(f.v[j]) * a[j]);
-        f.v[j + 4] = f32_to_bf16(bf16_to_f32(f.v[j + 4]) * b[j]);
-    }
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 w = {f32x2_to_bf16x2(bf16_to_f32(f.v[0]) * a[0], bf16_to_f32(f.v[1]) * a[1]),
+                     f32x2_to_bf16x2(bf16_to_f32(f.v[2]) * a[2], bf16_to_f32(f.v[3]) * a[3]),
+                     f32x2_to_bf16x2(bf16_to_f32(f.v[4]) * b[0], bf16_to_f32(f.v[5]) * b[1]),
+                     f32x2_to_bf16x2(bf16_to_f32(f.v[6]) * b[2], bf16_to_f32(f.v[7]) * b[3])};
+    f.v = __builtin_bit_cast(u16x8, w);
     return f;
 }
 __device__ __forceinline__ Frag<float> scale_frag(Frag<float> f, const float* s) {
@@ -289,12 +324,8 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
     }
     {
         E* p0 = KdTo + (ch * DK + c0) * C + part * RPT;
-        E* p1 = p0 + C;
-#pragma unroll
-        for (int r = 0; r < RPT; ++r) {
-            p0[r] = kd0[r];
-            p1[r] = kd1[r];
-        }
+        store_run<E, RPT>(p0, kd0);
+        store_run<E, RPT>(p0 + C, kd1);
         if (part == 0) {
             Gno[ch * DK + c0] = gate_exp<E>(last0);
             Gno[ch * DK + c0 + 1] = gate_exp<E>(last1);
@@ -324,6 +355,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
 
     // ---- 3. A = K K^T with decay (strictly lower, row-scaled by beta) -> LDS
     //         (fp32);  P = Q K^T with decay (lower incl. diagonal) -> workspace
+    f32x4 accPt[4];
     {
         const int ti = wave;
 #pragma unroll
@@ -349,12 +381,20 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * ti + 4 * lg + i, col = 16 * tj + lr;
-                sA[row * LDA + col] = (row > col) ? accA[i] * sBeta[row] : 0.f;
-                Po[(ch * C + row) * C + col] = Elt<E>::from((row >= col) ? accP[i] : 0.f);
+                lds_put(&sA[row * LDA + col], (row > col) ? accA[i] * sBeta[row] : 0.f);
+                accPt[tj][i] = (row >= col) ? accP[i] : 0.f;
             }
         }
     }
     __syncthreads();
+    {
+        E* sPst = reinterpret_cast<E*>(smem + L::off_Pst);
+#pragma unroll
+        for (int tj = 0; tj < 4; ++tj)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                lds_put(&sPst[(16 * wave + 4 * lg + i) * L::LDP + 16 * tj + lr], Elt<E>::from(accPt[tj][i]));
+    }
 
     // ---- 4. right-hand sides into the freed region; T = (I + A)^{-1} ---------
 #pragma unroll
@@ -389,6 +429,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
         }
     }
     __syncthreads();
+    copy_tile_out<E, C, C>(Po + ch * C * C, reinterpret_cast<const E*>(smem + L::off_Pst), L::LDP, tid);
     if (tid < 64) {
         const int blk = tid >> 4, jc = tid & 15;
         float* Tb = sA + (16 * blk) * LDA + 16 * blk;
@@ -429,28 +470,41 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
         }
     }
 
-    // ---- 5. W = T (beta K e^b),  U' = T (beta V) ------------------------------
+    // ---- 5. W = T (beta K e^b),  U' = T (beta V), staged for 16-byte stores --
     {
         const int ti = wave;
         const Frag<E> ft0 = ld_frag_from_f32<E>(sA + (16 * ti + lr) * LDA + 8 * lg);
         const Frag<E> ft1 = ld_frag_from_f32<E>(sA + (16 * ti + lr) * LDA + 32 + 8 * lg);
-        const bool two = ti >= 2;  // rows 0..31 of T vanish beyond token 31
-#pragma unroll 4
+        // (rows 0..31 of T are exactly zero beyond token 31, so for ti < 2 the
+        // second product adds exact zeros; it is issued anyway to keep the
+        // accumulation unconditional)
+        f32x4 accW[DK / 16], accU[DV / 16];
+#pragma unroll
         for (int tn = 0; tn < DK / 16; ++tn) {
-            f32x4 acc = mma(ft0, ld_frag(sKbt + (16 * tn + lr) * LDT + 8 * lg), zero4());
-            if (two) acc = mma(ft1, ld_frag(sKbt + (16 * tn + lr) * LDT + 32 + 8 * lg), acc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                Wo[(ch * C + 16 * ti + 4 * lg + i) * DK + 16 * tn + lr] = Elt<E>::from(acc[i]);
+            accW[tn] = mma(ft0, ld_frag(sKbt + (16 * tn + lr) * LDT + 8 * lg), zero4());
+            accW[tn] = mma(ft1, ld_frag(sKbt + (16 * tn + lr) * LDT + 32 + 8 * lg), accW[tn]);
         }
-#pragma unroll 4
+#pragma unroll
         for (int tn = 0; tn < DV / 16; ++tn) {
-            f32x4 acc = mma(ft0, ld_frag(sVt + (16 * tn + lr) * LDT + 8 * lg), zero4());
-            if (two) acc = mma(ft1, ld_frag(sVt + (16 * tn + lr) * LDT + 32 + 8 * lg), acc);
+            accU[tn] = mma(ft0, ld_frag(sVt + (16 * tn + lr) * LDT + 8 * lg), zero4());
+            accU[tn] = mma(ft1, ld_frag(sVt + (16 * tn + lr) * LDT + 32 + 8 * lg), accU[tn]);
+        }
+        __syncthreads();  // every wave is done with sKbt / sVt / sA
+        E* sWst = reinterpret_cast<E*>(smem);
+        E* sUst = sWst + C * LDK;
+#pragma unroll
+        for (int tn = 0; tn < DK / 16; ++tn)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                Upo[(ch * C + 16 * ti + 4 * lg + i) * DV + 16 * tn + lr] = Elt<E>::from(acc[i]);
-        }
+                lds_put(&sWst[(16 * ti + 4 * lg + i) * LDK + 16 * tn + lr], Elt<E>::from(accW[tn][i]));
+#pragma unroll
+        for (int tn = 0; tn < DV / 16; ++tn)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                lds_put(&sUst[(16 * ti + 4 * lg + i) * L::LDV + 16 * tn + lr], Elt<E>::from(accU[tn][i]));
+        __syncthreads();
+        copy_tile_out<E, C, DK>(Wo + ch * C * DK, sWst, LDK, tid);
+        copy_tile_out<E, C, DV>(Upo + ch * C * DV, sUst, L::LDV, tid);
     }
 }
 
@@ -505,14 +559,22 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(
 #pragma unroll
         for (int mm = 0; mm < MT; ++mm)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sSt[lr * LDS_S + 16 * (w * MT + mm) + 4 * lg + i] = Elt<E>::from(Sreg[mm][i]);
+            for (int i = 0; i < 4; ++i)
+                lds_put(&sSt[lr * LDS_S + 16 * (w * MT + mm) + 4 * lg + i], Elt<E>::from(Sreg[mm][i]));
     };
     put_state();
     __syncthreads();
 
     const int cbeg = chunk_off[n], cend = chunk_off[n + 1];
     const int64_t seq0 = cu[n], seqend = cu[n + 1];
-    for (int c = cbeg; c < cend; ++c) {
+
+    // Operands of one chunk as this wave needs them (register fragments).
+    struct Ops {
+        Frag<E> fW[KS], fQ[KS], fP[2], fK[MT][2];
+        float up[4];
+        f32x4 gn[MT];
+    };
+    auto load_ops = [&](Ops& op, int c) {
         const int64_t ch = (int64_t)c * H + h;
         const E* Wp = Wi + ch * C * DK;
         const E* Qp = QGi + ch * C * DK;
@@ -520,51 +582,51 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(
         const E* Up = Upi + ch * C * DV;
         const E* Pp = Pi + ch * C * C;
         const float* Gp = Gni + ch * DK;
-
-        Frag<E> fW[KS], fQ[KS], fP[2], fK[MT][2];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            fW[ks] = ld_frag(Wp + (16 * w + lr) * DK + 32 * ks + 8 * lg);
-            fQ[ks] = ld_frag(Qp + (16 * w + lr) * DK + 32 * ks + 8 * lg);
+            op.fW[ks] = ld_frag(Wp + (16 * w + lr) * DK + 32 * ks + 8 * lg);
+            op.fQ[ks] = ld_frag(Qp + (16 * w + lr) * DK + 32 * ks + 8 * lg);
         }
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) fP[kb] = ld_frag(Pp + (16 * w + lr) * C + 32 * kb + 8 * lg);
+        for (int kb = 0; kb < 2; ++kb) op.fP[kb] = ld_frag(Pp + (16 * w + lr) * C + 32 * kb + 8 * lg);
 #pragma unroll
         for (int mm = 0; mm < MT; ++mm)
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
-                fK[mm][kb] = ld_frag(Kp + (16 * (w * MT + mm) + lr) * C + 32 * kb + 8 * lg);
-        float up[4];
+                op.fK[mm][kb] = ld_frag(Kp + (16 * (w * MT + mm) + lr) * C + 32 * kb + 8 * lg);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) up[i] = Elt<E>::load(Up + (16 * w + 4 * lg + i) * DV + col);
-        f32x4 gn[MT];
+        for (int i = 0; i < 4; ++i) op.up[i] = Elt<E>::load(Up + (16 * w + 4 * lg + i) * DV + col);
 #pragma unroll
-        for (int mm = 0; mm < MT; ++mm) gn[mm] = *reinterpret_cast<const f32x4*>(Gp + 16 * (w * MT + mm) + 4 * lg);
-
+        for (int mm = 0; mm < MT; ++mm)
+            op.gn[mm] = *reinterpret_cast<const f32x4*>(Gp + 16 * (w * MT + mm) + 4 * lg);
+    };
+    auto run_chunk = [&](const Ops& op, int c) {
         // phase 1: U = U' - W S ;  O = QG S
         f32x4 accW = zero4(), accQ = zero4();
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const Frag<E> fs = ld_frag(sSt + lr * LDS_S + 32 * ks + 8 * lg);
-            accW = mma(fW[ks], fs, accW);
-            accQ = mma(fQ[ks], fs, accQ);
+            accW = mma(op.fW[ks], fs, accW);
+            accQ = mma(op.fQ[ks], fs, accQ);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sUt[lr * LDS_U + 16 * w + 4 * lg + i] = Elt<E>::from(up[i] - accW[i]);
+        for (int i = 0; i < 4; ++i) lds_put(&sUt[lr * LDS_U + 16 * w + 4 * lg + i], Elt<E>::from(op.up[i] - accW[i]));
         __syncthreads();
 
         // phase 2: O += P U ;  S <- Diag(Gn) S + KdT U
         const Frag<E> fu0 = ld_frag(sUt + lr * LDS_U + 8 * lg);
         const Frag<E> fu1 = ld_frag(sUt + lr * LDS_U + 32 + 8 * lg);
-        f32x4 O = mma(fP[0], fu0, accQ);
-        if (w >= 2) O = mma(fP[1], fu1, O);
+        // (P is exactly zero above its diagonal, so the second k-block adds
+        // exact zeros for w < 2)
+        f32x4 O = mma(op.fP[0], fu0, accQ);
+        O = mma(op.fP[1], fu1, O);
 #pragma unroll
         for (int mm = 0; mm < MT; ++mm) {
             f32x4 acc;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = gn[mm][i] * Sreg[mm][i];
-            acc = mma(fK[mm][0], fu0, acc);
-            acc = mma(fK[mm][1], fu1, acc);
+            for (int i = 0; i < 4; ++i) acc[i] = op.gn[mm][i] * Sreg[mm][i];
+            acc = mma(op.fK[mm][0], fu0, acc);
+            acc = mma(op.fK[mm][1], fu1, acc);
             Sreg[mm] = acc;
         }
         const int64_t tok0 = seq0 + (int64_t)(c - cbeg) * C;
@@ -575,6 +637,19 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(
         }
         put_state();
         __syncthreads();
+    };
+
+    // Two operand sets in flight: chunk c+1 loads while chunk c computes.
+    Ops opA, opB;
+    int c = cbeg;
+    if (c < cend) load_ops(opA, c);
+    while (c < cend) {
+        if (c + 1 < cend) load_ops(opB, c + 1);
+        run_chunk(opA, c);
+        if (++c >= cend) break;
+        if (c + 1 < cend) load_ops(opA, c + 1);
+        run_chunk(opB, c);
+        ++c;
     }
     if (S_T) {
 #pragma unroll
@@ -655,34 +730,43 @@ static hipError_t launch_intra(const ChunkArgs& a, const ChunkWorkspace& ws, hip
     return hipGetLastError();
 }
 
+static inline hipError_t mark(hipEvent_t* ev, int i, hipStream_t stream) {
+    return ev ? hipEventRecord(ev[i], stream) : hipSuccess;
+}
+
 template <typename E, int DK, int DV>
-static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkWorkspace& ws, hipStream_t stream) {
-    hipError_t e = hipSuccess;
+static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkWorkspace& ws, hipStream_t stream,
+                                 hipEvent_t* ev) {
+    hipError_t e = mark(ev, 1, stream);
+    if (e != hipSuccess) return e;
     if (a.T > 0) {
         e = a.head_gate ? launch_intra<E, DK, DV, true>(a, ws, stream) : launch_intra<E, DK, DV, false>(a, ws, stream);
         if (e != hipSuccess) return e;
     }
+    if ((e = mark(ev, 2, stream)) != hipSuccess) return e;
     const int64_t blocks = (int64_t)a.N * a.H * (DV / 16);
     hipLaunchKernelGGL((chunk_walk_kernel<E, DK, DV>), dim3((unsigned)blocks), dim3(256), 0, stream, ws.header,
                        ws.cu, ws.chunk_off, a.N, a.H, (const E*)ws.W, (const E*)ws.QG, (const E*)ws.KdT,
                        (const E*)ws.Up, (const E*)ws.P, (const float*)ws.Gn, a.S0, a.S_T, (E*)a.o);
-    return hipGetLastError();
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return mark(ev, 3, stream);
 }
 
 template <typename E>
-static hipError_t launch_chunk_e(const ChunkArgs& a, const ChunkWorkspace& ws, hipStream_t s) {
-    if (a.dk == 64 && a.dv == 64) return launch_chunk_t<E, 64, 64>(a, ws, s);
-    if (a.dk == 64 && a.dv == 128) return launch_chunk_t<E, 64, 128>(a, ws, s);
-    if (a.dk == 128 && a.dv == 64) return launch_chunk_t<E, 128, 64>(a, ws, s);
-    return launch_chunk_t<E, 128, 128>(a, ws, s);
+static hipError_t launch_chunk_e(const ChunkArgs& a, const ChunkWorkspace& ws, hipStream_t s, hipEvent_t* ev) {
+    if (a.dk == 64 && a.dv == 64) return launch_chunk_t<E, 64, 64>(a, ws, s, ev);
+    if (a.dk == 64 && a.dv == 128) return launch_chunk_t<E, 64, 128>(a, ws, s, ev);
+    if (a.dk == 128 && a.dv == 64) return launch_chunk_t<E, 128, 64>(a, ws, s, ev);
+    return launch_chunk_t<E, 128, 128>(a, ws, s, ev);
 }
 
-hipError_t launch_chunk_fwd(const ChunkArgs& a, const ChunkWorkspace& ws, hipStream_t stream) {
+hipError_t launch_chunk_fwd(const ChunkArgs& a, const ChunkWorkspace& ws, hipStream_t stream, hipEvent_t* ev) {
+    hipError_t e = mark(ev, 0, stream);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(256), 0, stream, a.cu_seqlens, a.N, a.T, ws.header, ws.cu,
                        ws.chunk_off);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return a.bf16 ? launch_chunk_e<bf16_t>(a, ws, stream) : launch_chunk_e<float>(a, ws, stream);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return a.bf16 ? launch_chunk_e<bf16_t>(a, ws, stream, ev) : launch_chunk_e<float>(a, ws, stream, ev);
 }
 
 }  // namespace kda

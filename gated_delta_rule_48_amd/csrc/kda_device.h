@@ -34,12 +34,15 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
     return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// fp32 -> bf16, round to nearest even (NaN stays NaN).
+// fp32 -> bf16, round to nearest even: one v_cvt_pk_bf16_f32 on gfx950.
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<bf16_t>(u >> 16);
+    return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
+}
+// Two values at once, packed low | high << 16.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{lo, hi}), b2));
 }
 
 template <typename E> struct Elt;
@@ -89,13 +92,28 @@ template <> __device__ __forceinline__ Frag<float> ld_frag_from_f32<float>(const
 template <> __device__ __forceinline__ Frag<bf16_t> ld_frag_from_f32<bf16_t>(const float* p) {
     const f32x4* q = reinterpret_cast<const f32x4*>(p);
     f32x4 a = q[0], b = q[1];
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 w = {f32x2_to_bf16x2(a[0], a[1]), f32x2_to_bf16x2(a[2], a[3]), f32x2_to_bf16x2(b[0], b[1]),
+                     f32x2_to_bf16x2(b[2], b[3])};
     Frag<bf16_t> f;
-    f.v = u16x8{f32_to_bf16(a[0]), f32_to_bf16(a[1]), f32_to_bf16(a[2]), f32_to_bf16(a[3]),
-                f32_to_bf16(b[0]), f32_to_bf16(b[1]), f32_to_bf16(b[2]), f32_to_bf16(b[3])};
+    f.v = __builtin_bit_cast(u16x8, w);
     return f;
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Scalar LDS store that the backend keeps as a single ds_write.  Used for
+// every store of matrix-core accumulator values into LDS: the gfx950 backend
+// of ROCm 7.2 can give a wrong offset to a ds_write2 pair it forms from such
+// values (seen with conditionally accumulated tiles), silently misplacing one
+// element.  A volatile access is never paired.
+// The pointer is cast to the LDS address space so that the volatile access
+// stays a plain ds_write (a generic volatile store becomes a flat store with
+// a full memory wait).
+template <typename T>
+__device__ __forceinline__ void lds_put(T* p, T v) {
+    *(volatile __attribute__((address_space(3))) T*)(p) = v;
+}
 
 // exp(x) for the gate factors.  bf16 inputs use the hardware exp2 path; fp32
 // inputs use the correctly-rounded-ish library expf.

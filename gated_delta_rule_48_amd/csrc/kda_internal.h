@@ -52,6 +52,8 @@ ChunkWorkspace carve_chunk_workspace(void* base, int64_t T, int32_t N, int32_t H
 int64_t max_chunks_for(int64_t T, int32_t N);
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_chunk_fwd(const ChunkArgs& a, const ChunkWorkspace& ws, hipStream_t stream);
+// events: null, or four events recorded before map / intra / walk and after walk.
+hipError_t launch_chunk_fwd(const ChunkArgs& a, const ChunkWorkspace& ws, hipStream_t stream,
+                            hipEvent_t* events = nullptr);
 
 }  // namespace kda

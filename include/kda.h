@@ -135,6 +135,24 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v,
                          size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Same as kda_chunk_fwd, and also records the four caller-created HIP events
+ * events[0..3] on `stream`: before the chunk-map kernel, before the
+ * intra-chunk kernel, before the chunk-walk kernel and after it, so that
+ * hipEventElapsedTime gives each kernel's duration.  For profiling; `events`
+ * must hold four valid hipEvent_t (KDA_ERR_INVALID_ARG if NULL).  If
+ * T_total == 0 the intra-chunk kernel is skipped and events[1] and
+ * events[2] coincide.
+ */
+typedef struct ihipEvent_t *hipEvent_t;
+kda_status kda_chunk_fwd_instrumented(const void *q, const void *k, const void *v,
+                                      const void *g, const void *beta, const float *S0,
+                                      const int32_t *cu_seqlens, int32_t N, int64_t T_total,
+                                      int32_t H, int32_t d_k, int32_t d_v, kda_dtype dt,
+                                      kda_gate gk, void *o, float *S_T, void *workspace,
+                                      size_t workspace_bytes, hipStream_t stream,
+                                      hipEvent_t *events);
+
+/*
  * Wait for `stream` and report whether the last kda_chunk_fwd that used this
  * workspace accepted its device cu_seqlens: KDA_OK, KDA_ERR_BAD_SEQLENS (the
  * offsets were not 0 = c_0 <= ... <= c_N = T_total; nothing was written), or

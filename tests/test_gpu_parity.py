@@ -73,6 +73,20 @@ def test_chunk_small(case):
     _assert_close("S_T", S, S_ref, TOL[dtype])
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("gate", ["channel", "head"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_chunk_every_instantiation(dtype, gate, dk, dv):
+    """Every compiled kernel variant (dtype x d_k x d_v x gate mode), with a
+    ragged tail, an empty sequence and a nonzero initial state."""
+    _announce(f"instantiation {dtype} {gate} {dk}x{dv}")
+    d = chunk_case(2, dk, dv, dtype, gate, [70, 0, 129], s0_sigma=0.1, seed=dk * 3 + dv)
+    o, S = _run_chunk(d, dtype, gate)
+    o_ref, S_ref = _oracle_chunk(d, gate)
+    _assert_close("o", o, o_ref, TOL[dtype])
+    _assert_close("S_T", S, S_ref, TOL[dtype])
+
+
 def test_chunk_strong_decay_tail():
     """Gates drawn from N(+3, 1) (alpha near e^-3 per step) push the
     chunk-local log-decay to about -200 over 64 tokens: exercises the range
