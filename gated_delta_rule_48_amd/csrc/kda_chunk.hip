@@ -136,6 +136,21 @@ struct IntraLayout {
     static_assert((size_t)NBND * DK * 4 <= (size_t)C * LDA * 4, "sBnd fits in sA");
 };
 
+// Two adjacent elements as one register-sized value (raw, not yet widened).
+template <typename E> struct Pair2;
+template <> struct Pair2<bf16_t> {
+    uint32_t w;
+    __device__ __forceinline__ void load(const bf16_t* p) { w = *reinterpret_cast<const uint32_t*>(p); }
+    __device__ __forceinline__ float lo() const { return __uint_as_float(w << 16); }
+    __device__ __forceinline__ float hi() const { return __uint_as_float(w & 0xffff0000u); }
+};
+template <> struct Pair2<float> {
+    float2 w;
+    __device__ __forceinline__ void load(const float* p) { w = *reinterpret_cast<const float2*>(p); }
+    __device__ __forceinline__ float lo() const { return w.x; }
+    __device__ __forceinline__ float hi() const { return w.y; }
+};
+
 template <typename E> __device__ __forceinline__ void load2(const E* p, float& a, float& b);
 template <> __device__ __forceinline__ void load2<bf16_t>(const bf16_t* p, float& a, float& b) {
     const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
@@ -242,34 +257,49 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
     const int lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
 
-    // ---- 1. chunk-local inclusive prefix sum of the log-gate ----------------
+    // ---- 0. every global load of the chunk, issued up front ----------------
     const int cp = tid % (DK / 2), part = tid / (DK / 2);
     const int c0 = 2 * cp;
+    const int jp = tid % (DV / 2), vpart = tid / (DV / 2);
+    const int j0 = 2 * jp;
+    Pair2<E> graw[RPT], kraw[RPT], qraw[RPT], vraw[RPTV];
+    float gh[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const int row = part * RPT + r;
+        const bool ok = row < len;
+        const int64_t off = ((t0 + row) * H + h) * DK + c0;
+        if (HG) {
+            gh[r] = ok ? Elt<E>::load(g + (t0 + row) * H + h) : 0.f;
+        } else {
+            if (ok) graw[r].load(g + off); else graw[r] = Pair2<E>{};
+        }
+        if (ok) { kraw[r].load(k + off); qraw[r].load(q + off); }
+        else { kraw[r] = Pair2<E>{}; qraw[r] = Pair2<E>{}; }
+    }
+#pragma unroll
+    for (int r = 0; r < RPTV; ++r) {
+        const int row = vpart * RPTV + r;
+        if (row < len) vraw[r].load(v + ((t0 + row) * H + h) * DV + j0); else vraw[r] = Pair2<E>{};
+    }
+    const float beta_t = (tid < len) ? Elt<E>::load(beta + (t0 + tid) * H + h) : 0.f;
+
+    // ---- 1. chunk-local inclusive prefix sum of the log-gate ----------------
     float bb[RPT][2];
     {
         float run0 = 0.f, run1 = 0.f;
 #pragma unroll
         for (int r = 0; r < RPT; ++r) {
-            const int row = part * RPT + r;
-            float g0 = 0.f, g1 = 0.f;
-            if (row < len) {
-                const int64_t tok = t0 + row;
-                if (HG) {
-                    g0 = g1 = Elt<E>::load(g + tok * H + h);
-                } else {
-                    load2<E>(g + (tok * H + h) * DK + c0, g0, g1);
-                }
-            }
-            run0 += g0;
-            run1 += g1;
+            run0 += HG ? gh[r] : graw[r].lo();
+            run1 += HG ? gh[r] : graw[r].hi();
             bb[r][0] = run0;
             bb[r][1] = run1;
         }
         sPart[part * DK + c0] = run0;
         sPart[part * DK + c0 + 1] = run1;
     }
-    if (tid < C) sBeta[tid] = (tid < len) ? Elt<E>::load(beta + (t0 + tid) * H + h) : 0.f;
-    __syncthreads();
+    if (tid < C) sBeta[tid] = beta_t;
+    lds_barrier();
     {
         float off0 = 0.f, off1 = 0.f;
 #pragma unroll
@@ -291,7 +321,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     const float last0 = sBnd[11 * DK + c0], last1 = sBnd[11 * DK + c0 + 1];
 
     // ---- 2. decayed operands (every factor <= 1) and tile-pair scales -------
@@ -302,12 +332,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
         const int row = part * RPT + r;
         const float* bs = sBnd + (3 * (row >> 4)) * DK;  // tile start
         const float* be = bs + 2 * DK;                  // tile end
-        float k0 = 0.f, k1 = 0.f, q0 = 0.f, q1 = 0.f;
-        if (row < len) {
-            const int64_t off = ((t0 + row) * H + h) * DK + c0;
-            load2<E>(k + off, k0, k1);
-            load2<E>(q + off, q0, q1);
-        }
+        const float k0 = kraw[r].lo(), k1 = kraw[r].hi(), q0 = qraw[r].lo(), q1 = qraw[r].hi();
         const float e0 = gate_exp<E>(bb[r][0] - bs[c0]), e1 = gate_exp<E>(bb[r][1] - bs[c0 + 1]);
         const float f0 = gate_exp<E>(be[c0] - bb[r][0]), f1 = gate_exp<E>(be[c0 + 1] - bb[r][1]);
         const float x0 = gate_exp<E>(bb[r][0]), x1 = gate_exp<E>(bb[r][1]);
@@ -351,7 +376,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
             sRowScale[ti * DK + c] = gate_exp<E>(fminf(x, 80.f));
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- 3. A = K K^T with decay (strictly lower, row-scaled by beta) -> LDS
     //         (fp32);  P = Q K^T with decay (lower incl. diagonal) -> workspace
@@ -386,7 +411,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     {
         E* sPst = reinterpret_cast<E*>(smem + L::off_Pst);
 #pragma unroll
@@ -397,23 +422,26 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
     }
 
     // ---- 4. right-hand sides into the freed region; T = (I + A)^{-1} ---------
+    {
+        E r0[RPT], r1[RPT];
 #pragma unroll
-    for (int r = 0; r < RPT; ++r) {
-        sKbt[c0 * LDT + part * RPT + r] = Elt<E>::from(kb[r][0]);
-        sKbt[(c0 + 1) * LDT + part * RPT + r] = Elt<E>::from(kb[r][1]);
+        for (int r = 0; r < RPT; ++r) {
+            r0[r] = Elt<E>::from(kb[r][0]);
+            r1[r] = Elt<E>::from(kb[r][1]);
+        }
+        store_run<E, RPT>(sKbt + c0 * LDT + part * RPT, r0);
+        store_run<E, RPT>(sKbt + (c0 + 1) * LDT + part * RPT, r1);
     }
     {
-        const int jp = tid % (DV / 2), vpart = tid / (DV / 2);
-        const int j0 = 2 * jp;
+        E r0[RPTV], r1[RPTV];
 #pragma unroll
         for (int r = 0; r < RPTV; ++r) {
-            const int row = vpart * RPTV + r;
-            float v0 = 0.f, v1 = 0.f;
-            if (row < len) load2<E>(v + ((t0 + row) * H + h) * DV + j0, v0, v1);
-            const float bt = sBeta[row];
-            sVt[j0 * LDT + row] = Elt<E>::from(bt * v0);
-            sVt[(j0 + 1) * LDT + row] = Elt<E>::from(bt * v1);
+            const float bt = sBeta[vpart * RPTV + r];
+            r0[r] = Elt<E>::from(bt * vraw[r].lo());
+            r1[r] = Elt<E>::from(bt * vraw[r].hi());
         }
+        store_run<E, RPTV>(sVt + j0 * LDT + vpart * RPTV, r0);
+        store_run<E, RPTV>(sVt + (j0 + 1) * LDT + vpart * RPTV, r1);
     }
     // (a) the four 16x16 diagonal blocks, one column per thread of wave 0
     float x[16];
@@ -428,7 +456,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
             x[t] = (t < jc) ? 0.f : ((t == jc) ? 1.f : acc);
         }
     }
-    __syncthreads();
+    lds_barrier();
     copy_tile_out<E, C, C>(Po + ch * C * C, reinterpret_cast<const E*>(smem + L::off_Pst), L::LDP, tid);
     if (tid < 64) {
         const int blk = tid >> 4, jc = tid & 15;
@@ -436,7 +464,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
 #pragma unroll
         for (int t = 0; t < 16; ++t) Tb[t * LDA + jc] = x[t];
     }
-    __syncthreads();
+    lds_barrier();
     // (b) off-diagonal blocks, block row by block row:
     //     T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj
     {
@@ -457,7 +485,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
             }
 #pragma unroll
             for (int bj = 0; bj < bi; ++bj) sX[bj * 256 + rr * 16 + cc] = xv[bj];
-            __syncthreads();
+            lds_barrier();
 #pragma unroll
             for (int bj = 0; bj < bi; ++bj) {
                 float acc = 0.f;
@@ -466,7 +494,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
                     acc += sA[(16 * bi + rr) * LDA + 16 * bi + e] * sX[bj * 256 + e * 16 + cc];
                 sA[(16 * bi + rr) * LDA + 16 * bj + cc] = -acc;
             }
-            __syncthreads();
+            lds_barrier();
         }
     }
 
@@ -489,7 +517,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
             accU[tn] = mma(ft0, ld_frag(sVt + (16 * tn + lr) * LDT + 8 * lg), zero4());
             accU[tn] = mma(ft1, ld_frag(sVt + (16 * tn + lr) * LDT + 32 + 8 * lg), accU[tn]);
         }
-        __syncthreads();  // every wave is done with sKbt / sVt / sA
+        lds_barrier();  // every wave is done with sKbt / sVt / sA
         E* sWst = reinterpret_cast<E*>(smem);
         E* sUst = sWst + C * LDK;
 #pragma unroll
@@ -502,7 +530,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 lds_put(&sUst[(16 * ti + 4 * lg + i) * L::LDV + 16 * tn + lr], Elt<E>::from(accU[tn][i]));
-        __syncthreads();
+        lds_barrier();
         copy_tile_out<E, C, DK>(Wo + ch * C * DK, sWst, LDK, tid);
         copy_tile_out<E, C, DV>(Upo + ch * C * DV, sUst, L::LDV, tid);
     }
@@ -510,10 +538,20 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
 
 // ----------------------------------------------------------------------------
 // State walk + output.  Workgroup = (sequence n, head h, 16-column slice of
-// d_v); wave w owns token rows 16w..16w+15 of the chunk for U and O, and the
-// state rows (key channels) 16m.., m = w*MT .. w*MT+MT-1.
+// d_v) with four compute waves and one prefetch wave.  Compute wave w owns
+// token rows 16w..16w+15 of the chunk for U and O, and the state rows (key
+// channels) 16m.., m = w*MT .. w*MT+MT-1.  The chain over chunks is
+// sequential, so the operands of the next chunk are loaded into registers
+// while the current one computes, and the prefetch wave touches the cache
+// lines of the chunk kWalkPrefetch steps ahead (LDS-DMA loads into a dummy
+// buffer: no registers, its own memory counter), so that the compute waves'
+// loads hit L2.  The NS slice workgroups of one (n, h) split the shared lines
+// between them.
+constexpr int kWalkPrefetch = 6;
+constexpr int kWalkThreads = 320;
+
 template <typename E, int DK, int DV>
-__global__ __launch_bounds__(256) void chunk_walk_kernel(
+__global__ __launch_bounds__(kWalkThreads) void chunk_walk_kernel(
     const WsHeader* __restrict__ hdr, const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
     int32_t N, int32_t H, const E* __restrict__ Wi, const E* __restrict__ QGi, const E* __restrict__ KdTi,
     const E* __restrict__ Upi, const E* __restrict__ Pi, const float* __restrict__ Gni,
@@ -526,6 +564,7 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(
     constexpr int LDS_U = C + PAD;
     __shared__ __align__(16) E sSt[DVS * LDS_S];  // S slice, transposed: [col][channel]
     __shared__ __align__(16) E sUt[DVS * LDS_U];  // U slice, transposed: [col][token]
+    __shared__ __align__(16) float sSink[64];     // destination of the prefetch wave's loads
 
     if (hdr->bad_seqlens) return;
     const int64_t NH = (int64_t)N * H;
@@ -544,17 +583,56 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(
     const int n = (int)(pair / H), h = (int)(pair % H);
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
+    const bool compute = w < 4;  // wave 4 only prefetches
     const int lr = lane & 15, lg = lane >> 4;
     const int col = slice * DVS + lr;
+    const int cbeg = chunk_off[n], cend = chunk_off[n + 1];
+    const int64_t seq0 = cu[n], seqend = cu[n + 1];
+
+    // Prefetch wave: one 4-byte LDS-DMA load per 128-byte line of chunk c.
+    auto prefetch = [&](int c) {
+        if (c >= cend) return;
+        const int64_t ch = (int64_t)c * H + h;
+        constexpr int LW = C * DK * (int)sizeof(E) / 128;  // lines of W, of QG, of KdT
+        constexpr int LP = C * C * (int)sizeof(E) / 128;
+        constexpr int LG = DK * 4 / 128;
+        constexpr int NL = 3 * LW + LP + LG;
+        auto sink = (__attribute__((address_space(3))) void*)sSink;
+        for (int j = slice + NS * lane; j < NL; j += NS * 64) {
+            const char* base;
+            int off;
+            if (j < LW) { base = (const char*)(Wi + ch * C * DK); off = j; }
+            else if (j < 2 * LW) { base = (const char*)(QGi + ch * C * DK); off = j - LW; }
+            else if (j < 3 * LW) { base = (const char*)(KdTi + ch * DK * C); off = j - 2 * LW; }
+            else if (j < 3 * LW + LP) { base = (const char*)(Pi + ch * C * C); off = j - 3 * LW; }
+            else { base = (const char*)(Gni + ch * DK); off = j - 3 * LW - LP; }
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base + 128 * off),
+                                             sink, 4, 0, 0);
+        }
+        // this slice's 32-byte piece of every row of U'
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(Upi + ch * C * DV + lane * DV + slice * DVS), sink, 4,
+            0, 0);
+    };
+
+    if (!compute) {
+        // Prefetch wave: its own loop, passing the same number of barriers
+        // as the compute waves (one before the chunk loop, two per chunk).
+        // Bare s_barrier: it orders nothing in LDS, so no wait is attached.
+        for (int c = cbeg; c < cbeg + kWalkPrefetch; ++c) prefetch(c);
+        __builtin_amdgcn_s_barrier();
+        for (int c = cbeg; c < cend; ++c) {
+            prefetch(c + kWalkPrefetch);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_s_barrier();
+        }
+        // No LDS-DMA load may still be in flight when the workgroup's LDS is
+        // released.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        return;
+    }
 
     f32x4 Sreg[MT];
-#pragma unroll
-    for (int mm = 0; mm < MT; ++mm)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 16 * (w * MT + mm) + 4 * lg + i;
-            Sreg[mm][i] = S0 ? S0[(pair * DK + row) * DV + col] : 0.f;
-        }
     auto put_state = [&]() {
 #pragma unroll
         for (int mm = 0; mm < MT; ++mm)
@@ -562,11 +640,15 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(
             for (int i = 0; i < 4; ++i)
                 lds_put(&sSt[lr * LDS_S + 16 * (w * MT + mm) + 4 * lg + i], Elt<E>::from(Sreg[mm][i]));
     };
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * (w * MT + mm) + 4 * lg + i;
+            Sreg[mm][i] = S0 ? S0[(pair * DK + row) * DV + col] : 0.f;
+        }
     put_state();
-    __syncthreads();
-
-    const int cbeg = chunk_off[n], cend = chunk_off[n + 1];
-    const int64_t seq0 = cu[n], seqend = cu[n + 1];
+    lds_barrier();
 
     // Operands of one chunk as this wave needs them (register fragments).
     struct Ops {
@@ -600,6 +682,7 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(
         for (int mm = 0; mm < MT; ++mm)
             op.gn[mm] = *reinterpret_cast<const f32x4*>(Gp + 16 * (w * MT + mm) + 4 * lg);
     };
+    // One chunk (compute waves).
     auto run_chunk = [&](const Ops& op, int c) {
         // phase 1: U = U' - W S ;  O = QG S
         f32x4 accW = zero4(), accQ = zero4();
@@ -610,8 +693,9 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(
             accQ = mma(op.fQ[ks], fs, accQ);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lds_put(&sUt[lr * LDS_U + 16 * w + 4 * lg + i], Elt<E>::from(op.up[i] - accW[i]));
-        __syncthreads();
+        for (int i = 0; i < 4; ++i)
+            lds_put(&sUt[lr * LDS_U + 16 * w + 4 * lg + i], Elt<E>::from(op.up[i] - accW[i]));
+        lds_barrier();
 
         // phase 2: O += P U ;  S <- Diag(Gn) S + KdT U
         const Frag<E> fu0 = ld_frag(sUt + lr * LDS_U + 8 * lg);
@@ -636,18 +720,21 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(
             if (tok < seqend) o[(tok * H + h) * DV + col] = Elt<E>::from(O[i]);
         }
         put_state();
-        __syncthreads();
+        lds_barrier();
     };
 
     // Two operand sets in flight: chunk c+1 loads while chunk c computes.
+    // The look-ahead load is unconditional (the last chunk is reloaded at the
+    // end) so that the compiler can count outstanding loads exactly instead of
+    // waiting for all of them.
     Ops opA, opB;
     int c = cbeg;
     if (c < cend) load_ops(opA, c);
     while (c < cend) {
-        if (c + 1 < cend) load_ops(opB, c + 1);
+        load_ops(opB, min(c + 1, cend - 1));
         run_chunk(opA, c);
         if (++c >= cend) break;
-        if (c + 1 < cend) load_ops(opA, c + 1);
+        load_ops(opA, min(c + 1, cend - 1));
         run_chunk(opB, c);
         ++c;
     }
@@ -745,7 +832,7 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkWorkspace& ws, h
     }
     if ((e = mark(ev, 2, stream)) != hipSuccess) return e;
     const int64_t blocks = (int64_t)a.N * a.H * (DV / 16);
-    hipLaunchKernelGGL((chunk_walk_kernel<E, DK, DV>), dim3((unsigned)blocks), dim3(256), 0, stream, ws.header,
+    hipLaunchKernelGGL((chunk_walk_kernel<E, DK, DV>), dim3((unsigned)blocks), dim3(kWalkThreads), 0, stream, ws.header,
                        ws.cu, ws.chunk_off, a.N, a.H, (const E*)ws.W, (const E*)ws.QG, (const E*)ws.KdT,
                        (const E*)ws.Up, (const E*)ws.P, (const float*)ws.Gn, a.S0, a.S_T, (E*)a.o);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     *reinterpret_cast<float4*>(&red_r[rg][4 * cg]) = pr;
     *reinterpret_cast<float4*>(&red_s[rg][4 * cg]) = ps;
     if (cg == 0) red_qk[rg] = pqk;
-    __syncthreads();
+    lds_barrier();
 
     float4 r = make_float4(0.f, 0.f, 0.f, 0.f), s = r;
     float qk = 0.f;

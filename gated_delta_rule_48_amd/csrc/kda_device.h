@@ -115,6 +115,17 @@ __device__ __forceinline__ void lds_put(T* p, T v) {
     *(volatile __attribute__((address_space(3))) T*)(p) = v;
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also releases
+// global memory, which on gfx9 means waiting for every outstanding global
+// load (one counter covers loads and stores) and so would drain any loads
+// issued ahead of their use.  Kernels whose waves communicate only through
+// LDS use this instead.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // exp(x) for the gate factors.  bf16 inputs use the hardware exp2 path; fp32
 // inputs use the correctly-rounded-ish library expf.
 template <typename E> __device__ __forceinline__ float gate_exp(float x);
