@@ -24,7 +24,7 @@ __all__ = ["chunk_fwd", "chunk_fwd_workspace_size", "chunk_fwd_check", "recurren
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "KDA_ERR_WORKSPACE",
-          4: "KDA_ERR_HIP", 5: "KDA_ERR_BAD_SEQLENS"}
+          4: "KDA_ERR_HIP", 5: "KDA_ERR_BAD_SEQLENS", 6: "KDA_ERR_TIMEOUT"}
 _BF16, _F32 = 0, 1
 _PER_CHANNEL, _PER_HEAD = 0, 1
 

@@ -33,6 +33,7 @@ const char* kda_status_string(kda_status status) {
         case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing, misaligned or too small";
         case KDA_ERR_HIP: return "KDA_ERR_HIP: a HIP runtime call or kernel launch failed";
         case KDA_ERR_BAD_SEQLENS: return "KDA_ERR_BAD_SEQLENS: device cu_seqlens rejected";
+        case KDA_ERR_TIMEOUT: return "KDA_ERR_TIMEOUT: an internal wait between waves gave up; results unspecified";
     }
     return "KDA_ERR_UNKNOWN";
 }
@@ -104,7 +105,8 @@ kda_status kda_chunk_fwd_check(const void* workspace, hipStream_t stream) {
     if (hipStreamSynchronize(stream) != hipSuccess) return KDA_ERR_HIP;
     kda::WsHeader h;
     if (hipMemcpy(&h, workspace, sizeof h, hipMemcpyDeviceToHost) != hipSuccess) return KDA_ERR_HIP;
-    return h.bad_seqlens ? KDA_ERR_BAD_SEQLENS : KDA_OK;
+    if (h.bad_seqlens) return KDA_ERR_BAD_SEQLENS;
+    return h.wait_timeout ? KDA_ERR_TIMEOUT : KDA_OK;
 }
 
 kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const void* g, const void* beta,

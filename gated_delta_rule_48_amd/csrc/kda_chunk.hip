@@ -85,6 +85,7 @@ __global__ __launch_bounds__(256) void chunk_map_kernel(const int32_t* __restric
         chunk_off[N] = carry;
         hdr->total_chunks = isbad ? 0 : carry;
         hdr->bad_seqlens = isbad;
+        hdr->wait_timeout = 0;
     }
 }
 
@@ -125,7 +126,7 @@ struct IntraLayout {
     static constexpr size_t off_Pst = off_X + 3 * 256 * 4;
     static constexpr size_t r1_a = (size_t)3 * C * LDK * sizeof(E);
     static constexpr size_t r1_b = off_Pst + (size_t)C * LDP * sizeof(E);
-    static constexpr size_t r1_c = (size_t)C * (LDK + LDV) * sizeof(E);
+    static constexpr size_t r1_c = ((size_t)C * LDK + (size_t)DV * LDT) * sizeof(E);
     static constexpr size_t r1_max = r1_a > r1_b ? (r1_a > r1_c ? r1_a : r1_c) : (r1_b > r1_c ? r1_b : r1_c);
     static constexpr size_t off_A = (r1_max + 15) / 16 * 16;  // sA; sBnd before A
     static constexpr size_t off_beta = off_A + (size_t)C * LDA * 4;
@@ -184,6 +185,16 @@ __device__ __forceinline__ void store_run(E* dst, const E (&vals)[N]) {
     }
 }
 
+// Store 4 contiguous elements (8 bytes for bf16, 16 for fp32).
+template <typename E> __device__ __forceinline__ void store_run4(E* dst, const E* vals);
+template <> __device__ __forceinline__ void store_run4<bf16_t>(bf16_t* dst, const bf16_t* v) {
+    *reinterpret_cast<uint2*>(dst) = make_uint2((uint32_t)v[0] | ((uint32_t)v[1] << 16),
+                                                (uint32_t)v[2] | ((uint32_t)v[3] << 16));
+}
+template <> __device__ __forceinline__ void store_run4<float>(float* dst, const float* v) {
+    *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+}
+
 // Copy a ROWS x COLS tile from LDS (row stride lds_ld elements) to a dense
 // global tile with 16-byte loads and stores spread over the 256 threads.
 template <typename E, int ROWS, int COLS>
@@ -194,6 +205,44 @@ __device__ __forceinline__ void copy_tile_out(E* __restrict__ dst, const E* src,
     for (int i = tid; i < ROWS * VPR; i += 256) {
         const int r = i / VPR, c = (i % VPR) * PER;
         *reinterpret_cast<uint4*>(dst + r * COLS + c) = *reinterpret_cast<const uint4*>(src + r * lds_ld + c);
+    }
+}
+
+// Position at which index x of a reduction dimension is stored so that the
+// chunk walk can feed accumulator registers straight back into the matrix
+// cores.  Within each block of 32, x = 16h + 4a + b is stored at 8a + 4h + b:
+// an A fragment read as 8 contiguous elements at 8g then holds indices
+// {4g..4g+3, 16+4g..16+4g+3}, which are exactly the rows a lane holds in the
+// accumulators of the two 16-row tiles of that block.
+__device__ __forceinline__ int frag_pos(int x) {
+    return (x & ~31) | ((x & 12) << 1) | ((x & 16) >> 2) | (x & 3);
+}
+
+// Fragment-major storage of an R x K operand whose K index is already in
+// fragment order: each 16 x 32 block is stored as 64 lanes x 8 contiguous
+// elements, lane = (row % 16) + 16 * ((col % 32) / 8), so that one fragment
+// load of a wave reads 1 KB (bf16) of contiguous memory.
+template <int K>
+__device__ __forceinline__ int64_t fm_off(int row, int colpos) {
+    const int lane = (row & 15) | (((colpos >> 3) & 3) << 4);
+    return ((int64_t)((row >> 4) * (K / 32) + (colpos >> 5)) * 64 + lane) * 8 + (colpos & 7);
+}
+
+// Copy an R x K tile held row-major in LDS (K already in fragment order) to
+// fragment-major global memory: thread i writes the i-th 16-byte piece.
+template <typename E, int R, int K>
+__device__ __forceinline__ void copy_tile_out_frag(E* __restrict__ dst, const E* src, int lds_ld, int tid) {
+    constexpr int PER = 16 / (int)sizeof(E);  // elements per 16-byte piece
+    constexpr int PIECES = R * K / PER;
+#pragma unroll
+    for (int i = tid; i < PIECES; i += 256) {
+        // piece i covers lane-part (i % (8 / PER)) of lane (i / (8 / PER)) % 64 of block i / (64 * 8 / PER)
+        const int sub = i % (8 / PER);
+        const int lane = (i / (8 / PER)) % 64;
+        const int blk = i / (64 * 8 / PER);
+        const int row = 16 * (blk / (K / 32)) + (lane & 15);
+        const int col = 32 * (blk % (K / 32)) + 8 * (lane >> 4) + sub * PER;
+        *reinterpret_cast<uint4*>(dst + (int64_t)i * PER) = *reinterpret_cast<const uint4*>(src + row * lds_ld + col);
     }
 }
 
@@ -340,7 +389,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
         store2<E>(sKr + row * LDK + c0, k0 * e0, k1 * e1);
         store2<E>(sQr + row * LDK + c0, q0 * e0, q1 * e1);
         store2<E>(sKt + row * LDK + c0, k0 * f0, k1 * f1);
-        store2<E>(QGo + (ch * C + row) * DK + c0, q0 * x0, q1 * x1);
+        store2<E>(QGo + ch * C * DK + fm_off<DK>(row, frag_pos(c0)), q0 * x0, q1 * x1);
         const float bt = sBeta[row];
         kb[r][0] = bt * k0 * x0;
         kb[r][1] = bt * k1 * x1;
@@ -348,9 +397,13 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
         kd1[r] = Elt<E>::from(k1 * d1);
     }
     {
-        E* p0 = KdTo + (ch * DK + c0) * C + part * RPT;
-        store_run<E, RPT>(p0, kd0);
-        store_run<E, RPT>(p0 + C, kd1);
+        E* p0 = KdTo + ch * DK * C;
+#pragma unroll
+        for (int r4 = 0; r4 < RPT / 4; ++r4) {
+            const int pos = frag_pos(part * RPT + 4 * r4);  // 4 consecutive tokens stay contiguous
+            store_run4<E>(p0 + fm_off<C>(c0, pos), kd0 + 4 * r4);
+            store_run4<E>(p0 + fm_off<C>(c0 + 1, pos), kd1 + 4 * r4);
+        }
         if (part == 0) {
             Gno[ch * DK + c0] = gate_exp<E>(last0);
             Gno[ch * DK + c0 + 1] = gate_exp<E>(last1);
@@ -418,7 +471,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
         for (int tj = 0; tj < 4; ++tj)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                lds_put(&sPst[(16 * wave + 4 * lg + i) * L::LDP + 16 * tj + lr], Elt<E>::from(accPt[tj][i]));
+                lds_put(&sPst[(16 * wave + 4 * lg + i) * L::LDP + frag_pos(16 * tj + lr)], Elt<E>::from(accPt[tj][i]));
     }
 
     // ---- 4. right-hand sides into the freed region; T = (I + A)^{-1} ---------
@@ -457,7 +510,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
         }
     }
     lds_barrier();
-    copy_tile_out<E, C, C>(Po + ch * C * C, reinterpret_cast<const E*>(smem + L::off_Pst), L::LDP, tid);
+    copy_tile_out_frag<E, C, C>(Po + ch * C * C, reinterpret_cast<const E*>(smem + L::off_Pst), L::LDP, tid);
     if (tid < 64) {
         const int blk = tid >> 4, jc = tid & 15;
         float* Tb = sA + (16 * blk) * LDA + 16 * blk;
@@ -517,54 +570,114 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
             accU[tn] = mma(ft0, ld_frag(sVt + (16 * tn + lr) * LDT + 8 * lg), zero4());
             accU[tn] = mma(ft1, ld_frag(sVt + (16 * tn + lr) * LDT + 32 + 8 * lg), accU[tn]);
         }
+        // U' for the walk: per 16-column slice tn and lane, the 16 values the
+        // lane holds in the walk's accumulator layout (token tiles ti = 0..3,
+        // rows 4 lg + i), contiguous: [tn][lane][ti][i].
+        {
+            E* up = Upo + ch * C * DV;
+#pragma unroll
+            for (int tn = 0; tn < DV / 16; ++tn) {
+                E vals[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) vals[i] = Elt<E>::from(accU[tn][i]);
+                store_run4<E>(up + (tn * 64 + lane) * 16 + 4 * ti, vals);
+            }
+        }
         lds_barrier();  // every wave is done with sKbt / sVt / sA
-        E* sWst = reinterpret_cast<E*>(smem);
-        E* sUst = sWst + C * LDK;
+        E* sWst = reinterpret_cast<E*>(smem);  // [C][DK], channel columns in fragment order
 #pragma unroll
         for (int tn = 0; tn < DK / 16; ++tn)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                lds_put(&sWst[(16 * ti + 4 * lg + i) * LDK + 16 * tn + lr], Elt<E>::from(accW[tn][i]));
-#pragma unroll
-        for (int tn = 0; tn < DV / 16; ++tn)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                lds_put(&sUst[(16 * ti + 4 * lg + i) * L::LDV + 16 * tn + lr], Elt<E>::from(accU[tn][i]));
+                lds_put(&sWst[(16 * ti + 4 * lg + i) * LDK + frag_pos(16 * tn + lr)], Elt<E>::from(accW[tn][i]));
         lds_barrier();
-        copy_tile_out<E, C, DK>(Wo + ch * C * DK, sWst, LDK, tid);
-        copy_tile_out<E, C, DV>(Upo + ch * C * DV, sUst, L::LDV, tid);
+        copy_tile_out_frag<E, C, DK>(Wo + ch * C * DK, sWst, LDK, tid);
     }
 }
 
 // ----------------------------------------------------------------------------
-// State walk + output.  Workgroup = (sequence n, head h, 16-column slice of
-// d_v) with four compute waves and one prefetch wave.  Compute wave w owns
-// token rows 16w..16w+15 of the chunk for U and O, and the state rows (key
-// channels) 16m.., m = w*MT .. w*MT+MT-1.  The chain over chunks is
-// sequential, so the operands of the next chunk are loaded into registers
-// while the current one computes, and the prefetch wave touches the cache
-// lines of the chunk kWalkPrefetch steps ahead (LDS-DMA loads into a dummy
-// buffer: no registers, its own memory counter), so that the compute waves'
-// loads hit L2.  The NS slice workgroups of one (n, h) split the shared lines
-// between them.
-constexpr int kWalkPrefetch = 6;
-constexpr int kWalkThreads = 320;
+// State walk + output.  One workgroup per (sequence n, head h, 16-column slice
+// of d_v), three waves that never meet at a barrier:
+//   wave 0 (chain)   keeps the fp32 d_k x 16 slice of S in accumulator
+//                    registers and walks the chunks: U = U' - W S, then
+//                    S <- Diag(Gn) S + KdT U.  The bf16 (or fp32) fragments of
+//                    S and U it builds for its own products are also handed to
+//                    wave 1 through a ring of kRing slots in LDS.
+//   wave 1 (output)  O = QG S + P U for each chunk from those fragments.
+//   wave 2 (prefetch) touches the cache lines of the chunks up to
+//                    kWalkPrefetch ahead of wave 0 (LDS-DMA loads into a sink:
+//                    no registers), so that waves 0 and 1 find them in L2.
+// Waves 0 and 1 load every operand of the next chunk right after the current
+// one has consumed it.  Hand-over is by two LDS progress counters; every wait
+// is bounded by kSpinLimit sleeps, past which the wave records a timeout in
+// the workspace header and proceeds (results are then unspecified).
+// Operands W, QG (channel columns) and KdT, P (token columns) are stored in
+// fragment order (frag_pos), so accumulator registers serve directly as the B
+// fragment of the next product, and fragment-major (fm_off), so every
+// fragment load is one contiguous 1 KB read; U' is stored per slice in the
+// accumulator layout of the walk's lanes.
+constexpr int kRing = 4;
+#ifndef KDA_WALK_PREFETCH
+#define KDA_WALK_PREFETCH 4
+#endif
+constexpr int kWalkPrefetch = KDA_WALK_PREFETCH;
+constexpr int kWalkThreads = 192;
+constexpr int kSpinLimit = 1 << 22;
+
+__device__ __forceinline__ int lds_read_int(const int* p) {
+    return *(volatile const __attribute__((address_space(3))) int*)(p);
+}
+
+// Accumulator tiles a (rows 0..15 of a 32-block) and b (rows 16..31) of one
+// lane -> the B fragment of that 32-block (see frag_pos).
+__device__ __forceinline__ Frag<bf16_t> acc_to_frag(bf16_t, f32x4 a, f32x4 b) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 w = {f32x2_to_bf16x2(a[0], a[1]), f32x2_to_bf16x2(a[2], a[3]), f32x2_to_bf16x2(b[0], b[1]),
+                     f32x2_to_bf16x2(b[2], b[3])};
+    Frag<bf16_t> f;
+    f.v = __builtin_bit_cast(u16x8, w);
+    return f;
+}
+__device__ __forceinline__ Frag<float> acc_to_frag(float, f32x4 a, f32x4 b) {
+    Frag<float> f;
+    f.v = f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return f;
+}
+
+// Four consecutive elements -> fp32 (8 bytes of bf16 or 16 bytes of fp32).
+__device__ __forceinline__ f32x4 load4(const bf16_t* p) {
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+                 __uint_as_float(w.y & 0xffff0000u)};
+}
+__device__ __forceinline__ f32x4 load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
+// 16-column tiles of d_v per workgroup (wider slices halve the L2 traffic of
+// W, QG, KdT, P but were measured slower: the chain is bound by per-wave
+// work, not by L2).
+template <typename E> struct WalkCols { static constexpr int NC = 1; };
+template <> struct WalkCols<float> { static constexpr int NC = 1; };
 
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(kWalkThreads) void chunk_walk_kernel(
-    const WsHeader* __restrict__ hdr, const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
-    int32_t N, int32_t H, const E* __restrict__ Wi, const E* __restrict__ QGi, const E* __restrict__ KdTi,
-    const E* __restrict__ Upi, const E* __restrict__ Pi, const float* __restrict__ Gni,
+    WsHeader* __restrict__ hdr, const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off, int32_t N,
+    int32_t H, const E* __restrict__ Wi, const E* __restrict__ QGi, const E* __restrict__ KdTi,
+    const E* __restrict__ UpTi, const E* __restrict__ Pi, const float* __restrict__ Gni,
     const float* __restrict__ S0, float* __restrict__ S_T, E* __restrict__ o) {
-    constexpr int C = kChunk, DVS = 16, NS = DV / DVS;
-    constexpr int MT = DK / 64;  // state row tiles per wave
-    constexpr int KS = DK / 32;  // k-blocks over channels
-    constexpr int PAD = 16 / (int)sizeof(E);
-    constexpr int LDS_S = DK + PAD;
-    constexpr int LDS_U = C + PAD;
-    __shared__ __align__(16) E sSt[DVS * LDS_S];  // S slice, transposed: [col][channel]
-    __shared__ __align__(16) E sUt[DVS * LDS_U];  // U slice, transposed: [col][token]
-    __shared__ __align__(16) float sSink[64];     // destination of the prefetch wave's loads
+    constexpr int C = kChunk;
+    constexpr int NC = WalkCols<E>::NC;
+    constexpr int DVS = 16 * NC, NS = DV / DVS;
+    constexpr int MT = DK / 16;  // 16-row tiles of the state slice
+    constexpr int KS = DK / 32;  // 32-blocks over channels
+    constexpr int TT = C / 16;   // 16-row tiles of tokens
+    constexpr int KB = C / 32;   // 32-blocks over tokens
+    constexpr int LDO = DVS + 16 / (int)sizeof(E);
+    __shared__ __align__(16) Frag<E> ringS[kRing][KS][NC][64];
+    __shared__ __align__(16) Frag<E> ringU[kRing][KB][NC][64];
+    __shared__ __align__(16) E sO[C * LDO];  // output wave: one chunk of O, row-major
+    __shared__ int progA;  // chunks published by wave 0 (absolute index of the next one)
+    __shared__ int doneB;  // chunks consumed by wave 1
+    __shared__ __align__(16) float sSink[64];
 
     if (hdr->bad_seqlens) return;
     const int64_t NH = (int64_t)N * H;
@@ -583,48 +696,60 @@ __global__ __launch_bounds__(kWalkThreads) void chunk_walk_kernel(
     const int n = (int)(pair / H), h = (int)(pair % H);
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
-    const bool compute = w < 4;  // wave 4 only prefetches
     const int lr = lane & 15, lg = lane >> 4;
-    const int col = slice * DVS + lr;
+    const int col0 = slice * DVS;
     const int cbeg = chunk_off[n], cend = chunk_off[n + 1];
     const int64_t seq0 = cu[n], seqend = cu[n + 1];
+    if (tid == 0) {
+        progA = cbeg;
+        doneB = cbeg;
+    }
+    lds_barrier();  // the only barrier: counters initialised before any wave reads them
 
-    // Prefetch wave: one 4-byte LDS-DMA load per 128-byte line of chunk c.
-    auto prefetch = [&](int c) {
-        if (c >= cend) return;
-        const int64_t ch = (int64_t)c * H + h;
+    auto wait_until = [&](const int* counter, int target) {
+        for (int spins = 0; lds_read_int(counter) < target; ++spins) {
+            if (spins >= kSpinLimit) {
+                hdr->wait_timeout = 1;
+                return;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    };
+    auto publish = [&](int* counter, int value) {
+        // prior LDS traffic of this wave completes before the counter moves
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        if (lane == 0) *(volatile __attribute__((address_space(3))) int*)(counter) = value;
+    };
+    auto chunk_base = [&](int c) { return (int64_t)c * H + h; };
+
+    if (w == 2) {
+        // ---------------- prefetch wave ----------------
         constexpr int LW = C * DK * (int)sizeof(E) / 128;  // lines of W, of QG, of KdT
         constexpr int LP = C * C * (int)sizeof(E) / 128;
         constexpr int LG = DK * 4 / 128;
         constexpr int NL = 3 * LW + LP + LG;
+        constexpr int LU = NC * 64 * 16 * (int)sizeof(E) / 128;  // this slice's part of U'
+        static_assert(LU <= 64, "one load per lane");
         auto sink = (__attribute__((address_space(3))) void*)sSink;
-        for (int j = slice + NS * lane; j < NL; j += NS * 64) {
-            const char* base;
-            int off;
-            if (j < LW) { base = (const char*)(Wi + ch * C * DK); off = j; }
-            else if (j < 2 * LW) { base = (const char*)(QGi + ch * C * DK); off = j - LW; }
-            else if (j < 3 * LW) { base = (const char*)(KdTi + ch * DK * C); off = j - 2 * LW; }
-            else if (j < 3 * LW + LP) { base = (const char*)(Pi + ch * C * C); off = j - 3 * LW; }
-            else { base = (const char*)(Gni + ch * DK); off = j - 3 * LW - LP; }
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base + 128 * off),
-                                             sink, 4, 0, 0);
-        }
-        // this slice's 32-byte piece of every row of U'
-        __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void*)(Upi + ch * C * DV + lane * DV + slice * DVS), sink, 4,
-            0, 0);
-    };
-
-    if (!compute) {
-        // Prefetch wave: its own loop, passing the same number of barriers
-        // as the compute waves (one before the chunk loop, two per chunk).
-        // Bare s_barrier: it orders nothing in LDS, so no wait is attached.
-        for (int c = cbeg; c < cbeg + kWalkPrefetch; ++c) prefetch(c);
-        __builtin_amdgcn_s_barrier();
         for (int c = cbeg; c < cend; ++c) {
-            prefetch(c + kWalkPrefetch);
-            __builtin_amdgcn_s_barrier();
-            __builtin_amdgcn_s_barrier();
+            wait_until(&progA, c - kWalkPrefetch + 1);
+            const int64_t ch = chunk_base(c);
+            for (int j = slice + NS * lane; j < NL; j += NS * 64) {
+                const char* base;
+                int off;
+                if (j < LW) { base = (const char*)(Wi + ch * C * DK); off = j; }
+                else if (j < 2 * LW) { base = (const char*)(QGi + ch * C * DK); off = j - LW; }
+                else if (j < 3 * LW) { base = (const char*)(KdTi + ch * DK * C); off = j - 2 * LW; }
+                else if (j < 3 * LW + LP) { base = (const char*)(Pi + ch * C * C); off = j - 3 * LW; }
+                else { base = (const char*)(Gni + ch * DK); off = j - 3 * LW - LP; }
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base + 128 * off),
+                                                 sink, 4, 0, 0);
+            }
+            if (lane < LU) {
+                const char* up = (const char*)(UpTi + ch * DV * C + slice * NC * 64 * 16);
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(up + 128 * lane),
+                                                 sink, 4, 0, 0);
+            }
         }
         // No LDS-DMA load may still be in flight when the workgroup's LDS is
         // released.
@@ -632,120 +757,181 @@ __global__ __launch_bounds__(kWalkThreads) void chunk_walk_kernel(
         return;
     }
 
-    f32x4 Sreg[MT];
-    auto put_state = [&]() {
+    if (w == 0) {
+        // ---------------- chain wave ----------------
+        f32x4 Sreg[MT][NC];
+        if (S0) {
 #pragma unroll
-        for (int mm = 0; mm < MT; ++mm)
+            for (int m = 0; m < MT; ++m)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                lds_put(&sSt[lr * LDS_S + 16 * (w * MT + mm) + 4 * lg + i], Elt<E>::from(Sreg[mm][i]));
-    };
+                for (int j = 0; j < NC; ++j)
 #pragma unroll
-    for (int mm = 0; mm < MT; ++mm)
+                    for (int i = 0; i < 4; ++i)
+                        Sreg[m][j][i] = S0[(pair * DK + 16 * m + 4 * lg + i) * DV + col0 + 16 * j + lr];
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 16 * (w * MT + mm) + 4 * lg + i;
-            Sreg[mm][i] = S0 ? S0[(pair * DK + row) * DV + col] : 0.f;
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int j = 0; j < NC; ++j) Sreg[m][j] = zero4();
         }
-    put_state();
-    lds_barrier();
-
-    // Operands of one chunk as this wave needs them (register fragments).
-    struct Ops {
-        Frag<E> fW[KS], fQ[KS], fP[2], fK[MT][2];
-        float up[4];
-        f32x4 gn[MT];
-    };
-    auto load_ops = [&](Ops& op, int c) {
-        const int64_t ch = (int64_t)c * H + h;
-        const E* Wp = Wi + ch * C * DK;
-        const E* Qp = QGi + ch * C * DK;
-        const E* Kp = KdTi + ch * DK * C;
-        const E* Up = Upi + ch * C * DV;
-        const E* Pp = Pi + ch * C * C;
-        const float* Gp = Gni + ch * DK;
+        Frag<E> fW[TT][KS], fK[MT][KB];
+        f32x4 up[TT][NC], gn[MT];
+        auto load_w = [&](int c) {
+            const E* Wp = Wi + chunk_base(c) * C * DK;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            op.fW[ks] = ld_frag(Wp + (16 * w + lr) * DK + 32 * ks + 8 * lg);
-            op.fQ[ks] = ld_frag(Qp + (16 * w + lr) * DK + 32 * ks + 8 * lg);
+            for (int t = 0; t < TT; ++t)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) fW[t][ks] = ld_frag(Wp + ((t * KS + ks) * 64 + lane) * 8);
+        };
+        auto load_rest = [&](int c) {
+            const int64_t ch = chunk_base(c);
+            const E* Kp = KdTi + ch * DK * C;
+            const E* Up = UpTi + ch * DV * C + (slice * NC * 64 + lane) * 16;
+            const float* Gp = Gni + ch * DK;
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) fK[m][kb] = ld_frag(Kp + ((m * KB + kb) * 64 + lane) * 8);
+#pragma unroll
+            for (int t = 0; t < TT; ++t)
+#pragma unroll
+                for (int j = 0; j < NC; ++j) up[t][j] = load4(Up + j * 64 * 16 + 4 * t);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) gn[m] = *reinterpret_cast<const f32x4*>(Gp + 16 * m + 4 * lg);
+        };
+        if (cbeg < cend) {
+            load_w(cbeg);
+            load_rest(cbeg);
         }
+        for (int c = cbeg; c < cend; ++c) {
+            const int slot = (c - cbeg) % kRing;
+            const int nxt = min(c + 1, cend - 1);
+            const int freeB = lds_read_int(&doneB);  // read early; checked after the products
+            Frag<E> sf[KS][NC];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) op.fP[kb] = ld_frag(Pp + (16 * w + lr) * C + 32 * kb + 8 * lg);
+            for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int mm = 0; mm < MT; ++mm)
+                for (int j = 0; j < NC; ++j) sf[ks][j] = acc_to_frag(E{}, Sreg[2 * ks][j], Sreg[2 * ks + 1][j]);
+            // U = U' - W S
+            f32x4 X[TT][NC];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                op.fK[mm][kb] = ld_frag(Kp + (16 * (w * MT + mm) + lr) * C + 32 * kb + 8 * lg);
+            for (int t = 0; t < TT; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) op.up[i] = Elt<E>::load(Up + (16 * w + 4 * lg + i) * DV + col);
+                for (int j = 0; j < NC; ++j) X[t][j] = zero4();
 #pragma unroll
-        for (int mm = 0; mm < MT; ++mm)
-            op.gn[mm] = *reinterpret_cast<const f32x4*>(Gp + 16 * (w * MT + mm) + 4 * lg);
-    };
-    // One chunk (compute waves).
-    auto run_chunk = [&](const Ops& op, int c) {
-        // phase 1: U = U' - W S ;  O = QG S
-        f32x4 accW = zero4(), accQ = zero4();
+            for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const Frag<E> fs = ld_frag(sSt + lr * LDS_S + 32 * ks + 8 * lg);
-            accW = mma(op.fW[ks], fs, accW);
-            accQ = mma(op.fQ[ks], fs, accQ);
+                for (int t = 0; t < TT; ++t)
+#pragma unroll
+                    for (int j = 0; j < NC; ++j) X[t][j] = mma(fW[t][ks], sf[ks][j], X[t][j]);
+            load_w(nxt);
+            Frag<E> uf[KB][NC];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int j = 0; j < NC; ++j)
+                    uf[kb][j] = acc_to_frag(E{}, up[2 * kb][j] - X[2 * kb][j], up[2 * kb + 1][j] - X[2 * kb + 1][j]);
+            // hand S and U to the output wave once its slot is free
+            if (freeB < c - kRing + 1) wait_until(&doneB, c - kRing + 1);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int j = 0; j < NC; ++j) ringS[slot][ks][j][lane] = sf[ks][j];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int j = 0; j < NC; ++j) ringU[slot][kb][j][lane] = uf[kb][j];
+            // S <- Diag(Gn) S + KdT U  (the ring writes drain meanwhile)
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int j = 0; j < NC; ++j) Sreg[m][j] = gn[m] * Sreg[m][j];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+#pragma unroll
+                    for (int j = 0; j < NC; ++j) Sreg[m][j] = mma(fK[m][kb], uf[kb][j], Sreg[m][j]);
+            publish(&progA, c + 1);
+            load_rest(nxt);
         }
+        if (S_T) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            lds_put(&sUt[lr * LDS_U + 16 * w + 4 * lg + i], Elt<E>::from(op.up[i] - accW[i]));
-        lds_barrier();
-
-        // phase 2: O += P U ;  S <- Diag(Gn) S + KdT U
-        const Frag<E> fu0 = ld_frag(sUt + lr * LDS_U + 8 * lg);
-        const Frag<E> fu1 = ld_frag(sUt + lr * LDS_U + 32 + 8 * lg);
-        // (P is exactly zero above its diagonal, so the second k-block adds
-        // exact zeros for w < 2)
-        f32x4 O = mma(op.fP[0], fu0, accQ);
-        O = mma(op.fP[1], fu1, O);
+            for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int mm = 0; mm < MT; ++mm) {
-            f32x4 acc;
+                for (int j = 0; j < NC; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = op.gn[mm][i] * Sreg[mm][i];
-            acc = mma(op.fK[mm][0], fu0, acc);
-            acc = mma(op.fK[mm][1], fu1, acc);
-            Sreg[mm] = acc;
+                    for (int i = 0; i < 4; ++i)
+                        S_T[(pair * DK + 16 * m + 4 * lg + i) * DV + col0 + 16 * j + lr] = Sreg[m][j][i];
         }
-        const int64_t tok0 = seq0 + (int64_t)(c - cbeg) * C;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t tok = tok0 + 16 * w + 4 * lg + i;
-            if (tok < seqend) o[(tok * H + h) * DV + col] = Elt<E>::from(O[i]);
-        }
-        put_state();
-        lds_barrier();
-    };
-
-    // Two operand sets in flight: chunk c+1 loads while chunk c computes.
-    // The look-ahead load is unconditional (the last chunk is reloaded at the
-    // end) so that the compiler can count outstanding loads exactly instead of
-    // waiting for all of them.
-    Ops opA, opB;
-    int c = cbeg;
-    if (c < cend) load_ops(opA, c);
-    while (c < cend) {
-        load_ops(opB, min(c + 1, cend - 1));
-        run_chunk(opA, c);
-        if (++c >= cend) break;
-        load_ops(opA, min(c + 1, cend - 1));
-        run_chunk(opB, c);
-        ++c;
+        return;
     }
-    if (S_T) {
+
+    // ---------------- output wave (w == 1) ----------------
+    Frag<E> fQ[TT][KS], fP[TT][KB];
+    auto load_qp = [&](int c) {
+        const int64_t ch = chunk_base(c);
+        const E* Qp = QGi + ch * C * DK;
+        const E* Pp = Pi + ch * C * C;
 #pragma unroll
-        for (int mm = 0; mm < MT; ++mm)
+        for (int t = 0; t < TT; ++t) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * (w * MT + mm) + 4 * lg + i;
-                S_T[(pair * DK + row) * DV + col] = Sreg[mm][i];
-            }
+            for (int ks = 0; ks < KS; ++ks) fQ[t][ks] = ld_frag(Qp + ((t * KS + ks) * 64 + lane) * 8);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) fP[t][kb] = ld_frag(Pp + ((t * KB + kb) * 64 + lane) * 8);
+        }
+    };
+    if (cbeg < cend) load_qp(cbeg);
+    for (int c = cbeg; c < cend; ++c) {
+        const int slot = (c - cbeg) % kRing;
+        wait_until(&progA, c + 1);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+        Frag<E> sf[KS][NC], uf[KB][NC];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int j = 0; j < NC; ++j) sf[ks][j] = ringS[slot][ks][j][lane];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int j = 0; j < NC; ++j) uf[kb][j] = ringU[slot][kb][j][lane];
+        publish(&doneB, c + 1);  // the reads above have completed
+        f32x4 O[TT][NC];
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int j = 0; j < NC; ++j) O[t][j] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int t = 0; t < TT; ++t)
+#pragma unroll
+                for (int j = 0; j < NC; ++j) O[t][j] = mma(fQ[t][ks], sf[ks][j], O[t][j]);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int t = 0; t < TT; ++t)
+#pragma unroll
+                for (int j = 0; j < NC; ++j) O[t][j] = mma(fP[t][kb], uf[kb][j], O[t][j]);
+        load_qp(min(c + 1, cend - 1));
+        // transpose through LDS so that each lane stores one token row of
+        // the slice (DVS contiguous outputs) with 16-byte stores
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int j = 0; j < NC; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    lds_put(&sO[(16 * t + 4 * lg + i) * LDO + 16 * j + lr], Elt<E>::from(O[t][j][i]));
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+        const int64_t tok = seq0 + (int64_t)(c - cbeg) * C + lane;
+        if (tok < seqend) {
+            const uint4* srow = reinterpret_cast<const uint4*>(sO + lane * LDO);
+            uint4* drow = reinterpret_cast<uint4*>(o + (tok * H + h) * DV + col0);
+#pragma unroll
+            for (int b = 0; b < DVS * (int)sizeof(E) / 16; ++b) drow[b] = srow[b];
+        }
     }
 }
 
@@ -831,7 +1017,7 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkWorkspace& ws, h
         if (e != hipSuccess) return e;
     }
     if ((e = mark(ev, 2, stream)) != hipSuccess) return e;
-    const int64_t blocks = (int64_t)a.N * a.H * (DV / 16);
+    const int64_t blocks = (int64_t)a.N * a.H * (DV / (16 * WalkCols<E>::NC));
     hipLaunchKernelGGL((chunk_walk_kernel<E, DK, DV>), dim3((unsigned)blocks), dim3(kWalkThreads), 0, stream, ws.header,
                        ws.cu, ws.chunk_off, a.N, a.H, (const E*)ws.W, (const E*)ws.QG, (const E*)ws.KdT,
                        (const E*)ws.Up, (const E*)ws.P, (const float*)ws.Gn, a.S0, a.S_T, (E*)a.o);

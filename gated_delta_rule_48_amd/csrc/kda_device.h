@@ -136,6 +136,7 @@ template <> __device__ __forceinline__ float gate_exp<float>(float x) { return e
 struct WsHeader {
     int32_t bad_seqlens;   // nonzero: cu_seqlens rejected, every later kernel exits
     int32_t total_chunks;  // number of chunks over all sequences
+    int32_t wait_timeout;  // nonzero: a bounded inter-wave wait gave up
 };
 
 }  // namespace kda

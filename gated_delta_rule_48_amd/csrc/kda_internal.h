@@ -25,11 +25,14 @@ struct ChunkWorkspace {
     WsHeader* header;     // flag + chunk count
     int32_t* cu;          // [N+1] sequence offsets (copied or synthesised)
     int32_t* chunk_off;   // [N+1] first chunk of each sequence
-    void* W;              // [max_chunks, H, C, dk]   T (beta K exp(b))
-    void* QG;             // [max_chunks, H, C, dk]   Q exp(b)
-    void* KdT;            // [max_chunks, H, dk, C]   (K exp(b_last - b))^T
-    void* Up;             // [max_chunks, H, C, dv]   T (beta V)
-    void* P;              // [max_chunks, H, C, C]    masked intra-chunk Q K^T with decay
+    // Per chunk and head.  "fragment-major": the reduction index is permuted
+    // by frag_pos() and every 16 x 32 block is stored as 64 lanes x 8
+    // contiguous elements (fm_off()).
+    void* W;              // C x dk,  T (beta K exp(b)), fragment-major
+    void* QG;             // C x dk,  Q exp(b), fragment-major
+    void* KdT;            // dk x C,  (K exp(b_last - b))^T, fragment-major
+    void* Up;             // dv x C values of T (beta V): [dv/16][64 lanes][16]
+    void* P;              // C x C,   masked intra-chunk Q K^T with decay, fragment-major
     float* Gn;            // [max_chunks, H, dk]      exp(b_last)
 };
 

@@ -72,7 +72,8 @@ typedef enum {
     KDA_ERR_UNSUPPORTED = 2,
     KDA_ERR_WORKSPACE = 3,
     KDA_ERR_HIP = 4,
-    KDA_ERR_BAD_SEQLENS = 5
+    KDA_ERR_BAD_SEQLENS = 5,
+    KDA_ERR_TIMEOUT = 6
 } kda_status;
 
 typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
@@ -153,10 +154,12 @@ kda_status kda_chunk_fwd_instrumented(const void *q, const void *k, const void *
                                       hipEvent_t *events);
 
 /*
- * Wait for `stream` and report whether the last kda_chunk_fwd that used this
- * workspace accepted its device cu_seqlens: KDA_OK, KDA_ERR_BAD_SEQLENS (the
- * offsets were not 0 = c_0 <= ... <= c_N = T_total; nothing was written), or
- * KDA_ERR_HIP if synchronisation fails.  Optional; it synchronises the host.
+ * Wait for `stream` and report how the last kda_chunk_fwd that used this
+ * workspace went on the device: KDA_OK; KDA_ERR_BAD_SEQLENS (the offsets were
+ * not 0 = c_0 <= ... <= c_N = T_total; nothing was written); KDA_ERR_TIMEOUT
+ * (a bounded wait between the cooperating waves of a workgroup gave up, which
+ * only a fault could cause; outputs unspecified); KDA_ERR_HIP if
+ * synchronisation fails.  Optional; it synchronises the host.
  */
 kda_status kda_chunk_fwd_check(const void *workspace, hipStream_t stream);
 

@@ -115,6 +115,6 @@ def test_status_strings(lib):
     f = lib.kda_status_string
     f.restype = ctypes.c_char_p
     f.argtypes = [ctypes.c_int]
-    for code in range(6):
+    for code in range(7):
         assert f(code).startswith(b"KDA_")
     assert f(99) == b"KDA_ERR_UNKNOWN"
