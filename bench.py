@@ -39,6 +39,33 @@ WALK_BYTES_PER_HT = 1416               # reads W,QG,KdT,U',P,Gn (1160); writes o
 DECODE_BYTES_PER_STEP = 1084243968     # state read + write (2 x 536870912) + tokens in (8404992) + o (2097152)
 
 
+def kernel_sources_sha():
+    """sha256[:16] over the HIP sources, as recorded next to counter readings."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "gated_delta_rule_48_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated) recorded in
+    profiles/traffic_counters.txt for these exact kernel sources, else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_counters.txt")
+    if not os.path.exists(path):
+        return None
+    sha = kernel_sources_sha()
+    with open(path) as f:
+        for line in f:
+            kv = dict(x.split("=", 1) for x in line.split())
+            if kv.get("kernel") == kernel and kv.get("sources_sha") == sha:
+                return float(kv["read_bytes"]) + float(kv["write_bytes"])
+    return None
+
+
 def _hip():
     lib = ctypes.CDLL("libamdhip64.so")
     lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
@@ -83,8 +110,8 @@ def cpu_baseline(d, prefix_tokens):
                       threads=threads)
     dt = time.perf_counter() - t0
     return {"value": T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {T} tokens of the 32K x 32-head prefill workload (all heads), fp64 sequential "
-                      f"recurrence, {dt:.2f} s"}
+            "sample": f"first {T} tokens of the 32K x 32-head prefill workload (all heads; the whole "
+                      f"workload when {T} = 32768), fp64 sequential recurrence, {dt:.2f} s"}
 
 
 def main():
@@ -93,7 +120,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-prefix", type=int, default=8192)
+    ap.add_argument("--cpu-prefix", type=int, default=32768)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one device-to-device copy of exactly 1 GiB before the timed steps, so that a "
+                         "counter run (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE) has a kernel of known traffic "
+                         "to scale by")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the KDA hot path here is not sharded, got --gpus {args.gpus}",
@@ -124,6 +155,15 @@ def main():
         toks.append({n: _to_dev(t[n], torch) for n in ("q", "k", "v", "g", "beta")})
     o_dec = torch.empty((dcfg.N, dcfg.H, dcfg.dv), dtype=torch.bfloat16, device="cuda")
     torch.cuda.synchronize()
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)  # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
 
     stream = torch.cuda.current_stream().cuda_stream
     K, W = args.steps, args.warmup
@@ -193,7 +233,8 @@ def main():
         "decode": {"us_per_step": t_dec * 1e3, "GB_per_s": dec_gbs, "frac_hbm_peak": dec_gbs / HBM_PEAK_GBS,
                    "tokens_per_s": dcfg.N / (t_dec * 1e-3), "bytes_per_step": DECODE_BYTES_PER_STEP},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(dom),
+                     "algorithmic_bytes": dom_bytes},
         "path_roofline": {"what": "whole kda_chunk_fwd call vs the method's minimum bytes (1282 B/head-token) "
                                   "and algorithmic FLOPs (139136 /head-token)",
                           "GB_per_s": path_gbs, "frac_hbm_peak": path_gbs / HBM_PEAK_GBS,
