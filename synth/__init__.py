@@ -8,6 +8,11 @@ Recipe (every config):
   * numpy ``default_rng(seed)`` (PCG64), all draws in float32.
   * Draw order: sequence lengths -> q -> k -> v -> beta -> g -> S0, each
     tensor drawn whole in token order (in blocks of rows for very long T).
+  * Streamed configs (``stream_rows`` > 0, one sequence, S0 = 0) instead draw
+    the tokens in blocks of ``stream_rows`` rows, block b from its own
+    generator ``default_rng([seed, b])`` in the same q -> k -> v -> beta -> g
+    order, so that a million-token input can be produced block by block, in
+    parallel, and fed to the GPU and to the oracle without holding it whole.
   * q and k ~ N(0, 1), each (token, head) vector L2-normalised in float32.
   * v ~ N(0, 1).
   * beta = sigmoid(N(0, 1)) per (token, head).
@@ -52,6 +57,7 @@ class ChunkConfig:
     T: int = 0            # equal-length sequences: total tokens (with N)
     N: int = 1
     lengths: tuple = ()   # varlen: (lo, hi) inclusive uniform, N draws
+    stream_rows: int = 0  # > 0: tokens drawn per block of rows (see module doc)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -82,7 +88,8 @@ CONFIGS = {
                                 gate_mu=-1.0, s0_sigma=0.0, seed=303, T=32768, N=1),
     # long-context KDA prefill: B=1, T=1,048,576, H=16, d=128
     "kda_1m_bf16": ChunkConfig("kda_1m_bf16", H=16, dk=128, dv=128, dtype="bf16", gate="channel",
-                               gate_mu=-1.0, s0_sigma=0.0, seed=404, T=1 << 20, N=1),
+                               gate_mu=-1.0, s0_sigma=0.0, seed=404, T=1 << 20, N=1,
+                               stream_rows=16384),
 }
 
 DECODE_CONFIGS = {
@@ -155,6 +162,15 @@ def chunk_inputs(cfg, seed=None, lengths=None):
             lengths = rng.integers(lo, hi, size=cfg.N, endpoint=True)
         else:
             lengths = [cfg.T // cfg.N] * cfg.N
+    if cfg.stream_rows:
+        if lengths is not None:
+            raise ValueError("a streamed config has fixed lengths")
+        out = {n: np.concatenate([blk[n] for _, _, blk in iter_token_blocks(cfg, workers=1)])
+               for n in ("q", "k", "v", "beta", "g")}
+        out["S0"] = None
+        out["cu_seqlens"] = np.array([0, cfg.T], dtype=np.int32)
+        out["cfg"] = cfg
+        return out
     lengths = np.asarray(lengths, dtype=np.int64)
     N = len(lengths)
     cu = np.zeros(N + 1, dtype=np.int32)
@@ -168,6 +184,39 @@ def chunk_inputs(cfg, seed=None, lengths=None):
     out["cu_seqlens"] = cu
     out["cfg"] = cfg
     return out
+
+
+def token_block(cfg, b):
+    """Block b (rows b*R .. b*R+R-1, R = stream_rows) of a streamed config."""
+    R = cfg.stream_rows
+    if R <= 0 or cfg.N != 1 or cfg.s0_sigma > 0:
+        raise ValueError("not a streamed config")
+    start = b * R
+    rows = min(R, cfg.T - start)
+    if rows <= 0:
+        raise IndexError(b)
+    rng = np.random.default_rng([cfg.seed, b])
+    return draw_tokens(rng, rows, cfg.H, cfg.dk, cfg.dv, cfg.dtype, cfg.gate, cfg.gate_mu)
+
+
+def iter_token_blocks(cfg, workers=8):
+    """Yield (b, start_row, block) in order for a streamed config, drawing up
+    to ``workers`` blocks ahead on threads (numpy releases the GIL while it
+    fills arrays, and every block has its own generator)."""
+    import concurrent.futures as cf
+    R = cfg.stream_rows
+    nb = (cfg.T + R - 1) // R
+    if workers <= 1:
+        for b in range(nb):
+            yield b, b * R, token_block(cfg, b)
+        return
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        pending = {}
+        for b in range(nb):
+            while len(pending) < workers and b + len(pending) < nb:
+                nxt = b + len(pending)
+                pending[nxt] = ex.submit(token_block, cfg, nxt)
+            yield b, b * R, pending.pop(b).result()
 
 
 def small_chunk_config(H=2, dk=64, dv=64, dtype="bf16", gate="channel", gate_mu=0.0,
