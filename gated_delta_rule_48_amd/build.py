@@ -20,6 +20,10 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs: the state walk scales its
+    # fp32 state between products, which would otherwise cost a copy out of
+    # and back into the accumulator registers for every element
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(HERE, "..", "include"),
 ]
 

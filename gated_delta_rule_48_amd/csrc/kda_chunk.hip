@@ -597,36 +597,64 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
 
 // ----------------------------------------------------------------------------
 // State walk + output.  One workgroup per (sequence n, head h, 16-column slice
-// of d_v), three waves that never meet at a barrier:
+// of d_v), four waves that never meet at a barrier:
 //   wave 0 (chain)   keeps the fp32 d_k x 16 slice of S in accumulator
 //                    registers and walks the chunks: U = U' - W S, then
 //                    S <- Diag(Gn) S + KdT U.  The bf16 (or fp32) fragments of
 //                    S and U it builds for its own products are also handed to
 //                    wave 1 through a ring of kRing slots in LDS.
-//   wave 1 (output)  O = QG S + P U for each chunk from those fragments.
-//   wave 2 (prefetch) touches the cache lines of the chunks up to
+//   wave 1 (output)  O = QG S + P U for each chunk from those fragments; QG
+//                    and P come straight from global memory.
+//   wave 2 (stager)  copies the chain's operands of each chunk (W, KdT, this
+//                    slice of U', Gn) into a ring of R operand slots in LDS
+//                    with 16-byte LDS-DMA loads, so that the chain wave issues
+//                    no global loads at all and reads its fragments from LDS.
+//                    When R slots do not fit in LDS (fp32 at d = 128) the
+//                    chain loads its operands from global memory itself and
+//                    this wave has nothing to do.
+//   wave 3 (prefetch) touches the cache lines of the chunks up to
 //                    kWalkPrefetch ahead of wave 0 (LDS-DMA loads into a sink:
-//                    no registers), so that waves 0 and 1 find them in L2.
-// Waves 0 and 1 load every operand of the next chunk right after the current
-// one has consumed it.  Hand-over is by two LDS progress counters; every wait
-// is bounded by kSpinLimit sleeps, past which the wave records a timeout in
-// the workspace header and proceeds (results are then unspecified).
+//                    no registers), so that waves 1 and 2 find them in L2.
+// Hand-over is by LDS progress counters (absolute chunk indices):
+//   ready  chunks whose operand slot the stager has filled,
+//   freed  chunks whose operand slot the chain has finished reading,
+//   progA  chunks whose S and U fragments the chain has published,
+//   doneB  chunks whose S and U slot the output wave has finished reading.
+// Every wait is bounded by kSpinLimit sleeps, past which the wave records a
+// timeout in the workspace header and proceeds (results are then
+// unspecified).
 // Operands W, QG (channel columns) and KdT, P (token columns) are stored in
 // fragment order (frag_pos), so accumulator registers serve directly as the B
 // fragment of the next product, and fragment-major (fm_off), so every
-// fragment load is one contiguous 1 KB read; U' is stored per slice in the
-// accumulator layout of the walk's lanes.
+// fragment is one contiguous 1 KB block, copied into LDS unchanged; U' is
+// stored per slice in the accumulator layout of the walk's lanes.
 constexpr int kRing = 4;
 #ifndef KDA_WALK_PREFETCH
 #define KDA_WALK_PREFETCH 4
 #endif
 constexpr int kWalkPrefetch = KDA_WALK_PREFETCH;
-constexpr int kWalkThreads = 192;
+constexpr int kWalkThreads = 256;
 constexpr int kSpinLimit = 1 << 22;
+constexpr int kLdsBytes = 160 * 1024;  // LDS of one gfx950 compute unit
 
 __device__ __forceinline__ int lds_read_int(const int* p) {
     return *(volatile const __attribute__((address_space(3))) int*)(p);
 }
+
+// Hand-over between waves of one workgroup through LDS.  The LDS performs the
+// accesses of a wave in the order it issues them, so a counter written after
+// a wave's data accesses is seen after them by every other wave.  Release
+// additionally waits until this wave's LDS accesses are done (lgkmcnt only:
+// the compiler's own fences would also wait for outstanding global loads,
+// which the walk keeps in flight on purpose); acquire only keeps the compiler
+// from hoisting later LDS reads above the counter read.
+// 32-bit LDS address of a pointer into shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+__device__ __forceinline__ void lds_release() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void lds_acquire() { asm volatile("" ::: "memory"); }
 
 // Accumulator tiles a (rows 0..15 of a 32-block) and b (rows 16..31) of one
 // lane -> the B fragment of that 32-block (see frag_pos).
@@ -644,19 +672,66 @@ __device__ __forceinline__ Frag<float> acc_to_frag(float, f32x4 a, f32x4 b) {
     return f;
 }
 
-// Four consecutive elements -> fp32 (8 bytes of bf16 or 16 bytes of fp32).
-__device__ __forceinline__ f32x4 load4(const bf16_t* p) {
-    const uint2 w = *reinterpret_cast<const uint2*>(p);
-    return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
-                 __uint_as_float(w.y & 0xffff0000u)};
-}
-__device__ __forceinline__ f32x4 load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+// Four consecutive elements in their stored form (8 bytes of bf16 or 16 bytes
+// of fp32), widened to fp32 only where they are used.
+template <typename E> struct Raw4;
+template <> struct Raw4<bf16_t> {
+    typedef uint2 T;
+    __device__ __forceinline__ static T load(const bf16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+    __device__ __forceinline__ static f32x4 widen(T w) {
+        return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+                     __uint_as_float(w.y & 0xffff0000u)};
+    }
+};
+template <> struct Raw4<float> {
+    typedef f32x4 T;
+    __device__ __forceinline__ static T load(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+    __device__ __forceinline__ static f32x4 widen(T w) { return w; }
+};
 
-// 16-column tiles of d_v per workgroup (wider slices halve the L2 traffic of
-// W, QG, KdT, P but were measured slower: the chain is bound by per-wave
-// work, not by L2).
-template <typename E> struct WalkCols { static constexpr int NC = 1; };
-template <> struct WalkCols<float> { static constexpr int NC = 1; };
+// One 16-byte LDS-DMA load per active lane: lane i copies 16 bytes from its
+// own global address to lds + 16 i (lds must be uniform over the wave).
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                     (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+// Wait until at most N vector-memory loads of this wave are outstanding (they
+// complete in order).  Also a compiler barrier for memory accesses.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// LDS layout of the walk workgroup (dynamic shared memory).
+template <typename E, int DK, int DV>
+struct WalkLayout {
+    static constexpr int C = kChunk;
+    static constexpr int KS = DK / 32, KB = C / 32;
+    static constexpr int ESZ = (int)sizeof(E);
+    static constexpr int LDO = 16 + 16 / ESZ;  // padded row of the O staging tile
+    // one operand slot: W | KdT | U' (this slice) | Gn
+    static constexpr int W_B = C * DK * ESZ, K_B = DK * C * ESZ, U_B = 64 * 16 * ESZ, G_B = DK * 4;
+    static constexpr int SLOT = W_B + K_B + U_B + G_B;
+    static constexpr int RING_S = kRing * KS * 64 * (int)sizeof(Frag<E>);
+    static constexpr int RING_U = kRing * KB * 64 * (int)sizeof(Frag<E>);
+    static constexpr int O_B = (C * LDO * ESZ + 15) / 16 * 16;
+    static constexpr int SINK_B = 256, CNT_B = 64;
+    static constexpr int FIXED = RING_S + RING_U + 2 * O_B + SINK_B + CNT_B;
+    static constexpr int RFIT = (kLdsBytes - FIXED) / SLOT;
+    static constexpr int R = RFIT > 3 ? 3 : RFIT;  // operand slots
+    static constexpr bool STAGED = R >= 2;
+    static constexpr int OPS_B = STAGED ? R * SLOT : 0;
+    static constexpr int off_ringS = OPS_B, off_ringU = off_ringS + RING_S, off_O = off_ringU + RING_U;
+    static constexpr int off_sink = off_O + 2 * O_B, off_cnt = off_sink + SINK_B;
+    static constexpr int bytes = off_cnt + CNT_B;
+    // LDS-DMA loads per chunk: 1 KB blocks of W, KdT and U', one load for Gn
+    static constexpr int LPC = W_B / 1024 + K_B / 1024 + U_B / 1024 + 1;
+    static_assert(W_B % 1024 == 0 && K_B % 1024 == 0 && U_B % 1024 == 0 && G_B <= 1024 && G_B % 16 == 0, "blocks");
+    static_assert(!STAGED || LPC <= 63, "one chunk of loads within the vector-memory counter");
+    static_assert(bytes <= kLdsBytes, "LDS budget");
+};
 
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(kWalkThreads) void chunk_walk_kernel(
@@ -664,20 +739,28 @@ __global__ __launch_bounds__(kWalkThreads) void chunk_walk_kernel(
     int32_t H, const E* __restrict__ Wi, const E* __restrict__ QGi, const E* __restrict__ KdTi,
     const E* __restrict__ UpTi, const E* __restrict__ Pi, const float* __restrict__ Gni,
     const float* __restrict__ S0, float* __restrict__ S_T, E* __restrict__ o) {
+    using L = WalkLayout<E, DK, DV>;
     constexpr int C = kChunk;
-    constexpr int NC = WalkCols<E>::NC;
-    constexpr int DVS = 16 * NC, NS = DV / DVS;
+    constexpr int NS = DV / 16;  // slices per (n, h)
     constexpr int MT = DK / 16;  // 16-row tiles of the state slice
-    constexpr int KS = DK / 32;  // 32-blocks over channels
+    constexpr int KS = L::KS;    // 32-blocks over channels
     constexpr int TT = C / 16;   // 16-row tiles of tokens
-    constexpr int KB = C / 32;   // 32-blocks over tokens
-    constexpr int LDO = DVS + 16 / (int)sizeof(E);
-    __shared__ __align__(16) Frag<E> ringS[kRing][KS][NC][64];
-    __shared__ __align__(16) Frag<E> ringU[kRing][KB][NC][64];
-    __shared__ __align__(16) E sO[C * LDO];  // output wave: one chunk of O, row-major
-    __shared__ int progA;  // chunks published by wave 0 (absolute index of the next one)
-    __shared__ int doneB;  // chunks consumed by wave 1
-    __shared__ __align__(16) float sSink[64];
+    constexpr int KB = L::KB;    // 32-blocks over tokens
+    constexpr int LDO = L::LDO;
+    constexpr int R = L::R;
+    extern __shared__ __align__(16) char walk_smem[];
+    char* const ops = walk_smem;
+    Frag<E>* const ringS = reinterpret_cast<Frag<E>*>(walk_smem + L::off_ringS);  // [kRing][KS][64]
+    Frag<E>* const ringU = reinterpret_cast<Frag<E>*>(walk_smem + L::off_ringU);  // [kRing][KB][64]
+    E* const sO = reinterpret_cast<E*>(walk_smem + L::off_O);                     // [2][O_B / ESZ]
+    float* const sSink = reinterpret_cast<float*>(walk_smem + L::off_sink);
+    int* const cnt = reinterpret_cast<int*>(walk_smem + L::off_cnt);
+    int* const progA = cnt;      // chunks published by the chain wave
+    int* const doneB = cnt + 1;  // chunks consumed by the output wave
+    int* const ready = cnt + 2;  // chunks staged by the stager wave
+    int* const freed = cnt + 3;  // chunks whose operand slot the chain released
+    int* const oready = cnt + 4;   // chunks whose O tile the output wave has staged
+    int* const ostored = cnt + 5;  // chunks whose O tile the store wave has read
 
     if (hdr->bad_seqlens) return;
     const int64_t NH = (int64_t)N * H;
@@ -697,42 +780,44 @@ __global__ __launch_bounds__(kWalkThreads) void chunk_walk_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
-    const int col0 = slice * DVS;
+    const int col0 = slice * 16;
     const int cbeg = chunk_off[n], cend = chunk_off[n + 1];
     const int64_t seq0 = cu[n], seqend = cu[n + 1];
-    if (tid == 0) {
-        progA = cbeg;
-        doneB = cbeg;
-    }
+    if (tid < 6) cnt[tid] = cbeg;
     lds_barrier();  // the only barrier: counters initialised before any wave reads them
 
+    // A wait that gives up only sets timed_out; each wave reports it once, on
+    // exit, so that no global store sits inside a loop (a store among this
+    // wave's loads would make the compiler wait for all of them at once).
+    bool timed_out = false;
+    auto report = [&]() {
+        if (timed_out) hdr->wait_timeout = 1;
+    };
     auto wait_until = [&](const int* counter, int target) {
         for (int spins = 0; lds_read_int(counter) < target; ++spins) {
             if (spins >= kSpinLimit) {
-                hdr->wait_timeout = 1;
+                timed_out = true;
                 return;
             }
             __builtin_amdgcn_s_sleep(1);
         }
     };
-    auto publish = [&](int* counter, int value) {
-        // prior LDS traffic of this wave completes before the counter moves
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    auto put_counter = [&](int* counter, int value) {
         if (lane == 0) *(volatile __attribute__((address_space(3))) int*)(counter) = value;
     };
     auto chunk_base = [&](int c) { return (int64_t)c * H + h; };
+    auto slot_of = [&](int c) { return ops + ((c - cbeg) % (R > 0 ? R : 1)) * L::SLOT; };
 
-    if (w == 2) {
-        // ---------------- prefetch wave ----------------
+    if (w == 3) {
+        // ---------------- prefetch + store wave ----------------
         constexpr int LW = C * DK * (int)sizeof(E) / 128;  // lines of W, of QG, of KdT
         constexpr int LP = C * C * (int)sizeof(E) / 128;
         constexpr int LG = DK * 4 / 128;
         constexpr int NL = 3 * LW + LP + LG;
-        constexpr int LU = NC * 64 * 16 * (int)sizeof(E) / 128;  // this slice's part of U'
+        constexpr int LU = 64 * 16 * (int)sizeof(E) / 128;  // this slice's part of U'
         static_assert(LU <= 64, "one load per lane");
         auto sink = (__attribute__((address_space(3))) void*)sSink;
-        for (int c = cbeg; c < cend; ++c) {
-            wait_until(&progA, c - kWalkPrefetch + 1);
+        auto prefetch = [&](int c) {
             const int64_t ch = chunk_base(c);
             for (int j = slice + NS * lane; j < NL; j += NS * 64) {
                 const char* base;
@@ -746,193 +831,288 @@ __global__ __launch_bounds__(kWalkThreads) void chunk_walk_kernel(
                                                  sink, 4, 0, 0);
             }
             if (lane < LU) {
-                const char* up = (const char*)(UpTi + ch * DV * C + slice * NC * 64 * 16);
+                const char* up = (const char*)(UpTi + ch * DV * C + slice * 64 * 16);
                 __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(up + 128 * lane),
                                                  sink, 4, 0, 0);
+            }
+        };
+        // prefetch every chunk fewer than kWalkPrefetch ahead of the chain
+        int pcur = cbeg;
+        auto pump = [&]() {
+            const int lim = min(cend, lds_read_int(progA) + kWalkPrefetch);
+            for (; pcur < lim; ++pcur) prefetch(pcur);
+        };
+        for (int c = cbeg; c < cend; ++c) {
+            // wait for the O tile of chunk c, prefetching meanwhile
+            for (int spins = 0;; ++spins) {
+                pump();
+                if (lds_read_int(oready) > c) break;
+                if (spins >= kSpinLimit) {
+                    timed_out = true;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            lds_acquire();
+            // each lane stores one token row of the slice (16 outputs); the
+            // LDS reads are issued before the counter write, so the output
+            // wave cannot overwrite the tile before they are performed
+            const E* tile = sO + (c & 1) * (L::O_B / (int)sizeof(E));
+            const uint32_t srow = lds_addr(tile + lane * LDO);
+            constexpr int NB = 16 * (int)sizeof(E) / 16;  // 16-byte pieces of a row
+            uint4 r0, r1, r2, r3;
+            // in asm: the compiler would otherwise wait for this wave's
+            // prefetch loads (it cannot tell that they write elsewhere in LDS)
+            if constexpr (NB == 2) {
+                asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:16\n\ts_waitcnt lgkmcnt(0)"
+                             : "=v"(r0), "=v"(r1)
+                             : "v"(srow)
+                             : "memory");
+            } else {
+                asm volatile(
+                    "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:16\n\t"
+                    "ds_read_b128 %2, %4 offset:32\n\tds_read_b128 %3, %4 offset:48\n\ts_waitcnt lgkmcnt(0)"
+                    : "=v"(r0), "=v"(r1), "=v"(r2), "=v"(r3)
+                    : "v"(srow)
+                    : "memory");
+            }
+            put_counter(ostored, c + 1);
+            const int64_t tok = seq0 + (int64_t)(c - cbeg) * C + lane;
+            if (tok < seqend) {
+                uint4* drow = reinterpret_cast<uint4*>(o + (tok * H + h) * DV + col0);
+                drow[0] = r0;
+                drow[1] = r1;
+                if constexpr (NB == 4) {
+                    drow[2] = r2;
+                    drow[3] = r3;
+                }
             }
         }
         // No LDS-DMA load may still be in flight when the workgroup's LDS is
         // released.
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        wait_vmcnt<0>();
+        report();
+        return;
+    }
+
+    if (w == 2) {
+        // ---------------- stager wave ----------------
+        if constexpr (L::STAGED) {
+            for (int c = cbeg; c < cend; ++c) {
+                if (lds_read_int(freed) < c - R + 1) {
+                    // about to block on a slot: first finish and announce
+                    // every chunk already in flight
+                    wait_vmcnt<0>();
+                    put_counter(ready, c);
+                    wait_until(freed, c - R + 1);
+                    lds_acquire();
+                }
+                const int64_t ch = chunk_base(c);
+                char* s = slot_of(c);
+                const char* gw = (const char*)(Wi + ch * C * DK) + 16 * lane;
+                const char* gk = (const char*)(KdTi + ch * DK * C) + 16 * lane;
+                const char* gu = (const char*)(UpTi + ch * DV * C + slice * 64 * 16) + 16 * lane;
+#pragma unroll
+                for (int i = 0; i < L::W_B / 1024; ++i) lds_dma16(gw + 1024 * i, s + 1024 * i);
+#pragma unroll
+                for (int i = 0; i < L::K_B / 1024; ++i) lds_dma16(gk + 1024 * i, s + L::W_B + 1024 * i);
+#pragma unroll
+                for (int i = 0; i < L::U_B / 1024; ++i) lds_dma16(gu + 1024 * i, s + L::W_B + L::K_B + 1024 * i);
+                if (lane < L::G_B / 16)
+                    lds_dma16((const char*)(Gni + ch * DK) + 16 * lane, s + L::W_B + L::K_B + L::U_B);
+                // every load before this chunk's has landed in LDS
+                wait_vmcnt<L::LPC>();
+                put_counter(ready, c);
+            }
+            wait_vmcnt<0>();
+            put_counter(ready, cend);
+        }
+        report();
         return;
     }
 
     if (w == 0) {
         // ---------------- chain wave ----------------
-        f32x4 Sreg[MT][NC];
+        f32x4 Sreg[MT];
         if (S0) {
 #pragma unroll
             for (int m = 0; m < MT; ++m)
 #pragma unroll
-                for (int j = 0; j < NC; ++j)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        Sreg[m][j][i] = S0[(pair * DK + 16 * m + 4 * lg + i) * DV + col0 + 16 * j + lr];
+                for (int i = 0; i < 4; ++i) Sreg[m][i] = S0[(pair * DK + 16 * m + 4 * lg + i) * DV + col0 + lr];
         } else {
 #pragma unroll
-            for (int m = 0; m < MT; ++m)
-#pragma unroll
-                for (int j = 0; j < NC; ++j) Sreg[m][j] = zero4();
+            for (int m = 0; m < MT; ++m) Sreg[m] = zero4();
         }
         Frag<E> fW[TT][KS], fK[MT][KB];
-        f32x4 up[TT][NC], gn[MT];
+        typename Raw4<E>::T up[TT];  // U' kept in its stored form until used
+        f32x4 gn[MT];
+        // operand c is in LDS once `ready` has passed it (staged), else in
+        // global memory; `seen` is a value of `ready` read earlier
+        auto acquire_ops = [&](int c, int seen) {
+            if constexpr (L::STAGED) {
+                if (seen < c + 1) wait_until(ready, c + 1);
+                lds_acquire();
+            }
+        };
         auto load_w = [&](int c) {
-            const E* Wp = Wi + chunk_base(c) * C * DK;
+            const E* Wp;
+            if constexpr (L::STAGED) Wp = reinterpret_cast<const E*>(slot_of(c));
+            else Wp = Wi + chunk_base(c) * C * DK;
 #pragma unroll
             for (int t = 0; t < TT; ++t)
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) fW[t][ks] = ld_frag(Wp + ((t * KS + ks) * 64 + lane) * 8);
         };
         auto load_rest = [&](int c) {
-            const int64_t ch = chunk_base(c);
-            const E* Kp = KdTi + ch * DK * C;
-            const E* Up = UpTi + ch * DV * C + (slice * NC * 64 + lane) * 16;
-            const float* Gp = Gni + ch * DK;
+            const E *Kp, *Up;
+            const float* Gp;
+            if constexpr (L::STAGED) {
+                const char* s = slot_of(c);
+                Kp = reinterpret_cast<const E*>(s + L::W_B);
+                Up = reinterpret_cast<const E*>(s + L::W_B + L::K_B) + lane * 16;
+                Gp = reinterpret_cast<const float*>(s + L::W_B + L::K_B + L::U_B);
+            } else {
+                const int64_t ch = chunk_base(c);
+                Kp = KdTi + ch * DK * C;
+                Up = UpTi + ch * DV * C + (slice * 64 + lane) * 16;
+                Gp = Gni + ch * DK;
+            }
 #pragma unroll
             for (int m = 0; m < MT; ++m)
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) fK[m][kb] = ld_frag(Kp + ((m * KB + kb) * 64 + lane) * 8);
 #pragma unroll
-            for (int t = 0; t < TT; ++t)
-#pragma unroll
-                for (int j = 0; j < NC; ++j) up[t][j] = load4(Up + j * 64 * 16 + 4 * t);
+            for (int t = 0; t < TT; ++t) up[t] = Raw4<E>::load(Up + 4 * t);
 #pragma unroll
             for (int m = 0; m < MT; ++m) gn[m] = *reinterpret_cast<const f32x4*>(Gp + 16 * m + 4 * lg);
         };
         if (cbeg < cend) {
+            acquire_ops(cbeg, cbeg);
             load_w(cbeg);
             load_rest(cbeg);
         }
         for (int c = cbeg; c < cend; ++c) {
             const int slot = (c - cbeg) % kRing;
             const int nxt = min(c + 1, cend - 1);
-            const int freeB = lds_read_int(&doneB);  // read early; checked after the products
-            Frag<E> sf[KS][NC];
+            // counters read early, checked after the products
+            const int freeB = lds_read_int(doneB);
+            const int seen = L::STAGED ? lds_read_int(ready) : 0;
+            Frag<E> sf[KS];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
+            for (int ks = 0; ks < KS; ++ks) sf[ks] = acc_to_frag(E{}, Sreg[2 * ks], Sreg[2 * ks + 1]);
+            // Diag(Gn) S now (S itself is needed again only as the
+            // accumulator of KdT U below), overlapping the products
 #pragma unroll
-                for (int j = 0; j < NC; ++j) sf[ks][j] = acc_to_frag(E{}, Sreg[2 * ks][j], Sreg[2 * ks + 1][j]);
+            for (int m = 0; m < MT; ++m) Sreg[m] = gn[m] * Sreg[m];
             // U = U' - W S
-            f32x4 X[TT][NC];
+            f32x4 X[TT];
 #pragma unroll
-            for (int t = 0; t < TT; ++t)
-#pragma unroll
-                for (int j = 0; j < NC; ++j) X[t][j] = zero4();
+            for (int t = 0; t < TT; ++t) X[t] = zero4();
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                for (int t = 0; t < TT; ++t)
-#pragma unroll
-                    for (int j = 0; j < NC; ++j) X[t][j] = mma(fW[t][ks], sf[ks][j], X[t][j]);
+                for (int t = 0; t < TT; ++t) X[t] = mma(fW[t][ks], sf[ks], X[t]);
+            acquire_ops(nxt, seen);
             load_w(nxt);
-            Frag<E> uf[KB][NC];
+            Frag<E> uf[KB];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int j = 0; j < NC; ++j)
-                    uf[kb][j] = acc_to_frag(E{}, up[2 * kb][j] - X[2 * kb][j], up[2 * kb + 1][j] - X[2 * kb + 1][j]);
+                uf[kb] = acc_to_frag(E{}, Raw4<E>::widen(up[2 * kb]) - X[2 * kb],
+                                     Raw4<E>::widen(up[2 * kb + 1]) - X[2 * kb + 1]);
             // hand S and U to the output wave once its slot is free
-            if (freeB < c - kRing + 1) wait_until(&doneB, c - kRing + 1);
+            if (freeB < c - kRing + 1) wait_until(doneB, c - kRing + 1);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
+            for (int ks = 0; ks < KS; ++ks) ringS[(slot * KS + ks) * 64 + lane] = sf[ks];
 #pragma unroll
-                for (int j = 0; j < NC; ++j) ringS[slot][ks][j][lane] = sf[ks][j];
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int j = 0; j < NC; ++j) ringU[slot][kb][j][lane] = uf[kb][j];
+            for (int kb = 0; kb < KB; ++kb) ringU[(slot * KB + kb) * 64 + lane] = uf[kb];
             // S <- Diag(Gn) S + KdT U  (the ring writes drain meanwhile)
 #pragma unroll
-            for (int m = 0; m < MT; ++m)
-#pragma unroll
-                for (int j = 0; j < NC; ++j) Sreg[m][j] = gn[m] * Sreg[m][j];
-#pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int m = 0; m < MT; ++m)
-#pragma unroll
-                    for (int j = 0; j < NC; ++j) Sreg[m][j] = mma(fK[m][kb], uf[kb][j], Sreg[m][j]);
-            publish(&progA, c + 1);
+                for (int m = 0; m < MT; ++m) Sreg[m] = mma(fK[m][kb], uf[kb], Sreg[m]);
+            // every operand of chunk c has been read (its registers are in
+            // use above), and S, U of chunk c are in the ring
+            lds_release();
+            put_counter(progA, c + 1);
+            if constexpr (L::STAGED) put_counter(freed, c + 1);
             load_rest(nxt);
         }
         if (S_T) {
 #pragma unroll
             for (int m = 0; m < MT; ++m)
 #pragma unroll
-                for (int j = 0; j < NC; ++j)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        S_T[(pair * DK + 16 * m + 4 * lg + i) * DV + col0 + 16 * j + lr] = Sreg[m][j][i];
+                for (int i = 0; i < 4; ++i) S_T[(pair * DK + 16 * m + 4 * lg + i) * DV + col0 + lr] = Sreg[m][i];
         }
+        report();
         return;
     }
 
     // ---------------- output wave (w == 1) ----------------
-    Frag<E> fQ[TT][KS], fP[TT][KB];
-    auto load_qp = [&](int c) {
-        const int64_t ch = chunk_base(c);
+    // QG and P of chunk c + 2 are loaded while chunk c is computed (two
+    // register sets).  The O tile goes to LDS and wave 3 stores it, so that
+    // this wave issues loads only and can wait for exactly the ones it needs.
+    struct QP {
+        Frag<E> q[TT][KS], p[TT][KB];
+    };
+    QP opA, opB;
+    auto load_qp = [&](QP& x, int c) {
+        const int64_t ch = chunk_base(min(c, cend - 1));
         const E* Qp = QGi + ch * C * DK;
         const E* Pp = Pi + ch * C * C;
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) fQ[t][ks] = ld_frag(Qp + ((t * KS + ks) * 64 + lane) * 8);
+            for (int ks = 0; ks < KS; ++ks) x.q[t][ks] = ld_frag(Qp + ((t * KS + ks) * 64 + lane) * 8);
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) fP[t][kb] = ld_frag(Pp + ((t * KB + kb) * 64 + lane) * 8);
+            for (int kb = 0; kb < KB; ++kb) x.p[t][kb] = ld_frag(Pp + ((t * KB + kb) * 64 + lane) * 8);
         }
     };
-    if (cbeg < cend) load_qp(cbeg);
-    for (int c = cbeg; c < cend; ++c) {
+    auto out_chunk = [&](QP& x, int c) {
         const int slot = (c - cbeg) % kRing;
-        wait_until(&progA, c + 1);
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-        Frag<E> sf[KS][NC], uf[KB][NC];
+        wait_until(progA, c + 1);
+        lds_acquire();
+        Frag<E> sf[KS], uf[KB];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) sf[ks] = ringS[(slot * KS + ks) * 64 + lane];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) uf[kb] = ringU[(slot * KB + kb) * 64 + lane];
+        lds_release();  // the reads above have completed
+        put_counter(doneB, c + 1);
+        f32x4 O[TT];
+#pragma unroll
+        for (int t = 0; t < TT; ++t) O[t] = zero4();
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int j = 0; j < NC; ++j) sf[ks][j] = ringS[slot][ks][j][lane];
+            for (int t = 0; t < TT; ++t) O[t] = mma(x.q[t][ks], sf[ks], O[t]);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int j = 0; j < NC; ++j) uf[kb][j] = ringU[slot][kb][j][lane];
-        publish(&doneB, c + 1);  // the reads above have completed
-        f32x4 O[TT][NC];
+            for (int t = 0; t < TT; ++t) O[t] = mma(x.p[t][kb], uf[kb], O[t]);
+        load_qp(x, c + 2);
+        // O tile slot c & 1 is free once wave 3 has read chunk c - 2 from it
+        wait_until(ostored, c - 1);
+        lds_acquire();
+        E* tile = sO + (c & 1) * (L::O_B / (int)sizeof(E));
 #pragma unroll
         for (int t = 0; t < TT; ++t)
 #pragma unroll
-            for (int j = 0; j < NC; ++j) O[t][j] = zero4();
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int t = 0; t < TT; ++t)
-#pragma unroll
-                for (int j = 0; j < NC; ++j) O[t][j] = mma(fQ[t][ks], sf[ks][j], O[t][j]);
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int t = 0; t < TT; ++t)
-#pragma unroll
-                for (int j = 0; j < NC; ++j) O[t][j] = mma(fP[t][kb], uf[kb][j], O[t][j]);
-        load_qp(min(c + 1, cend - 1));
-        // transpose through LDS so that each lane stores one token row of
-        // the slice (DVS contiguous outputs) with 16-byte stores
-#pragma unroll
-        for (int t = 0; t < TT; ++t)
-#pragma unroll
-            for (int j = 0; j < NC; ++j)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    lds_put(&sO[(16 * t + 4 * lg + i) * LDO + 16 * j + lr], Elt<E>::from(O[t][j][i]));
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-        const int64_t tok = seq0 + (int64_t)(c - cbeg) * C + lane;
-        if (tok < seqend) {
-            const uint4* srow = reinterpret_cast<const uint4*>(sO + lane * LDO);
-            uint4* drow = reinterpret_cast<uint4*>(o + (tok * H + h) * DV + col0);
-#pragma unroll
-            for (int b = 0; b < DVS * (int)sizeof(E) / 16; ++b) drow[b] = srow[b];
-        }
+            for (int i = 0; i < 4; ++i) lds_put(&tile[(16 * t + 4 * lg + i) * LDO + lr], Elt<E>::from(O[t][i]));
+        lds_release();
+        put_counter(oready, c + 1);
+    };
+    if (cbeg < cend) {
+        load_qp(opA, cbeg);
+        lds_acquire();  // compiler barrier: keep every load of opA ahead of opB's
+        load_qp(opB, cbeg + 1);
     }
+    for (int c = cbeg; c < cend;) {
+        out_chunk(opA, c);
+        if (++c >= cend) break;
+        out_chunk(opB, c);
+        ++c;
+    }
+    report();
 }
 
 // ----------------------------------------------------------------------------
@@ -1003,6 +1183,23 @@ static hipError_t launch_intra(const ChunkArgs& a, const ChunkWorkspace& ws, hip
     return hipGetLastError();
 }
 
+template <typename E, int DK, int DV>
+static hipError_t launch_walk(const ChunkArgs& a, const ChunkWorkspace& ws, int64_t blocks, hipStream_t stream) {
+    using L = WalkLayout<E, DK, DV>;
+    auto kern = chunk_walk_kernel<E, DK, DV>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kWalkThreads), L::bytes, stream, ws.header, ws.cu,
+                       ws.chunk_off, a.N, a.H, (const E*)ws.W, (const E*)ws.QG, (const E*)ws.KdT, (const E*)ws.Up,
+                       (const E*)ws.P, (const float*)ws.Gn, a.S0, a.S_T, (E*)a.o);
+    return hipGetLastError();
+}
+
 static inline hipError_t mark(hipEvent_t* ev, int i, hipStream_t stream) {
     return ev ? hipEventRecord(ev[i], stream) : hipSuccess;
 }
@@ -1017,11 +1214,9 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkWorkspace& ws, h
         if (e != hipSuccess) return e;
     }
     if ((e = mark(ev, 2, stream)) != hipSuccess) return e;
-    const int64_t blocks = (int64_t)a.N * a.H * (DV / (16 * WalkCols<E>::NC));
-    hipLaunchKernelGGL((chunk_walk_kernel<E, DK, DV>), dim3((unsigned)blocks), dim3(kWalkThreads), 0, stream, ws.header,
-                       ws.cu, ws.chunk_off, a.N, a.H, (const E*)ws.W, (const E*)ws.QG, (const E*)ws.KdT,
-                       (const E*)ws.Up, (const E*)ws.P, (const float*)ws.Gn, a.S0, a.S_T, (E*)a.o);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t blocks = (int64_t)a.N * a.H * (DV / 16);
+    e = launch_walk<E, DK, DV>(a, ws, blocks, stream);
+    if (e != hipSuccess) return e;
     return mark(ev, 3, stream);
 }
 
