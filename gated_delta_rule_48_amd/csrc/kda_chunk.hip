@@ -101,6 +101,8 @@ __device__ __forceinline__ int find_sequence(const int32_t* __restrict__ chunk_o
 
 // ----------------------------------------------------------------------------
 // Intra-chunk transform.
+constexpr int kIntraThreads = 512;  // eight waves per (chunk, head)
+
 template <typename E, int DK, int DV>
 struct IntraLayout {
     static constexpr int C = kChunk;
@@ -108,22 +110,22 @@ struct IntraLayout {
     static constexpr int LDK = DK + PAD;  // [token][channel] row stride
     static constexpr int LDT = C + PAD;   // [channel][token] row stride
     static constexpr int LDA = C + 4;     // fp32 A / T row stride
-    static constexpr int NPART = 512 / DK;
+    // threads hold two adjacent channels (values) of RPT (RPTV) consecutive rows
+    static constexpr int NPART = kIntraThreads / (DK / 2);
     static constexpr int RPT = C / NPART;
-    static constexpr int NPARTV = 512 / DV;
+    static constexpr int NPARTV = kIntraThreads / (DV / 2);
     static constexpr int RPTV = C / NPARTV;
+    static_assert(RPT % 4 == 0 && RPTV % 4 == 0, "row runs of four");
     static constexpr int NBND = 12;       // b at rows 16i, 16i+8, 16i+15 of the four 16-row tiles
     static constexpr int NCS = 10;        // column scales of the lower tile pairs (ti, tj <= ti)
     // Region R1: [Kr | Qr | Kt] ([token][channel], E) while A and P are
-    // formed; afterwards [Kbt | Vt] ([channel][token], E) and the 3 x 16 x 16
-    // fp32 scratch of the off-diagonal inversion.
-    // Also in R1 after A and P: the P staging tile [C][C+PAD]; at the very end
-    // the W and U' staging tiles [C][DK+PAD], [C][DV+PAD] for coalesced stores.
+    // formed; afterwards [Kbt | Vt] ([channel][token], E) followed by the P
+    // staging tile [C][C+PAD]; at the very end the W staging tile [C][DK+PAD]
+    // for coalesced stores.
     static constexpr int LDP = C + PAD;
     static constexpr int LDV = DV + PAD;
     static constexpr size_t rhs_bytes = (size_t)(DK + DV) * LDT * sizeof(E);
-    static constexpr size_t off_X = (rhs_bytes + 15) / 16 * 16;
-    static constexpr size_t off_Pst = off_X + 3 * 256 * 4;
+    static constexpr size_t off_Pst = (rhs_bytes + 15) / 16 * 16;
     static constexpr size_t r1_a = (size_t)3 * C * LDK * sizeof(E);
     static constexpr size_t r1_b = off_Pst + (size_t)C * LDP * sizeof(E);
     static constexpr size_t r1_c = ((size_t)C * LDK + (size_t)DV * LDT) * sizeof(E);
@@ -195,14 +197,26 @@ template <> __device__ __forceinline__ void store_run4<float>(float* dst, const 
     *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
 }
 
+// Store N contiguous elements (N a multiple of 4; dst aligned to the store
+// width): 16-byte stores where the run allows, else 4-element stores.
+template <typename E, int N>
+__device__ __forceinline__ void store_seq(E* dst, const E (&vals)[N]) {
+    if constexpr (N * sizeof(E) % 16 == 0) {
+        store_run<E, N>(dst, vals);
+    } else {
+#pragma unroll
+        for (int i = 0; i < N / 4; ++i) store_run4<E>(dst + 4 * i, vals + 4 * i);
+    }
+}
+
 // Copy a ROWS x COLS tile from LDS (row stride lds_ld elements) to a dense
-// global tile with 16-byte loads and stores spread over the 256 threads.
+// global tile with 16-byte loads and stores spread over the workgroup.
 template <typename E, int ROWS, int COLS>
 __device__ __forceinline__ void copy_tile_out(E* __restrict__ dst, const E* src, int lds_ld, int tid) {
     constexpr int VPR = COLS * (int)sizeof(E) / 16;
     constexpr int PER = 16 / (int)sizeof(E);
 #pragma unroll
-    for (int i = tid; i < ROWS * VPR; i += 256) {
+    for (int i = tid; i < ROWS * VPR; i += kIntraThreads) {
         const int r = i / VPR, c = (i % VPR) * PER;
         *reinterpret_cast<uint4*>(dst + r * COLS + c) = *reinterpret_cast<const uint4*>(src + r * lds_ld + c);
     }
@@ -235,7 +249,7 @@ __device__ __forceinline__ void copy_tile_out_frag(E* __restrict__ dst, const E*
     constexpr int PER = 16 / (int)sizeof(E);  // elements per 16-byte piece
     constexpr int PIECES = R * K / PER;
 #pragma unroll
-    for (int i = tid; i < PIECES; i += 256) {
+    for (int i = tid; i < PIECES; i += kIntraThreads) {
         // piece i covers lane-part (i % (8 / PER)) of lane (i / (8 / PER)) % 64 of block i / (64 * 8 / PER)
         const int sub = i % (8 / PER);
         const int lane = (i / (8 / PER)) % 64;
@@ -270,7 +284,7 @@ __device__ __forceinline__ Frag<float> scale_frag(Frag<float> f, const float* s)
 }
 
 template <typename E, int DK, int DV, bool HG>
-__global__ __launch_bounds__(256) void intra_chunk_kernel(
+__global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v, const E* __restrict__ g,
     const E* __restrict__ beta, const WsHeader* __restrict__ hdr, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ chunk_off, int32_t N, int32_t H, E* __restrict__ Wo, E* __restrict__ QGo,
@@ -285,7 +299,6 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
     E* sKt = sQr + C * LDK;                // k_i e^{b_e(i) - b_i}, e(i) = last row of i's tile
     E* sKbt = reinterpret_cast<E*>(smem);  // reuses R1 once A and P are done
     E* sVt = sKbt + DK * LDT;
-    float* sX = reinterpret_cast<float*>(smem + L::off_X);
     float* sA = reinterpret_cast<float*>(smem + L::off_A);
     float* sBnd = sA;  // [12][DK] tile-boundary prefix sums, dead before A is written
     float* sBeta = reinterpret_cast<float*>(smem + L::off_beta);
@@ -414,7 +427,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
     // Diagonal tile ti: reference m = 16 ti + 8: the row side takes
     //   e^{b_s - b_m} and the column side e^{b_m - b_e}; each spans at most
     //   eight tokens of decay.  The exponent is capped at 80 to stay finite.
-    for (int e = tid; e < 14 * DK; e += 256) {
+    for (int e = tid; e < 14 * DK; e += kIntraThreads) {
         const int v = e / DK, c = e % DK;
         float x;
         if (v < L::NCS) {
@@ -433,45 +446,82 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
 
     // ---- 3. A = K K^T with decay (strictly lower, row-scaled by beta) -> LDS
     //         (fp32);  P = Q K^T with decay (lower incl. diagonal) -> workspace
-    f32x4 accPt[4];
-    {
-        const int ti = wave;
+    // The ten lower tile pairs (ti, tj) over the eight waves: a diagonal pair
+    // costs about three off-diagonal ones (both operands are rescaled), so
+    // waves 0-3 take one diagonal pair each and waves 4-7 the six others;
+    // waves 6 and 7 also write the zero tiles above the diagonal.
+    int npair = 1, pti0 = wave, ptj0 = wave, pti1 = 0, ptj1 = 0;
+    if (wave == 4) { npair = 2; pti0 = 1; ptj0 = 0; pti1 = 2; ptj1 = 0; }
+    if (wave == 5) { npair = 2; pti0 = 2; ptj0 = 1; pti1 = 3; ptj1 = 0; }
+    if (wave == 6) { pti0 = 3; ptj0 = 1; }
+    if (wave == 7) { pti0 = 3; ptj0 = 2; }
+    f32x4 accPt[2];
 #pragma unroll
-        for (int tj = 0; tj < 4; ++tj) {
+    for (int pq = 0; pq < 2; ++pq) {
+        if (pq < npair) {
+            const int ti = pq ? pti1 : pti0, tj = pq ? ptj1 : ptj0;
             f32x4 accA = zero4(), accP = zero4();
-            if (tj <= ti) {
-                const float* cs = sColScale + (ti * (ti + 1) / 2 + tj) * DK;
-                const float* rs = sRowScale + ti * DK;
+            const float* cs = sColScale + (ti * (ti + 1) / 2 + tj) * DK;
+            const float* rs = sRowScale + ti * DK;
 #pragma unroll
-                for (int ks = 0; ks < DK / 32; ++ks) {
-                    const int cb = 32 * ks + 8 * lg;
-                    const Frag<E> fb = scale_frag(ld_frag(sKt + (16 * tj + lr) * LDK + cb), cs + cb);
-                    Frag<E> fa = ld_frag(sKr + (16 * ti + lr) * LDK + cb);
-                    Frag<E> fq = ld_frag(sQr + (16 * ti + lr) * LDK + cb);
-                    if (tj == ti) {
-                        fa = scale_frag(fa, rs + cb);
-                        fq = scale_frag(fq, rs + cb);
-                    }
-                    accA = mma(fa, fb, accA);
-                    accP = mma(fq, fb, accP);
+            for (int ks = 0; ks < DK / 32; ++ks) {
+                const int cb = 32 * ks + 8 * lg;
+                const Frag<E> fb = scale_frag(ld_frag(sKt + (16 * tj + lr) * LDK + cb), cs + cb);
+                Frag<E> fa = ld_frag(sKr + (16 * ti + lr) * LDK + cb);
+                Frag<E> fq = ld_frag(sQr + (16 * ti + lr) * LDK + cb);
+                if (tj == ti) {
+                    fa = scale_frag(fa, rs + cb);
+                    fq = scale_frag(fq, rs + cb);
                 }
+                accA = mma(fa, fb, accA);
+                accP = mma(fq, fb, accP);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * ti + 4 * lg + i, col = 16 * tj + lr;
                 lds_put(&sA[row * LDA + col], (row > col) ? accA[i] * sBeta[row] : 0.f);
-                accPt[tj][i] = (row >= col) ? accP[i] : 0.f;
+                accPt[pq][i] = (row >= col) ? accP[i] : 0.f;
             }
+        }
+    }
+    // zero tiles of A above the diagonal: (0,1) (0,2) (0,3) by wave 6,
+    // (1,2) (1,3) (2,3) by wave 7
+    auto upper_tile = [&](int z, int& ti, int& tj) {
+        const int zz = (wave == 6) ? z : z + 3;  // 0..5 over (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+        ti = zz < 3 ? 0 : (zz < 5 ? 1 : 2);
+        tj = zz < 3 ? zz + 1 : (zz < 5 ? zz - 1 : 3);
+    };
+    if (wave >= 6) {
+#pragma unroll
+        for (int z = 0; z < 3; ++z) {
+            int ti, tj;
+            upper_tile(z, ti, tj);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lds_put(&sA[(16 * ti + 4 * lg + i) * LDA + 16 * tj + lr], 0.f);
         }
     }
     lds_barrier();
     {
         E* sPst = reinterpret_cast<E*>(smem + L::off_Pst);
 #pragma unroll
-        for (int tj = 0; tj < 4; ++tj)
+        for (int pq = 0; pq < 2; ++pq) {
+            if (pq < npair) {
+                const int ti = pq ? pti1 : pti0, tj = pq ? ptj1 : ptj0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                lds_put(&sPst[(16 * wave + 4 * lg + i) * L::LDP + frag_pos(16 * tj + lr)], Elt<E>::from(accPt[tj][i]));
+                for (int i = 0; i < 4; ++i)
+                    lds_put(&sPst[(16 * ti + 4 * lg + i) * L::LDP + frag_pos(16 * tj + lr)], Elt<E>::from(accPt[pq][i]));
+            }
+        }
+        if (wave >= 6) {
+#pragma unroll
+            for (int z = 0; z < 3; ++z) {
+                int ti, tj;
+                upper_tile(z, ti, tj);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    lds_put(&sPst[(16 * ti + 4 * lg + i) * L::LDP + frag_pos(16 * tj + lr)], Elt<E>::from(0.f));
+            }
+        }
     }
 
     // ---- 4. right-hand sides into the freed region; T = (I + A)^{-1} ---------
@@ -482,8 +532,8 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
             r0[r] = Elt<E>::from(kb[r][0]);
             r1[r] = Elt<E>::from(kb[r][1]);
         }
-        store_run<E, RPT>(sKbt + c0 * LDT + part * RPT, r0);
-        store_run<E, RPT>(sKbt + (c0 + 1) * LDT + part * RPT, r1);
+        store_seq<E, RPT>(sKbt + c0 * LDT + part * RPT, r0);
+        store_seq<E, RPT>(sKbt + (c0 + 1) * LDT + part * RPT, r1);
     }
     {
         E r0[RPTV], r1[RPTV];
@@ -493,8 +543,8 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
             r0[r] = Elt<E>::from(bt * vraw[r].lo());
             r1[r] = Elt<E>::from(bt * vraw[r].hi());
         }
-        store_run<E, RPTV>(sVt + j0 * LDT + vpart * RPTV, r0);
-        store_run<E, RPTV>(sVt + (j0 + 1) * LDT + vpart * RPTV, r1);
+        store_seq<E, RPTV>(sVt + j0 * LDT + vpart * RPTV, r0);
+        store_seq<E, RPTV>(sVt + (j0 + 1) * LDT + vpart * RPTV, r1);
     }
     // (a) the four 16x16 diagonal blocks, one column per thread of wave 0
     float x[16];
@@ -518,57 +568,58 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
         for (int t = 0; t < 16; ++t) Tb[t * LDA + jc] = x[t];
     }
     lds_barrier();
-    // (b) off-diagonal blocks, block row by block row:
-    //     T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj
-    {
-        const int rr = tid >> 4, cc = tid & 15;
+    // (b) off-diagonal blocks, block row by block row, on the matrix cores in
+    //     fp32:  X = sum_{m=j}^{i-1} A_im T_mj,  T_ij = -T_ii X.  Wave j
+    //     takes block (i, j).  With k = 4g + s for lane group g and step s,
+    //     the product X comes out of the accumulators exactly as the B
+    //     operand of the second product needs it.
 #pragma unroll
-        for (int bi = 1; bi < 4; ++bi) {
-            float xv[3];
+    for (int bi = 1; bi < 4; ++bi) {
+        const int bj = wave;
+        f32x4 X = zero4();
+        if (bj < bi) {
+            for (int m = bj; m < bi; ++m) {
+                const f32x4 am = *reinterpret_cast<const f32x4*>(sA + (16 * bi + lr) * LDA + 16 * m + 4 * lg);
 #pragma unroll
-            for (int bj = 0; bj < bi; ++bj) {
-                float acc = 0.f;
-#pragma unroll
-                for (int m = bj; m < bi; ++m) {
-#pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        acc += sA[(16 * bi + rr) * LDA + 16 * m + e] * sA[(16 * m + e) * LDA + 16 * bj + cc];
-                }
-                xv[bj] = acc;
+                for (int j = 0; j < 4; ++j)
+                    X = __builtin_amdgcn_mfma_f32_16x16x4f32(am[j], sA[(16 * m + 4 * lg + j) * LDA + 16 * bj + lr], X,
+                                                             0, 0, 0);
             }
-#pragma unroll
-            for (int bj = 0; bj < bi; ++bj) sX[bj * 256 + rr * 16 + cc] = xv[bj];
-            lds_barrier();
-#pragma unroll
-            for (int bj = 0; bj < bi; ++bj) {
-                float acc = 0.f;
-#pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    acc += sA[(16 * bi + rr) * LDA + 16 * bi + e] * sX[bj * 256 + e * 16 + cc];
-                sA[(16 * bi + rr) * LDA + 16 * bj + cc] = -acc;
-            }
-            lds_barrier();
         }
+        lds_barrier();  // every read of A's block row bi is done before T overwrites it
+        if (bj < bi) {
+            const f32x4 tii = *reinterpret_cast<const f32x4*>(sA + (16 * bi + lr) * LDA + 16 * bi + 4 * lg);
+            f32x4 Y = zero4();
+#pragma unroll
+            for (int j = 0; j < 4; ++j) Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tii[j], X[j], Y, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lds_put(&sA[(16 * bi + 4 * lg + i) * LDA + 16 * bj + lr], -Y[i]);
+        }
+        lds_barrier();
     }
 
     // ---- 5. W = T (beta K e^b),  U' = T (beta V), staged for 16-byte stores --
     {
-        const int ti = wave;
+        // wave w: token tile ti = w % 4, half (w / 4) of the W and U' columns
+        const int ti = wave & 3, half = wave >> 2;
+        constexpr int TNW = DK / 32, TNU = DV / 32;  // 16-column tiles per half
         const Frag<E> ft0 = ld_frag_from_f32<E>(sA + (16 * ti + lr) * LDA + 8 * lg);
         const Frag<E> ft1 = ld_frag_from_f32<E>(sA + (16 * ti + lr) * LDA + 32 + 8 * lg);
         // (rows 0..31 of T are exactly zero beyond token 31, so for ti < 2 the
         // second product adds exact zeros; it is issued anyway to keep the
         // accumulation unconditional)
-        f32x4 accW[DK / 16], accU[DV / 16];
+        f32x4 accW[TNW], accU[TNU];
 #pragma unroll
-        for (int tn = 0; tn < DK / 16; ++tn) {
-            accW[tn] = mma(ft0, ld_frag(sKbt + (16 * tn + lr) * LDT + 8 * lg), zero4());
-            accW[tn] = mma(ft1, ld_frag(sKbt + (16 * tn + lr) * LDT + 32 + 8 * lg), accW[tn]);
+        for (int u = 0; u < TNW; ++u) {
+            const int tn = half * TNW + u;
+            accW[u] = mma(ft0, ld_frag(sKbt + (16 * tn + lr) * LDT + 8 * lg), zero4());
+            accW[u] = mma(ft1, ld_frag(sKbt + (16 * tn + lr) * LDT + 32 + 8 * lg), accW[u]);
         }
 #pragma unroll
-        for (int tn = 0; tn < DV / 16; ++tn) {
-            accU[tn] = mma(ft0, ld_frag(sVt + (16 * tn + lr) * LDT + 8 * lg), zero4());
-            accU[tn] = mma(ft1, ld_frag(sVt + (16 * tn + lr) * LDT + 32 + 8 * lg), accU[tn]);
+        for (int u = 0; u < TNU; ++u) {
+            const int tn = half * TNU + u;
+            accU[u] = mma(ft0, ld_frag(sVt + (16 * tn + lr) * LDT + 8 * lg), zero4());
+            accU[u] = mma(ft1, ld_frag(sVt + (16 * tn + lr) * LDT + 32 + 8 * lg), accU[u]);
         }
         // U' for the walk: per 16-column slice tn and lane, the 16 values the
         // lane holds in the walk's accumulator layout (token tiles ti = 0..3,
@@ -576,20 +627,22 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
         {
             E* up = Upo + ch * C * DV;
 #pragma unroll
-            for (int tn = 0; tn < DV / 16; ++tn) {
+            for (int u = 0; u < TNU; ++u) {
+                const int tn = half * TNU + u;
                 E vals[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) vals[i] = Elt<E>::from(accU[tn][i]);
+                for (int i = 0; i < 4; ++i) vals[i] = Elt<E>::from(accU[u][i]);
                 store_run4<E>(up + (tn * 64 + lane) * 16 + 4 * ti, vals);
             }
         }
         lds_barrier();  // every wave is done with sKbt / sVt / sA
         E* sWst = reinterpret_cast<E*>(smem);  // [C][DK], channel columns in fragment order
 #pragma unroll
-        for (int tn = 0; tn < DK / 16; ++tn)
+        for (int u = 0; u < TNW; ++u)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                lds_put(&sWst[(16 * ti + 4 * lg + i) * LDK + frag_pos(16 * tn + lr)], Elt<E>::from(accW[tn][i]));
+                lds_put(&sWst[(16 * ti + 4 * lg + i) * LDK + frag_pos(16 * (half * TNW + u) + lr)],
+                        Elt<E>::from(accW[u][i]));
         lds_barrier();
         copy_tile_out_frag<E, C, DK>(Wo + ch * C * DK, sWst, LDK, tid);
     }
@@ -1176,7 +1229,7 @@ static hipError_t launch_intra(const ChunkArgs& a, const ChunkWorkspace& ws, hip
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)a.max_chunks, (unsigned)a.H), dim3(256), L::bytes, stream,
+    hipLaunchKernelGGL(kern, dim3((unsigned)a.max_chunks, (unsigned)a.H), dim3(kIntraThreads), L::bytes, stream,
                        (const E*)a.q, (const E*)a.k, (const E*)a.v, (const E*)a.g, (const E*)a.beta, ws.header,
                        ws.cu, ws.chunk_off, a.N, a.H, (E*)ws.W, (E*)ws.QG, (E*)ws.KdT, (E*)ws.Up, (E*)ws.P,
                        ws.Gn);
