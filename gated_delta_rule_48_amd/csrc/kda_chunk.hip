@@ -681,9 +681,16 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
 // fragment of the next product, and fragment-major (fm_off), so every
 // fragment is one contiguous 1 KB block, copied into LDS unchanged; U' is
 // stored per slice in the accumulator layout of the walk's lanes.
-constexpr int kRing = 4;
+#ifndef KDA_WALK_RING
+#define KDA_WALK_RING 2
+#endif
+#ifndef KDA_WALK_SLOTS
+#define KDA_WALK_SLOTS 4
+#endif
+constexpr int kRing = KDA_WALK_RING;          // S/U hand-over slots
+constexpr int kMaxSlots = KDA_WALK_SLOTS;     // most operand slots staged ahead
 #ifndef KDA_WALK_PREFETCH
-#define KDA_WALK_PREFETCH 4
+#define KDA_WALK_PREFETCH 5
 #endif
 constexpr int kWalkPrefetch = KDA_WALK_PREFETCH;
 constexpr int kWalkThreads = 256;
@@ -773,7 +780,7 @@ struct WalkLayout {
     static constexpr int SINK_B = 256, CNT_B = 64;
     static constexpr int FIXED = RING_S + RING_U + 2 * O_B + SINK_B + CNT_B;
     static constexpr int RFIT = (kLdsBytes - FIXED) / SLOT;
-    static constexpr int R = RFIT > 3 ? 3 : RFIT;  // operand slots
+    static constexpr int R = RFIT > kMaxSlots ? kMaxSlots : RFIT;  // operand slots
     static constexpr bool STAGED = R >= 2;
     static constexpr int OPS_B = STAGED ? R * SLOT : 0;
     static constexpr int off_ringS = OPS_B, off_ringU = off_ringS + RING_S, off_O = off_ringU + RING_U;
