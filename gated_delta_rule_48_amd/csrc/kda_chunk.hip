@@ -132,8 +132,8 @@ struct IntraLayout {
     static constexpr size_t r1_max = r1_a > r1_b ? (r1_a > r1_c ? r1_a : r1_c) : (r1_b > r1_c ? r1_b : r1_c);
     static constexpr size_t off_A = (r1_max + 15) / 16 * 16;  // sA; sBnd before A
     static constexpr size_t off_beta = off_A + (size_t)C * LDA * 4;
-    static constexpr size_t off_scale = off_beta + C * 4;  // sColScale, sRowScale; sPart before them
-    static constexpr size_t scale_bytes = (size_t)(NCS + 4) * DK * 4;
+    static constexpr size_t off_scale = off_beta + C * 4;  // sColScale; sPart before it
+    static constexpr size_t scale_bytes = (size_t)NCS * DK * 4;
     static constexpr size_t part_bytes = (size_t)NPART * DK * 4;
     static constexpr size_t bytes = off_scale + (scale_bytes > part_bytes ? scale_bytes : part_bytes);
     static_assert((size_t)NBND * DK * 4 <= (size_t)C * LDA * 4, "sBnd fits in sA");
@@ -303,7 +303,6 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
     float* sBnd = sA;  // [12][DK] tile-boundary prefix sums, dead before A is written
     float* sBeta = reinterpret_cast<float*>(smem + L::off_beta);
     float* sColScale = reinterpret_cast<float*>(smem + L::off_scale);  // [10][DK]
-    float* sRowScale = sColScale + L::NCS * DK;                          // [4][DK]
     float* sPart = sColScale;  // [NPART][DK], dead before the scales are written
 
     if (hdr->bad_seqlens) return;
@@ -386,19 +385,28 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
     lds_barrier();
     const float last0 = sBnd[11 * DK + c0], last1 = sBnd[11 * DK + c0 + 1];
 
-    // ---- 2. decayed operands (every factor <= 1) and tile-pair scales -------
+    // ---- 2. decayed operands and tile-pair scales ---------------------------
+    // Every 16-row tile uses its middle row m as the row-side reference:
+    // Kr = k e^{b - b_m}, Qr = q e^{b - b_m} span at most eight tokens of
+    // decay on either side of m (exponent capped at 80); Kt = k e^{b_e - b}
+    // <= 1 with b_e the tile's last row.  e^{b} and e^{b_last - b} follow by
+    // multiplying with the per-tile factors e^{b_m} and e^{b_last - b_e}.
+    static_assert(16 % RPT == 0, "a thread's rows lie in one tile");
     float kb[RPT][2];  // beta k e^b, kept for the W right-hand side
     E kd0[RPT], kd1[RPT];
+    const float* bm = sBnd + (3 * ((part * RPT) >> 4) + 1) * DK;  // tile middle
+    const float* be = bm + DK;                                    // tile end
+    const float em0 = gate_exp<E>(bm[c0]), em1 = gate_exp<E>(bm[c0 + 1]);
+    const float le0 = gate_exp<E>(last0 - be[c0]), le1 = gate_exp<E>(last1 - be[c0 + 1]);
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
         const int row = part * RPT + r;
-        const float* bs = sBnd + (3 * (row >> 4)) * DK;  // tile start
-        const float* be = bs + 2 * DK;                  // tile end
         const float k0 = kraw[r].lo(), k1 = kraw[r].hi(), q0 = qraw[r].lo(), q1 = qraw[r].hi();
-        const float e0 = gate_exp<E>(bb[r][0] - bs[c0]), e1 = gate_exp<E>(bb[r][1] - bs[c0 + 1]);
+        const float e0 = gate_exp<E>(fminf(bb[r][0] - bm[c0], 80.f));
+        const float e1 = gate_exp<E>(fminf(bb[r][1] - bm[c0 + 1], 80.f));
         const float f0 = gate_exp<E>(be[c0] - bb[r][0]), f1 = gate_exp<E>(be[c0 + 1] - bb[r][1]);
-        const float x0 = gate_exp<E>(bb[r][0]), x1 = gate_exp<E>(bb[r][1]);
-        const float d0 = gate_exp<E>(last0 - bb[r][0]), d1 = gate_exp<E>(last1 - bb[r][1]);
+        const float x0 = em0 * e0, x1 = em1 * e1;  // e^{b}
+        const float d0 = le0 * f0, d1 = le1 * f1;  // e^{b_last - b}
         store2<E>(sKr + row * LDK + c0, k0 * e0, k1 * e1);
         store2<E>(sQr + row * LDK + c0, q0 * e0, q1 * e1);
         store2<E>(sKt + row * LDK + c0, k0 * f0, k1 * f1);
@@ -422,25 +430,15 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
             Gno[ch * DK + c0 + 1] = gate_exp<E>(last1);
         }
     }
-    // Tile pair (ti, tj), tj < ti: e^{b_t - b_i} = [k-side e^{b_t - b_s(ti)}]
-    //   * e^{b_s(ti) - b_e(tj)} * [e^{b_e(tj) - b_i}], all three <= 1.
-    // Diagonal tile ti: reference m = 16 ti + 8: the row side takes
-    //   e^{b_s - b_m} and the column side e^{b_m - b_e}; each spans at most
-    //   eight tokens of decay.  The exponent is capped at 80 to stay finite.
-    for (int e = tid; e < 14 * DK; e += kIntraThreads) {
+    // Tile pair (ti, tj), tj <= ti:  e^{b_t - b_i} = [row side e^{b_t - b_m(ti)}]
+    //   * e^{b_m(ti) - b_e(tj)} * [column side e^{b_e(tj) - b_i}].  The middle
+    // factor is <= 1 for tj < ti and spans at most eight tokens for tj = ti.
+    for (int e = tid; e < L::NCS * DK; e += kIntraThreads) {
         const int v = e / DK, c = e % DK;
-        float x;
-        if (v < L::NCS) {
-            const int ti = (v >= 6) ? 3 : (v >= 3) ? 2 : (v >= 1) ? 1 : 0;
-            const int tj = v - ti * (ti + 1) / 2;
-            x = (tj < ti) ? sBnd[(3 * ti) * DK + c] - sBnd[(3 * tj + 2) * DK + c]
-                          : sBnd[(3 * ti + 1) * DK + c] - sBnd[(3 * ti + 2) * DK + c];
-            sColScale[v * DK + c] = gate_exp<E>(fminf(x, 80.f));
-        } else {
-            const int ti = v - L::NCS;
-            x = sBnd[(3 * ti) * DK + c] - sBnd[(3 * ti + 1) * DK + c];
-            sRowScale[ti * DK + c] = gate_exp<E>(fminf(x, 80.f));
-        }
+        const int ti = (v >= 6) ? 3 : (v >= 3) ? 2 : (v >= 1) ? 1 : 0;
+        const int tj = v - ti * (ti + 1) / 2;
+        const float x = sBnd[(3 * ti + 1) * DK + c] - sBnd[(3 * tj + 2) * DK + c];
+        sColScale[v * DK + c] = gate_exp<E>(fminf(x, 80.f));
     }
     lds_barrier();
 
@@ -462,17 +460,12 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
             const int ti = pq ? pti1 : pti0, tj = pq ? ptj1 : ptj0;
             f32x4 accA = zero4(), accP = zero4();
             const float* cs = sColScale + (ti * (ti + 1) / 2 + tj) * DK;
-            const float* rs = sRowScale + ti * DK;
 #pragma unroll
             for (int ks = 0; ks < DK / 32; ++ks) {
                 const int cb = 32 * ks + 8 * lg;
                 const Frag<E> fb = scale_frag(ld_frag(sKt + (16 * tj + lr) * LDK + cb), cs + cb);
-                Frag<E> fa = ld_frag(sKr + (16 * ti + lr) * LDK + cb);
-                Frag<E> fq = ld_frag(sQr + (16 * ti + lr) * LDK + cb);
-                if (tj == ti) {
-                    fa = scale_frag(fa, rs + cb);
-                    fq = scale_frag(fq, rs + cb);
-                }
+                const Frag<E> fa = ld_frag(sKr + (16 * ti + lr) * LDK + cb);
+                const Frag<E> fq = ld_frag(sQr + (16 * ti + lr) * LDK + cb);
                 accA = mma(fa, fb, accA);
                 accP = mma(fq, fb, accP);
             }
