@@ -117,7 +117,7 @@ struct IntraLayout {
     static constexpr int RPTV = C / NPARTV;
     static_assert(RPT % 4 == 0 && RPTV % 4 == 0, "row runs of four");
     static constexpr int NBND = 12;       // b at rows 16i, 16i+8, 16i+15 of the four 16-row tiles
-    static constexpr int NCS = 10;        // column scales of the lower tile pairs (ti, tj <= ti)
+    static constexpr int NCS = 12;        // tile-pair decay factors (see the intra-chunk kernel)
     // Region R1: [Kr | Qr | Kt] ([token][channel], E) while A and P are
     // formed; afterwards [Kbt | Vt] ([channel][token], E) followed by the P
     // staging tile [C][C+PAD]; at the very end the W staging tile [C][DK+PAD]
@@ -132,7 +132,7 @@ struct IntraLayout {
     static constexpr size_t r1_max = r1_a > r1_b ? (r1_a > r1_c ? r1_a : r1_c) : (r1_b > r1_c ? r1_b : r1_c);
     static constexpr size_t off_A = (r1_max + 15) / 16 * 16;  // sA; sBnd before A
     static constexpr size_t off_beta = off_A + (size_t)C * LDA * 4;
-    static constexpr size_t off_scale = off_beta + C * 4;  // sColScale; sPart before it
+    static constexpr size_t off_scale = off_beta + C * 4;  // sTileF; sPart before it
     static constexpr size_t scale_bytes = (size_t)NCS * DK * 4;
     static constexpr size_t part_bytes = (size_t)NPART * DK * 4;
     static constexpr size_t bytes = off_scale + (scale_bytes > part_bytes ? scale_bytes : part_bytes);
@@ -260,6 +260,29 @@ __device__ __forceinline__ void copy_tile_out_frag(E* __restrict__ dst, const E*
     }
 }
 
+// f[j] <- (f[j] * s[j]) * t[j], j = 0..7, the two products in this order.
+__device__ __forceinline__ Frag<bf16_t> scale_frag(Frag<bf16_t> f, const float* s, const float* t) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(s), b = *reinterpret_cast<const f32x4*>(s + 4);
+    const f32x4 c = *reinterpret_cast<const f32x4*>(t), d = *reinterpret_cast<const f32x4*>(t + 4);
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 w = {f32x2_to_bf16x2(bf16_to_f32(f.v[0]) * a[0] * c[0], bf16_to_f32(f.v[1]) * a[1] * c[1]),
+                     f32x2_to_bf16x2(bf16_to_f32(f.v[2]) * a[2] * c[2], bf16_to_f32(f.v[3]) * a[3] * c[3]),
+                     f32x2_to_bf16x2(bf16_to_f32(f.v[4]) * b[0] * d[0], bf16_to_f32(f.v[5]) * b[1] * d[1]),
+                     f32x2_to_bf16x2(bf16_to_f32(f.v[6]) * b[2] * d[2], bf16_to_f32(f.v[7]) * b[3] * d[3])};
+    f.v = __builtin_bit_cast(u16x8, w);
+    return f;
+}
+__device__ __forceinline__ Frag<float> scale_frag(Frag<float> f, const float* s, const float* t) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(s), b = *reinterpret_cast<const f32x4*>(s + 4);
+    const f32x4 c = *reinterpret_cast<const f32x4*>(t), d = *reinterpret_cast<const f32x4*>(t + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f.v[j] = f.v[j] * a[j] * c[j];
+        f.v[j + 4] = f.v[j + 4] * b[j] * d[j];
+    }
+    return f;
+}
+
 // f[j] <- f[j] * s[j], j = 0..7 (s: 8 contiguous fp32 in LDS).
 __device__ __forceinline__ Frag<bf16_t> scale_frag(Frag<bf16_t> f, const float* s) {
     const f32x4 a = *reinterpret_cast<const f32x4*>(s);
@@ -302,8 +325,8 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
     float* sA = reinterpret_cast<float*>(smem + L::off_A);
     float* sBnd = sA;  // [12][DK] tile-boundary prefix sums, dead before A is written
     float* sBeta = reinterpret_cast<float*>(smem + L::off_beta);
-    float* sColScale = reinterpret_cast<float*>(smem + L::off_scale);  // [10][DK]
-    float* sPart = sColScale;  // [NPART][DK], dead before the scales are written
+    float* sTileF = reinterpret_cast<float*>(smem + L::off_scale);  // [12][DK] tile-pair factors
+    float* sPart = sTileF;  // [NPART][DK], dead before the tile factors are written
 
     if (hdr->bad_seqlens) return;
     const int cid = blockIdx.x;
@@ -386,27 +409,26 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
     const float last0 = sBnd[11 * DK + c0], last1 = sBnd[11 * DK + c0 + 1];
 
     // ---- 2. decayed operands and tile-pair scales ---------------------------
-    // Every 16-row tile uses its middle row m as the row-side reference:
-    // Kr = k e^{b - b_m}, Qr = q e^{b - b_m} span at most eight tokens of
-    // decay on either side of m (exponent capped at 80); Kt = k e^{b_e - b}
-    // <= 1 with b_e the tile's last row.  e^{b} and e^{b_last - b} follow by
-    // multiplying with the per-tile factors e^{b_m} and e^{b_last - b_e}.
+    // All three operands of A and P are referred to the middle row m of
+    // their 16-row tile: Kr = k e^{b - b_m}, Qr = q e^{b - b_m},
+    // Kt = k e^{b_m - b}.  Each factor spans at most eight tokens of decay,
+    // so it stays a normal fp32 / bf16 number whenever the decay over eight
+    // tokens is above e^-80 (exponents are capped at 80 beyond that).
+    // e^{b} and e^{b_last - b} are <= 1 and taken directly.
     static_assert(16 % RPT == 0, "a thread's rows lie in one tile");
     float kb[RPT][2];  // beta k e^b, kept for the W right-hand side
     E kd0[RPT], kd1[RPT];
     const float* bm = sBnd + (3 * ((part * RPT) >> 4) + 1) * DK;  // tile middle
-    const float* be = bm + DK;                                    // tile end
-    const float em0 = gate_exp<E>(bm[c0]), em1 = gate_exp<E>(bm[c0 + 1]);
-    const float le0 = gate_exp<E>(last0 - be[c0]), le1 = gate_exp<E>(last1 - be[c0 + 1]);
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
         const int row = part * RPT + r;
         const float k0 = kraw[r].lo(), k1 = kraw[r].hi(), q0 = qraw[r].lo(), q1 = qraw[r].hi();
         const float e0 = gate_exp<E>(fminf(bb[r][0] - bm[c0], 80.f));
         const float e1 = gate_exp<E>(fminf(bb[r][1] - bm[c0 + 1], 80.f));
-        const float f0 = gate_exp<E>(be[c0] - bb[r][0]), f1 = gate_exp<E>(be[c0 + 1] - bb[r][1]);
-        const float x0 = em0 * e0, x1 = em1 * e1;  // e^{b}
-        const float d0 = le0 * f0, d1 = le1 * f1;  // e^{b_last - b}
+        const float f0 = gate_exp<E>(fminf(bm[c0] - bb[r][0], 80.f));
+        const float f1 = gate_exp<E>(fminf(bm[c0 + 1] - bb[r][1], 80.f));
+        const float x0 = gate_exp<E>(bb[r][0]), x1 = gate_exp<E>(bb[r][1]);
+        const float d0 = gate_exp<E>(last0 - bb[r][0]), d1 = gate_exp<E>(last1 - bb[r][1]);
         store2<E>(sKr + row * LDK + c0, k0 * e0, k1 * e1);
         store2<E>(sQr + row * LDK + c0, q0 * e0, q1 * e1);
         store2<E>(sKt + row * LDK + c0, k0 * f0, k1 * f1);
@@ -430,15 +452,31 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
             Gno[ch * DK + c0 + 1] = gate_exp<E>(last1);
         }
     }
-    // Tile pair (ti, tj), tj <= ti:  e^{b_t - b_i} = [row side e^{b_t - b_m(ti)}]
-    //   * e^{b_m(ti) - b_e(tj)} * [column side e^{b_e(tj) - b_i}].  The middle
-    // factor is <= 1 for tj < ti and spans at most eight tokens for tj = ti.
+    // Tile pairs.  Diagonal (ti, ti): e^{b_t - b_i} = Kr-side e^{b_t - b_m} times
+    // Kt-side e^{b_m - b_i}, no further factor.  Below the diagonal (tj < ti)
+    // the row operand is taken to the tile start s(ti) and then to the end
+    // e(tj) of the column tile, and the column operand to e(tj):
+    //   e^{b_t - b_i} = (e^{b_t - b_m(ti)} e^{b_m(ti) - b_s(ti)}) e^{b_s(ti) - b_e(tj)}
+    //                   * (e^{b_m(tj) - b_i} e^{b_e(tj) - b_m(tj)}),
+    // three factors <= 1 applied one after another, so no intermediate value
+    // drops below the final product (anything that underflows is negligible).
+    //   sTileF[ti - 1]     e^{b_m(ti) - b_s(ti)}, ti = 1..3
+    //   sTileF[3 + tj]     e^{b_e(tj) - b_m(tj)}, tj = 0..2
+    //   sTileF[6 + p]      e^{b_s(ti) - b_e(tj)}, p = ti (ti - 1) / 2 + tj
     for (int e = tid; e < L::NCS * DK; e += kIntraThreads) {
         const int v = e / DK, c = e % DK;
-        const int ti = (v >= 6) ? 3 : (v >= 3) ? 2 : (v >= 1) ? 1 : 0;
-        const int tj = v - ti * (ti + 1) / 2;
-        const float x = sBnd[(3 * ti + 1) * DK + c] - sBnd[(3 * tj + 2) * DK + c];
-        sColScale[v * DK + c] = gate_exp<E>(fminf(x, 80.f));
+        float x;
+        if (v < 3) {
+            x = sBnd[(3 * (v + 1) + 1) * DK + c] - sBnd[(3 * (v + 1)) * DK + c];
+        } else if (v < 6) {
+            x = sBnd[(3 * (v - 3) + 2) * DK + c] - sBnd[(3 * (v - 3) + 1) * DK + c];
+        } else {
+            const int p = v - 6;
+            const int ti = (p >= 3) ? 3 : (p >= 1) ? 2 : 1;
+            const int tj = p - ti * (ti - 1) / 2;
+            x = sBnd[(3 * ti) * DK + c] - sBnd[(3 * tj + 2) * DK + c];
+        }
+        sTileF[v * DK + c] = gate_exp<E>(x);
     }
     lds_barrier();
 
@@ -459,13 +497,21 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
         if (pq < npair) {
             const int ti = pq ? pti1 : pti0, tj = pq ? ptj1 : ptj0;
             f32x4 accA = zero4(), accP = zero4();
-            const float* cs = sColScale + (ti * (ti + 1) / 2 + tj) * DK;
+            const bool diag = tj == ti;
+            const float* rowf = sTileF + (ti - 1) * DK;                       // off-diagonal only
+            const float* colf = sTileF + (3 + tj) * DK;
+            const float* midf = sTileF + (6 + ti * (ti - 1) / 2 + tj) * DK;
 #pragma unroll
             for (int ks = 0; ks < DK / 32; ++ks) {
                 const int cb = 32 * ks + 8 * lg;
-                const Frag<E> fb = scale_frag(ld_frag(sKt + (16 * tj + lr) * LDK + cb), cs + cb);
-                const Frag<E> fa = ld_frag(sKr + (16 * ti + lr) * LDK + cb);
-                const Frag<E> fq = ld_frag(sQr + (16 * ti + lr) * LDK + cb);
+                Frag<E> fb = ld_frag(sKt + (16 * tj + lr) * LDK + cb);
+                Frag<E> fa = ld_frag(sKr + (16 * ti + lr) * LDK + cb);
+                Frag<E> fq = ld_frag(sQr + (16 * ti + lr) * LDK + cb);
+                if (!diag) {
+                    fb = scale_frag(fb, colf + cb);
+                    fa = scale_frag(fa, rowf + cb, midf + cb);
+                    fq = scale_frag(fq, rowf + cb, midf + cb);
+                }
                 accA = mma(fa, fb, accA);
                 accP = mma(fq, fb, accP);
             }

@@ -110,6 +110,85 @@ def test_chunk_no_decay_deltanet():
     _assert_close("S_T", S, S_ref, TOL["f32"])
 
 
+def test_chunk_beta_zero_pure_decay():
+    """beta = 0: nothing is written, the initial state only decays (A = 0,
+    T = I, W = U' = 0 inside the chunked path)."""
+    _announce("beta zero")
+    d = chunk_case(2, 128, 128, "f32", "channel", [150, 64], s0_sigma=0.1, seed=11)
+    d["beta"] = np.zeros_like(d["beta"])
+    o, S = _run_chunk(d, "f32", "channel")
+    o_ref, S_ref = _oracle_chunk(d, "channel")
+    _assert_close("o", o, o_ref, TOL["f32"])
+    _assert_close("S_T", S, S_ref, TOL["f32"])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunk_gate_at_contract_edge(dtype):
+    """g = -10 on every channel of every token: decay over eight tokens is
+    exactly e^-80, the edge of the documented gate range, where the in-tile
+    decay factors reach e^80."""
+    _announce(f"gate edge {dtype}")
+    d = chunk_case(2, 128, 64, dtype, "channel", [130, 64], s0_sigma=0.1, seed=12)
+    g = np.full(d["g"].shape, -10.0, dtype=np.float32)
+    d["g"] = synth.bf16_bits(g) if dtype == "bf16" else g
+    o, S = _run_chunk(d, dtype, "channel")
+    o_ref, S_ref = _oracle_chunk(d, "channel")
+    _assert_close("o", o, o_ref, TOL[dtype])
+    _assert_close("S_T", S, S_ref, TOL[dtype])
+
+
+def test_chunk_many_ragged_sequences():
+    """300 packed sequences of 0..150 tokens (many empty, single-token and
+    chunk-boundary lengths), H = 3: more sequences than one pass of the
+    chunk-map scan, and a head count that is not a multiple of 8."""
+    _announce("many ragged sequences")
+    rng = np.random.default_rng(13)
+    lengths = rng.integers(0, 151, size=300)
+    lengths[:12] = [0, 1, 63, 64, 65, 127, 128, 129, 0, 0, 1, 150]
+    d = chunk_case(3, 64, 64, "bf16", "channel", list(lengths), s0_sigma=0.1, seed=13)
+    o, S = _run_chunk(d, "bf16", "channel")
+    o_ref, S_ref = _oracle_chunk(d, "channel")
+    _assert_close("o", o, o_ref, TOL["bf16"])
+    _assert_close("S_T", S, S_ref, TOL["bf16"])
+
+
+def test_chunk_head_gate_equals_broadcast_channel_gate():
+    """A per-head gate gives bit-identical results to the per-channel gate
+    filled with the same value on every channel (boundary semantics, no
+    oracle involved)."""
+    _announce("head gate = broadcast channel gate")
+    d = chunk_case(2, 128, 128, "bf16", "head", [100, 37], s0_sigma=0.1, seed=14)
+    x = dev_inputs(d, "bf16")
+    g_ch = x["g"][:, :, None].expand(-1, -1, 128).contiguous()
+    o1, S1 = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], S0=x["S0"], cu_seqlens=x["cu_seqlens"],
+                           per_head_gate=True)
+    o2, S2 = kda.chunk_fwd(x["q"], x["k"], x["v"], g_ch, x["beta"], S0=x["S0"], cu_seqlens=x["cu_seqlens"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(S1, S2)
+
+
+def test_chunk_workspace_reused_across_sizes():
+    """One workspace serves a large call, then a smaller one, then the large
+    one again: every result equals a call with a fresh workspace."""
+    _announce("workspace reuse")
+    big = chunk_case(2, 128, 128, "bf16", "channel", [300, 5, 129], s0_sigma=0.1, seed=15)
+    small = chunk_case(2, 128, 128, "bf16", "channel", [70], s0_sigma=0.1, seed=16)
+    xb, xs = dev_inputs(big, "bf16"), dev_inputs(small, "bf16")
+    T = xb["q"].shape[0]
+    ws = torch.full((kda.chunk_fwd_workspace_size(T, 3, 2, 128, 128),), 255, dtype=torch.uint8, device="cuda")
+    outs = []
+    for x in (xb, xs, xb):
+        outs.append(kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], S0=x["S0"],
+                                  cu_seqlens=x["cu_seqlens"], workspace=ws))
+    fresh_b = kda.chunk_fwd(xb["q"], xb["k"], xb["v"], xb["g"], xb["beta"], S0=xb["S0"], cu_seqlens=xb["cu_seqlens"])
+    fresh_s = kda.chunk_fwd(xs["q"], xs["k"], xs["v"], xs["g"], xs["beta"], S0=xs["S0"], cu_seqlens=xs["cu_seqlens"])
+    torch.cuda.synchronize()
+    for (o, S), (fo, fS) in zip(outs, (fresh_b, fresh_s, fresh_b)):
+        assert torch.equal(o, fo)
+        assert torch.equal(S, fS)
+
+
 def test_chunk_deterministic_and_s0_none_equals_zeros():
     _announce("determinism")
     d = chunk_case(2, 128, 128, "bf16", "channel", [200, 77], seed=9)
