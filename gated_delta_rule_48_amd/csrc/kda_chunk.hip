@@ -342,31 +342,36 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
     const int lr = lane & 15, lg = lane >> 4;
 
     // ---- 0. every global load of the chunk, issued up front ----------------
+    // In the order of first use (g for step 1, k and q for step 2, v and beta
+    // by the end of step 2); loads complete in order, so each step waits only
+    // for its own inputs.  Rows past the chunk's end load the last valid row
+    // and are zeroed where they are first used: a load under a condition
+    // would make the compiler wait for it right at the branch.
     const int cp = tid % (DK / 2), part = tid / (DK / 2);
     const int c0 = 2 * cp;
     const int jp = tid % (DV / 2), vpart = tid / (DV / 2);
     const int j0 = 2 * jp;
+    auto clamp_row = [&](int row) { return min(row, len - 1); };
     Pair2<E> graw[RPT], kraw[RPT], qraw[RPT], vraw[RPTV];
     float gh[RPT];
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
-        const int row = part * RPT + r;
-        const bool ok = row < len;
-        const int64_t off = ((t0 + row) * H + h) * DK + c0;
-        if (HG) {
-            gh[r] = ok ? Elt<E>::load(g + (t0 + row) * H + h) : 0.f;
-        } else {
-            if (ok) graw[r].load(g + off); else graw[r] = Pair2<E>{};
-        }
-        if (ok) { kraw[r].load(k + off); qraw[r].load(q + off); }
-        else { kraw[r] = Pair2<E>{}; qraw[r] = Pair2<E>{}; }
+        const int64_t tr = t0 + clamp_row(part * RPT + r);
+        if (HG) gh[r] = Elt<E>::load(g + tr * H + h);
+        else graw[r].load(g + (tr * H + h) * DK + c0);
     }
 #pragma unroll
-    for (int r = 0; r < RPTV; ++r) {
-        const int row = vpart * RPTV + r;
-        if (row < len) vraw[r].load(v + ((t0 + row) * H + h) * DV + j0); else vraw[r] = Pair2<E>{};
+    for (int r = 0; r < RPT; ++r) {
+        const int64_t off = ((t0 + clamp_row(part * RPT + r)) * H + h) * DK + c0;
+        kraw[r].load(k + off);
+        qraw[r].load(q + off);
     }
-    const float beta_t = (tid < len) ? Elt<E>::load(beta + (t0 + tid) * H + h) : 0.f;
+#pragma unroll
+    for (int r = 0; r < RPTV; ++r) vraw[r].load(v + ((t0 + clamp_row(vpart * RPTV + r)) * H + h) * DV + j0);
+    // beta of token `lane`, loaded by every wave (same 64 values) so that its
+    // store into LDS needs no branch for the compiler to sink the load into
+    const float beta_raw = Elt<E>::load(beta + (t0 + clamp_row(lane)) * H + h);
+    auto row_ok = [&](int r) { return part * RPT + r < len; };
 
     // ---- 1. chunk-local inclusive prefix sum of the log-gate ----------------
     float bb[RPT][2];
@@ -374,15 +379,14 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
         float run0 = 0.f, run1 = 0.f;
 #pragma unroll
         for (int r = 0; r < RPT; ++r) {
-            run0 += HG ? gh[r] : graw[r].lo();
-            run1 += HG ? gh[r] : graw[r].hi();
+            run0 += row_ok(r) ? (HG ? gh[r] : graw[r].lo()) : 0.f;
+            run1 += row_ok(r) ? (HG ? gh[r] : graw[r].hi()) : 0.f;
             bb[r][0] = run0;
             bb[r][1] = run1;
         }
         sPart[part * DK + c0] = run0;
         sPart[part * DK + c0 + 1] = run1;
     }
-    if (tid < C) sBeta[tid] = beta_t;
     lds_barrier();
     {
         float off0 = 0.f, off1 = 0.f;
@@ -416,13 +420,15 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
     // tokens is above e^-80 (exponents are capped at 80 beyond that).
     // e^{b} and e^{b_last - b} are <= 1 and taken directly.
     static_assert(16 % RPT == 0, "a thread's rows lie in one tile");
-    float kb[RPT][2];  // beta k e^b, kept for the W right-hand side
+    float kx[RPT][2];  // k e^b; times beta it is the W right-hand side
     E kd0[RPT], kd1[RPT];
     const float* bm = sBnd + (3 * ((part * RPT) >> 4) + 1) * DK;  // tile middle
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
         const int row = part * RPT + r;
-        const float k0 = kraw[r].lo(), k1 = kraw[r].hi(), q0 = qraw[r].lo(), q1 = qraw[r].hi();
+        const bool ok = row_ok(r);
+        const float k0 = ok ? kraw[r].lo() : 0.f, k1 = ok ? kraw[r].hi() : 0.f;
+        const float q0 = ok ? qraw[r].lo() : 0.f, q1 = ok ? qraw[r].hi() : 0.f;
         const float e0 = gate_exp<E>(fminf(bb[r][0] - bm[c0], 80.f));
         const float e1 = gate_exp<E>(fminf(bb[r][1] - bm[c0 + 1], 80.f));
         const float f0 = gate_exp<E>(fminf(bm[c0] - bb[r][0], 80.f));
@@ -433,9 +439,8 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
         store2<E>(sQr + row * LDK + c0, q0 * e0, q1 * e1);
         store2<E>(sKt + row * LDK + c0, k0 * f0, k1 * f1);
         store2<E>(QGo + ch * C * DK + fm_off<DK>(row, frag_pos(c0)), q0 * x0, q1 * x1);
-        const float bt = sBeta[row];
-        kb[r][0] = bt * k0 * x0;
-        kb[r][1] = bt * k1 * x1;
+        kx[r][0] = k0 * x0;
+        kx[r][1] = k1 * x1;
         kd0[r] = Elt<E>::from(k0 * d0);
         kd1[r] = Elt<E>::from(k1 * d1);
     }
@@ -478,6 +483,7 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
         }
         sTileF[v * DK + c] = gate_exp<E>(x);
     }
+    sBeta[lane] = lane < len ? beta_raw : 0.f;  // every wave writes the same values
     lds_barrier();
 
     // ---- 3. A = K K^T with decay (strictly lower, row-scaled by beta) -> LDS
@@ -568,8 +574,9 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
         E r0[RPT], r1[RPT];
 #pragma unroll
         for (int r = 0; r < RPT; ++r) {
-            r0[r] = Elt<E>::from(kb[r][0]);
-            r1[r] = Elt<E>::from(kb[r][1]);
+            const float bt = sBeta[part * RPT + r];
+            r0[r] = Elt<E>::from(bt * kx[r][0]);
+            r1[r] = Elt<E>::from(bt * kx[r][1]);
         }
         store_seq<E, RPT>(sKbt + c0 * LDT + part * RPT, r0);
         store_seq<E, RPT>(sKbt + (c0 + 1) * LDT + part * RPT, r1);
@@ -578,9 +585,10 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
         E r0[RPTV], r1[RPTV];
 #pragma unroll
         for (int r = 0; r < RPTV; ++r) {
+            const bool ok = vpart * RPTV + r < len;
             const float bt = sBeta[vpart * RPTV + r];
-            r0[r] = Elt<E>::from(bt * vraw[r].lo());
-            r1[r] = Elt<E>::from(bt * vraw[r].hi());
+            r0[r] = Elt<E>::from(ok ? bt * vraw[r].lo() : 0.f);
+            r1[r] = Elt<E>::from(ok ? bt * vraw[r].hi() : 0.f);
         }
         store_seq<E, RPTV>(sVt + j0 * LDT + vpart * RPTV, r0);
         store_seq<E, RPTV>(sVt + (j0 + 1) * LDT + vpart * RPTV, r1);
