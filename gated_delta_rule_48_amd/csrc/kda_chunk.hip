@@ -25,7 +25,8 @@
 // factors <= 1.  Masks are applied by selection, never by multiplication.
 //
 // Kernels (one stream, in order):
-//   chunk_map_kernel   validate cu_seqlens, first chunk of every sequence
+//   chunk_map_kernel   validate cu_seqlens, first chunk of every sequence,
+//                      first token and length of every chunk
 //   intra_chunk_kernel one workgroup per (chunk, head): prefix sum of the
 //                      gate, decayed operands, A and P on MFMA, (I+A)^{-1} by
 //                      blocked forward substitution in LDS (fp32), W and U'
@@ -40,12 +41,15 @@
 namespace kda {
 
 // ----------------------------------------------------------------------------
-// Chunk map: copy (or synthesise) the sequence offsets, validate them, and
-// exclusive-scan the per-sequence chunk counts.
+// Chunk map: copy (or synthesise) the sequence offsets, validate them,
+// exclusive-scan the per-sequence chunk counts, and write every chunk's first
+// token and length, so that a chunk's workgroup finds its tokens with a single
+// load that does not depend on another.
 __global__ __launch_bounds__(256) void chunk_map_kernel(const int32_t* __restrict__ cu_in, int32_t N,
                                                         int64_t T, WsHeader* __restrict__ hdr,
                                                         int32_t* __restrict__ cu,
-                                                        int32_t* __restrict__ chunk_off) {
+                                                        int32_t* __restrict__ chunk_off,
+                                                        int2* __restrict__ chunk_tab) {
     __shared__ int bad;
     __shared__ int carry;
     __shared__ int scan[256];
@@ -87,16 +91,17 @@ __global__ __launch_bounds__(256) void chunk_map_kernel(const int32_t* __restric
         hdr->bad_seqlens = isbad;
         hdr->wait_timeout = 0;
     }
-}
-
-// Largest n in [0, N) with chunk_off[n] <= cid (cid < chunk_off[N]).
-__device__ __forceinline__ int find_sequence(const int32_t* __restrict__ chunk_off, int N, int cid) {
-    int lo = 0, hi = N;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (chunk_off[mid] <= cid) lo = mid; else hi = mid;
+    __syncthreads();  // chunk_off of every sequence is written
+    const int total = isbad ? 0 : carry;
+    for (int cid = tid; cid < total; cid += 256) {
+        int lo = 0, hi = N;  // largest n with chunk_off[n] <= cid
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (chunk_off[mid] <= cid) lo = mid; else hi = mid;
+        }
+        const int t0 = cu[lo] + (cid - chunk_off[lo]) * kChunk;
+        chunk_tab[cid] = make_int2(t0, min(kChunk, cu[lo + 1] - t0));
     }
-    return lo;
 }
 
 // ----------------------------------------------------------------------------
@@ -309,17 +314,17 @@ __device__ __forceinline__ Frag<float> scale_frag(Frag<float> f, const float* s)
 template <typename E, int DK, int DV, bool HG>
 __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v, const E* __restrict__ g,
-    const E* __restrict__ beta, const WsHeader* __restrict__ hdr, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ chunk_off, int32_t N, int32_t H, E* __restrict__ Wo, E* __restrict__ QGo,
+    const E* __restrict__ beta, const WsHeader* __restrict__ hdr, const int2* __restrict__ chunk_tab,
+    int32_t H, E* __restrict__ Wo, E* __restrict__ QGo,
     E* __restrict__ KdTo, E* __restrict__ Upo, E* __restrict__ Po, float* __restrict__ Gno) {
     using L = IntraLayout<E, DK, DV>;
     constexpr int C = L::C, LDK = L::LDK, LDT = L::LDT, LDA = L::LDA;
     constexpr int NPART = L::NPART, RPT = L::RPT, RPTV = L::RPTV;
 
     extern __shared__ __align__(16) unsigned char smem[];
-    E* sKr = reinterpret_cast<E*>(smem);   // k_t e^{b_t - b_s(t)}, s(t) = first row of t's tile
-    E* sQr = sKr + C * LDK;                // q_t e^{b_t - b_s(t)}
-    E* sKt = sQr + C * LDK;                // k_i e^{b_e(i) - b_i}, e(i) = last row of i's tile
+    E* sKr = reinterpret_cast<E*>(smem);   // k_t e^{b_t - b_m(t)}, m(t) = middle row of t's tile
+    E* sQr = sKr + C * LDK;                // q_t e^{b_t - b_m(t)}
+    E* sKt = sQr + C * LDK;                // k_i e^{b_m(i) - b_i}
     E* sKbt = reinterpret_cast<E*>(smem);  // reuses R1 once A and P are done
     E* sVt = sKbt + DK * LDT;
     float* sA = reinterpret_cast<float*>(smem + L::off_A);
@@ -328,13 +333,17 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
     float* sTileF = reinterpret_cast<float*>(smem + L::off_scale);  // [12][DK] tile-pair factors
     float* sPart = sTileF;  // [NPART][DK], dead before the tile factors are written
 
-    if (hdr->bad_seqlens) return;
     const int cid = blockIdx.x;
-    if (cid >= hdr->total_chunks) return;
+    // Both loads are issued together: the table entry (within the grid, set
+    // for every chunk below the total) is only trusted once the total admits
+    // it.  The length test never fires for a valid chunk; it is there so that
+    // the compiler cannot defer the table load past the branch.
+    const int total = hdr->total_chunks;  // zero when the sequence offsets were rejected
+    const int2 tab = chunk_tab[cid];
+    if ((cid >= total) | (tab.y <= 0)) return;
     const int h = blockIdx.y;
-    const int n = find_sequence(chunk_off, N, cid);
-    const int64_t t0 = (int64_t)cu[n] + (int64_t)(cid - chunk_off[n]) * C;
-    const int len = (int)min((int64_t)C, (int64_t)cu[n + 1] - t0);
+    const int64_t t0 = tab.x;
+    const int len = tab.y;
     const int64_t ch = (int64_t)cid * H + h;  // chunk-head index into the workspace
 
     const int tid = threadIdx.x;
@@ -1230,7 +1239,7 @@ int64_t max_chunks_for(int64_t T, int32_t N) { return (T + kChunk - 1) / kChunk 
 
 namespace {
 struct WsSizes {
-    size_t header, cu, chunk_off, W, QG, KdT, Up, P, Gn;
+    size_t header, cu, chunk_off, chunk_tab, W, QG, KdT, Up, P, Gn;
 };
 WsSizes ws_sizes(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, bool bf16) {
     const size_t esz = bf16 ? 2 : 4;
@@ -1240,6 +1249,7 @@ WsSizes ws_sizes(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, bool b
     s.header = 256;
     s.cu = align256((size_t)(N + 1) * 4);
     s.chunk_off = align256((size_t)(N + 1) * 4);
+    s.chunk_tab = align256(mc * sizeof(int2));
     s.W = align256(mc * H * C * dk * esz);
     s.QG = s.W;
     s.KdT = s.W;
@@ -1252,7 +1262,7 @@ WsSizes ws_sizes(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, bool b
 
 size_t chunk_workspace_bytes(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, bool bf16) {
     const WsSizes s = ws_sizes(T, N, H, dk, dv, bf16);
-    return s.header + s.cu + s.chunk_off + s.W + s.QG + s.KdT + s.Up + s.P + s.Gn;
+    return s.header + s.cu + s.chunk_off + s.chunk_tab + s.W + s.QG + s.KdT + s.Up + s.P + s.Gn;
 }
 
 ChunkWorkspace carve_chunk_workspace(void* base, int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv,
@@ -1263,6 +1273,7 @@ ChunkWorkspace carve_chunk_workspace(void* base, int64_t T, int32_t N, int32_t H
     w.header = reinterpret_cast<WsHeader*>(p); p += s.header;
     w.cu = reinterpret_cast<int32_t*>(p); p += s.cu;
     w.chunk_off = reinterpret_cast<int32_t*>(p); p += s.chunk_off;
+    w.chunk_tab = reinterpret_cast<int2*>(p); p += s.chunk_tab;
     w.W = p; p += s.W;
     w.QG = p; p += s.QG;
     w.KdT = p; p += s.KdT;
@@ -1285,8 +1296,7 @@ static hipError_t launch_intra(const ChunkArgs& a, const ChunkWorkspace& ws, hip
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)a.max_chunks, (unsigned)a.H), dim3(kIntraThreads), L::bytes, stream,
                        (const E*)a.q, (const E*)a.k, (const E*)a.v, (const E*)a.g, (const E*)a.beta, ws.header,
-                       ws.cu, ws.chunk_off, a.N, a.H, (E*)ws.W, (E*)ws.QG, (E*)ws.KdT, (E*)ws.Up, (E*)ws.P,
-                       ws.Gn);
+                       ws.chunk_tab, a.H, (E*)ws.W, (E*)ws.QG, (E*)ws.KdT, (E*)ws.Up, (E*)ws.P, ws.Gn);
     return hipGetLastError();
 }
 
@@ -1339,7 +1349,7 @@ hipError_t launch_chunk_fwd(const ChunkArgs& a, const ChunkWorkspace& ws, hipStr
     hipError_t e = mark(ev, 0, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(256), 0, stream, a.cu_seqlens, a.N, a.T, ws.header, ws.cu,
-                       ws.chunk_off);
+                       ws.chunk_off, ws.chunk_tab);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return a.bf16 ? launch_chunk_e<bf16_t>(a, ws, stream, ev) : launch_chunk_e<float>(a, ws, stream, ev);
 }

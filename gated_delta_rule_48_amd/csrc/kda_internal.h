@@ -25,6 +25,7 @@ struct ChunkWorkspace {
     WsHeader* header;     // flag + chunk count
     int32_t* cu;          // [N+1] sequence offsets (copied or synthesised)
     int32_t* chunk_off;   // [N+1] first chunk of each sequence
+    int2* chunk_tab;      // [max_chunks] first token and length of each chunk
     // Per chunk and head.  "fragment-major": the reduction index is permuted
     // by frag_pos() and every 16 x 32 block is stored as 64 lanes x 8
     // contiguous elements (fm_off()).
