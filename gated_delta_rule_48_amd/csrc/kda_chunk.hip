@@ -383,13 +383,15 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
     auto row_ok = [&](int r) { return part * RPT + r < len; };
 
     // ---- 1. chunk-local inclusive prefix sum of the log-gate ----------------
+    // in base-2 units (b log2(e)), so that every decay factor below is a bare
+    // exp2
     float bb[RPT][2];
     {
         float run0 = 0.f, run1 = 0.f;
 #pragma unroll
         for (int r = 0; r < RPT; ++r) {
-            run0 += row_ok(r) ? (HG ? gh[r] : graw[r].lo()) : 0.f;
-            run1 += row_ok(r) ? (HG ? gh[r] : graw[r].hi()) : 0.f;
+            run0 = fmaf(row_ok(r) ? (HG ? gh[r] : graw[r].lo()) : 0.f, kLog2e, run0);
+            run1 = fmaf(row_ok(r) ? (HG ? gh[r] : graw[r].hi()) : 0.f, kLog2e, run1);
             bb[r][0] = run0;
             bb[r][1] = run1;
         }
@@ -427,7 +429,9 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
     // Kt = k e^{b_m - b}.  Each factor spans at most eight tokens of decay,
     // so it stays a normal fp32 / bf16 number whenever the decay over eight
     // tokens is above e^-80 (exponents are capped at 80 beyond that).
-    // e^{b} and e^{b_last - b} are <= 1 and taken directly.
+    // e^{b} and e^{b_last - b} are <= 1 and taken directly.  (b is held in
+    // base-2 units: e^{x} is computed as 2^{x log2(e)}.)
+    constexpr float kCap2 = 80.f * kLog2e;
     static_assert(16 % RPT == 0, "a thread's rows lie in one tile");
     float kx[RPT][2];  // k e^b; times beta it is the W right-hand side
     E kd0[RPT], kd1[RPT];
@@ -438,12 +442,12 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
         const bool ok = row_ok(r);
         const float k0 = ok ? kraw[r].lo() : 0.f, k1 = ok ? kraw[r].hi() : 0.f;
         const float q0 = ok ? qraw[r].lo() : 0.f, q1 = ok ? qraw[r].hi() : 0.f;
-        const float e0 = gate_exp<E>(fminf(bb[r][0] - bm[c0], 80.f));
-        const float e1 = gate_exp<E>(fminf(bb[r][1] - bm[c0 + 1], 80.f));
-        const float f0 = gate_exp<E>(fminf(bm[c0] - bb[r][0], 80.f));
-        const float f1 = gate_exp<E>(fminf(bm[c0 + 1] - bb[r][1], 80.f));
-        const float x0 = gate_exp<E>(bb[r][0]), x1 = gate_exp<E>(bb[r][1]);
-        const float d0 = gate_exp<E>(last0 - bb[r][0]), d1 = gate_exp<E>(last1 - bb[r][1]);
+        const float e0 = gate_exp2<E>(fminf(bb[r][0] - bm[c0], kCap2));
+        const float e1 = gate_exp2<E>(fminf(bb[r][1] - bm[c0 + 1], kCap2));
+        const float f0 = gate_exp2<E>(fminf(bm[c0] - bb[r][0], kCap2));
+        const float f1 = gate_exp2<E>(fminf(bm[c0 + 1] - bb[r][1], kCap2));
+        const float x0 = gate_exp2<E>(bb[r][0]), x1 = gate_exp2<E>(bb[r][1]);
+        const float d0 = gate_exp2<E>(last0 - bb[r][0]), d1 = gate_exp2<E>(last1 - bb[r][1]);
         store2<E>(sKr + row * LDK + c0, k0 * e0, k1 * e1);
         store2<E>(sQr + row * LDK + c0, q0 * e0, q1 * e1);
         store2<E>(sKt + row * LDK + c0, k0 * f0, k1 * f1);
@@ -462,18 +466,19 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
             store_run4<E>(p0 + fm_off<C>(c0 + 1, pos), kd1 + 4 * r4);
         }
         if (part == 0) {
-            Gno[ch * DK + c0] = gate_exp<E>(last0);
-            Gno[ch * DK + c0 + 1] = gate_exp<E>(last1);
+            Gno[ch * DK + c0] = gate_exp2<E>(last0);
+            Gno[ch * DK + c0 + 1] = gate_exp2<E>(last1);
         }
     }
     // Tile pairs.  Diagonal (ti, ti): e^{b_t - b_i} = Kr-side e^{b_t - b_m} times
     // Kt-side e^{b_m - b_i}, no further factor.  Below the diagonal (tj < ti)
-    // the row operand is taken to the tile start s(ti) and then to the end
-    // e(tj) of the column tile, and the column operand to e(tj):
-    //   e^{b_t - b_i} = (e^{b_t - b_m(ti)} e^{b_m(ti) - b_s(ti)}) e^{b_s(ti) - b_e(tj)}
-    //                   * (e^{b_m(tj) - b_i} e^{b_e(tj) - b_m(tj)}),
-    // three factors <= 1 applied one after another, so no intermediate value
-    // drops below the final product (anything that underflows is negligible).
+    // the row operands are taken to the tile start s(ti), and the column
+    // operand (shared by A and P) to the end e(tj) of its tile and then on to
+    // s(ti):
+    //   e^{b_t - b_i} = (e^{b_t - b_m(ti)} e^{b_m(ti) - b_s(ti)})
+    //                   * ((e^{b_m(tj) - b_i} e^{b_e(tj) - b_m(tj)}) e^{b_s(ti) - b_e(tj)}),
+    // factors <= 1 applied one after another, so no intermediate value drops
+    // below the final product (anything that underflows is negligible).
     //   sTileF[ti - 1]     e^{b_m(ti) - b_s(ti)}, ti = 1..3
     //   sTileF[3 + tj]     e^{b_e(tj) - b_m(tj)}, tj = 0..2
     //   sTileF[6 + p]      e^{b_s(ti) - b_e(tj)}, p = ti (ti - 1) / 2 + tj
@@ -490,7 +495,7 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
             const int tj = p - ti * (ti - 1) / 2;
             x = sBnd[(3 * ti) * DK + c] - sBnd[(3 * tj + 2) * DK + c];
         }
-        sTileF[v * DK + c] = gate_exp<E>(x);
+        sTileF[v * DK + c] = gate_exp2<E>(x);
     }
     sBeta[lane] = lane < len ? beta_raw : 0.f;  // every wave writes the same values
     lds_barrier();
@@ -523,9 +528,9 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
                 Frag<E> fa = ld_frag(sKr + (16 * ti + lr) * LDK + cb);
                 Frag<E> fq = ld_frag(sQr + (16 * ti + lr) * LDK + cb);
                 if (!diag) {
-                    fb = scale_frag(fb, colf + cb);
-                    fa = scale_frag(fa, rowf + cb, midf + cb);
-                    fq = scale_frag(fq, rowf + cb, midf + cb);
+                    fb = scale_frag(fb, colf + cb, midf + cb);
+                    fa = scale_frag(fa, rowf + cb);
+                    fq = scale_frag(fq, rowf + cb);
                 }
                 accA = mma(fa, fb, accA);
                 accP = mma(fq, fb, accP);

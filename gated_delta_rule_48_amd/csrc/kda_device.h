@@ -132,6 +132,14 @@ template <typename E> __device__ __forceinline__ float gate_exp(float x);
 template <> __device__ __forceinline__ float gate_exp<bf16_t>(float x) { return __expf(x); }
 template <> __device__ __forceinline__ float gate_exp<float>(float x) { return expf(x); }
 
+// 2^x for decay exponents already in base-2 units (the chunk kernels keep the
+// gate's prefix sums scaled by log2(e)).  bf16 inputs use the hardware exp2;
+// fp32 inputs the library exp2f.
+constexpr float kLog2e = 1.44269504088896340736f;
+template <typename E> __device__ __forceinline__ float gate_exp2(float x);
+template <> __device__ __forceinline__ float gate_exp2<bf16_t>(float x) { return __builtin_amdgcn_exp2f(x); }
+template <> __device__ __forceinline__ float gate_exp2<float>(float x) { return exp2f(x); }
+
 // Workspace header written by the chunk-map kernel.
 struct WsHeader {
     int32_t bad_seqlens;   // nonzero: cu_seqlens rejected, every later kernel exits
