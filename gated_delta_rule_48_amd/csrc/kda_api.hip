@@ -56,6 +56,7 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
     if (st != KDA_OK) return st;
     if (N <= 0 || T_total < 0 || T_total > INT32_MAX) return KDA_ERR_INVALID_ARG;
     if (!cu_seqlens && T_total % N != 0) return KDA_ERR_INVALID_ARG;
+    if (!kda::chunk_grid_fits(kda::max_chunks_for(T_total, N), H)) return KDA_ERR_UNSUPPORTED;
     if (T_total > 0) {
         if (!q || !k || !v || !g || !beta || !o) return KDA_ERR_INVALID_ARG;
         // q, k, v and a per-channel g are read two elements at a time

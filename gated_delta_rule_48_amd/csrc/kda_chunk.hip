@@ -333,7 +333,11 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
     float* sTileF = reinterpret_cast<float*>(smem + L::off_scale);  // [12][DK] tile-pair factors
     float* sPart = sTileF;  // [NPART][DK], dead before the tile factors are written
 
-    const int cid = blockIdx.x;
+    // One workgroup per (chunk, head), heads fastest over the grid, so that the
+    // workgroups resident at any time cover a few consecutive chunks of every
+    // head: one contiguous span of the token-major inputs and of the workspace.
+    const int cid = (int)(blockIdx.x / (unsigned)H);
+    const int h = (int)(blockIdx.x - (unsigned)cid * (unsigned)H);
     // Both loads are issued together: the table entry (within the grid, set
     // for every chunk below the total) is only trusted once the total admits
     // it.  The length test never fires for a valid chunk; it is there so that
@@ -341,7 +345,6 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
     const int total = hdr->total_chunks;  // zero when the sequence offsets were rejected
     const int2 tab = chunk_tab[cid];
     if ((cid >= total) | (tab.y <= 0)) return;
-    const int h = blockIdx.y;
     const int64_t t0 = tab.x;
     const int len = tab.y;
     const int64_t ch = (int64_t)cid * H + h;  // chunk-head index into the workspace
@@ -1242,6 +1245,12 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int64_t max_chunks_for(int64_t T, int32_t N) { return (T + kChunk - 1) / kChunk + N; }
 
+// The intra-chunk grid (one workgroup per chunk and head, in one dimension)
+// must stay within the 2^32 work-items a grid dimension can hold.
+bool chunk_grid_fits(int64_t max_chunks, int32_t H) {
+    return max_chunks * H * kIntraThreads <= (int64_t)UINT32_MAX;
+}
+
 namespace {
 struct WsSizes {
     size_t header, cu, chunk_off, chunk_tab, W, QG, KdT, Up, P, Gn;
@@ -1299,7 +1308,7 @@ static hipError_t launch_intra(const ChunkArgs& a, const ChunkWorkspace& ws, hip
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)a.max_chunks, (unsigned)a.H), dim3(kIntraThreads), L::bytes, stream,
+    hipLaunchKernelGGL(kern, dim3((unsigned)(a.max_chunks * a.H)), dim3(kIntraThreads), L::bytes, stream,
                        (const E*)a.q, (const E*)a.k, (const E*)a.v, (const E*)a.g, (const E*)a.beta, ws.header,
                        ws.chunk_tab, a.H, (E*)ws.W, (E*)ws.QG, (E*)ws.KdT, (E*)ws.Up, (E*)ws.P, ws.Gn);
     return hipGetLastError();

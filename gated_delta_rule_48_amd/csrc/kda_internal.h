@@ -54,6 +54,7 @@ size_t chunk_workspace_bytes(int64_t T, int32_t N, int32_t H, int32_t dk, int32_
 ChunkWorkspace carve_chunk_workspace(void* base, int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv,
                                      bool bf16);
 int64_t max_chunks_for(int64_t T, int32_t N);
+bool chunk_grid_fits(int64_t max_chunks, int32_t H);
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 // events: null, or four events recorded before map / intra / walk and after walk.

@@ -50,7 +50,8 @@
  *  - Errors are returned, never thrown.  Argument checks run on the host
  *    before anything is launched: KDA_ERR_INVALID_ARG (null pointer,
  *    misalignment, negative or inconsistent sizes), KDA_ERR_UNSUPPORTED
- *    (d_k or d_v outside {64,128}, unknown dtype or gate mode),
+ *    (d_k or d_v outside {64,128}, unknown dtype or gate mode, or 2^23 or
+ *    more (chunk, head) pairs: (ceil(T_total / 64) + N) * H),
  *    KDA_ERR_WORKSPACE (workspace null or smaller than required).  A failed
  *    launch returns KDA_ERR_HIP.  Input values are not inspected.
  */

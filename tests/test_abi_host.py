@@ -95,6 +95,11 @@ def test_chunk_fwd_rejects_bad_arguments(lib):
     assert call(ws=None) == WORKSPACE
     assert call(ws=P + 16) == WORKSPACE           # workspace must be 256-byte aligned
     assert call(wsb=16) == WORKSPACE
+    # one intra-chunk workgroup per (chunk, head) in a single grid dimension:
+    # ceil(T / 64) + N chunks times H must stay below 2^23
+    assert call(T=64 * (2**23 - 2), H=1, ws=None) == WORKSPACE   # 2^23 - 1 pairs: accepted
+    assert call(T=64 * (2**23 - 1), H=1, ws=None) == UNSUPPORTED  # 2^23 pairs
+    assert call(T=2**31 - 64, H=64) == UNSUPPORTED
 
 
 def test_recurrent_step_rejects_bad_arguments(lib):
