@@ -505,15 +505,22 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
 
     // ---- 3. A = K K^T with decay (strictly lower, row-scaled by beta) -> LDS
     //         (fp32);  P = Q K^T with decay (lower incl. diagonal) -> workspace
-    // The ten lower tile pairs (ti, tj) over the eight waves: a diagonal pair
-    // costs about three off-diagonal ones (both operands are rescaled), so
-    // waves 0-3 take one diagonal pair each and waves 4-7 the six others;
-    // waves 6 and 7 also write the zero tiles above the diagonal.
-    int npair = 1, pti0 = wave, ptj0 = wave, pti1 = 0, ptj1 = 0;
-    if (wave == 4) { npair = 2; pti0 = 1; ptj0 = 0; pti1 = 2; ptj1 = 0; }
-    if (wave == 5) { npair = 2; pti0 = 2; ptj0 = 1; pti1 = 3; ptj1 = 0; }
-    if (wave == 6) { pti0 = 3; ptj0 = 1; }
-    if (wave == 7) { pti0 = 3; ptj0 = 2; }
+    // The ten lower tile pairs (ti, tj) over the eight waves.  An off-diagonal
+    // pair rescales its fragments before every product, a diagonal pair does
+    // not, so each of waves 2-7 takes one off-diagonal pair, (1,0) (2,0) (2,1)
+    // (3,0) (3,1) (3,2), and waves 0 and 1 two diagonal pairs each plus the
+    // zero tiles above the diagonal: no wave has two rescaled pairs in a row.
+    int npair, pti0, ptj0, pti1 = 0, ptj1 = 0;
+    if (wave < 2) {
+        npair = 2;
+        pti0 = ptj0 = 2 * wave;
+        pti1 = ptj1 = 2 * wave + 1;
+    } else {
+        npair = 1;
+        const int p = wave - 2;
+        pti0 = p < 1 ? 1 : (p < 3 ? 2 : 3);
+        ptj0 = p - pti0 * (pti0 - 1) / 2;
+    }
     f32x4 accPt[2];
 #pragma unroll
     for (int pq = 0; pq < 2; ++pq) {
@@ -546,14 +553,14 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
             }
         }
     }
-    // zero tiles of A above the diagonal: (0,1) (0,2) (0,3) by wave 6,
-    // (1,2) (1,3) (2,3) by wave 7
+    // zero tiles of A above the diagonal: (0,1) (0,2) (0,3) by wave 0,
+    // (1,2) (1,3) (2,3) by wave 1
     auto upper_tile = [&](int z, int& ti, int& tj) {
-        const int zz = (wave == 6) ? z : z + 3;  // 0..5 over (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+        const int zz = (wave == 0) ? z : z + 3;  // 0..5 over (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
         ti = zz < 3 ? 0 : (zz < 5 ? 1 : 2);
         tj = zz < 3 ? zz + 1 : (zz < 5 ? zz - 1 : 3);
     };
-    if (wave >= 6) {
+    if (wave < 2) {
 #pragma unroll
         for (int z = 0; z < 3; ++z) {
             int ti, tj;
@@ -574,7 +581,7 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
                     lds_put(&sPst[(16 * ti + 4 * lg + i) * L::LDP + frag_pos(16 * tj + lr)], Elt<E>::from(accPt[pq][i]));
             }
         }
-        if (wave >= 6) {
+        if (wave < 2) {
 #pragma unroll
             for (int z = 0; z < 3; ++z) {
                 int ti, tj;
