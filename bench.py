@@ -194,6 +194,8 @@ def main():
     wall_ms = (time.perf_counter() - t0) * 1e3 / K
 
     avg = lambda i, j: float(np.mean([e.ms(i, j) for e in evs]))
+    stats = lambda i, j: {"mean": avg(i, j), "median": float(np.median([e.ms(i, j) for e in evs])),
+                          "min": float(np.min([e.ms(i, j) for e in evs]))}
     t_map, t_intra, t_walk = avg(0, 1), avg(1, 2), avg(2, 3)
     t_fwd, t_dec = avg(0, 3), avg(4, 5)
     ht = T * H
@@ -229,6 +231,8 @@ def main():
                                "32 heads, d=128, fp32 state",
                    "global_batch": 1, "seq_len": T, "heads": H, "d_k": dk, "d_v": dv, "chunk": 64},
         "prefill_ms": t_fwd,
+        "prefill_ms_stats": stats(0, 3),
+        "decode_us_stats": {k: v * 1e3 for k, v in stats(4, 5).items()},
         "kernels_ms": {"chunk_map": t_map, "intra_chunk": t_intra, "chunk_walk": t_walk, "decode_step": t_dec},
         "decode": {"us_per_step": t_dec * 1e3, "GB_per_s": dec_gbs, "frac_hbm_peak": dec_gbs / HBM_PEAK_GBS,
                    "tokens_per_s": dcfg.N / (t_dec * 1e-3), "bytes_per_step": DECODE_BYTES_PER_STEP},
