@@ -247,9 +247,16 @@ __device__ __forceinline__ int64_t fm_off(int row, int colpos) {
     return ((int64_t)((row >> 4) * (K / 32) + (colpos >> 5)) * 64 + lane) * 8 + (colpos & 7);
 }
 
+// The 16 x 32 fragment blocks of the C x C matrix P (rows: query tokens of
+// 16-row tile t; columns: key tokens of 32-block kb) that lie wholly above the
+// diagonal.  P is lower triangular, so they are zero: the intra-chunk kernel
+// does not store them and the walk neither loads nor multiplies them.
+__host__ __device__ constexpr bool p_block_zero(int t, int kb) { return 16 * t + 15 < 32 * kb; }
+
 // Copy an R x K tile held row-major in LDS (K already in fragment order) to
-// fragment-major global memory: thread i writes the i-th 16-byte piece.
-template <typename E, int R, int K>
+// fragment-major global memory: thread i writes the i-th 16-byte piece.  With
+// LOWER the blocks p_block_zero names are skipped (R = K = C only).
+template <typename E, int R, int K, bool LOWER = false>
 __device__ __forceinline__ void copy_tile_out_frag(E* __restrict__ dst, const E* src, int lds_ld, int tid) {
     constexpr int PER = 16 / (int)sizeof(E);  // elements per 16-byte piece
     constexpr int PIECES = R * K / PER;
@@ -259,6 +266,7 @@ __device__ __forceinline__ void copy_tile_out_frag(E* __restrict__ dst, const E*
         const int sub = i % (8 / PER);
         const int lane = (i / (8 / PER)) % 64;
         const int blk = i / (64 * 8 / PER);
+        if (LOWER && p_block_zero(blk / (K / 32), blk % (K / 32))) continue;
         const int row = 16 * (blk / (K / 32)) + (lane & 15);
         const int col = 32 * (blk % (K / 32)) + 8 * (lane >> 4) + sub * PER;
         *reinterpret_cast<uint4*>(dst + (int64_t)i * PER) = *reinterpret_cast<const uint4*>(src + row * lds_ld + col);
@@ -631,7 +639,7 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
         }
     }
     lds_barrier();
-    copy_tile_out_frag<E, C, C>(Po + ch * C * C, reinterpret_cast<const E*>(smem + L::off_Pst), L::LDP, tid);
+    copy_tile_out_frag<E, C, C, true>(Po + ch * C * C, reinterpret_cast<const E*>(smem + L::off_Pst), L::LDP, tid);
     if (tid < 64) {
         const int blk = tid >> 4, jc = tid & 15;
         float* Tb = sA + (16 * blk) * LDA + 16 * blk;
@@ -956,8 +964,12 @@ __global__ __launch_bounds__(kWalkThreads) void chunk_walk_kernel(
                 if (j < LW) { base = (const char*)(Wi + ch * C * DK); off = j; }
                 else if (j < 2 * LW) { base = (const char*)(QGi + ch * C * DK); off = j - LW; }
                 else if (j < 3 * LW) { base = (const char*)(KdTi + ch * DK * C); off = j - 2 * LW; }
-                else if (j < 3 * LW + LP) { base = (const char*)(Pi + ch * C * C); off = j - 3 * LW; }
-                else { base = (const char*)(Gni + ch * DK); off = j - 3 * LW - LP; }
+                else if (j < 3 * LW + LP) {
+                    base = (const char*)(Pi + ch * C * C);
+                    off = j - 3 * LW;
+                    constexpr int LB = 64 * 8 * (int)sizeof(E) / 128;  // lines per fragment block
+                    if (p_block_zero(off / LB / KB, off / LB % KB)) continue;
+                } else { base = (const char*)(Gni + ch * DK); off = j - 3 * LW - LP; }
                 __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base + 128 * off),
                                                  sink, 4, 0, 0);
             }
@@ -1195,7 +1207,8 @@ __global__ __launch_bounds__(kWalkThreads) void chunk_walk_kernel(
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) x.q[t][ks] = ld_frag(Qp + ((t * KS + ks) * 64 + lane) * 8);
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) x.p[t][kb] = ld_frag(Pp + ((t * KB + kb) * 64 + lane) * 8);
+            for (int kb = 0; kb < KB; ++kb)
+                if (!p_block_zero(t, kb)) x.p[t][kb] = ld_frag(Pp + ((t * KB + kb) * 64 + lane) * 8);
         }
     };
     auto out_chunk = [&](QP& x, int c) {
@@ -1219,7 +1232,8 @@ __global__ __launch_bounds__(kWalkThreads) void chunk_walk_kernel(
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int t = 0; t < TT; ++t) O[t] = mma(x.p[t][kb], uf[kb], O[t]);
+            for (int t = 0; t < TT; ++t)
+                if (!p_block_zero(t, kb)) O[t] = mma(x.p[t][kb], uf[kb], O[t]);
         load_qp(x, c + 2);
         // O tile slot c & 1 is free once wave 3 has read chunk c - 2 from it
         wait_until(ostored, c - 1);
