@@ -34,8 +34,9 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 # Algorithmic figures (per head-token for the chunked path, d = 128, C = 64)
 PATH_MIN_BYTES_PER_HT = 1282           # bf16 q, k, v, g, o (5 x 2 x 128) + beta (2)
 PATH_FLOP_PER_HT = 139136              # 6 d^2 + (5C - 1) d
-INTRA_BYTES_PER_HT = 2186              # reads q,k,v,g,beta (1026); writes W,QG,KdT,U' (4 x 256), P (128), Gn (8)
-WALK_BYTES_PER_HT = 1416               # reads W,QG,KdT,U',P,Gn (1160); writes o (256)
+INTRA_BYTES_PER_HT = 2154              # reads q,k,v,g,beta (1026); writes W,QG,KdT,U' (4 x 256), P (96: the 6 of
+                                       # its 8 fragment blocks on or below the diagonal), Gn (8)
+WALK_BYTES_PER_HT = 1384               # reads W,QG,KdT,U' (4 x 256), P (96), Gn (8); writes o (256)
 DECODE_BYTES_PER_STEP = 1084243968     # state read + write (2 x 536870912) + tokens in (8404992) + o (2097152)
 
 
