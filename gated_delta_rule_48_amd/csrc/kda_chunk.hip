@@ -453,10 +453,11 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
         const bool ok = row_ok(r);
         const float k0 = ok ? kraw[r].lo() : 0.f, k1 = ok ? kraw[r].hi() : 0.f;
         const float q0 = ok ? qraw[r].lo() : 0.f, q1 = ok ? qraw[r].hi() : 0.f;
-        const float e0 = gate_exp2<E>(fminf(bb[r][0] - bm[c0], kCap2));
-        const float e1 = gate_exp2<E>(fminf(bb[r][1] - bm[c0 + 1], kCap2));
-        const float f0 = gate_exp2<E>(fminf(bm[c0] - bb[r][0], kCap2));
-        const float f1 = gate_exp2<E>(fminf(bm[c0 + 1] - bb[r][1], kCap2));
+        // min(b_m - b, cap) written as -max(b - b_m, -cap): the same value, from
+        // the difference already formed for e
+        const float df0 = bb[r][0] - bm[c0], df1 = bb[r][1] - bm[c0 + 1];
+        const float e0 = gate_exp2<E>(fminf(df0, kCap2)), e1 = gate_exp2<E>(fminf(df1, kCap2));
+        const float f0 = gate_exp2<E>(-fmaxf(df0, -kCap2)), f1 = gate_exp2<E>(-fmaxf(df1, -kCap2));
         const float x0 = gate_exp2<E>(bb[r][0]), x1 = gate_exp2<E>(bb[r][1]);
         const float d0 = gate_exp2<E>(last0 - bb[r][0]), d1 = gate_exp2<E>(last1 - bb[r][1]);
         store2<E>(sKr + row * LDK + c0, k0 * e0, k1 * e1);
@@ -647,32 +648,65 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
         for (int t = 0; t < 16; ++t) Tb[t * LDA + jc] = x[t];
     }
     lds_barrier();
-    // (b) off-diagonal blocks, block row by block row, on the matrix cores in
-    //     fp32:  X = sum_{m=j}^{i-1} A_im T_mj,  T_ij = -T_ii X.  Wave j
-    //     takes block (i, j).  With k = 4g + s for lane group g and step s,
-    //     the product X comes out of the accumulators exactly as the B
-    //     operand of the second product needs it.
+    // (b) off-diagonal blocks in two levels, on the matrix cores in fp32
+    //     (16x16x4).  With T_a and T_b the inverses of the leading and the
+    //     trailing 32 x 32 diagonal blocks of I + A (T of a block-triangular
+    //     [[M_a, 0], [A_ba, M_b]] is [[T_a, 0], [-T_b A_ba T_a, T_b]]):
+    //       level 1  T10 = -T11 A10 T00 (wave 0),  T32 = -T33 A32 T22 (wave 1);
+    //       level 2  Z = A_ba T_a:  Z20 = A20 T00 + A21 T10,  Z21 = A21 T11,
+    //                Z30 = A30 T00 + A31 T10,  Z31 = A31 T11   (waves 0-3),
+    //                then T_ba = -T_b Z:  T20 = -T22 Z20,  T21 = -T22 Z21,
+    //                T30 = -(T32 Z20 + T33 Z30),  T31 = -(T32 Z21 + T33 Z31).
+    //     With k = 4g + s for lane group g and step s, the accumulators of a
+    //     product are exactly the B operand of the next one.  Z goes through
+    //     the P staging tile, free once P has been copied out.
+    {
+        constexpr int LDZ = 36;  // [32][LDZ] fp32: rows of block rows 2 and 3, columns of block columns 0 and 1
+        float* sZ = reinterpret_cast<float*>(smem + L::off_Pst);
+        static_assert((size_t)32 * LDZ * 4 <= (size_t)C * L::LDP * sizeof(E), "Z fits in the P staging tile");
+        // X += A[bi][m] T[m][bj]
+        auto mul_AT = [&](int bi, int m, int bj, f32x4 X) {
+            const f32x4 am = *reinterpret_cast<const f32x4*>(sA + (16 * bi + lr) * LDA + 16 * m + 4 * lg);
 #pragma unroll
-    for (int bi = 1; bi < 4; ++bi) {
-        const int bj = wave;
-        f32x4 X = zero4();
-        if (bj < bi) {
-            for (int m = bj; m < bi; ++m) {
-                const f32x4 am = *reinterpret_cast<const f32x4*>(sA + (16 * bi + lr) * LDA + 16 * m + 4 * lg);
+            for (int jj = 0; jj < 4; ++jj)
+                X = __builtin_amdgcn_mfma_f32_16x16x4f32(am[jj], sA[(16 * m + 4 * lg + jj) * LDA + 16 * bj + lr], X, 0,
+                                                         0, 0);
+            return X;
+        };
+        // Y += T[bi][m] X, X in accumulator layout
+        auto mul_TX = [&](int bi, int m, f32x4 X, f32x4 Y) {
+            const f32x4 tm = *reinterpret_cast<const f32x4*>(sA + (16 * bi + lr) * LDA + 16 * m + 4 * lg);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    X = __builtin_amdgcn_mfma_f32_16x16x4f32(am[j], sA[(16 * m + 4 * lg + j) * LDA + 16 * bj + lr], X,
-                                                             0, 0, 0);
-            }
+            for (int jj = 0; jj < 4; ++jj) Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tm[jj], X[jj], Y, 0, 0, 0);
+            return Y;
+        };
+        auto put_block = [&](int bi, int bj, f32x4 Y) {
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) lds_put(&sA[(16 * bi + 4 * lg + ii) * LDA + 16 * bj + lr], -Y[ii]);
+        };
+        if (wave < 2) {  // level 1: block (i0 + 1, i0), i0 = 0 or 2
+            const int i0 = 2 * wave;
+            const f32x4 X = mul_AT(i0 + 1, i0, i0, zero4());
+            put_block(i0 + 1, i0, mul_TX(i0 + 1, i0 + 1, X, zero4()));
         }
-        lds_barrier();  // every read of A's block row bi is done before T overwrites it
-        if (bj < bi) {
-            const f32x4 tii = *reinterpret_cast<const f32x4*>(sA + (16 * bi + lr) * LDA + 16 * bi + 4 * lg);
+        lds_barrier();
+        const int zi = 2 + (wave >> 1), zj = wave & 1;  // block (zi, zj) of level 2, waves 0-3
+        if (wave < 4) {
+            f32x4 Z = zero4();
+            for (int m = zj; m < 2; ++m) Z = mul_AT(zi, m, zj, Z);
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) lds_put(&sZ[(16 * (zi - 2) + 4 * lg + ii) * LDZ + 16 * zj + lr], Z[ii]);
+        }
+        lds_barrier();
+        if (wave < 4) {
             f32x4 Y = zero4();
+            for (int m = 2; m <= zi; ++m) {
+                f32x4 Zm;  // Z[m][zj] in accumulator layout
 #pragma unroll
-            for (int j = 0; j < 4; ++j) Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tii[j], X[j], Y, 0, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) lds_put(&sA[(16 * bi + 4 * lg + i) * LDA + 16 * bj + lr], -Y[i]);
+                for (int jj = 0; jj < 4; ++jj) Zm[jj] = sZ[(16 * (m - 2) + 4 * lg + jj) * LDZ + 16 * zj + lr];
+                Y = mul_TX(zi, m, Zm, Y);
+            }
+            put_block(zi, zj, Y);
         }
         lds_barrier();
     }
