@@ -440,34 +440,68 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
     // Kt = k e^{b_m - b}.  Each factor spans at most eight tokens of decay,
     // so it stays a normal fp32 / bf16 number whenever the decay over eight
     // tokens is above e^-80 (exponents are capped at 80 beyond that).
-    // e^{b} and e^{b_last - b} are <= 1 and taken directly.  (b is held in
-    // base-2 units: e^{x} is computed as 2^{x log2(e)}.)
+    // e^{b} and e^{b_last - b} are <= 1.  (b is held in base-2 units: e^{x} is
+    // computed as 2^{x log2(e)}.)
+    // Over a thread's consecutive rows each of the four factors changes by
+    // the row's own gate factor e^{g_t}: e^{b - b_m} and e^{b} shrink along
+    // the rows, e^{b_m - b} and e^{b_last - b} grow.  So each is taken
+    // directly at its largest row only and follows from there by products
+    // with the gate factors (all <= 1): 24 exponentials per thread instead of
+    // 64, and no intermediate value exceeds the first.
     constexpr float kCap2 = 80.f * kLog2e;
     static_assert(16 % RPT == 0, "a thread's rows lie in one tile");
     float kx[RPT][2];  // k e^b; times beta it is the W right-hand side
     E kd0[RPT], kd1[RPT];
     const float* bm = sBnd + (3 * ((part * RPT) >> 4) + 1) * DK;  // tile middle
+    float eg[RPT][2];  // e^{g} of rows 1..RPT-1 (1 past the end of the chunk)
+#pragma unroll
+    for (int r = 1; r < RPT; ++r) {
+        const bool ok = row_ok(r);
+        if (HG) {
+            eg[r][0] = eg[r][1] = gate_exp2<E>(ok ? gh[r] * kLog2e : 0.f);
+        } else {
+            eg[r][0] = gate_exp2<E>(ok ? graw[r].lo() * kLog2e : 0.f);
+            eg[r][1] = gate_exp2<E>(ok ? graw[r].hi() * kLog2e : 0.f);
+        }
+    }
+    // e^{b_m - b} and e^{b_last - b}: from the last row back.  min(b_m - b, cap)
+    // is written as -max(b - b_m, -cap), the same value.
+    float ff[RPT][2], dd[RPT][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        ff[RPT - 1][j] = gate_exp2<E>(-fmaxf(bb[RPT - 1][j] - bm[c0 + j], -kCap2));
+        dd[RPT - 1][j] = gate_exp2<E>((j ? last1 : last0) - bb[RPT - 1][j]);
+    }
+#pragma unroll
+    for (int r = RPT - 2; r >= 0; --r)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            ff[r][j] = ff[r + 1][j] * eg[r + 1][j];
+            dd[r][j] = dd[r + 1][j] * eg[r + 1][j];
+        }
+    // e^{b - b_m} and e^{b}: from the first row on
+    float e0 = gate_exp2<E>(fminf(bb[0][0] - bm[c0], kCap2)), e1 = gate_exp2<E>(fminf(bb[0][1] - bm[c0 + 1], kCap2));
+    float x0 = gate_exp2<E>(bb[0][0]), x1 = gate_exp2<E>(bb[0][1]);
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
         const int row = part * RPT + r;
         const bool ok = row_ok(r);
         const float k0 = ok ? kraw[r].lo() : 0.f, k1 = ok ? kraw[r].hi() : 0.f;
         const float q0 = ok ? qraw[r].lo() : 0.f, q1 = ok ? qraw[r].hi() : 0.f;
-        // min(b_m - b, cap) written as -max(b - b_m, -cap): the same value, from
-        // the difference already formed for e
-        const float df0 = bb[r][0] - bm[c0], df1 = bb[r][1] - bm[c0 + 1];
-        const float e0 = gate_exp2<E>(fminf(df0, kCap2)), e1 = gate_exp2<E>(fminf(df1, kCap2));
-        const float f0 = gate_exp2<E>(-fmaxf(df0, -kCap2)), f1 = gate_exp2<E>(-fmaxf(df1, -kCap2));
-        const float x0 = gate_exp2<E>(bb[r][0]), x1 = gate_exp2<E>(bb[r][1]);
-        const float d0 = gate_exp2<E>(last0 - bb[r][0]), d1 = gate_exp2<E>(last1 - bb[r][1]);
+        if (r > 0) {
+            e0 *= eg[r][0];
+            e1 *= eg[r][1];
+            x0 *= eg[r][0];
+            x1 *= eg[r][1];
+        }
         store2<E>(sKr + row * LDK + c0, k0 * e0, k1 * e1);
         store2<E>(sQr + row * LDK + c0, q0 * e0, q1 * e1);
-        store2<E>(sKt + row * LDK + c0, k0 * f0, k1 * f1);
+        store2<E>(sKt + row * LDK + c0, k0 * ff[r][0], k1 * ff[r][1]);
         store2<E>(QGo + ch * C * DK + fm_off<DK>(row, frag_pos(c0)), q0 * x0, q1 * x1);
         kx[r][0] = k0 * x0;
         kx[r][1] = k1 * x1;
-        kd0[r] = Elt<E>::from(k0 * d0);
-        kd1[r] = Elt<E>::from(k1 * d1);
+        kd0[r] = Elt<E>::from(k0 * dd[r][0]);
+        kd1[r] = Elt<E>::from(k1 * dd[r][1]);
     }
     {
         E* p0 = KdTo + ch * DK * C;
