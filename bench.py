@@ -194,6 +194,21 @@ def main():
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / K
 
+    # decode steps back to back on one state (the serving pattern), after the
+    # timed region: the step above follows a prefill, these follow each other
+    n_b2b = 20
+    ev_b2b = Events(hip, n_b2b + 1)
+    for i in range(3):
+        tk = toks[i % n_tok]
+        kda.recurrent_step(tk["q"], tk["k"], tk["v"], tk["g"], tk["beta"], S_dec, out=o_dec)
+    ev_b2b.record(0, stream)
+    for i in range(n_b2b):
+        tk = toks[i % n_tok]
+        kda.recurrent_step(tk["q"], tk["k"], tk["v"], tk["g"], tk["beta"], S_dec, out=o_dec)
+        ev_b2b.record(i + 1, stream)
+    torch.cuda.synchronize()
+    t_b2b = float(np.median([ev_b2b.ms(i, i + 1) for i in range(n_b2b)]))
+
     avg = lambda i, j: float(np.mean([e.ms(i, j) for e in evs]))
     stats = lambda i, j: {"mean": avg(i, j), "median": float(np.median([e.ms(i, j) for e in evs])),
                           "min": float(np.min([e.ms(i, j) for e in evs]))}
@@ -236,7 +251,10 @@ def main():
         "decode_us_stats": {k: v * 1e3 for k, v in stats(4, 5).items()},
         "kernels_ms": {"chunk_map": t_map, "intra_chunk": t_intra, "chunk_walk": t_walk, "decode_step": t_dec},
         "decode": {"us_per_step": t_dec * 1e3, "GB_per_s": dec_gbs, "frac_hbm_peak": dec_gbs / HBM_PEAK_GBS,
-                   "tokens_per_s": dcfg.N / (t_dec * 1e-3), "bytes_per_step": DECODE_BYTES_PER_STEP},
+                   "tokens_per_s": dcfg.N / (t_dec * 1e-3), "bytes_per_step": DECODE_BYTES_PER_STEP,
+                   "back_to_back": {"steps": n_b2b, "us_per_step_median": t_b2b * 1e3,
+                                    "GB_per_s": DECODE_BYTES_PER_STEP / (t_b2b * 1e-3) / 1e9,
+                                    "frac_hbm_peak": DECODE_BYTES_PER_STEP / (t_b2b * 1e-3) / 1e9 / HBM_PEAK_GBS}},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(dom),
                      "algorithmic_bytes": dom_bytes},
