@@ -575,19 +575,29 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
             const int ti = pq ? pti1 : pti0, tj = pq ? ptj1 : ptj0;
             f32x4 accA = zero4(), accP = zero4();
             const bool diag = tj == ti;
-            const float* rowf = sTileF + (ti - 1) * DK;                       // off-diagonal only
-            const float* colf = sTileF + (3 + tj) * DK;
-            const float* midf = sTileF + (6 + ti * (ti - 1) / 2 + tj) * DK;
+            // the factors are read for diagonal pairs too (and not used), so
+            // that every read of a step goes out together; the rows are
+            // clamped into the table
+            const float* rowf = sTileF + max(ti - 1, 0) * DK;
+            const float* colf = sTileF + min(3 + tj, 5) * DK;
+            const float* midf = sTileF + min(6 + ti * (ti - 1) / 2 + tj, L::NCS - 1) * DK;
 #pragma unroll
             for (int ks = 0; ks < DK / 32; ++ks) {
                 const int cb = 32 * ks + 8 * lg;
                 Frag<E> fb = ld_frag(sKt + (16 * tj + lr) * LDK + cb);
                 Frag<E> fa = ld_frag(sKr + (16 * ti + lr) * LDK + cb);
                 Frag<E> fq = ld_frag(sQr + (16 * ti + lr) * LDK + cb);
+                float fr[8], fc[8], fm[8];
+#pragma unroll
+                for (int h4 = 0; h4 < 2; ++h4) {
+                    *reinterpret_cast<f32x4*>(fr + 4 * h4) = *reinterpret_cast<const f32x4*>(rowf + cb + 4 * h4);
+                    *reinterpret_cast<f32x4*>(fc + 4 * h4) = *reinterpret_cast<const f32x4*>(colf + cb + 4 * h4);
+                    *reinterpret_cast<f32x4*>(fm + 4 * h4) = *reinterpret_cast<const f32x4*>(midf + cb + 4 * h4);
+                }
                 if (!diag) {
-                    fb = scale_frag(fb, colf + cb, midf + cb);
-                    fa = scale_frag(fa, rowf + cb);
-                    fq = scale_frag(fq, rowf + cb);
+                    fb = scale_frag(fb, fc, fm);
+                    fa = scale_frag(fa, fr);
+                    fq = scale_frag(fq, fr);
                 }
                 accA = mma(fa, fb, accA);
                 accP = mma(fq, fb, accP);
