@@ -6,6 +6,8 @@ in the library's HIP kernels.  PyTorch provides device memory and streams.
 
     chunk_fwd(q, k, v, g, beta, S0=..., cu_seqlens=...) -> (o, S_T)
     recurrent_step(q, k, v, g, beta, S) -> o            (S updated in place)
+    chunk_bwd(q, k, v, g, beta, dO, S0=..., dS_T=..., cu_seqlens=...)
+        -> (dq, dk, dv, dg, dbeta, dS0)                  (gradients of the forward)
 
 The library must have been built (``__graft_entry__.build()`` or
 ``python gated_delta_rule_48_amd/build.py``); importing the functions'
@@ -19,6 +21,7 @@ import os
 import torch
 
 __all__ = ["chunk_fwd", "chunk_fwd_workspace_size", "chunk_fwd_check", "recurrent_step",
+           "chunk_bwd", "chunk_bwd_workspace_size",
            "KDAError", "LIB_PATH", "load_library", "STATUS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
@@ -57,6 +60,11 @@ def load_library():
         lib.kda_chunk_fwd_instrumented.argtypes = lib.kda_chunk_fwd.argtypes + [vp]
         lib.kda_chunk_fwd_check.restype = ctypes.c_int
         lib.kda_chunk_fwd_check.argtypes = [vp, vp]
+        lib.kda_chunk_bwd_workspace_size.restype = sz
+        lib.kda_chunk_bwd_workspace_size.argtypes = lib.kda_chunk_fwd_workspace_size.argtypes
+        lib.kda_chunk_bwd.restype = ctypes.c_int
+        lib.kda_chunk_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, ctypes.c_int,
+                                      ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.kda_recurrent_step.restype = ctypes.c_int
         lib.kda_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int,
                                            ctypes.c_int, vp, vp]
@@ -212,3 +220,55 @@ def recurrent_step(q, k, v, g, beta, S, *, per_head_gate=False, out=None, stream
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), N, H, dk, dv, _dt(q),
         _PER_HEAD if per_head_gate else _PER_CHANNEL, _ptr(o), _stream(stream)))
     return o
+
+
+def chunk_bwd_workspace_size(T_total, N, H, d_k, d_v, dtype=torch.bfloat16, per_head_gate=False):
+    """Bytes of workspace ``chunk_bwd`` needs (0 for unsupported sizes)."""
+    dt = _BF16 if dtype == torch.bfloat16 else _F32
+    return int(load_library().kda_chunk_bwd_workspace_size(
+        int(T_total), int(N), int(H), int(d_k), int(d_v), dt, _PER_HEAD if per_head_gate else _PER_CHANNEL))
+
+
+def chunk_bwd(q, k, v, g, beta, dO, *, S0=None, dS_T=None, cu_seqlens=None, N=None, per_head_gate=False,
+              need_dS0=True, workspace=None, stream=None):
+    """Gradients of ``chunk_fwd`` (kda_chunk_bwd).
+
+    Takes the forward's inputs (packed [T, H, d] layout, as for ``chunk_fwd``)
+    and the cotangents dO ([T, H, dv], q's dtype) and dS_T (fp32
+    [N, H, dk, dv] or None = zeros).  Returns (dq, dk, dv, dg, dbeta, dS0):
+    the first five with the shapes and dtype of q, k, v, g, beta; dS0 fp32
+    [N, H, dk, dv] (None when ``need_dS0`` is False).
+    """
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be [T, H, d]")
+    T_total, H, dk = q.shape
+    dv = v.shape[2]
+    _shapes(k=(k, (T_total, H, dk)), v=(v, (T_total, H, dv)), beta=(beta, (T_total, H)),
+            g=(g, (T_total, H) if per_head_gate else (T_total, H, dk)), dO=(dO, (T_total, H, dv)))
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("dO", dO)):
+        _dev_contig(name, t, q.dtype)
+    if cu_seqlens is not None:
+        _dev_contig("cu_seqlens", cu_seqlens, torch.int32)
+        N = cu_seqlens.numel() - 1
+    elif N is None:
+        N = 1
+    for name, t in (("S0", S0), ("dS_T", dS_T)):
+        if t is not None:
+            _dev_contig(name, t, torch.float32)
+            _shapes(**{name: (t, (N, H, dk, dv))})
+    dt = _dt(q)
+    gk = _PER_HEAD if per_head_gate else _PER_CHANNEL
+    dq, dk_, dv_, dg, db = (torch.empty_like(x) for x in (q, k, v, g, beta))
+    dS0 = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device) if need_dS0 else None
+    lib = load_library()
+    need = int(lib.kda_chunk_bwd_workspace_size(T_total, N, H, dk, dv, dt, gk))
+    if need == 0:
+        raise KDAError(2, f"unsupported sizes T={T_total} N={N} H={H} dk={dk} dv={dv}")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _dev_contig("workspace", workspace)
+    _check(lib.kda_chunk_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(cu_seqlens), N, T_total, H, dk, dv,
+        dt, gk, _ptr(dO), _ptr(dS_T), _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dg), _ptr(db), _ptr(dS0),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return dq, dk_, dv_, dg, db, dS0

@@ -110,6 +110,46 @@ kda_status kda_chunk_fwd_check(const void* workspace, hipStream_t stream) {
     return h.wait_timeout ? KDA_ERR_TIMEOUT : KDA_OK;
 }
 
+size_t kda_chunk_bwd_workspace_size(int64_t T_total, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                                    kda_dtype dt, kda_gate gk) {
+    if (check_common(H, d_k, d_v, dt, gk) != KDA_OK) return 0;
+    if (N <= 0 || T_total < 0 || T_total > INT32_MAX) return 0;
+    return kda::bwd_workspace_bytes(T_total, N, H, d_k, d_v);
+}
+
+kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                         const float* S0, const int32_t* cu_seqlens, int32_t N, int64_t T_total, int32_t H,
+                         int32_t d_k, int32_t d_v, kda_dtype dt, kda_gate gk, const void* dO, const float* dS_T,
+                         void* dq, void* dk, void* dv, void* dg, void* dbeta, float* dS0, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+    const kda_status st = check_common(H, d_k, d_v, dt, gk);
+    if (st != KDA_OK) return st;
+    if (N <= 0 || T_total < 0 || T_total > INT32_MAX) return KDA_ERR_INVALID_ARG;
+    if (!cu_seqlens && T_total % N != 0) return KDA_ERR_INVALID_ARG;
+    if (!kda::chunk_grid_fits(kda::max_chunks_for(T_total, N), H)) return KDA_ERR_UNSUPPORTED;
+    const size_t esz = dt == KDA_BF16 ? 2 : 4;
+    if (T_total > 0) {
+        const void* need[] = {q, k, v, g, beta, dO, dq, dk, dv, dg, dbeta};
+        for (const void* p : need)
+            if (!p || !aligned(p, esz)) return KDA_ERR_INVALID_ARG;
+    }
+    if ((S0 && !aligned(S0, 4)) || (dS_T && !aligned(dS_T, 4)) || (dS0 && !aligned(dS0, 4)) ||
+        (cu_seqlens && !aligned(cu_seqlens, 4)))
+        return KDA_ERR_INVALID_ARG;
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERR_WORKSPACE;
+    if (workspace_bytes < kda::bwd_workspace_bytes(T_total, N, H, d_k, d_v)) return KDA_ERR_WORKSPACE;
+
+    kda::BwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.S0 = S0; a.cu_seqlens = cu_seqlens; a.dO = dO; a.dS_T = dS_T;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dS0 = dS0;
+    a.N = N; a.H = H; a.dk_ = d_k; a.dv_ = d_v; a.T = T_total;
+    a.max_chunks = kda::max_chunks_for(T_total, N);
+    a.bf16 = dt == KDA_BF16;
+    a.head_gate = gk == KDA_GATE_PER_HEAD;
+    return kda::launch_chunk_bwd(a, workspace, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const void* g, const void* beta,
                               float* S, int32_t N, int32_t H, int32_t d_k, int32_t d_v, kda_dtype dt, kda_gate gk,
                               void* o, hipStream_t stream) {

@@ -1462,12 +1462,18 @@ static hipError_t launch_chunk_e(const ChunkArgs& a, const ChunkWorkspace& ws, h
     return launch_chunk_t<E, 128, 128>(a, ws, s, ev);
 }
 
+hipError_t launch_chunk_map(const int32_t* cu_seqlens, int32_t N, int64_t T, WsHeader* header, int32_t* cu,
+                            int32_t* chunk_off, int2* chunk_tab, hipStream_t stream) {
+    hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(256), 0, stream, cu_seqlens, N, T, header, cu, chunk_off,
+                       chunk_tab);
+    return hipGetLastError();
+}
+
 hipError_t launch_chunk_fwd(const ChunkArgs& a, const ChunkWorkspace& ws, hipStream_t stream, hipEvent_t* ev) {
     hipError_t e = mark(ev, 0, stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(256), 0, stream, a.cu_seqlens, a.N, a.T, ws.header, ws.cu,
-                       ws.chunk_off, ws.chunk_tab);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    e = launch_chunk_map(a.cu_seqlens, a.N, a.T, ws.header, ws.cu, ws.chunk_off, ws.chunk_tab, stream);
+    if (e != hipSuccess) return e;
     return a.bf16 ? launch_chunk_e<bf16_t>(a, ws, stream, ev) : launch_chunk_e<float>(a, ws, stream, ev);
 }
 

@@ -56,9 +56,32 @@ ChunkWorkspace carve_chunk_workspace(void* base, int64_t T, int32_t N, int32_t H
 int64_t max_chunks_for(int64_t T, int32_t N);
 bool chunk_grid_fits(int64_t max_chunks, int32_t H);
 
+// Validate cu_seqlens (or synthesise N equal sequences when it is null) and
+// write the header, the sequence offsets, the first chunk of every sequence
+// and every chunk's first token and length.
+hipError_t launch_chunk_map(const int32_t* cu_seqlens, int32_t N, int64_t T, WsHeader* header, int32_t* cu,
+                            int32_t* chunk_off, int2* chunk_tab, hipStream_t stream);
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 // events: null, or four events recorded before map / intra / walk and after walk.
 hipError_t launch_chunk_fwd(const ChunkArgs& a, const ChunkWorkspace& ws, hipStream_t stream,
                             hipEvent_t* events = nullptr);
+
+struct BwdArgs {
+    const void *q, *k, *v, *g, *beta;
+    const float* S0;            // may be null (zeros)
+    const int32_t* cu_seqlens;  // device, may be null
+    const void* dO;             // [T, H, dv], element type of q
+    const float* dS_T;          // may be null (zeros)
+    void *dq, *dk, *dv, *dg, *dbeta;
+    float* dS0;                 // may be null (not written)
+    int32_t N, H, dk_, dv_;
+    int64_t T;
+    int64_t max_chunks;
+    bool bf16, head_gate;
+};
+
+size_t bwd_workspace_bytes(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv);
+hipError_t launch_chunk_bwd(const BwdArgs& a, void* workspace, hipStream_t stream);
 
 }  // namespace kda

@@ -182,6 +182,58 @@ kda_status kda_recurrent_step(const void *q, const void *k, const void *v,
                               kda_dtype dt, kda_gate gk, void *o,
                               hipStream_t stream);
 
+/*
+ * Bytes of device workspace kda_chunk_bwd needs for these sizes (0 if the
+ * sizes are invalid or unsupported).  About 900 KB per (chunk, head) at
+ * d_k = d_v = 128: every intermediate of a chunk is kept in fp32.
+ */
+size_t kda_chunk_bwd_workspace_size(int64_t T_total, int32_t N, int32_t H,
+                                    int32_t d_k, int32_t d_v, kda_dtype dt,
+                                    kda_gate gk);
+
+/*
+ * Chunked KDA backward pass over a packed batch: the vector-Jacobian product
+ * of the map (q, k, v, g, beta, S0) -> (o, S_T) computed by kda_chunk_fwd,
+ * with cotangents dO and dS_T.  That is, for
+ *     L = sum_t <dO_t, o_t> + sum_{n,h} <dS_T[n,h], S_T[n,h]>,
+ * it writes dq = dL/dq, dk, dv, dg, dbeta and dS0 = dL/dS0.  The chunked form
+ * is what the pages present as the training path ("From GPT-2 to Kimi K3",
+ * section on the parallelisation trick; "Kimi Linear architecture", section
+ * on linear attention: chunkwise for training and prefill).  The chunk
+ * algebra of the forward pass is differentiated as written: a reverse walk
+ * over the chunks carries the state cotangent, and every chunk then forms its
+ * inputs' gradients, including those through the triangular solve and the
+ * gate's prefix sums, on its own.
+ *
+ *   q, k, v, g, beta, S0, cu_seqlens, N, T_total, H, d_k, d_v, dt, gk
+ *                     exactly as passed to kda_chunk_fwd (the forward outputs
+ *                     are not needed: the pass recomputes what it uses)
+ *   dO                [T_total, H, d_v], element type dt
+ *   dS_T              fp32 [N, H, d_k, d_v] or NULL (= zeros)
+ *   dq, dk, dg        [T_total, H, d_k] (dg is [T_total, H] with
+ *                     KDA_GATE_PER_HEAD: the sum over channels), type dt
+ *   dv                [T_total, H, d_v], type dt;  dbeta [T_total, H], type dt
+ *   dS0               fp32 [N, H, d_k, d_v] or NULL (not written); an empty
+ *                     sequence gives dS0 = dS_T
+ *   workspace         >= kda_chunk_bwd_workspace_size() bytes, 256-byte
+ *                     aligned, clobbered; kda_chunk_fwd_check accepts it too
+ *                     and reports rejected cu_seqlens the same way
+ *
+ * Alignment: every pointer to its element size.  Errors as for
+ * kda_chunk_fwd.  Numerics: all arithmetic in fp32, gradients rounded once
+ * to dt.  Domain: besides the forward's, the decay accumulated over any 32
+ * consecutive tokens of a chunk must stay above e^-80 (e.g. every g >= -2.5),
+ * since the operands are referred to the chunk's middle row.
+ */
+kda_status kda_chunk_bwd(const void *q, const void *k, const void *v,
+                         const void *g, const void *beta, const float *S0,
+                         const int32_t *cu_seqlens, int32_t N, int64_t T_total,
+                         int32_t H, int32_t d_k, int32_t d_v, kda_dtype dt,
+                         kda_gate gk, const void *dO, const float *dS_T,
+                         void *dq, void *dk, void *dv, void *dg, void *dbeta,
+                         float *dS0, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -148,6 +148,14 @@ def draw_tokens(rng, T, H, dk, dv, dtype, gate, gate_mu):
     return out
 
 
+def draw_cotangents(rng, T, N, H, dk, dv, dtype, sigma_state=1.0):
+    """Cotangents for a backward pass: dO ~ N(0,1) [T, H, dv] rounded to dtype,
+    and dS_T ~ N(0, sigma_state^2) fp32 [N, H, dk, dv] (drawn in that order)."""
+    dO = _round(_normal(rng, (T, H, dv)), dtype)
+    dST = (_normal(rng, (N, H, dk, dv)) * np.float32(sigma_state)).astype(np.float32)
+    return dO, dST
+
+
 def chunk_inputs(cfg, seed=None, lengths=None):
     """Inputs of a chunked-forward config.
 

@@ -29,7 +29,8 @@ def lib():
 def test_header_declares_expected_entry_points():
     names = _declared()
     for n in ("kda_chunk_fwd", "kda_recurrent_step", "kda_chunk_fwd_workspace_size",
-              "kda_chunk_fwd_check", "kda_status_string", "kda_version"):
+              "kda_chunk_fwd_check", "kda_status_string", "kda_version", "kda_chunk_bwd",
+              "kda_chunk_bwd_workspace_size"):
         assert n in names
 
 
@@ -114,6 +115,40 @@ def test_recurrent_step_rejects_bad_arguments(lib):
     assert f(P, P, P, P, P, P + 4, 4, 2, 64, 64, 0, 0, P, None) == INVALID   # S needs 16 bytes
     assert f(P, P, P, P, P + 1, P, 4, 2, 64, 64, 0, 0, P, None) == INVALID
     assert f(None, None, None, None, None, None, 0, 2, 64, 64, 0, 0, None, None) == OK   # nothing to do
+
+
+def test_chunk_bwd_rejects_bad_arguments(lib):
+    f = lib.kda_chunk_bwd
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    f.restype = ctypes.c_int
+    f.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, ctypes.c_int, ctypes.c_int, vp, vp,
+                  vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    sz = lib.kda_chunk_bwd_workspace_size
+    sz.restype = ctypes.c_size_t
+    sz.argtypes = [i64, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int]
+    P = FAKE
+    names = ["q", "k", "v", "g", "beta", "S0", "cu", "N", "T", "H", "dk", "dv", "dt", "gk", "dO", "dST",
+             "dq", "dkk", "dvv", "dg", "db", "dS0", "ws", "wsb", "stream"]
+    args = dict(q=P, k=P, v=P, g=P, beta=P, S0=None, cu=None, N=1, T=128, H=2, dk=64, dv=64, dt=0, gk=0,
+                dO=P, dST=None, dq=P, dkk=P, dvv=P, dg=P, db=P, dS0=None, ws=P, wsb=1 << 40, stream=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(*[a[n] for n in names])
+
+    assert call(dk=96) == UNSUPPORTED
+    assert call(dt=5) == UNSUPPORTED
+    assert call(H=0) == INVALID
+    assert call(N=3) == INVALID
+    assert call(dO=None) == INVALID
+    assert call(dg=None) == INVALID
+    assert call(db=P + 1) == INVALID
+    assert call(dS0=P + 2) == INVALID
+    assert call(ws=P + 16) == WORKSPACE
+    assert call(wsb=1024) == WORKSPACE
+    assert sz(128, 1, 2, 64, 64, 0, 0) > 0
+    assert sz(128, 1, 2, 64, 80, 0, 0) == 0
+    assert sz(256, 1, 2, 64, 64, 0, 0) > sz(128, 1, 2, 64, 64, 0, 0)
 
 
 def test_status_strings(lib):
