@@ -11,9 +11,11 @@ resident in HBM before the timed region.  `value` is prefill tokens/s over
 the chunked-forward time of the timed steps; `decode` reports the decode step
 in GB/s of its algorithmic bytes.  Each kernel is timed with HIP events
 recorded on the stream it runs on.  The oracle (fp64, host cores) is timed
-on a bounded prefix of the same workload as `cpu_baseline`.
+on a bounded prefix of the same workload as `cpu_baseline`.  After the timed
+steps, the chunked backward pass (kda_chunk_bwd) over the same prefill inputs
+is timed on its own and reported under `backward`.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-backward]
 """
 import argparse
 import ctypes
@@ -115,6 +117,34 @@ def cpu_baseline(d, prefix_tokens):
                       f"workload when {T} = 32768), fp64 sequential recurrence, {dt:.2f} s"}
 
 
+def time_backward(kda, torch, hip, x, d, T, H, dk, dv, stream, steps=5, warmup=2):
+    """The chunked backward pass (kda_chunk_bwd) over the same 32K x 32 inputs,
+    with seeded cotangents dO ~ N(0,1) (bf16) and dS_T ~ N(0,1); the whole
+    call is timed with HIP events on its stream.  Reported beside the
+    forward, not part of `value`."""
+    import synth
+    dO, dST = synth.draw_cotangents(np.random.default_rng(3030), T, 1, H, dk, dv, "bf16")
+    dO, dST = _to_dev(dO, torch), torch.from_numpy(dST).cuda()
+    ws = torch.empty(kda.chunk_bwd_workspace_size(T, 1, H, dk, dv), dtype=torch.uint8, device="cuda")
+    ev = Events(hip, steps + 1)
+
+    def run():
+        return kda.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], dO, dS_T=dST, workspace=ws)
+
+    for _ in range(warmup):
+        run()
+    ev.record(0, stream)
+    for i in range(steps):
+        run()
+        ev.record(i + 1, stream)
+    torch.cuda.synchronize()
+    ms = [ev.ms(i, i + 1) for i in range(steps)]
+    t = float(np.median(ms))
+    return {"ms_median": t, "ms_min": float(np.min(ms)), "tokens_per_s": T / (t * 1e-3),
+            "workspace_GB": ws.numel() / 1e9,
+            "what": "kda_chunk_bwd: dq, dk, dv, dg, dbeta, dS0 of the 32K x 32 prefill for dO, dS_T"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +152,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-prefix", type=int, default=32768)
+    ap.add_argument("--no-backward", action="store_true", help="skip timing the chunked backward pass")
+    ap.add_argument("--backward-steps", type=int, default=5)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one device-to-device copy of exactly 1 GiB before the timed steps, so that a "
                          "counter run (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE) has a kernel of known traffic "
@@ -209,6 +241,9 @@ def main():
     torch.cuda.synchronize()
     t_b2b = float(np.median([ev_b2b.ms(i, i + 1) for i in range(n_b2b)]))
 
+    bwd = None if args.no_backward else time_backward(kda, torch, hip, x, d, T, H, dk, dv, stream,
+                                                      steps=args.backward_steps)
+
     avg = lambda i, j: float(np.mean([e.ms(i, j) for e in evs]))
     stats = lambda i, j: {"mean": avg(i, j), "median": float(np.median([e.ms(i, j) for e in evs])),
                           "min": float(np.min([e.ms(i, j) for e in evs]))}
@@ -263,6 +298,8 @@ def main():
                           "GB_per_s": path_gbs, "frac_hbm_peak": path_gbs / HBM_PEAK_GBS,
                           "TFLOP_per_s": path_tflops, "frac_bf16_mfma_peak": path_tflops / BF16_MFMA_PEAK_TFLOPS},
     }
+    if bwd is not None:
+        res["backward"] = bwd
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(d, args.cpu_prefix)
     print(json.dumps(res), flush=True)

@@ -35,9 +35,10 @@
 //   dg = reverse cumulative sum of db over the chunk (summed over channels
 //        for a per-head gate).
 //
-// This first version computes in fp32 on the vector units and keeps every
-// intermediate of a chunk in the workspace; loops are arranged so that the
-// 64 lanes of a wave read contiguous or identical addresses.
+// All arithmetic is fp32 on the vector units.  Every intermediate of a chunk
+// is kept in the workspace; the two walks stage each chunk's operands into LDS
+// with 16-byte loads, and every matrix product of the per-chunk kernels runs
+// as a 64 x N block product tiled through LDS with 4 x N/16 register tiles.
 #include "kda_internal.h"
 
 namespace kda {
@@ -73,6 +74,79 @@ __device__ __forceinline__ float ld(const E* p, int64_t i) {
 }
 
 // ---------------------------------------------------------------------------
+// 64 x N block product on the 256 threads of a workgroup:
+//   acc(m, n) += sum_k a(m, k) b(k, n),   m < 64, n < N, k < K.
+// a and b are element loaders; A_KFAST / B_NFAST say which index is the
+// contiguous one in memory, so that the staging loads are coalesced.  Tiles
+// of 16 k-steps pass through LDS (k-major); thread (ty, tx) = (tid / 16,
+// tid % 16) owns rows 4ty..4ty+3 and columns tx*N/16 .. tx*N/16 + N/16 - 1.
+// Every thread of the workgroup must call it (it contains barriers).
+constexpr int kGemmLds = 16 * (64 + 4) + 16 * (128 + 4);  // floats
+
+template <int N>
+struct Acc {
+    float v[4][N / 16];
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < N / 16; ++j) v[i][j] = 0.f;
+    }
+    __device__ __forceinline__ static int row(int i) { return (threadIdx.x / 16) * 4 + i; }
+    __device__ __forceinline__ static int col(int j) { return (threadIdx.x % 16) * (N / 16) + j; }
+};
+
+template <int N, int K, bool A_KFAST, bool B_NFAST, typename LA, typename LB>
+__device__ __forceinline__ void gemm64(Acc<N>& acc, LA la, LB lb, float* lds) {
+    constexpr int KT = 16, M = 64, SA = M + 4, SB = N + 4, NT = N / 16;
+    float* sA = lds;
+    float* sB = lds + KT * SA;
+    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+    for (int k0 = 0; k0 < K; k0 += KT) {
+#pragma unroll
+        for (int idx = tid; idx < M * KT; idx += kBwdThreads) {
+            const int m = A_KFAST ? idx / KT : idx % M;
+            const int kk = A_KFAST ? idx % KT : idx / M;
+            sA[kk * SA + m] = la(m, k0 + kk);
+        }
+#pragma unroll
+        for (int idx = tid; idx < N * KT; idx += kBwdThreads) {
+            const int n = B_NFAST ? idx % N : idx / KT;
+            const int kk = B_NFAST ? idx / N : idx % KT;
+            sB[kk * SB + n] = lb(k0 + kk, n);
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int kk = 0; kk < KT; ++kk) {
+            const float4 a = *reinterpret_cast<const float4*>(sA + kk * SA + ty * 4);
+            float b[NT];
+#pragma unroll
+            for (int j = 0; j < NT; j += 4) {
+                const float4 x = *reinterpret_cast<const float4*>(sB + kk * SB + tx * NT + j);
+                b[j] = x.x; b[j + 1] = x.y; b[j + 2] = x.z; b[j + 3] = x.w;
+            }
+            const float av[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < NT; ++j) acc.v[i][j] += av[i] * b[j];
+        }
+        __syncthreads();
+    }
+}
+
+// Copy `count` floats (a multiple of 4, both ends 16-byte aligned) from global
+// memory into LDS rows of `width` floats with a row stride of `stride`.
+__device__ __forceinline__ void stage_rows(float* dst, const float* src, int rows, int width, int stride) {
+    const int per_row = width / 4;
+    for (int idx = threadIdx.x; idx < rows * per_row; idx += kBwdThreads) {
+        const int r = idx / per_row, c4 = idx % per_row;
+        *reinterpret_cast<float4*>(dst + r * stride + 4 * c4) =
+            *reinterpret_cast<const float4*>(src + (size_t)r * width + 4 * c4);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Per (chunk, head): prefix sums, decayed operands, M, P, T = (I + A)^{-1},
 // W and U'.
 template <typename E, int DK, int DV, bool HG>
@@ -82,6 +156,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const E* __restri
     __shared__ float sA[C][C + 1];
     __shared__ float sT[C][C + 1];
     __shared__ float sbeta[C];
+    __shared__ __align__(16) float lds[kGemmLds];
     const int64_t slot = blockIdx.x;
     const int64_t chunk = slot / H;
     const int h = (int)(slot % H);
@@ -135,24 +210,28 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const E* __restri
         w.XuT[oCV + (size_t)c * C + t] = sbeta[t] * vv;
     }
     __syncthreads();
-    // M (strictly lower) and P (lower, diagonal included)
-    for (int idx = tid; idx < C * C; idx += kBwdThreads) {
-        const int t = idx / C, i = idx % C;
-        float sm = 0.f, sp = 0.f;
-        if (t < n && i <= t) {
-            const float* kr = w.Kr + oCK + (size_t)t * DK;
-            const float* qr = w.Qr + oCK + (size_t)t * DK;
-            const float* kit = w.KiT + oCK + i;
-            for (int c = 0; c < DK; ++c) {
-                const float x = kit[(size_t)c * C];
-                sm += kr[c] * x;
-                sp += qr[c] * x;
+    // M = strict_tril(Kr Ki^T) and P = tril(Qr Ki^T)
+    {
+        const float* Kr = w.Kr + oCK;
+        const float* Qr = w.Qr + oCK;
+        const float* KiT = w.KiT + oCK;
+        Acc<C> am, ap;
+        am.zero();
+        ap.zero();
+        gemm64<C, DK, true, true>(am, [&](int t, int c) { return Kr[(size_t)t * DK + c]; },
+                                  [&](int c, int i) { return KiT[(size_t)c * C + i]; }, lds);
+        gemm64<C, DK, true, true>(ap, [&](int t, int c) { return Qr[(size_t)t * DK + c]; },
+                                  [&](int c, int i) { return KiT[(size_t)c * C + i]; }, lds);
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < C / 16; ++b) {
+                const int t = Acc<C>::row(a), i = Acc<C>::col(b);
+                const float mv = (i < t && t < n) ? am.v[a][b] : 0.f;
+                w.M[oCC + (size_t)t * C + i] = mv;
+                w.P[oCC + (size_t)t * C + i] = (i <= t && t < n) ? ap.v[a][b] : 0.f;
+                sA[t][i] = sbeta[t] * mv;
             }
-        }
-        const float mv = i < t ? sm : 0.f;
-        w.M[oCC + idx] = mv;
-        w.P[oCC + idx] = sp;
-        sA[t][i] = sbeta[t] * mv;
     }
     __syncthreads();
     // T = (I + A)^{-1}: column j by forward substitution (one thread per column)
@@ -178,30 +257,55 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const E* __restri
         w.T[oCC + idx] = sT[t][i];
         w.TT[oCC + idx] = sT[i][t];
     }
-    // W = T diag(beta) KG,  U' = T diag(beta) V
-    for (int idx = tid; idx < C * DK; idx += kBwdThreads) {
-        const int t = idx / DK, c = idx % DK;
-        float s = 0.f;
-        for (int i = 0; i <= t; ++i) s += sT[t][i] * sbeta[i] * w.KG[oCK + (size_t)i * DK + c];
-        w.W[oCK + idx] = s;
-    }
-    for (int idx = tid; idx < C * DV; idx += kBwdThreads) {
-        const int t = idx / DV, c = idx % DV;
-        float s = 0.f;
-        for (int i = 0; i <= t && i < n; ++i) s += sT[t][i] * sbeta[i] * ld(v, ((t0 + i) * H + h) * DV + c);
-        w.Up[oCV + idx] = s;
+    // W = T Xw (Xw = diag(beta) KG),  U' = T Xu (Xu = diag(beta) V)
+    {
+        const float* XwT = w.XwT + oCK;
+        const float* XuT = w.XuT + oCV;
+        Acc<DK> aw;
+        aw.zero();
+        gemm64<DK, C, true, false>(aw, [&](int t, int i) { return sT[t][i]; },
+                                   [&](int i, int c) { return XwT[(size_t)c * C + i]; }, lds);
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < DK / 16; ++b)
+                w.W[oCK + (size_t)Acc<DK>::row(a) * DK + Acc<DK>::col(b)] = aw.v[a][b];
+        Acc<DV> au;
+        au.zero();
+        gemm64<DV, C, true, false>(au, [&](int t, int i) { return sT[t][i]; },
+                                   [&](int i, int c) { return XuT[(size_t)c * C + i]; }, lds);
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < DV / 16; ++b)
+                w.Up[oCV + (size_t)Acc<DV>::row(a) * DV + Acc<DV>::col(b)] = au.v[a][b];
     }
 }
 
 // ---------------------------------------------------------------------------
 // Forward state walk per (sequence, head, 16-column slice): saves the start
-// state of every chunk (transposed) and U = U' - W S (transposed).
+// state of every chunk (transposed) and U = U' - W S (transposed).  Each
+// chunk's W, Kd, U' slice and Gn are first staged into LDS.
+template <int DK, int DV>
+struct StateWalkLds {
+    static constexpr int SK = DK + 4;
+    static constexpr int W = 0, Kd = W + C * SK, S = Kd + C * SK, U = S + DK * 16, Up = U + C * 16,
+                         Gn = Up + C * 16, floats = Gn + DK;
+    static constexpr size_t bytes = (size_t)floats * 4;
+};
+
 template <int DK, int DV>
 __global__ __launch_bounds__(kBwdThreads) void bwd_state_walk_kernel(int32_t H, const float* __restrict__ S0,
                                                                      BwdWs w) {
-    constexpr int NS = DV / 16;
-    __shared__ float sS[DK][16];
-    __shared__ float sU[C][16];
+    using L = StateWalkLds<DK, DV>;
+    constexpr int NS = DV / 16, SK = L::SK;
+    extern __shared__ __align__(16) float smem[];
+    float* sW = smem + L::W;
+    float* sKd = smem + L::Kd;
+    float* sS = smem + L::S;    // [DK][16]
+    float* sU = smem + L::U;    // [C][16]
+    float* sUp = smem + L::Up;  // [C][16]
+    float* sGn = smem + L::Gn;
     const int bid = blockIdx.x;
     const int sl = bid % NS;
     const int nh = bid / NS;
@@ -212,31 +316,41 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_state_walk_kernel(int32_t H, 
     const int col0 = sl * 16;
     for (int idx = tid; idx < DK * 16; idx += kBwdThreads) {
         const int c = idx / 16, vv = idx % 16;
-        sS[c][vv] = S0 ? S0[(((size_t)seq * H + h) * DK + c) * DV + col0 + vv] : 0.f;
+        sS[idx] = S0 ? S0[(((size_t)seq * H + h) * DK + c) * DV + col0 + vv] : 0.f;
     }
-    __syncthreads();
     const int c0 = w.chunk_off[seq], c1 = w.chunk_off[seq + 1];
     for (int ch = c0; ch < c1; ++ch) {
         const size_t slot = (size_t)ch * H + h;
         const size_t oCK = slot * C * DK, oCV = slot * C * DV, oKV = slot * DK * DV;
+        stage_rows(sW, w.W + oCK, C, DK, SK);
+        stage_rows(sKd, w.Kd + oCK, C, DK, SK);
+        for (int idx = tid; idx < C * 4; idx += kBwdThreads) {
+            const int t = idx / 4, c4 = idx % 4;
+            *reinterpret_cast<float4*>(sUp + t * 16 + 4 * c4) =
+                *reinterpret_cast<const float4*>(w.Up + oCV + (size_t)t * DV + col0 + 4 * c4);
+        }
+        for (int c = tid; c < DK; c += kBwdThreads) sGn[c] = w.Gn[slot * DK + c];
+        __syncthreads();
         for (int idx = tid; idx < DK * 16; idx += kBwdThreads) {
             const int c = idx / 16, vv = idx % 16;
-            w.ST[oKV + (size_t)(col0 + vv) * DK + c] = sS[c][vv];
+            w.ST[oKV + (size_t)(col0 + vv) * DK + c] = sS[idx];
         }
         for (int idx = tid; idx < C * 16; idx += kBwdThreads) {
             const int t = idx / 16, vv = idx % 16;
-            const float* wr = w.W + oCK + (size_t)t * DK;
-            float s = w.Up[oCV + (size_t)t * DV + col0 + vv];
-            for (int c = 0; c < DK; ++c) s -= wr[c] * sS[c][vv];
-            sU[t][vv] = s;
+            const float* wr = sW + t * SK;
+            float s = sUp[idx];
+#pragma unroll 8
+            for (int c = 0; c < DK; ++c) s -= wr[c] * sS[c * 16 + vv];
+            sU[idx] = s;
             w.UT[oCV + (size_t)(col0 + vv) * C + t] = s;
         }
         __syncthreads();
         for (int idx = tid; idx < DK * 16; idx += kBwdThreads) {
             const int c = idx / 16, vv = idx % 16;
-            float s = w.Gn[slot * DK + c] * sS[c][vv];
-            for (int t = 0; t < C; ++t) s += w.Kd[oCK + (size_t)t * DK + c] * sU[t][vv];
-            sS[c][vv] = s;
+            float s = sGn[c] * sS[idx];
+#pragma unroll 8
+            for (int t = 0; t < C; ++t) s += sKd[t * SK + c] * sU[t * 16 + vv];
+            sS[idx] = s;
         }
         __syncthreads();
     }
@@ -244,15 +358,31 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_state_walk_kernel(int32_t H, 
 
 // ---------------------------------------------------------------------------
 // Reverse state walk per (sequence, head, 16-column slice): dU of every chunk
-// and the state cotangent after it (transposed); dS0 at the end.
+// and the state cotangent after it (transposed); dS0 at the end.  Each
+// chunk's P, Kd, QG, W, Gn and dO slice are first staged into LDS.
+template <int DK, int DV>
+struct DStateWalkLds {
+    static constexpr int SK = DK + 4, SC = C + 4;
+    static constexpr int P = 0, Kd = P + C * SC, QG = Kd + C * SK, W = QG + C * SK, dS = W + C * SK,
+                         dU = dS + DK * 16, dO = dU + C * 16, Gn = dO + C * 16, floats = Gn + DK;
+    static constexpr size_t bytes = (size_t)floats * 4;
+};
+
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dstate_walk_kernel(int32_t H, const E* __restrict__ dO,
                                                                       const float* __restrict__ dST,
                                                                       float* __restrict__ dS0, BwdWs w) {
-    constexpr int NS = DV / 16;
-    __shared__ float sdS[DK][16];
-    __shared__ float sdU[C][16];
-    __shared__ float sdO[C][16];
+    using L = DStateWalkLds<DK, DV>;
+    constexpr int NS = DV / 16, SK = L::SK, SC = L::SC;
+    extern __shared__ __align__(16) float smem[];
+    float* sP = smem + L::P;
+    float* sKd = smem + L::Kd;
+    float* sQG = smem + L::QG;
+    float* sW = smem + L::W;
+    float* sdS = smem + L::dS;  // [DK][16]
+    float* sdU = smem + L::dU;  // [C][16]
+    float* sdO = smem + L::dO;  // [C][16]
+    float* sGn = smem + L::Gn;
     const int bid = blockIdx.x;
     const int sl = bid % NS;
     const int nh = bid / NS;
@@ -263,49 +393,53 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dstate_walk_kernel(int32_t H,
     const int col0 = sl * 16;
     for (int idx = tid; idx < DK * 16; idx += kBwdThreads) {
         const int c = idx / 16, vv = idx % 16;
-        sdS[c][vv] = dST ? dST[(((size_t)seq * H + h) * DK + c) * DV + col0 + vv] : 0.f;
+        sdS[idx] = dST ? dST[(((size_t)seq * H + h) * DK + c) * DV + col0 + vv] : 0.f;
     }
-    __syncthreads();
     const int c0 = w.chunk_off[seq], c1 = w.chunk_off[seq + 1];
     for (int ch = c1 - 1; ch >= c0; --ch) {
         const size_t slot = (size_t)ch * H + h;
-        const size_t oCK = slot * C * DK, oCV = slot * C * DV, oCC = slot * C * C, oKV = slot * DK * DV;
+        const size_t oCK = slot * C * DK, oCC = slot * C * C, oCV = slot * C * DV, oKV = slot * DK * DV;
         const int2 ct = w.chunk_tab[ch];
         const int64_t t0 = ct.x;
         const int n = ct.y;
-        for (int idx = tid; idx < DK * 16; idx += kBwdThreads) {
-            const int c = idx / 16, vv = idx % 16;
-            w.dSnT[oKV + (size_t)(col0 + vv) * DK + c] = sdS[c][vv];
-        }
+        stage_rows(sP, w.P + oCC, C, C, SC);
+        stage_rows(sKd, w.Kd + oCK, C, DK, SK);
+        stage_rows(sQG, w.QG + oCK, C, DK, SK);
+        stage_rows(sW, w.W + oCK, C, DK, SK);
+        for (int c = tid; c < DK; c += kBwdThreads) sGn[c] = w.Gn[slot * DK + c];
         for (int idx = tid; idx < C * 16; idx += kBwdThreads) {
             const int t = idx / 16, vv = idx % 16;
-            sdO[t][vv] = t < n ? ld(dO, ((t0 + t) * H + h) * DV + col0 + vv) : 0.f;
+            sdO[idx] = t < n ? ld(dO, ((t0 + t) * H + h) * DV + col0 + vv) : 0.f;
         }
         __syncthreads();
+        for (int idx = tid; idx < DK * 16; idx += kBwdThreads) {
+            const int c = idx / 16, vv = idx % 16;
+            w.dSnT[oKV + (size_t)(col0 + vv) * DK + c] = sdS[idx];
+        }
         for (int idx = tid; idx < C * 16; idx += kBwdThreads) {
             const int t = idx / 16, vv = idx % 16;
             float s = 0.f;
-            for (int i = t; i < C; ++i) s += w.P[oCC + (size_t)i * C + t] * sdO[i][vv];
-            for (int c = 0; c < DK; ++c) s += w.Kd[oCK + (size_t)t * DK + c] * sdS[c][vv];
-            sdU[t][vv] = s;
+            for (int i = t; i < C; ++i) s += sP[i * SC + t] * sdO[i * 16 + vv];
+            const float* kr = sKd + t * SK;
+#pragma unroll 8
+            for (int c = 0; c < DK; ++c) s += kr[c] * sdS[c * 16 + vv];
+            sdU[idx] = s;
             w.dU[oCV + (size_t)t * DV + col0 + vv] = s;
         }
         __syncthreads();
         for (int idx = tid; idx < DK * 16; idx += kBwdThreads) {
             const int c = idx / 16, vv = idx % 16;
-            float s = w.Gn[slot * DK + c] * sdS[c][vv];
-            for (int t = 0; t < C; ++t) {
-                const size_t i = oCK + (size_t)t * DK + c;
-                s += w.QG[i] * sdO[t][vv] - w.W[i] * sdU[t][vv];
-            }
-            sdS[c][vv] = s;
+            float s = sGn[c] * sdS[idx];
+#pragma unroll 8
+            for (int t = 0; t < C; ++t) s += sQG[t * SK + c] * sdO[t * 16 + vv] - sW[t * SK + c] * sdU[t * 16 + vv];
+            sdS[idx] = s;
         }
         __syncthreads();
     }
     if (dS0) {
         for (int idx = tid; idx < DK * 16; idx += kBwdThreads) {
             const int c = idx / 16, vv = idx % 16;
-            dS0[(((size_t)seq * H + h) * DK + c) * DV + col0 + vv] = sdS[c][vv];
+            dS0[(((size_t)seq * H + h) * DK + c) * DV + col0 + vv] = sdS[idx];
         }
     }
 }
@@ -321,6 +455,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
     __shared__ float sbeta[C];
     __shared__ float sr[DK];
     __shared__ float sbl[DK];
+    __shared__ __align__(16) float lds[kGemmLds];
     const int64_t slot = blockIdx.x;
     const int64_t chunk = slot / H;
     const int h = (int)(slot % H);
@@ -336,109 +471,165 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
         sr[tid] = w.B[oCK + (size_t)((n - 1) / 2) * DK + tid];
         sbl[tid] = w.B[oCK + (size_t)(n - 1) * DK + tid];
     }
-    auto dOat = [&](int t, int c) -> float { return ld(dO, ((t0 + t) * H + h) * DV + c); };
-    auto vat = [&](int t, int c) -> float { return ld(v, ((t0 + t) * H + h) * DV + c); };
-
-    // phase 1: dW, dQG, dKd, dGn, dP
-    for (int idx = tid; idx < C * DK; idx += kBwdThreads) {
-        const int t = idx / DK, c = idx % DK;
-        float a1 = 0.f, a2 = 0.f, a3 = 0.f;
-        if (t < n) {
-            for (int x = 0; x < DV; ++x) {
-                const float s = w.ST[oKV + (size_t)x * DK + c];
-                a1 += w.dU[oCV + (size_t)t * DV + x] * s;
-                a2 += dOat(t, x) * s;
-                a3 += w.UT[oCV + (size_t)x * C + t] * w.dSnT[oKV + (size_t)x * DK + c];
+    const float* ST = w.ST + oKV;
+    const float* dSnT = w.dSnT + oKV;
+    const float* UT = w.UT + oCV;
+    const float* dUm = w.dU + oCV;
+    const float* TT = w.TT + oCC;
+    auto dOat = [&](int t, int x) -> float { return t < n ? ld(dO, ((t0 + t) * H + h) * DV + x) : 0.f; };
+    // store a 64 x N accumulator tile (times s) to dst (row stride N), rows >= n as zero
+    auto put = [&](auto& acc, float* dst, int N, float s) {
+        constexpr int NT = sizeof(acc.v[0]) / sizeof(float);
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < NT; ++b) {
+                const int t = (tid / 16) * 4 + a, c = (tid % 16) * NT + b;
+                dst[(size_t)t * N + c] = t < n ? s * acc.v[a][b] : 0.f;
             }
-        }
-        w.dW[oCK + idx] = -a1;
-        w.dQG[oCK + idx] = a2;
-        w.dKd[oCK + idx] = a3;
+    };
+
+    // phase 1: dW = -dU S^T, dQG = dO S^T, dKd = U dS_next^T, dP = tril(dO U^T), dGn
+    {
+        Acc<DK> acc;
+        acc.zero();
+        gemm64<DK, DV, true, true>(acc, [&](int t, int x) { return dUm[(size_t)t * DV + x]; },
+                                   [&](int x, int c) { return ST[(size_t)x * DK + c]; }, lds);
+        put(acc, w.dW + oCK, DK, -1.f);
+        acc.zero();
+        gemm64<DK, DV, true, true>(acc, dOat, [&](int x, int c) { return ST[(size_t)x * DK + c]; }, lds);
+        put(acc, w.dQG + oCK, DK, 1.f);
+        acc.zero();
+        gemm64<DK, DV, false, true>(acc, [&](int t, int x) { return UT[(size_t)x * C + t]; },
+                                    [&](int x, int c) { return dSnT[(size_t)x * DK + c]; }, lds);
+        put(acc, w.dKd + oCK, DK, 1.f);
+        Acc<C> ap;
+        ap.zero();
+        gemm64<C, DV, true, true>(ap, dOat, [&](int x, int i) { return UT[(size_t)x * C + i]; }, lds);
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < C / 16; ++b) {
+                const int t = Acc<C>::row(a), i = Acc<C>::col(b);
+                w.dP[oCC + (size_t)t * C + i] = (i <= t && t < n) ? ap.v[a][b] : 0.f;
+            }
     }
     for (int c = tid; c < DK; c += kBwdThreads) {
         float s = 0.f;
-        for (int x = 0; x < DV; ++x) s += w.ST[oKV + (size_t)x * DK + c] * w.dSnT[oKV + (size_t)x * DK + c];
+        for (int x = 0; x < DV; ++x) s += ST[(size_t)x * DK + c] * dSnT[(size_t)x * DK + c];
         w.dGn[oK + c] = s;
     }
-    for (int idx = tid; idx < C * C; idx += kBwdThreads) {
-        const int t = idx / C, i = idx % C;
-        float s = 0.f;
-        if (i <= t && t < n)
-            for (int x = 0; x < DV; ++x) s += dOat(t, x) * w.UT[oCV + (size_t)x * C + i];
-        w.dP[oCC + idx] = s;
+    __syncthreads();
+
+    // phase 2: dT = strict_tril(dW Xw^T + dU Xu^T), dXw = T^T dW, dXu = T^T dU
+    {
+        const float* dW = w.dW + oCK;
+        const float* XwT = w.XwT + oCK;
+        const float* XuT = w.XuT + oCV;
+        Acc<C> at;
+        at.zero();
+        gemm64<C, DK, true, true>(at, [&](int t, int c) { return dW[(size_t)t * DK + c]; },
+                                  [&](int c, int i) { return XwT[(size_t)c * C + i]; }, lds);
+        gemm64<C, DV, true, true>(at, [&](int t, int x) { return dUm[(size_t)t * DV + x]; },
+                                  [&](int x, int i) { return XuT[(size_t)x * C + i]; }, lds);
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < C / 16; ++b) {
+                const int t = Acc<C>::row(a), i = Acc<C>::col(b);
+                w.dT[oCC + (size_t)t * C + i] = (i < t && t < n) ? at.v[a][b] : 0.f;
+            }
+        Acc<DK> ax;
+        ax.zero();
+        gemm64<DK, C, true, true>(ax, [&](int t, int a) { return TT[(size_t)t * C + a]; },
+                                  [&](int a, int c) { return dW[(size_t)a * DK + c]; }, lds);
+        put(ax, w.dXw + oCK, DK, 1.f);
+        Acc<DV> au;
+        au.zero();
+        gemm64<DV, C, true, true>(au, [&](int t, int a) { return TT[(size_t)t * C + a]; },
+                                  [&](int a, int x) { return dUm[(size_t)a * DV + x]; }, lds);
+        put(au, w.dXu + oCV, DV, 1.f);
     }
     __syncthreads();
 
-    // phase 2: dT (strictly lower), dXw = T^T dW, dXu = T^T dU
-    for (int idx = tid; idx < C * C; idx += kBwdThreads) {
-        const int t = idx / C, i = idx % C;
-        float s = 0.f;
-        if (i < t && t < n) {
-            for (int c = 0; c < DK; ++c) s += w.dW[oCK + (size_t)t * DK + c] * w.XwT[oCK + (size_t)c * C + i];
-            for (int x = 0; x < DV; ++x) s += w.dU[oCV + (size_t)t * DV + x] * w.XuT[oCV + (size_t)x * C + i];
-        }
-        w.dT[oCC + idx] = s;
-    }
-    for (int idx = tid; idx < C * DK; idx += kBwdThreads) {
-        const int t = idx / DK, c = idx % DK;
-        float s = 0.f;
-        for (int a = t; a < n; ++a) s += w.T[oCC + (size_t)a * C + t] * w.dW[oCK + (size_t)a * DK + c];
-        w.dXw[oCK + idx] = s;
-    }
-    for (int idx = tid; idx < C * DV; idx += kBwdThreads) {
-        const int t = idx / DV, x = idx % DV;
-        float s = 0.f;
-        for (int a = t; a < n; ++a) s += w.T[oCC + (size_t)a * C + t] * w.dU[oCV + (size_t)a * DV + x];
-        w.dXu[oCV + idx] = s;
-    }
-    __syncthreads();
-
-    // phase 3: Y = dT T^T (needed where column < row)
-    for (int idx = tid; idx < C * C; idx += kBwdThreads) {
-        const int a = idx / C, i = idx % C;
-        float s = 0.f;
-        if (i < a && a < n)
-            for (int b = 0; b <= i; ++b) s += w.dT[oCC + (size_t)a * C + b] * w.TT[oCC + (size_t)b * C + i];
-        w.Y[oCC + idx] = s;
+    // phase 3: Y = dT T^T (kept where column < row)
+    {
+        const float* dT = w.dT + oCC;
+        Acc<C> ay;
+        ay.zero();
+        gemm64<C, C, true, true>(ay, [&](int a, int b) { return dT[(size_t)a * C + b]; },
+                                 [&](int b, int i) { return TT[(size_t)b * C + i]; }, lds);
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < C / 16; ++b) {
+                const int r = Acc<C>::row(a), i = Acc<C>::col(b);
+                w.Y[oCC + (size_t)r * C + i] = (i < r && r < n) ? ay.v[a][b] : 0.f;
+            }
     }
     __syncthreads();
 
     // phase 4: dA = strict_tril(-T^T Y)
-    for (int idx = tid; idx < C * C; idx += kBwdThreads) {
-        const int t = idx / C, i = idx % C;
-        float s = 0.f;
-        if (i < t && t < n)
-            for (int a = t; a < n; ++a) s += w.T[oCC + (size_t)a * C + t] * w.Y[oCC + (size_t)a * C + i];
-        w.dA[oCC + idx] = -s;
+    {
+        const float* Y = w.Y + oCC;
+        Acc<C> aa;
+        aa.zero();
+        gemm64<C, C, true, true>(aa, [&](int t, int a) { return TT[(size_t)t * C + a]; },
+                                 [&](int a, int i) { return Y[(size_t)a * C + i]; }, lds);
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < C / 16; ++b) {
+                const int t = Acc<C>::row(a), i = Acc<C>::col(b);
+                w.dA[oCC + (size_t)t * C + i] = (i < t && t < n) ? -aa.v[a][b] : 0.f;
+            }
     }
     __syncthreads();
 
-    // phase 5: dq, dk, db (kept in dW's slot), dbeta, dv
-    for (int idx = tid; idx < C * DK; idx += kBwdThreads) {
-        const int t = idx / DK, c = idx % DK;
-        if (t >= n) continue;
-        float dKr = 0.f, dKi = 0.f, dQr = 0.f;
-        for (int i = 0; i < t; ++i) dKr += w.dA[oCC + (size_t)t * C + i] * w.Ki[oCK + (size_t)i * DK + c];
-        dKr *= sbeta[t];
-        for (int a = t + 1; a < n; ++a)
-            dKi += sbeta[a] * w.dA[oCC + (size_t)a * C + t] * w.Kr[oCK + (size_t)a * DK + c];
-        for (int a = t; a < n; ++a) dKi += w.dP[oCC + (size_t)a * C + t] * w.Qr[oCK + (size_t)a * DK + c];
-        for (int i = 0; i <= t; ++i) dQr += w.dP[oCC + (size_t)t * C + i] * w.Ki[oCK + (size_t)i * DK + c];
-        const size_t j = oCK + idx;
-        const float dKG = sbeta[t] * w.dXw[j];
-        const float dQG = w.dQG[j], dKd = w.dKd[j];
-        const float b = w.B[j], r = sr[c], bl = sbl[c];
-        const float e = expf(b), er = expf(b - r), eir = expf(r - b), ed = expf(bl - b);
-        const int64_t o = ((t0 + t) * H + h) * DK + c;
-        dq[o] = Elt<E>::from(dQG * e + dQr * er);
-        dk[o] = Elt<E>::from(dKG * e + dKr * er + dKi * eir + dKd * ed);
-        w.dW[j] = dQG * w.QG[j] + dQr * w.Qr[j] + dKG * w.KG[j] + dKr * w.Kr[j] - dKi * w.Ki[j] - dKd * w.Kd[j];
+    // phase 5: dKr = diag(beta) dA Ki, dKi = (diag(beta) dA)^T Kr + dP^T Qr,
+    // dQr = dP Ki; then dq, dk and db (kept in dW's slot), dbeta, dv
+    {
+        const float* dA = w.dA + oCC;
+        const float* dP = w.dP + oCC;
+        const float* Ki = w.Ki + oCK;
+        const float* Kr = w.Kr + oCK;
+        const float* Qr = w.Qr + oCK;
+        Acc<DK> akr, aki, aqr;
+        akr.zero();
+        aki.zero();
+        aqr.zero();
+        gemm64<DK, C, true, true>(akr, [&](int t, int i) { return dA[(size_t)t * C + i]; },
+                                  [&](int i, int c) { return Ki[(size_t)i * DK + c]; }, lds);
+        gemm64<DK, C, false, true>(aki, [&](int t, int a) { return sbeta[a] * dA[(size_t)a * C + t]; },
+                                   [&](int a, int c) { return Kr[(size_t)a * DK + c]; }, lds);
+        gemm64<DK, C, false, true>(aki, [&](int t, int a) { return dP[(size_t)a * C + t]; },
+                                   [&](int a, int c) { return Qr[(size_t)a * DK + c]; }, lds);
+        gemm64<DK, C, true, true>(aqr, [&](int t, int i) { return dP[(size_t)t * C + i]; },
+                                  [&](int i, int c) { return Ki[(size_t)i * DK + c]; }, lds);
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < DK / 16; ++b) {
+                const int t = Acc<DK>::row(a), c = Acc<DK>::col(b);
+                if (t >= n) continue;
+                const size_t j = oCK + (size_t)t * DK + c;
+                const float dKr = sbeta[t] * akr.v[a][b], dKi = aki.v[a][b], dQr = aqr.v[a][b];
+                const float dKG = sbeta[t] * w.dXw[j];
+                const float dQG = w.dQG[j], dKd = w.dKd[j];
+                const float bb = w.B[j], r = sr[c], bl = sbl[c];
+                const float e = expf(bb), er = expf(bb - r), eir = expf(r - bb), ed = expf(bl - bb);
+                const int64_t o = ((t0 + t) * H + h) * DK + c;
+                dq[o] = Elt<E>::from(dQG * e + dQr * er);
+                dk[o] = Elt<E>::from(dKG * e + dKr * er + dKi * eir + dKd * ed);
+                w.dW[j] = dQG * w.QG[j] + dQr * w.Qr[j] + dKG * w.KG[j] + dKr * w.Kr[j] - dKi * w.Ki[j] -
+                          dKd * w.Kd[j];
+            }
     }
     for (int t = tid; t < n; t += kBwdThreads) {
         float s = 0.f;
         for (int i = 0; i < t; ++i) s += w.dA[oCC + (size_t)t * C + i] * w.M[oCC + (size_t)t * C + i];
         for (int c = 0; c < DK; ++c) s += w.dXw[oCK + (size_t)t * DK + c] * w.KG[oCK + (size_t)t * DK + c];
-        for (int x = 0; x < DV; ++x) s += w.dXu[oCV + (size_t)t * DV + x] * vat(t, x);
+        for (int x = 0; x < DV; ++x) s += w.dXu[oCV + (size_t)t * DV + x] * ld(v, ((t0 + t) * H + h) * DV + x);
         dbeta[(t0 + t) * H + h] = Elt<E>::from(s);
     }
     for (int idx = tid; idx < C * DV; idx += kBwdThreads) {
@@ -514,22 +705,32 @@ BwdWs carve_bwd(void* base, int64_t T, int32_t N, int32_t H, int32_t dk, int32_t
     return w;
 }
 
+// Allow a kernel more than the default 64 KB of dynamic LDS.
+hipError_t lds_attr(const void* kern, size_t bytes) {
+    return hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
 template <typename E, int DK, int DV, bool HG>
 hipError_t launch_bwd_t(const BwdArgs& a, const BwdWs& w, hipStream_t stream) {
     const unsigned slots = (unsigned)(a.max_chunks * a.H);
     const unsigned walks = (unsigned)((int64_t)a.N * a.H * (DV / 16));
+    hipError_t e = hipSuccess;
     if (a.T > 0) {
         hipLaunchKernelGGL((bwd_prep_kernel<E, DK, DV, HG>), dim3(slots), dim3(kBwdThreads), 0, stream,
                            (const E*)a.q, (const E*)a.k, (const E*)a.v, (const E*)a.g, (const E*)a.beta, a.H, w);
-        hipError_t e = hipGetLastError();
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((bwd_state_walk_kernel<DK, DV>), dim3(walks), dim3(kBwdThreads), 0, stream, a.H, a.S0,
-                           w);
+        auto sw = bwd_state_walk_kernel<DK, DV>;
+        constexpr size_t sw_lds = StateWalkLds<DK, DV>::bytes;
+        if ((e = lds_attr(reinterpret_cast<const void*>(sw), sw_lds)) != hipSuccess) return e;
+        hipLaunchKernelGGL(sw, dim3(walks), dim3(kBwdThreads), sw_lds, stream, a.H, a.S0, w);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((bwd_dstate_walk_kernel<E, DK, DV>), dim3(walks), dim3(kBwdThreads), 0, stream, a.H,
-                       (const E*)a.dO, a.dS_T, a.dS0, w);
-    hipError_t e = hipGetLastError();
+    auto dw = bwd_dstate_walk_kernel<E, DK, DV>;
+    constexpr size_t dw_lds = DStateWalkLds<DK, DV>::bytes;
+    if ((e = lds_attr(reinterpret_cast<const void*>(dw), dw_lds)) != hipSuccess) return e;
+    hipLaunchKernelGGL(dw, dim3(walks), dim3(kBwdThreads), dw_lds, stream, a.H, (const E*)a.dO, a.dS_T, a.dS0, w);
+    e = hipGetLastError();
     if (e != hipSuccess || a.T == 0) return e;
     hipLaunchKernelGGL((bwd_local_kernel<E, DK, DV, HG>), dim3(slots), dim3(kBwdThreads), 0, stream,
                        (const E*)a.v, (const E*)a.beta, (const E*)a.dO, a.H, w, (E*)a.dq, (E*)a.dk, (E*)a.dv,
