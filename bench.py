@@ -42,12 +42,18 @@ WALK_BYTES_PER_HT = 1384               # reads W,QG,KdT,U' (4 x 256), P (96), Gn
 DECODE_BYTES_PER_STEP = 1084243968     # state read + write (2 x 536870912) + tokens in (8404992) + o (2097152)
 
 
+# The files the forward and decode kernels are compiled from (the backward
+# pass and the host-side ABI live elsewhere and do not change them).
+KERNEL_SOURCES = ("kda_chunk.hip", "kda_decode.hip", "kda_device.h")
+
+
 def kernel_sources_sha():
-    """sha256[:16] over the HIP sources, as recorded next to counter readings."""
-    import glob
+    """sha256[:16] over the forward and decode kernel sources, as recorded next
+    to counter readings."""
     import hashlib
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "gated_delta_rule_48_amd", "csrc", "*"))):
+    for name in KERNEL_SOURCES:
+        f = os.path.join(ROOT, "gated_delta_rule_48_amd", "csrc", name)
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
             h.update(fh.read())
