@@ -36,9 +36,10 @@
 //        for a per-head gate).
 //
 // All arithmetic is fp32 on the vector units.  Every intermediate of a chunk
-// is kept in the workspace; the two walks stage each chunk's operands into LDS
-// with 16-byte loads, and every matrix product of the per-chunk kernels runs
-// as a 64 x N block product tiled through LDS with 4 x N/16 register tiles.
+// is kept in the workspace.  The two walks run one workgroup per (sequence,
+// head, 16-column slice) with register tiles and the next chunk's operands in
+// flight; every product of the per-chunk kernels runs as a 64 x N block
+// product tiled through LDS with 4 x N/16 register tiles.
 #include "kda_internal.h"
 
 namespace kda {
@@ -58,14 +59,14 @@ struct BwdWs {
     float *B, *QG, *KG, *Kd, *Qr, *Kr, *Ki, *W, *dW, *dQG, *dKd, *dXw;
     // [DK][C]
     float *KiT, *XwT;
-    // [C][DV] (UT and XuT are stored [DV][C])
-    float *Up, *UT, *dU, *dXu, *XuT;
+    // [C][DV] (XuT is stored [DV][C])
+    float *Up, *U, *dU, *dXu, *XuT;
     // [C][C]
     float *M, *P, *T, *TT, *dP, *dT, *Y, *dA;
     // [DK]
     float *Gn, *dGn;
-    // [DV][DK]: chunk start state and the state cotangent after the chunk, transposed
-    float *ST, *dSnT;
+    // [DK][DV]: chunk start state and the state cotangent after the chunk
+    float *S, *dSn;
 };
 
 template <typename E>
@@ -80,7 +81,9 @@ __device__ __forceinline__ float ld(const E* p, int64_t i) {
 // contiguous one in memory, so that the staging loads are coalesced.  Tiles
 // of 16 k-steps pass through LDS (k-major); thread (ty, tx) = (tid / 16,
 // tid % 16) owns rows 4ty..4ty+3 and columns tx*N/16 .. tx*N/16 + N/16 - 1.
-// Every thread of the workgroup must call it (it contains barriers).
+// The next tile is fetched into registers while the current one is
+// multiplied.  Every thread of the workgroup must call it (it contains
+// barriers); whatever the loaders read must be complete before the call.
 constexpr int kGemmLds = 16 * (64 + 4) + 16 * (128 + 4);  // floats
 
 template <int N>
@@ -99,23 +102,54 @@ struct Acc {
 template <int N, int K, bool A_KFAST, bool B_NFAST, typename LA, typename LB>
 __device__ __forceinline__ void gemm64(Acc<N>& acc, LA la, LB lb, float* lds) {
     constexpr int KT = 16, M = 64, SA = M + 4, SB = N + 4, NT = N / 16;
+    constexpr int RA = M * KT / kBwdThreads, RB = N * KT / kBwdThreads;
     float* sA = lds;
     float* sB = lds + KT * SA;
     const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+    // element r of this thread's share of a tile
+    auto a_mk = [&](int r, int& m, int& kk) {
+        const int idx = tid + r * kBwdThreads;
+        m = A_KFAST ? idx / KT : idx % M;
+        kk = A_KFAST ? idx % KT : idx / M;
+    };
+    auto b_kn = [&](int r, int& kk, int& n) {
+        const int idx = tid + r * kBwdThreads;
+        n = B_NFAST ? idx % N : idx / KT;
+        kk = B_NFAST ? idx / N : idx % KT;
+    };
+    float ra[RA], rb[RB];
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int r = 0; r < RA; ++r) {
+            int m, kk;
+            a_mk(r, m, kk);
+            ra[r] = la(m, k0 + kk);
+        }
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            int kk, n;
+            b_kn(r, kk, n);
+            rb[r] = lb(k0 + kk, n);
+        }
+    };
+    fetch(0);
     for (int k0 = 0; k0 < K; k0 += KT) {
 #pragma unroll
-        for (int idx = tid; idx < M * KT; idx += kBwdThreads) {
-            const int m = A_KFAST ? idx / KT : idx % M;
-            const int kk = A_KFAST ? idx % KT : idx / M;
-            sA[kk * SA + m] = la(m, k0 + kk);
+        for (int r = 0; r < RA; ++r) {
+            int m, kk;
+            a_mk(r, m, kk);
+            sA[kk * SA + m] = ra[r];
         }
 #pragma unroll
-        for (int idx = tid; idx < N * KT; idx += kBwdThreads) {
-            const int n = B_NFAST ? idx % N : idx / KT;
-            const int kk = B_NFAST ? idx / N : idx % KT;
-            sB[kk * SB + n] = lb(k0 + kk, n);
+        for (int r = 0; r < RB; ++r) {
+            int kk, n;
+            b_kn(r, kk, n);
+            sB[kk * SB + n] = rb[r];
         }
-        __syncthreads();
+        // the tiles are shared through LDS only: the next tile's global loads
+        // stay in flight across these barriers
+        lds_barrier();
+        if (k0 + KT < K) fetch(k0 + KT);
 #pragma unroll 4
         for (int kk = 0; kk < KT; ++kk) {
             const float4 a = *reinterpret_cast<const float4*>(sA + kk * SA + ty * 4);
@@ -131,18 +165,7 @@ __device__ __forceinline__ void gemm64(Acc<N>& acc, LA la, LB lb, float* lds) {
 #pragma unroll
                 for (int j = 0; j < NT; ++j) acc.v[i][j] += av[i] * b[j];
         }
-        __syncthreads();
-    }
-}
-
-// Copy `count` floats (a multiple of 4, both ends 16-byte aligned) from global
-// memory into LDS rows of `width` floats with a row stride of `stride`.
-__device__ __forceinline__ void stage_rows(float* dst, const float* src, int rows, int width, int stride) {
-    const int per_row = width / 4;
-    for (int idx = threadIdx.x; idx < rows * per_row; idx += kBwdThreads) {
-        const int r = idx / per_row, c4 = idx % per_row;
-        *reinterpret_cast<float4*>(dst + r * stride + 4 * c4) =
-            *reinterpret_cast<const float4*>(src + (size_t)r * width + 4 * c4);
+        lds_barrier();
     }
 }
 
@@ -283,164 +306,285 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const E* __restri
 }
 
 // ---------------------------------------------------------------------------
-// Forward state walk per (sequence, head, 16-column slice): saves the start
-// state of every chunk (transposed) and U = U' - W S (transposed).  Each
-// chunk's W, Kd, U' slice and Gn are first staged into LDS.
-template <int DK, int DV>
-struct StateWalkLds {
-    static constexpr int SK = DK + 4;
-    static constexpr int W = 0, Kd = W + C * SK, S = Kd + C * SK, U = S + DK * 16, Up = U + C * 16,
-                         Gn = Up + C * 16, floats = Gn + DK;
-    static constexpr size_t bytes = (size_t)floats * 4;
-};
+// The two walks run one workgroup per (sequence, head, 16-column slice of
+// d_v).  Threads own register tiles: (rg, v) = (tid / 16, tid % 16) computes
+// rows R*rg .. R*rg + R-1 of column v.  A chunk's operands sit in LDS
+// (rows padded by 4 floats); the next ones are loaded into registers while the
+// current chunk is computed and written to LDS afterwards.  The waves share
+// only LDS, so the barriers order LDS alone and leave those loads in flight.
 
-template <int DK, int DV>
-__global__ __launch_bounds__(kBwdThreads) void bwd_state_walk_kernel(int32_t H, const float* __restrict__ S0,
-                                                                     BwdWs w) {
-    using L = StateWalkLds<DK, DV>;
-    constexpr int NS = DV / 16, SK = L::SK;
-    extern __shared__ __align__(16) float smem[];
-    float* sW = smem + L::W;
-    float* sKd = smem + L::Kd;
-    float* sS = smem + L::S;    // [DK][16]
-    float* sU = smem + L::U;    // [C][16]
-    float* sUp = smem + L::Up;  // [C][16]
-    float* sGn = smem + L::Gn;
-    const int bid = blockIdx.x;
-    const int sl = bid % NS;
-    const int nh = bid / NS;
-    const int h = nh % H;
-    const int seq = nh / H;
-    if (w.header->bad_seqlens) return;
-    const int tid = threadIdx.x;
-    const int col0 = sl * 16;
-    for (int idx = tid; idx < DK * 16; idx += kBwdThreads) {
-        const int c = idx / 16, vv = idx % 16;
-        sS[idx] = S0 ? S0[(((size_t)seq * H + h) * DK + c) * DV + col0 + vv] : 0.f;
+// Load a C x WIDTH fp32 block (row-major, 16-byte aligned) into registers:
+// this thread's share, C * WIDTH / 1024 float4; then write it to LDS rows of
+// `stride` floats.
+template <int WIDTH>
+constexpr int block_regs() { return C * WIDTH / 4 / kBwdThreads; }
+
+template <int WIDTH>
+__device__ __forceinline__ void block_load(f32x4 (&r)[block_regs<WIDTH>()], const float* src) {
+    const f32x4* s4 = reinterpret_cast<const f32x4*>(src) + threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < block_regs<WIDTH>(); ++i) r[i] = s4[i * kBwdThreads];
+}
+
+template <int WIDTH>
+__device__ __forceinline__ void block_store(const f32x4 (&r)[block_regs<WIDTH>()], float* dst, int stride) {
+#pragma unroll
+    for (int i = 0; i < block_regs<WIDTH>(); ++i) {
+        const int idx = threadIdx.x + i * kBwdThreads;
+        *reinterpret_cast<f32x4*>(dst + (idx / (WIDTH / 4)) * stride + 4 * (idx % (WIDTH / 4))) = r[i];
     }
-    const int c0 = w.chunk_off[seq], c1 = w.chunk_off[seq + 1];
-    for (int ch = c0; ch < c1; ++ch) {
-        const size_t slot = (size_t)ch * H + h;
-        const size_t oCK = slot * C * DK, oCV = slot * C * DV, oKV = slot * DK * DV;
-        stage_rows(sW, w.W + oCK, C, DK, SK);
-        stage_rows(sKd, w.Kd + oCK, C, DK, SK);
-        for (int idx = tid; idx < C * 4; idx += kBwdThreads) {
-            const int t = idx / 4, c4 = idx % 4;
-            *reinterpret_cast<float4*>(sUp + t * 16 + 4 * c4) =
-                *reinterpret_cast<const float4*>(w.Up + oCV + (size_t)t * DV + col0 + 4 * c4);
+}
+
+// out[t] (t = 4 rows of this thread) += sum_k X[t][k] y[k], X rows in LDS
+// (stride SX), y a column of a [K][16] LDS block.
+template <int K, int SX>
+__device__ __forceinline__ void rows4_dot(float (&out)[4], const float* X, int t0, const float* y, int v) {
+#pragma unroll 4
+    for (int k = 0; k < K; k += 4) {
+        const float y0 = y[(k + 0) * 16 + v], y1 = y[(k + 1) * 16 + v], y2 = y[(k + 2) * 16 + v],
+                    y3 = y[(k + 3) * 16 + v];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 x = *reinterpret_cast<const float4*>(X + (t0 + i) * SX + k);
+            out[i] += x.x * y0 + x.y * y1 + x.z * y2 + x.w * y3;
         }
-        for (int c = tid; c < DK; c += kBwdThreads) sGn[c] = w.Gn[slot * DK + c];
-        __syncthreads();
-        for (int idx = tid; idx < DK * 16; idx += kBwdThreads) {
-            const int c = idx / 16, vv = idx % 16;
-            w.ST[oKV + (size_t)(col0 + vv) * DK + c] = sS[idx];
-        }
-        for (int idx = tid; idx < C * 16; idx += kBwdThreads) {
-            const int t = idx / 16, vv = idx % 16;
-            const float* wr = sW + t * SK;
-            float s = sUp[idx];
-#pragma unroll 8
-            for (int c = 0; c < DK; ++c) s -= wr[c] * sS[c * 16 + vv];
-            sU[idx] = s;
-            w.UT[oCV + (size_t)(col0 + vv) * C + t] = s;
-        }
-        __syncthreads();
-        for (int idx = tid; idx < DK * 16; idx += kBwdThreads) {
-            const int c = idx / 16, vv = idx % 16;
-            float s = sGn[c] * sS[idx];
-#pragma unroll 8
-            for (int t = 0; t < C; ++t) s += sKd[t * SK + c] * sU[t * 16 + vv];
-            sS[idx] = s;
-        }
-        __syncthreads();
+    }
+}
+
+// out[i] += sum_t X[t][c0 + i] y[t], i < 8: X columns in LDS (stride SX), y a
+// column of a [C][16] LDS block; s scales X.
+template <int SX>
+__device__ __forceinline__ void cols8_dot(float (&out)[8], const float* X, int c0, const float* y, int v,
+                                          float s) {
+#pragma unroll 4
+    for (int t = 0; t < C; ++t) {
+        const float yt = s * y[t * 16 + v];
+        const float4 a = *reinterpret_cast<const float4*>(X + t * SX + c0);
+        const float4 b = *reinterpret_cast<const float4*>(X + t * SX + c0 + 4);
+        out[0] += a.x * yt; out[1] += a.y * yt; out[2] += a.z * yt; out[3] += a.w * yt;
+        out[4] += b.x * yt; out[5] += b.y * yt; out[6] += b.z * yt; out[7] += b.w * yt;
     }
 }
 
 // ---------------------------------------------------------------------------
-// Reverse state walk per (sequence, head, 16-column slice): dU of every chunk
-// and the state cotangent after it (transposed); dS0 at the end.  Each
-// chunk's P, Kd, QG, W, Gn and dO slice are first staged into LDS.
+// Forward state walk: saves the start state S of every chunk and
+// U = U' - W S, then S <- Diag(Gn) S + Kd^T U.
+template <int DK, int DV>
+struct StateWalkLds {
+    static constexpr int SK = DK + 4;
+    static constexpr int W = 0, Kd = W + C * SK, S = Kd + C * SK, U = S + DK * 16, floats = U + C * 16;
+    static constexpr size_t bytes = (size_t)floats * 4;
+};
+
+// One workgroup of four waves per CU at most (LDS), so a wave may use the
+// whole register file: the next chunk's operands are held in registers.
+template <int DK, int DV>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_state_walk_kernel(int32_t H, const float* __restrict__ S0,
+                                                                     BwdWs w) {
+    using L = StateWalkLds<DK, DV>;
+    constexpr int NS = DV / 16, SK = L::SK, RS = DK / 16;  // rows of S per thread
+    extern __shared__ __align__(16) float smem[];
+    float* sW = smem + L::W;    // [C][SK]
+    float* sKd = smem + L::Kd;  // [C][SK]
+    float* sS = smem + L::S;    // [DK][16]
+    float* sU = smem + L::U;    // [C][16]
+    const int sl = blockIdx.x % NS;
+    const int nh = blockIdx.x / NS;
+    const int h = nh % H;
+    const int seq = nh / H;
+    if (w.header->bad_seqlens) return;
+    const int tid = threadIdx.x, rg = tid / 16, v = tid % 16;
+    const int col = sl * 16 + v;
+    const int c0 = w.chunk_off[seq], c1 = w.chunk_off[seq + 1];
+    // this thread's rows of S stay in registers; sS mirrors them for the U step
+    float S[RS];
+#pragma unroll
+    for (int i = 0; i < RS; ++i)
+        S[i] = S0 ? S0[(((size_t)seq * H + h) * DK + rg * RS + i) * DV + col] : 0.f;
+    f32x4 rW[block_regs<DK>()], rK[block_regs<DK>()];
+    if (c0 < c1) {
+        const size_t slot = (size_t)c0 * H + h;
+        block_load<DK>(rW, w.W + slot * C * DK);
+        block_load<DK>(rK, w.Kd + slot * C * DK);
+    }
+    for (int ch = c0; ch < c1; ++ch) {
+        const size_t slot = (size_t)ch * H + h;
+        const size_t oCV = slot * C * DV, oKV = slot * DK * DV;
+        block_store<DK>(rW, sW, SK);
+        block_store<DK>(rK, sKd, SK);
+#pragma unroll
+        for (int i = 0; i < RS; ++i) {
+            sS[(rg * RS + i) * 16 + v] = S[i];
+            w.S[oKV + (size_t)(rg * RS + i) * DV + col] = S[i];
+        }
+        float gn[RS];
+#pragma unroll
+        for (int i = 0; i < RS; ++i) gn[i] = w.Gn[slot * DK + rg * RS + i];
+        float up[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) up[i] = w.Up[oCV + (size_t)(rg * 4 + i) * DV + col];
+        lds_barrier();
+        if (ch + 1 < c1) {  // next chunk's operands, in flight during this one
+            const size_t nslot = slot + H;
+            block_load<DK>(rW, w.W + nslot * C * DK);
+            block_load<DK>(rK, w.Kd + nslot * C * DK);
+        }
+        // U = U' - W S (rows 4rg..4rg+3)
+        float u[4] = {0.f, 0.f, 0.f, 0.f};
+        rows4_dot<DK, SK>(u, sW, rg * 4, sS, v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float x = up[i] - u[i];
+            sU[(rg * 4 + i) * 16 + v] = x;
+            w.U[oCV + (size_t)(rg * 4 + i) * DV + col] = x;
+        }
+        lds_barrier();
+        // S <- Diag(Gn) S + Kd^T U (rows RS*rg ..)
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if constexpr (RS == 8) {
+            cols8_dot<SK>(acc, sKd, rg * 8, sU, v, 1.f);
+        } else {
+            // d_k = 64: four rows per thread, read as the first half of eight
+#pragma unroll 4
+            for (int t = 0; t < C; ++t) {
+                const float yt = sU[t * 16 + v];
+                const float4 a = *reinterpret_cast<const float4*>(sKd + t * SK + rg * 4);
+                acc[0] += a.x * yt; acc[1] += a.y * yt; acc[2] += a.z * yt; acc[3] += a.w * yt;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < RS; ++i) S[i] = gn[i] * S[i] + acc[i];
+        lds_barrier();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Reverse state walk: saves dS_next and dU = P^T dO + Kd dS_next of every
+// chunk, then dS = Diag(Gn) dS_next + QG^T dO - W^T dU; dS0 at the end.
 template <int DK, int DV>
 struct DStateWalkLds {
     static constexpr int SK = DK + 4, SC = C + 4;
     static constexpr int P = 0, Kd = P + C * SC, QG = Kd + C * SK, W = QG + C * SK, dS = W + C * SK,
-                         dU = dS + DK * 16, dO = dU + C * 16, Gn = dO + C * 16, floats = Gn + DK;
+                         dU = dS + DK * 16, dO = dU + C * 16, floats = dO + 2 * C * 16;
     static constexpr size_t bytes = (size_t)floats * 4;
 };
 
 template <typename E, int DK, int DV>
-__global__ __launch_bounds__(kBwdThreads) void bwd_dstate_walk_kernel(int32_t H, const E* __restrict__ dO,
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dstate_walk_kernel(int32_t H, const E* __restrict__ dO,
                                                                       const float* __restrict__ dST,
                                                                       float* __restrict__ dS0, BwdWs w) {
     using L = DStateWalkLds<DK, DV>;
-    constexpr int NS = DV / 16, SK = L::SK, SC = L::SC;
+    constexpr int NS = DV / 16, SK = L::SK, SC = L::SC, RS = DK / 16;
     extern __shared__ __align__(16) float smem[];
-    float* sP = smem + L::P;
-    float* sKd = smem + L::Kd;
-    float* sQG = smem + L::QG;
-    float* sW = smem + L::W;
+    float* sP = smem + L::P;    // [C][SC]
+    float* sKd = smem + L::Kd;  // [C][SK]
+    float* sQG = smem + L::QG;  // [C][SK]
+    float* sW = smem + L::W;    // [C][SK]
     float* sdS = smem + L::dS;  // [DK][16]
     float* sdU = smem + L::dU;  // [C][16]
-    float* sdO = smem + L::dO;  // [C][16]
-    float* sGn = smem + L::Gn;
-    const int bid = blockIdx.x;
-    const int sl = bid % NS;
-    const int nh = bid / NS;
+    float* sdO = smem + L::dO;  // two [C][16] buffers
+    const int sl = blockIdx.x % NS;
+    const int nh = blockIdx.x / NS;
     const int h = nh % H;
     const int seq = nh / H;
     if (w.header->bad_seqlens) return;
-    const int tid = threadIdx.x;
-    const int col0 = sl * 16;
-    for (int idx = tid; idx < DK * 16; idx += kBwdThreads) {
-        const int c = idx / 16, vv = idx % 16;
-        sdS[idx] = dST ? dST[(((size_t)seq * H + h) * DK + c) * DV + col0 + vv] : 0.f;
-    }
+    const int tid = threadIdx.x, rg = tid / 16, v = tid % 16;
+    const int col = sl * 16 + v;
     const int c0 = w.chunk_off[seq], c1 = w.chunk_off[seq + 1];
+    float dS[RS];
+#pragma unroll
+    for (int i = 0; i < RS; ++i)
+        dS[i] = dST ? dST[(((size_t)seq * H + h) * DK + rg * RS + i) * DV + col] : 0.f;
+    // dO of a chunk for this thread's 4 rows of column `col`
+    auto load_dO = [&](int ch, float (&r)[4]) {
+        const int2 ct = w.chunk_tab[ch];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = rg * 4 + i;
+            r[i] = t < ct.y ? ld(dO, (((int64_t)ct.x + t) * H + h) * DV + col) : 0.f;
+        }
+    };
+    f32x4 rP[block_regs<C>()], rK[block_regs<DK>()], rQ[block_regs<DK>()], rW[block_regs<DK>()];
+    float rO[4];
+    int buf = 0;
+    if (c0 < c1) {
+        const size_t slot = (size_t)(c1 - 1) * H + h;
+        block_load<C>(rP, w.P + slot * C * C);
+        block_load<DK>(rK, w.Kd + slot * C * DK);
+        load_dO(c1 - 1, rO);
+        block_store<C>(rP, sP, SC);
+        block_store<DK>(rK, sKd, SK);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sdO[(rg * 4 + i) * 16 + v] = rO[i];
+    }
     for (int ch = c1 - 1; ch >= c0; --ch) {
         const size_t slot = (size_t)ch * H + h;
-        const size_t oCK = slot * C * DK, oCC = slot * C * C, oCV = slot * C * DV, oKV = slot * DK * DV;
-        const int2 ct = w.chunk_tab[ch];
-        const int64_t t0 = ct.x;
-        const int n = ct.y;
-        stage_rows(sP, w.P + oCC, C, C, SC);
-        stage_rows(sKd, w.Kd + oCK, C, DK, SK);
-        stage_rows(sQG, w.QG + oCK, C, DK, SK);
-        stage_rows(sW, w.W + oCK, C, DK, SK);
-        for (int c = tid; c < DK; c += kBwdThreads) sGn[c] = w.Gn[slot * DK + c];
-        for (int idx = tid; idx < C * 16; idx += kBwdThreads) {
-            const int t = idx / 16, vv = idx % 16;
-            sdO[idx] = t < n ? ld(dO, ((t0 + t) * H + h) * DV + col0 + vv) : 0.f;
+        const size_t oCK = slot * C * DK, oCV = slot * C * DV, oKV = slot * DK * DV;
+        float* dOc = sdO + buf * C * 16;
+#pragma unroll
+        for (int i = 0; i < RS; ++i) {
+            sdS[(rg * RS + i) * 16 + v] = dS[i];
+            w.dSn[oKV + (size_t)(rg * RS + i) * DV + col] = dS[i];
         }
-        __syncthreads();
-        for (int idx = tid; idx < DK * 16; idx += kBwdThreads) {
-            const int c = idx / 16, vv = idx % 16;
-            w.dSnT[oKV + (size_t)(col0 + vv) * DK + c] = sdS[idx];
+        float gn[RS];
+#pragma unroll
+        for (int i = 0; i < RS; ++i) gn[i] = w.Gn[slot * DK + rg * RS + i];
+        lds_barrier();
+        block_load<DK>(rQ, w.QG + oCK);  // this chunk's QG and W, in flight during dU
+        block_load<DK>(rW, w.W + oCK);
+        // dU = P^T dO + Kd dS_next (rows 4rg..4rg+3)
+        float du[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int i = 0; i < C; ++i) {
+            const float y = dOc[i * 16 + v];
+            const float4 p = *reinterpret_cast<const float4*>(sP + i * SC + rg * 4);  // P[i][t..t+3]
+            du[0] += p.x * y; du[1] += p.y * y; du[2] += p.z * y; du[3] += p.w * y;
         }
-        for (int idx = tid; idx < C * 16; idx += kBwdThreads) {
-            const int t = idx / 16, vv = idx % 16;
-            float s = 0.f;
-            for (int i = t; i < C; ++i) s += sP[i * SC + t] * sdO[i * 16 + vv];
-            const float* kr = sKd + t * SK;
-#pragma unroll 8
-            for (int c = 0; c < DK; ++c) s += kr[c] * sdS[c * 16 + vv];
-            sdU[idx] = s;
-            w.dU[oCV + (size_t)t * DV + col0 + vv] = s;
+        rows4_dot<DK, SK>(du, sKd, rg * 4, sdS, v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sdU[(rg * 4 + i) * 16 + v] = du[i];
+            w.dU[oCV + (size_t)(rg * 4 + i) * DV + col] = du[i];
         }
-        __syncthreads();
-        for (int idx = tid; idx < DK * 16; idx += kBwdThreads) {
-            const int c = idx / 16, vv = idx % 16;
-            float s = sGn[c] * sdS[idx];
-#pragma unroll 8
-            for (int t = 0; t < C; ++t) s += sQG[t * SK + c] * sdO[t * 16 + vv] - sW[t * SK + c] * sdU[t * 16 + vv];
-            sdS[idx] = s;
+        block_store<DK>(rQ, sQG, SK);
+        block_store<DK>(rW, sW, SK);
+        lds_barrier();
+        if (ch > c0) {  // the previous chunk's P, Kd and dO, in flight during dS
+            const size_t pslot = slot - H;
+            block_load<C>(rP, w.P + pslot * C * C);
+            block_load<DK>(rK, w.Kd + pslot * C * DK);
+            load_dO(ch - 1, rO);
         }
-        __syncthreads();
+        // dS = Diag(Gn) dS_next + QG^T dO - W^T dU (rows RS*rg ..)
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if constexpr (RS == 8) {
+            cols8_dot<SK>(acc, sQG, rg * 8, dOc, v, 1.f);
+            cols8_dot<SK>(acc, sW, rg * 8, sdU, v, -1.f);
+        } else {
+#pragma unroll 4
+            for (int t = 0; t < C; ++t) {
+                const float yo = dOc[t * 16 + v], yu = sdU[t * 16 + v];
+                const float4 a = *reinterpret_cast<const float4*>(sQG + t * SK + rg * 4);
+                const float4 b = *reinterpret_cast<const float4*>(sW + t * SK + rg * 4);
+                acc[0] += a.x * yo - b.x * yu; acc[1] += a.y * yo - b.y * yu;
+                acc[2] += a.z * yo - b.z * yu; acc[3] += a.w * yo - b.w * yu;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < RS; ++i) dS[i] = gn[i] * dS[i] + acc[i];
+        if (ch > c0) {
+            block_store<C>(rP, sP, SC);
+            block_store<DK>(rK, sKd, SK);
+            float* dOn = sdO + (buf ^ 1) * C * 16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dOn[(rg * 4 + i) * 16 + v] = rO[i];
+        }
+        buf ^= 1;
+        lds_barrier();
     }
     if (dS0) {
-        for (int idx = tid; idx < DK * 16; idx += kBwdThreads) {
-            const int c = idx / 16, vv = idx % 16;
-            dS0[(((size_t)seq * H + h) * DK + c) * DV + col0 + vv] = sdS[idx];
-        }
+#pragma unroll
+        for (int i = 0; i < RS; ++i) dS0[(((size_t)seq * H + h) * DK + rg * RS + i) * DV + col] = dS[i];
     }
 }
 
@@ -471,9 +615,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
         sr[tid] = w.B[oCK + (size_t)((n - 1) / 2) * DK + tid];
         sbl[tid] = w.B[oCK + (size_t)(n - 1) * DK + tid];
     }
-    const float* ST = w.ST + oKV;
-    const float* dSnT = w.dSnT + oKV;
-    const float* UT = w.UT + oCV;
+    const float* Sm = w.S + oKV;
+    const float* dSn = w.dSn + oKV;
+    const float* Um = w.U + oCV;
     const float* dUm = w.dU + oCV;
     const float* TT = w.TT + oCC;
     auto dOat = [&](int t, int x) -> float { return t < n ? ld(dO, ((t0 + t) * H + h) * DV + x) : 0.f; };
@@ -493,19 +637,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
     {
         Acc<DK> acc;
         acc.zero();
-        gemm64<DK, DV, true, true>(acc, [&](int t, int x) { return dUm[(size_t)t * DV + x]; },
-                                   [&](int x, int c) { return ST[(size_t)x * DK + c]; }, lds);
+        gemm64<DK, DV, true, false>(acc, [&](int t, int x) { return dUm[(size_t)t * DV + x]; },
+                                    [&](int x, int c) { return Sm[(size_t)c * DV + x]; }, lds);
         put(acc, w.dW + oCK, DK, -1.f);
         acc.zero();
-        gemm64<DK, DV, true, true>(acc, dOat, [&](int x, int c) { return ST[(size_t)x * DK + c]; }, lds);
+        gemm64<DK, DV, true, false>(acc, dOat, [&](int x, int c) { return Sm[(size_t)c * DV + x]; }, lds);
         put(acc, w.dQG + oCK, DK, 1.f);
         acc.zero();
-        gemm64<DK, DV, false, true>(acc, [&](int t, int x) { return UT[(size_t)x * C + t]; },
-                                    [&](int x, int c) { return dSnT[(size_t)x * DK + c]; }, lds);
+        gemm64<DK, DV, true, false>(acc, [&](int t, int x) { return Um[(size_t)t * DV + x]; },
+                                    [&](int x, int c) { return dSn[(size_t)c * DV + x]; }, lds);
         put(acc, w.dKd + oCK, DK, 1.f);
         Acc<C> ap;
         ap.zero();
-        gemm64<C, DV, true, true>(ap, dOat, [&](int x, int i) { return UT[(size_t)x * C + i]; }, lds);
+        gemm64<C, DV, true, false>(ap, dOat, [&](int x, int i) { return Um[(size_t)i * DV + x]; }, lds);
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -516,7 +660,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
     }
     for (int c = tid; c < DK; c += kBwdThreads) {
         float s = 0.f;
-        for (int x = 0; x < DV; ++x) s += ST[(size_t)x * DK + c] * dSnT[(size_t)x * DK + c];
+        for (int x = 0; x < DV; ++x) s += Sm[(size_t)c * DV + x] * dSn[(size_t)c * DV + x];
         w.dGn[oK + c] = s;
     }
     __syncthreads();
@@ -694,14 +838,14 @@ BwdWs carve_bwd(void* base, int64_t T, int32_t N, int32_t H, int32_t dk, int32_t
     float** ck[] = {&w.B, &w.QG, &w.KG, &w.Kd, &w.Qr, &w.Kr, &w.Ki, &w.W, &w.dW, &w.dQG, &w.dKd, &w.dXw,
                     &w.KiT, &w.XwT};
     for (float** f : ck) *f = take(s.ck);
-    float** cv[] = {&w.Up, &w.UT, &w.dU, &w.dXu, &w.XuT};
+    float** cv[] = {&w.Up, &w.U, &w.dU, &w.dXu, &w.XuT};
     for (float** f : cv) *f = take(s.cv);
     float** cc[] = {&w.M, &w.P, &w.T, &w.TT, &w.dP, &w.dT, &w.Y, &w.dA};
     for (float** f : cc) *f = take(s.cc);
     w.Gn = take(s.k);
     w.dGn = take(s.k);
-    w.ST = take(s.kv);
-    w.dSnT = take(s.kv);
+    w.S = take(s.kv);
+    w.dSn = take(s.kv);
     return w;
 }
 
