@@ -738,18 +738,25 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
         const float* Ki = w.Ki + oCK;
         const float* Kr = w.Kr + oCK;
         const float* Qr = w.Qr + oCK;
-        Acc<DK> akr, aki, aqr;
-        akr.zero();
-        aki.zero();
-        aqr.zero();
-        gemm64<DK, C, true, true>(akr, [&](int t, int i) { return dA[(size_t)t * C + i]; },
+        // one accumulator tile at a time: dKr and dQr are parked in KiT and XwT
+        // (neither is read again by this chunk)
+        float* dKr_s = w.KiT + oCK;
+        float* dQr_s = w.XwT + oCK;
+        Acc<DK> acc;
+        acc.zero();
+        gemm64<DK, C, true, true>(acc, [&](int t, int i) { return dA[(size_t)t * C + i]; },
                                   [&](int i, int c) { return Ki[(size_t)i * DK + c]; }, lds);
-        gemm64<DK, C, false, true>(aki, [&](int t, int a) { return sbeta[a] * dA[(size_t)a * C + t]; },
+        put(acc, dKr_s, DK, 1.f);
+        acc.zero();
+        gemm64<DK, C, true, true>(acc, [&](int t, int i) { return dP[(size_t)t * C + i]; },
+                                  [&](int i, int c) { return Ki[(size_t)i * DK + c]; }, lds);
+        put(acc, dQr_s, DK, 1.f);
+        acc.zero();
+        gemm64<DK, C, false, true>(acc, [&](int t, int a) { return sbeta[a] * dA[(size_t)a * C + t]; },
                                    [&](int a, int c) { return Kr[(size_t)a * DK + c]; }, lds);
-        gemm64<DK, C, false, true>(aki, [&](int t, int a) { return dP[(size_t)a * C + t]; },
+        gemm64<DK, C, false, true>(acc, [&](int t, int a) { return dP[(size_t)a * C + t]; },
                                    [&](int a, int c) { return Qr[(size_t)a * DK + c]; }, lds);
-        gemm64<DK, C, true, true>(aqr, [&](int t, int i) { return dP[(size_t)t * C + i]; },
-                                  [&](int i, int c) { return Ki[(size_t)i * DK + c]; }, lds);
+        // the parked tiles were written by this thread: same (t, c) positions
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -757,7 +764,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
                 const int t = Acc<DK>::row(a), c = Acc<DK>::col(b);
                 if (t >= n) continue;
                 const size_t j = oCK + (size_t)t * DK + c;
-                const float dKr = sbeta[t] * akr.v[a][b], dKi = aki.v[a][b], dQr = aqr.v[a][b];
+                const size_t jt = (size_t)t * DK + c;
+                const float dKr = sbeta[t] * dKr_s[jt], dKi = acc.v[a][b], dQr = dQr_s[jt];
                 const float dKG = sbeta[t] * w.dXw[j];
                 const float dQG = w.dQG[j], dKd = w.dKd[j];
                 const float bb = w.B[j], r = sr[c], bl = sbl[c];
