@@ -8,6 +8,8 @@ in the library's HIP kernels.  PyTorch provides device memory and streams.
     recurrent_step(q, k, v, g, beta, S) -> o            (S updated in place)
     chunk_bwd(q, k, v, g, beta, dO, S0=..., dS_T=..., cu_seqlens=...)
         -> (dq, dk, dv, dg, dbeta, dS0)                  (gradients of the forward)
+    prepare_inputs(q_raw, k_raw, g_raw, beta_raw) -> (q, k, g, beta)
+    recurrent_step_raw(q_raw, k_raw, v, g_raw, beta_raw, S) -> o
 
 The library must have been built (``__graft_entry__.build()`` or
 ``python gated_delta_rule_48_amd/build.py``); importing the functions'
@@ -21,7 +23,7 @@ import os
 import torch
 
 __all__ = ["chunk_fwd", "chunk_fwd_workspace_size", "chunk_fwd_check", "recurrent_step",
-           "chunk_bwd", "chunk_bwd_workspace_size",
+           "chunk_bwd", "chunk_bwd_workspace_size", "prepare_inputs", "recurrent_step_raw",
            "KDAError", "LIB_PATH", "load_library", "STATUS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
@@ -65,6 +67,12 @@ def load_library():
         lib.kda_chunk_bwd.restype = ctypes.c_int
         lib.kda_chunk_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, ctypes.c_int,
                                       ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.kda_prepare_inputs.restype = ctypes.c_int
+        lib.kda_prepare_inputs.argtypes = [vp, vp, vp, vp, i64, i32, i32, ctypes.c_int, ctypes.c_int,
+                                           vp, vp, vp, vp, vp]
+        lib.kda_recurrent_step_raw.restype = ctypes.c_int
+        lib.kda_recurrent_step_raw.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int,
+                                               ctypes.c_int, vp, vp]
         lib.kda_recurrent_step.restype = ctypes.c_int
         lib.kda_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int,
                                            ctypes.c_int, vp, vp]
@@ -196,7 +204,41 @@ def chunk_fwd_check(workspace, stream=None):
     _check(load_library().kda_chunk_fwd_check(_ptr(workspace), _stream(stream)))
 
 
-def recurrent_step(q, k, v, g, beta, S, *, per_head_gate=False, out=None, stream=None):
+def prepare_inputs(q_raw, k_raw, g_raw, beta_raw, *, per_head_gate=False, out=None, stream=None):
+    """Pre-path transforms in one pass (kda_prepare_inputs): q, k L2-normalised
+    per token and head, g = -softplus(g_raw), beta = sigmoid(beta_raw).
+
+    q_raw, k_raw: [T, H, dk]; g_raw: [T, H, dk] (or [T, H] with
+    ``per_head_gate``); beta_raw: [T, H]; one dtype (bfloat16 or float32).
+    ``out``: optional (q, k, g, beta) to write into (may be the inputs
+    themselves).  Returns (q, k, g, beta).
+    """
+    if q_raw.dim() != 3:
+        raise ValueError("q_raw, k_raw must be [T, H, d]")
+    T, H, dk = q_raw.shape
+    _shapes(k_raw=(k_raw, (T, H, dk)), beta_raw=(beta_raw, (T, H)),
+            g_raw=(g_raw, (T, H) if per_head_gate else (T, H, dk)))
+    for name, t in (("q_raw", q_raw), ("k_raw", k_raw), ("g_raw", g_raw), ("beta_raw", beta_raw)):
+        _dev_contig(name, t, q_raw.dtype)
+    outs = out if out is not None else tuple(torch.empty_like(x) for x in (q_raw, k_raw, g_raw, beta_raw))
+    for name, t, ref in zip(("q", "k", "g", "beta"), outs, (q_raw, k_raw, g_raw, beta_raw)):
+        _dev_contig(name, t, q_raw.dtype)
+        _shapes(**{name: (t, tuple(ref.shape))})
+    _check(load_library().kda_prepare_inputs(
+        _ptr(q_raw), _ptr(k_raw), _ptr(g_raw), _ptr(beta_raw), T, H, dk, _dt(q_raw),
+        _PER_HEAD if per_head_gate else _PER_CHANNEL, *[_ptr(t) for t in outs], _stream(stream)))
+    return tuple(outs)
+
+
+def recurrent_step_raw(q_raw, k_raw, v, g_raw, beta_raw, S, *, per_head_gate=False, out=None, stream=None):
+    """One decode step from raw projections (kda_recurrent_step_raw): the
+    pre-path transforms of ``prepare_inputs`` are applied inside the step.
+    Shapes as for ``recurrent_step``; S updated in place; returns o."""
+    return recurrent_step(q_raw, k_raw, v, g_raw, beta_raw, S, per_head_gate=per_head_gate, out=out,
+                          stream=stream, _raw=True)
+
+
+def recurrent_step(q, k, v, g, beta, S, *, per_head_gate=False, out=None, stream=None, _raw=False):
     """One decode step, in place on S (fp32 [N, H, dk, dv]).
 
     q, k: [N, H, dk]; v: [N, H, dv]; g: [N, H, dk] (or [N, H] with
@@ -216,9 +258,10 @@ def recurrent_step(q, k, v, g, beta, S, *, per_head_gate=False, out=None, stream
     o = out if out is not None else torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
     _dev_contig("out", o, q.dtype)
     _shapes(out=(o, (N, H, dv)))
-    _check(load_library().kda_recurrent_step(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), N, H, dk, dv, _dt(q),
-        _PER_HEAD if per_head_gate else _PER_CHANNEL, _ptr(o), _stream(stream)))
+    lib = load_library()
+    fn = lib.kda_recurrent_step_raw if _raw else lib.kda_recurrent_step
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), N, H, dk, dv, _dt(q),
+              _PER_HEAD if per_head_gate else _PER_CHANNEL, _ptr(o), _stream(stream)))
     return o
 
 

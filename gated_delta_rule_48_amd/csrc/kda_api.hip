@@ -150,9 +150,10 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
     return kda::launch_chunk_bwd(a, workspace, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
-kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const void* g, const void* beta,
-                              float* S, int32_t N, int32_t H, int32_t d_k, int32_t d_v, kda_dtype dt, kda_gate gk,
-                              void* o, hipStream_t stream) {
+namespace {
+kda_status recurrent_step_impl(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                               float* S, int32_t N, int32_t H, int32_t d_k, int32_t d_v, kda_dtype dt,
+                               kda_gate gk, void* o, hipStream_t stream, bool raw) {
     const kda_status st = check_common(H, d_k, d_v, dt, gk);
     if (st != KDA_OK) return st;
     if (N < 0 || (int64_t)N * H > INT32_MAX) return KDA_ERR_INVALID_ARG;
@@ -167,7 +168,43 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const
     a.N = N; a.H = H; a.dk = d_k; a.dv = d_v;
     a.bf16 = dt == KDA_BF16;
     a.head_gate = gk == KDA_GATE_PER_HEAD;
+    a.raw = raw;
     return kda::launch_decode(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+}  // namespace
+
+kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                              float* S, int32_t N, int32_t H, int32_t d_k, int32_t d_v, kda_dtype dt, kda_gate gk,
+                              void* o, hipStream_t stream) {
+    return recurrent_step_impl(q, k, v, g, beta, S, N, H, d_k, d_v, dt, gk, o, stream, false);
+}
+
+kda_status kda_recurrent_step_raw(const void* q_raw, const void* k_raw, const void* v, const void* g_raw,
+                                  const void* beta_raw, float* S, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                                  kda_dtype dt, kda_gate gk, void* o, hipStream_t stream) {
+    return recurrent_step_impl(q_raw, k_raw, v, g_raw, beta_raw, S, N, H, d_k, d_v, dt, gk, o, stream, true);
+}
+
+kda_status kda_prepare_inputs(const void* q_raw, const void* k_raw, const void* g_raw, const void* beta_raw,
+                              int64_t T_total, int32_t H, int32_t d_k, kda_dtype dt, kda_gate gk, void* q, void* k,
+                              void* g, void* beta, hipStream_t stream) {
+    if (H <= 0 || T_total < 0) return KDA_ERR_INVALID_ARG;
+    if (dt != KDA_BF16 && dt != KDA_F32) return KDA_ERR_UNSUPPORTED;
+    if (gk != KDA_GATE_PER_CHANNEL && gk != KDA_GATE_PER_HEAD) return KDA_ERR_UNSUPPORTED;
+    if (!supported_d(d_k)) return KDA_ERR_UNSUPPORTED;
+    if ((T_total * H + 3) / 4 > (int64_t)UINT32_MAX) return KDA_ERR_UNSUPPORTED;
+    if (T_total == 0) return KDA_OK;
+    const size_t esz = dt == KDA_BF16 ? 2 : 4;
+    const void* ptrs[] = {q_raw, k_raw, g_raw, beta_raw, q, k, g, beta};
+    for (const void* p : ptrs)
+        if (!p || !aligned(p, esz)) return KDA_ERR_INVALID_ARG;
+    kda::PrepArgs a;
+    a.q_raw = q_raw; a.k_raw = k_raw; a.g_raw = g_raw; a.b_raw = beta_raw;
+    a.q = q; a.k = k; a.g = g; a.beta = beta;
+    a.T = T_total; a.H = H; a.dk = d_k;
+    a.bf16 = dt == KDA_BF16;
+    a.head_gate = gk == KDA_GATE_PER_HEAD;
+    return kda::launch_prepare(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 }  // extern "C"

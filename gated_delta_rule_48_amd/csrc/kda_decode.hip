@@ -10,6 +10,13 @@
 // which equals one token of S_t = (I - beta k k^T) Diag(a) S_{t-1} + beta k v^T,
 // o_t = S_t^T q_t.
 //
+// RAW: q and k arrive unnormalised and g, beta as raw projections; the step
+// then also applies q <- q/||q||, k <- k/||k||, a = exp(-softplus(g)) =
+// 1 / (1 + e^g), beta <- sigmoid(beta) (the transforms of kda_prepare_inputs).
+// The norms are per (n, h) scalars, so they are reduced next to q.k and
+// applied to the reduced reads: r, s and q.k scale by 1/||k||, 1/||q|| and
+// both, and the write uses k/||k||.
+//
 // Layout: one workgroup of 256 threads per (n, h).  Thread (rg, cg) owns the
 // four columns 4cg..4cg+3 of the rows rg*RPT .. rg*RPT+RPT-1 of S, which it
 // loads once as float4s (a row of d_v floats is read by DV/4 consecutive
@@ -18,7 +25,7 @@
 
 namespace kda {
 
-template <typename E, int DK, int DV, bool HEAD_GATE>
+template <typename E, int DK, int DV, bool HEAD_GATE, bool RAW = false>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const E* __restrict__ g, const E* __restrict__ beta, float* __restrict__ S,
@@ -38,6 +45,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     __shared__ float red_r[NRG][DV];
     __shared__ float red_s[NRG][DV];
     __shared__ float red_qk[NRG];
+    __shared__ float red_n[RAW ? 2 : 1][NRG];
 
     // State block: issue every load first so they are all in flight.
     float4* Sp = reinterpret_cast<float4*>(S + pair * (int64_t)DK * DV);
@@ -50,11 +58,12 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int c = rg * RPT + i;
-        a[i] = gate_exp<E>(HEAD_GATE ? gh : Elt<E>::load(g + kbase + c));
+        const float gi = HEAD_GATE ? gh : Elt<E>::load(g + kbase + c);
+        a[i] = RAW ? 1.f / (1.f + expf(gi)) : gate_exp<E>(gi);
         kk[i] = Elt<E>::load(k + kbase + c);
         qq[i] = Elt<E>::load(q + kbase + c);
     }
-    const float b = Elt<E>::load(beta + pair);
+    const float b = RAW ? sigmoid(Elt<E>::load(beta + pair)) : Elt<E>::load(beta + pair);
 
     // Partial reads over this thread's rows: r = S^T (a*k), s = S^T (a*q).
     float4 pr = make_float4(0.f, 0.f, 0.f, 0.f), ps = pr;
@@ -69,6 +78,16 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     *reinterpret_cast<float4*>(&red_r[rg][4 * cg]) = pr;
     *reinterpret_cast<float4*>(&red_s[rg][4 * cg]) = ps;
     if (cg == 0) red_qk[rg] = pqk;
+    if (RAW && cg == 0) {
+        float nq = 0.f, nk = 0.f;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            nq += qq[i] * qq[i];
+            nk += kk[i] * kk[i];
+        }
+        red_n[0][rg] = nq;
+        red_n[RAW ? 1 : 0][rg] = nk;
+    }
     lds_barrier();
 
     float4 r = make_float4(0.f, 0.f, 0.f, 0.f), s = r;
@@ -80,6 +99,21 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         r.x += x.x; r.y += x.y; r.z += x.z; r.w += x.w;
         s.x += y.x; s.y += y.y; s.z += y.z; s.w += y.w;
         qk += red_qk[j];
+    }
+    if (RAW) {
+        float nq = 0.f, nk = 0.f;
+#pragma unroll
+        for (int j = 0; j < NRG; ++j) {
+            nq += red_n[0][j];
+            nk += red_n[RAW ? 1 : 0][j];
+        }
+        const float iq = nq > 0.f ? 1.f / sqrtf(nq) : 0.f;
+        const float ik = nk > 0.f ? 1.f / sqrtf(nk) : 0.f;
+        r.x *= ik; r.y *= ik; r.z *= ik; r.w *= ik;
+        s.x *= iq; s.y *= iq; s.z *= iq; s.w *= iq;
+        qk *= iq * ik;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) kk[i] *= ik;
     }
     const int c0 = 4 * cg;
     float4 u;
@@ -110,9 +144,14 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 template <typename E, int DK, int DV, bool HG>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     const int64_t pairs = (int64_t)a.N * a.H;
-    hipLaunchKernelGGL((decode_step_kernel<E, DK, DV, HG>), dim3((unsigned)pairs), dim3(256), 0, stream,
-                       (const E*)a.q, (const E*)a.k, (const E*)a.v, (const E*)a.g, (const E*)a.beta, a.S,
-                       (E*)a.o, a.H);
+    if (a.raw)
+        hipLaunchKernelGGL((decode_step_kernel<E, DK, DV, HG, true>), dim3((unsigned)pairs), dim3(256), 0, stream,
+                           (const E*)a.q, (const E*)a.k, (const E*)a.v, (const E*)a.g, (const E*)a.beta, a.S,
+                           (E*)a.o, a.H);
+    else
+        hipLaunchKernelGGL((decode_step_kernel<E, DK, DV, HG>), dim3((unsigned)pairs), dim3(256), 0, stream,
+                           (const E*)a.q, (const E*)a.k, (const E*)a.v, (const E*)a.g, (const E*)a.beta, a.S,
+                           (E*)a.o, a.H);
     return hipGetLastError();
 }
 

@@ -140,6 +140,14 @@ template <typename E> __device__ __forceinline__ float gate_exp2(float x);
 template <> __device__ __forceinline__ float gate_exp2<bf16_t>(float x) { return __builtin_amdgcn_exp2f(x); }
 template <> __device__ __forceinline__ float gate_exp2<float>(float x) { return exp2f(x); }
 
+// -softplus(x) = -log(1 + e^x) and the logistic function 1 / (1 + e^-x),
+// without overflow for large |x| (library expf / log1pf).
+__device__ __forceinline__ float neg_softplus(float x) { return -(fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)))); }
+__device__ __forceinline__ float sigmoid(float x) {
+    const float e = expf(-fabsf(x));
+    return x >= 0.f ? 1.f / (1.f + e) : e / (1.f + e);
+}
+
 // Workspace header written by the chunk-map kernel.
 struct WsHeader {
     int32_t bad_seqlens;   // nonzero: cu_seqlens rejected, every later kernel exits

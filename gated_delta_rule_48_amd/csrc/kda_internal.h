@@ -18,7 +18,18 @@ struct DecodeArgs {
     void* o;
     int32_t N, H, dk, dv;
     bool bf16, head_gate;
+    bool raw = false;  // q, k unnormalised; g, beta before -softplus / sigmoid
 };
+
+struct PrepArgs {
+    const void *q_raw, *k_raw, *g_raw, *b_raw;
+    void *q, *k, *g, *beta;
+    int64_t T;
+    int32_t H, dk;
+    bool bf16, head_gate;
+};
+
+hipError_t launch_prepare(const PrepArgs& a, hipStream_t stream);
 
 // Carved-up workspace of one kda_chunk_fwd call (all device pointers).
 struct ChunkWorkspace {

@@ -183,6 +183,45 @@ kda_status kda_recurrent_step(const void *q, const void *k, const void *v,
                               hipStream_t stream);
 
 /*
+ * The steps just before the recurrence, from raw projections, in one pass
+ * over HBM:
+ *     q <- q / ||q||,  k <- k / ||k||   (per token and head, over d_k; an
+ *                                        all-zero row stays zero)
+ *     g <- -softplus(g) = -log(1 + e^g) (so alpha = exp(g) = 1 / (1 + e^x)
+ *                                        lies in (0, 1))
+ *     beta <- sigmoid(beta)
+ * "Kimi Linear architecture" (ttj.ttj.kr), section "KDA: a memo that erases
+ * and rewrites": one forget rate in (0, 1) per channel; "From GPT-2 to Kimi
+ * K3", section "Gated DeltaNet: now it can forget": alpha in [0, 1].  The
+ * pages print no parametrisation; this is the plainest one that gives those
+ * ranges.  Outputs are ready for kda_chunk_fwd / kda_recurrent_step.
+ *
+ *   q_raw, k_raw, q, k   [T_total, H, d_k], type dt
+ *   g_raw, g             [T_total, H, d_k] ([T_total, H] with KDA_GATE_PER_HEAD)
+ *   beta_raw, beta       [T_total, H]
+ * Outputs may alias their inputs exactly (in place).  Arithmetic in fp32,
+ * outputs rounded once to dt.  d_k in {64, 128}.
+ */
+kda_status kda_prepare_inputs(const void *q_raw, const void *k_raw,
+                              const void *g_raw, const void *beta_raw,
+                              int64_t T_total, int32_t H, int32_t d_k,
+                              kda_dtype dt, kda_gate gk, void *q, void *k,
+                              void *g, void *beta, hipStream_t stream);
+
+/*
+ * kda_recurrent_step with the pre-path transforms of kda_prepare_inputs
+ * fused into the step: q_raw, k_raw are normalised, g_raw and beta_raw
+ * activated, inside the kernel (in fp32, without rounding the transformed
+ * values).  Arguments and layouts as for kda_recurrent_step.
+ */
+kda_status kda_recurrent_step_raw(const void *q_raw, const void *k_raw,
+                                  const void *v, const void *g_raw,
+                                  const void *beta_raw, float *S, int32_t N,
+                                  int32_t H, int32_t d_k, int32_t d_v,
+                                  kda_dtype dt, kda_gate gk, void *o,
+                                  hipStream_t stream);
+
+/*
  * Bytes of device workspace kda_chunk_bwd needs for these sizes (0 if the
  * sizes are invalid or unsupported).  About 900 KB per (chunk, head) at
  * d_k = d_v = 128: every intermediate of a chunk is kept in fp32.

@@ -148,6 +148,19 @@ def draw_tokens(rng, T, H, dk, dv, dtype, gate, gate_mu):
     return out
 
 
+def draw_raw_tokens(rng, T, H, dk, dv, dtype, gate, gate_mu):
+    """Raw projections for T tokens, before the pre-path transforms: q, k ~ N(0,1)
+    (not normalised), v ~ N(0,1), beta ~ N(0,1) (before the logistic), g ~ N(mu,1)
+    (before -softplus); drawn in the order of draw_tokens and rounded to dtype."""
+    out = {}
+    for name in ("q", "k"):
+        out[name] = _round(_normal(rng, (T, H, dk)), dtype)
+    out["v"] = _round(_normal(rng, (T, H, dv)), dtype)
+    out["beta"] = _round(_normal(rng, (T, H)), dtype)
+    out["g"] = _round(_normal(rng, (T, H, dk) if gate == "channel" else (T, H), gate_mu), dtype)
+    return out
+
+
 def draw_cotangents(rng, T, N, H, dk, dv, dtype, sigma_state=1.0):
     """Cotangents for a backward pass: dO ~ N(0,1) [T, H, dv] rounded to dtype,
     and dS_T ~ N(0, sigma_state^2) fp32 [N, H, dk, dv] (drawn in that order)."""

@@ -30,7 +30,7 @@ def test_header_declares_expected_entry_points():
     names = _declared()
     for n in ("kda_chunk_fwd", "kda_recurrent_step", "kda_chunk_fwd_workspace_size",
               "kda_chunk_fwd_check", "kda_status_string", "kda_version", "kda_chunk_bwd",
-              "kda_chunk_bwd_workspace_size"):
+              "kda_chunk_bwd_workspace_size", "kda_prepare_inputs", "kda_recurrent_step_raw"):
         assert n in names
 
 
@@ -149,6 +149,31 @@ def test_chunk_bwd_rejects_bad_arguments(lib):
     assert sz(128, 1, 2, 64, 64, 0, 0) > 0
     assert sz(128, 1, 2, 64, 80, 0, 0) == 0
     assert sz(256, 1, 2, 64, 64, 0, 0) > sz(128, 1, 2, 64, 64, 0, 0)
+
+
+def test_prepare_inputs_rejects_bad_arguments(lib):
+    f = lib.kda_prepare_inputs
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    f.restype = ctypes.c_int
+    f.argtypes = [vp, vp, vp, vp, i64, i32, i32, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp]
+    P = FAKE
+    assert f(P, P, P, P, 16, 2, 96, 0, 0, P, P, P, P, None) == UNSUPPORTED
+    assert f(P, P, P, P, 16, 2, 64, 4, 0, P, P, P, P, None) == UNSUPPORTED
+    assert f(P, P, P, P, 16, 0, 64, 0, 0, P, P, P, P, None) == INVALID
+    assert f(P, P, P, P, -1, 2, 64, 0, 0, P, P, P, P, None) == INVALID
+    assert f(None, P, P, P, 16, 2, 64, 0, 0, P, P, P, P, None) == INVALID
+    assert f(P, P, P, P, 16, 2, 64, 1, 0, P, P, P + 2, P, None) == INVALID   # fp32 needs 4-byte alignment
+    assert f(None, None, None, None, 0, 2, 64, 0, 0, None, None, None, None, None) == OK   # nothing to do
+
+
+def test_recurrent_step_raw_rejects_bad_arguments(lib):
+    f = lib.kda_recurrent_step_raw
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    f.restype = ctypes.c_int
+    f.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, vp, vp]
+    P = FAKE
+    assert f(P, P, P, P, P, P, 4, 2, 64, 48, 0, 0, P, None) == UNSUPPORTED
+    assert f(P, P, P, P, P, P + 4, 4, 2, 64, 64, 0, 0, P, None) == INVALID
 
 
 def test_status_strings(lib):
