@@ -13,7 +13,9 @@ in GB/s of its algorithmic bytes.  Each kernel is timed with HIP events
 recorded on the stream it runs on.  The oracle (fp64, host cores) is timed
 on a bounded prefix of the same workload as `cpu_baseline`.  After the timed
 steps, the chunked backward pass (kda_chunk_bwd) over the same prefill inputs
-is timed on its own and reported under `backward`.
+is timed on its own and reported under `backward`, and the pre-path
+transforms (kda_prepare_inputs on the prefill inputs, and the decode step with
+them fused in) under `prepath`.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-backward]
 """
@@ -151,6 +153,42 @@ def time_backward(kda, torch, hip, x, d, T, H, dk, dv, stream, steps=5, warmup=2
             "what": "kda_chunk_bwd: dq, dk, dv, dg, dbeta, dS0 of the 32K x 32 prefill for dO, dS_T"}
 
 
+def time_prepath(kda, torch, hip, x, T, H, dk, stream, S_dec, toks, steps=10):
+    """kda_prepare_inputs over the 32K x 32 prefill inputs (q, k, per-channel g
+    and beta, read and written once: 2 x (3 d_k + 1) x 2 bytes per head-token),
+    and the decode step with the same transforms fused in (kda_recurrent_step_raw)
+    on the decode workload, each timed with HIP events on its stream."""
+    outs = tuple(torch.empty_like(x[n]) for n in ("q", "k", "g", "beta"))
+    ev = Events(hip, steps + 1)
+    for _ in range(2):
+        kda.prepare_inputs(x["q"], x["k"], x["g"], x["beta"], out=outs)
+    ev.record(0, stream)
+    for i in range(steps):
+        kda.prepare_inputs(x["q"], x["k"], x["g"], x["beta"], out=outs)
+        ev.record(i + 1, stream)
+    torch.cuda.synchronize()
+    t_prep = float(np.median([ev.ms(i, i + 1) for i in range(steps)]))
+    prep_bytes = 2 * (3 * dk + 1) * 2 * T * H
+    ev2 = Events(hip, steps + 1)
+    for i in range(2):
+        tk = toks[i % len(toks)]
+        kda.recurrent_step_raw(tk["q"], tk["k"], tk["v"], tk["g"], tk["beta"], S_dec)
+    ev2.record(0, stream)
+    for i in range(steps):
+        tk = toks[i % len(toks)]
+        kda.recurrent_step_raw(tk["q"], tk["k"], tk["v"], tk["g"], tk["beta"], S_dec)
+        ev2.record(i + 1, stream)
+    torch.cuda.synchronize()
+    t_raw = float(np.median([ev2.ms(i, i + 1) for i in range(steps)]))
+    return {
+        "prepare_inputs": {"us": t_prep * 1e3, "bytes": prep_bytes, "GB_per_s": prep_bytes / (t_prep * 1e-3) / 1e9,
+                           "frac_hbm_peak": prep_bytes / (t_prep * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "decode_raw_back_to_back": {"us_per_step": t_raw * 1e3,
+                                    "GB_per_s": DECODE_BYTES_PER_STEP / (t_raw * 1e-3) / 1e9,
+                                    "frac_hbm_peak": DECODE_BYTES_PER_STEP / (t_raw * 1e-3) / 1e9 / HBM_PEAK_GBS},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -247,6 +285,7 @@ def main():
     torch.cuda.synchronize()
     t_b2b = float(np.median([ev_b2b.ms(i, i + 1) for i in range(n_b2b)]))
 
+    prepath = time_prepath(kda, torch, hip, x, T, H, dk, stream, S_dec, toks)
     bwd = None if args.no_backward else time_backward(kda, torch, hip, x, d, T, H, dk, dv, stream,
                                                       steps=args.backward_steps)
 
@@ -304,6 +343,7 @@ def main():
                           "GB_per_s": path_gbs, "frac_hbm_peak": path_gbs / HBM_PEAK_GBS,
                           "TFLOP_per_s": path_tflops, "frac_bf16_mfma_peak": path_tflops / BF16_MFMA_PEAK_TFLOPS},
     }
+    res["prepath"] = prepath
     if bwd is not None:
         res["backward"] = bwd
     if not args.no_cpu_baseline:

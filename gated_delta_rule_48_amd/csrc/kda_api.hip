@@ -192,12 +192,17 @@ kda_status kda_prepare_inputs(const void* q_raw, const void* k_raw, const void* 
     if (dt != KDA_BF16 && dt != KDA_F32) return KDA_ERR_UNSUPPORTED;
     if (gk != KDA_GATE_PER_CHANNEL && gk != KDA_GATE_PER_HEAD) return KDA_ERR_UNSUPPORTED;
     if (!supported_d(d_k)) return KDA_ERR_UNSUPPORTED;
-    if ((T_total * H + 3) / 4 > (int64_t)UINT32_MAX) return KDA_ERR_UNSUPPORTED;
+    if (T_total * H > (int64_t)UINT32_MAX) return KDA_ERR_UNSUPPORTED;
     if (T_total == 0) return KDA_OK;
     const size_t esz = dt == KDA_BF16 ? 2 : 4;
     const void* ptrs[] = {q_raw, k_raw, g_raw, beta_raw, q, k, g, beta};
     for (const void* p : ptrs)
         if (!p || !aligned(p, esz)) return KDA_ERR_INVALID_ARG;
+    // q, k and a per-channel g move in 16-byte pieces
+    const void* rows[] = {q_raw, k_raw, q, k};
+    for (const void* p : rows)
+        if (!aligned(p, 16)) return KDA_ERR_INVALID_ARG;
+    if (gk == KDA_GATE_PER_CHANNEL && (!aligned(g_raw, 16) || !aligned(g, 16))) return KDA_ERR_INVALID_ARG;
     kda::PrepArgs a;
     a.q_raw = q_raw; a.k_raw = k_raw; a.g_raw = g_raw; a.b_raw = beta_raw;
     a.q = q; a.k = k; a.g = g; a.beta = beta;

@@ -59,11 +59,11 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     for (int i = 0; i < RPT; ++i) {
         const int c = rg * RPT + i;
         const float gi = HEAD_GATE ? gh : Elt<E>::load(g + kbase + c);
-        a[i] = RAW ? 1.f / (1.f + expf(gi)) : gate_exp<E>(gi);
+        a[i] = RAW ? recip<E>(1.f + gate_exp<E>(gi)) : gate_exp<E>(gi);
         kk[i] = Elt<E>::load(k + kbase + c);
         qq[i] = Elt<E>::load(q + kbase + c);
     }
-    const float b = RAW ? sigmoid(Elt<E>::load(beta + pair)) : Elt<E>::load(beta + pair);
+    const float b = RAW ? sigmoid<E>(Elt<E>::load(beta + pair)) : Elt<E>::load(beta + pair);
 
     // Partial reads over this thread's rows: r = S^T (a*k), s = S^T (a*q).
     float4 pr = make_float4(0.f, 0.f, 0.f, 0.f), ps = pr;

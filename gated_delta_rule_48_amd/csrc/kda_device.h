@@ -140,11 +140,29 @@ template <typename E> __device__ __forceinline__ float gate_exp2(float x);
 template <> __device__ __forceinline__ float gate_exp2<bf16_t>(float x) { return __builtin_amdgcn_exp2f(x); }
 template <> __device__ __forceinline__ float gate_exp2<float>(float x) { return exp2f(x); }
 
-// -softplus(x) = -log(1 + e^x) and the logistic function 1 / (1 + e^-x),
-// without overflow for large |x| (library expf / log1pf).
-__device__ __forceinline__ float neg_softplus(float x) { return -(fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)))); }
+// -softplus(x) = -(max(x, 0) + log(1 + e^-|x|)) and the logistic function
+// 1 / (1 + e^-x), without overflow for large |x|.  fp32 inputs use the
+// library expf / log1pf; bf16 inputs the hardware exp and log, with
+// log(1 + t) = t - t^2/2 + t^3/3 - t^4/4 below t = 1/16, where rounding 1 + t
+// would lose the small result (series error < 3e-6 relative).
+template <typename E> __device__ __forceinline__ float softplus_tail(float t);
+template <> __device__ __forceinline__ float softplus_tail<float>(float t) { return log1pf(t); }
+template <> __device__ __forceinline__ float softplus_tail<bf16_t>(float t) {
+    return t < 0.0625f ? t * (1.f - t * (0.5f - t * (1.f / 3.f - t * 0.25f))) : __logf(1.f + t);
+}
+template <typename E>
+__device__ __forceinline__ float neg_softplus(float x) {
+    return -(fmaxf(x, 0.f) + softplus_tail<E>(gate_exp<E>(-fabsf(x))));
+}
+// 1 / x: exact division for fp32 inputs, the hardware reciprocal (about one
+// ulp) for bf16 inputs.
+template <typename E> __device__ __forceinline__ float recip(float x);
+template <> __device__ __forceinline__ float recip<float>(float x) { return 1.f / x; }
+template <> __device__ __forceinline__ float recip<bf16_t>(float x) { return __builtin_amdgcn_rcpf(x); }
+
+template <typename E>
 __device__ __forceinline__ float sigmoid(float x) {
-    const float e = expf(-fabsf(x));
+    const float e = gate_exp<E>(-fabsf(x));
     return x >= 0.f ? 1.f / (1.f + e) : e / (1.f + e);
 }
 

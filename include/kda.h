@@ -200,7 +200,9 @@ kda_status kda_recurrent_step(const void *q, const void *k, const void *v,
  *   g_raw, g             [T_total, H, d_k] ([T_total, H] with KDA_GATE_PER_HEAD)
  *   beta_raw, beta       [T_total, H]
  * Outputs may alias their inputs exactly (in place).  Arithmetic in fp32,
- * outputs rounded once to dt.  d_k in {64, 128}.
+ * outputs rounded once to dt.  d_k in {64, 128}.  q_raw, k_raw, q, k and a
+ * per-channel g_raw, g must be 16-byte aligned (KDA_ERR_INVALID_ARG
+ * otherwise); T_total * H must stay below 2^32 (KDA_ERR_UNSUPPORTED).
  */
 kda_status kda_prepare_inputs(const void *q_raw, const void *k_raw,
                               const void *g_raw, const void *beta_raw,
