@@ -204,7 +204,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const E* __restri
             if (t == m) r = b;
         }
         const float bl = b;
-        w.Gn[(size_t)slot * DK + c] = expf(bl);
+        w.Gn[(size_t)slot * DK + c] = gate_exp<E>(bl);
         // pass 2: the same sums again, and every decayed operand
         b = 0.f;
         for (int t = 0; t < C; ++t) {
@@ -214,7 +214,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const E* __restri
                 qv = ld(q, ((t0 + t) * H + h) * DK + c);
                 kv = ld(k, ((t0 + t) * H + h) * DK + c);
             }
-            const float e = expf(b), er = expf(b - r), eir = expf(r - b), ed = expf(bl - b);
+            const float e = gate_exp<E>(b), er = gate_exp<E>(b - r), eir = gate_exp<E>(r - b),
+                        ed = gate_exp<E>(bl - b);
             const size_t i = oCK + (size_t)t * DK + c;
             w.B[i] = b;
             w.QG[i] = qv * e;
@@ -590,7 +591,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
 
 // ---------------------------------------------------------------------------
 // Per (chunk, head): gradients of the chunk's inputs from dU, dS_next, S, U.
-template <typename E, int DK, int DV, bool HG>
+// Three launches, PH = 0, 1, 2: phase 1; phases 2-4; phases 5-6.  The
+// phases exchange everything through the workspace, so the split only moves
+// barriers to kernel boundaries; each launch holds far fewer registers.
+template <typename E, int DK, int DV, bool HG, int PH>
 __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restrict__ v, const E* __restrict__ beta,
                                                                 const E* __restrict__ dO, int32_t H, BwdWs w,
                                                                 E* __restrict__ dq, E* __restrict__ dk,
@@ -633,6 +637,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
             }
     };
 
+    if constexpr (PH == 0) {
     // phase 1: dW = -dU S^T, dQG = dO S^T, dKd = U dS_next^T, dP = tril(dO U^T), dGn
     {
         Acc<DK> acc;
@@ -660,11 +665,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
     }
     for (int c = tid; c < DK; c += kBwdThreads) {
         float s = 0.f;
+#pragma unroll 8
         for (int x = 0; x < DV; ++x) s += Sm[(size_t)c * DV + x] * dSn[(size_t)c * DV + x];
         w.dGn[oK + c] = s;
     }
-    __syncthreads();
+    }  // PH == 0
 
+    if constexpr (PH == 1) {
     // phase 2: dT = strict_tril(dW Xw^T + dU Xu^T), dXw = T^T dW, dXu = T^T dU
     {
         const float* dW = w.dW + oCK;
@@ -728,7 +735,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
                 w.dA[oCC + (size_t)t * C + i] = (i < t && t < n) ? -aa.v[a][b] : 0.f;
             }
     }
-    __syncthreads();
+    }  // PH == 1
+
+    if constexpr (PH == 2) {
 
     // phase 5: dKr = diag(beta) dA Ki, dKi = (diag(beta) dA)^T Kr + dP^T Qr,
     // dQr = dP Ki; then dq, dk and db (kept in dW's slot), dbeta, dv
@@ -769,7 +778,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
                 const float dKG = sbeta[t] * w.dXw[j];
                 const float dQG = w.dQG[j], dKd = w.dKd[j];
                 const float bb = w.B[j], r = sr[c], bl = sbl[c];
-                const float e = expf(bb), er = expf(bb - r), eir = expf(r - bb), ed = expf(bl - bb);
+                const float e = gate_exp<E>(bb), er = gate_exp<E>(bb - r), eir = gate_exp<E>(r - bb),
+                            ed = gate_exp<E>(bl - bb);
                 const int64_t o = ((t0 + t) * H + h) * DK + c;
                 dq[o] = Elt<E>::from(dQG * e + dQr * er);
                 dk[o] = Elt<E>::from(dKG * e + dKr * er + dKi * eir + dKd * ed);
@@ -777,12 +787,22 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
                           dKd * w.Kd[j];
             }
     }
-    for (int t = tid; t < n; t += kBwdThreads) {
+    // dbeta: four adjacent lanes per row, each a quarter of the row's sums
+    {
+        const int t = tid / 4, q = tid % 4;
         float s = 0.f;
-        for (int i = 0; i < t; ++i) s += w.dA[oCC + (size_t)t * C + i] * w.M[oCC + (size_t)t * C + i];
-        for (int c = 0; c < DK; ++c) s += w.dXw[oCK + (size_t)t * DK + c] * w.KG[oCK + (size_t)t * DK + c];
-        for (int x = 0; x < DV; ++x) s += w.dXu[oCV + (size_t)t * DV + x] * ld(v, ((t0 + t) * H + h) * DV + x);
-        dbeta[(t0 + t) * H + h] = Elt<E>::from(s);
+        if (t < n) {
+#pragma unroll 4
+            for (int i = q; i < t; i += 4) s += w.dA[oCC + (size_t)t * C + i] * w.M[oCC + (size_t)t * C + i];
+#pragma unroll 8
+            for (int c = q; c < DK; c += 4) s += w.dXw[oCK + (size_t)t * DK + c] * w.KG[oCK + (size_t)t * DK + c];
+#pragma unroll 8
+            for (int x = q; x < DV; x += 4)
+                s += w.dXu[oCV + (size_t)t * DV + x] * ld(v, ((t0 + t) * H + h) * DV + x);
+        }
+        s += __shfl_xor(s, 1, 64);
+        s += __shfl_xor(s, 2, 64);
+        if (t < n && q == 0) dbeta[(t0 + t) * H + h] = Elt<E>::from(s);
     }
     for (int idx = tid; idx < C * DV; idx += kBwdThreads) {
         const int t = idx / DV, x = idx % DV;
@@ -794,7 +814,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
     // also carries e^{b_last} (Gn) and the e^{b_last} factor of Kd
     for (int c = tid; c < DK; c += kBwdThreads) {
         float acc = w.dGn[oK + c] * w.Gn[oK + c];
+#pragma unroll 8
         for (int t = 0; t < n; ++t) acc += w.dKd[oCK + (size_t)t * DK + c] * w.Kd[oCK + (size_t)t * DK + c];
+#pragma unroll 8
         for (int t = n - 1; t >= 0; --t) {
             acc += w.dW[oCK + (size_t)t * DK + c];
             if (HG)
@@ -807,10 +829,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
         __syncthreads();
         for (int t = tid; t < n; t += kBwdThreads) {
             float s = 0.f;
+#pragma unroll 8
             for (int c = 0; c < DK; ++c) s += w.dQG[oCK + (size_t)t * DK + c];
             dg[(t0 + t) * H + h] = Elt<E>::from(s);
         }
     }
+    }  // PH == 2
 }
 
 // ---------------------------------------------------------------------------
@@ -884,7 +908,15 @@ hipError_t launch_bwd_t(const BwdArgs& a, const BwdWs& w, hipStream_t stream) {
     hipLaunchKernelGGL(dw, dim3(walks), dim3(kBwdThreads), dw_lds, stream, a.H, (const E*)a.dO, a.dS_T, a.dS0, w);
     e = hipGetLastError();
     if (e != hipSuccess || a.T == 0) return e;
-    hipLaunchKernelGGL((bwd_local_kernel<E, DK, DV, HG>), dim3(slots), dim3(kBwdThreads), 0, stream,
+    hipLaunchKernelGGL((bwd_local_kernel<E, DK, DV, HG, 0>), dim3(slots), dim3(kBwdThreads), 0, stream,
+                       (const E*)a.v, (const E*)a.beta, (const E*)a.dO, a.H, w, (E*)a.dq, (E*)a.dk, (E*)a.dv,
+                       (E*)a.dg, (E*)a.dbeta);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_local_kernel<E, DK, DV, HG, 1>), dim3(slots), dim3(kBwdThreads), 0, stream,
+                       (const E*)a.v, (const E*)a.beta, (const E*)a.dO, a.H, w, (E*)a.dq, (E*)a.dk, (E*)a.dv,
+                       (E*)a.dg, (E*)a.dbeta);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_local_kernel<E, DK, DV, HG, 2>), dim3(slots), dim3(kBwdThreads), 0, stream,
                        (const E*)a.v, (const E*)a.beta, (const E*)a.dO, a.H, w, (E*)a.dq, (E*)a.dk, (E*)a.dv,
                        (E*)a.dg, (E*)a.dbeta);
     return hipGetLastError();
