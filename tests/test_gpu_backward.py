@@ -126,3 +126,36 @@ def test_bwd_full_size_prefix_support():
         e = rel_err(gv, rv)
         print(f"bwd 32k prefix {n}={e:.2e}", flush=True)
         assert e <= TOL["bf16"], (n, e)
+
+
+def test_bwd_varlen_gated_deltanet_full_size_prefix_support():
+    """The packed 8-sequence Gated DeltaNet workload (per-head gate, S0 given,
+    H = 16, d = 128, bf16): dO is zero except on the first 128 tokens of every
+    sequence and dS_T = 0, so each sequence's prefix gradients and dS0 are
+    those of the 128-token problems, and every other gradient is zero."""
+    cfg = synth.CONFIGS["gdn_varlen_bf16"]
+    d = synth.chunk_inputs(cfg)
+    cu = d["cu_seqlens"].astype(np.int64)
+    T, H, dk, dv, N = int(cu[-1]), cfg.H, cfg.dk, cfg.dv, len(cu) - 1
+    P = 128
+    rng = np.random.default_rng(2021)
+    dO = np.zeros((T, H, dv), dtype=np.uint16)
+    rows = np.concatenate([np.arange(cu[n], cu[n] + P) for n in range(N)])
+    dO[rows] = synth.bf16_bits(rng.standard_normal((len(rows), H, dv), dtype=np.float32))
+    x = {n: to_dev(d[n], "bf16") for n in ("q", "k", "v", "g", "beta")}
+    got = kda.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], to_dev(dO, "bf16"),
+                        S0=torch.from_numpy(d["S0"]).cuda(),
+                        cu_seqlens=torch.from_numpy(d["cu_seqlens"].astype(np.int32)).cuda(), per_head_gate=True)
+    torch.cuda.synchronize()
+    got = [t.float().cpu().numpy() for t in got]
+    mask = np.zeros(T, dtype=bool)
+    mask[rows] = True
+    for gv in got[:5]:
+        assert not np.any(gv[~mask]), "gradient beyond the support of dO"
+    sub = {n: d[n][rows] for n in ("q", "k", "v", "g", "beta")}
+    ref = recurrence_grad(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], dO[rows], S0=d["S0"],
+                          cu_seqlens=np.arange(N + 1) * P, per_head_gate=True)
+    for n_, gv, rv in zip(NAMES, [g[rows] for g in got[:5]] + [got[5]], ref):
+        e = rel_err(gv, rv)
+        print(f"bwd gdn varlen prefix {n_}={e:.2e}", flush=True)
+        assert e <= TOL["bf16"], (n_, e)
