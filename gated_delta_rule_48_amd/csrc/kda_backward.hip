@@ -176,10 +176,14 @@ template <typename E, int DK, int DV, bool HG>
 __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const E* __restrict__ q, const E* __restrict__ k,
                                                                const E* __restrict__ v, const E* __restrict__ g,
                                                                const E* __restrict__ beta, int32_t H, BwdWs w) {
-    __shared__ float sA[C][C + 1];
-    __shared__ float sT[C][C + 1];
+    // sA | sT for the solve; before that, the chunk's prefix sums b [C][DK]
+    __shared__ float sAT[2 * C * (C + 1)];
     __shared__ float sbeta[C];
     __shared__ __align__(16) float lds[kGemmLds];
+    static_assert(C * DK <= 2 * C * (C + 1), "prefix sums fit in the solve's LDS");
+    float (*sA)[C + 1] = reinterpret_cast<float (*)[C + 1]>(sAT);
+    float (*sT)[C + 1] = reinterpret_cast<float (*)[C + 1]>(sAT + C * (C + 1));
+    float* sB = sAT;
     const int64_t slot = blockIdx.x;
     const int64_t chunk = slot / H;
     const int h = (int)(slot % H);
@@ -190,43 +194,43 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const E* __restri
     const int tid = threadIdx.x;
     const size_t oCK = (size_t)slot * C * DK, oCV = (size_t)slot * C * DV, oCC = (size_t)slot * C * C;
     if (tid < C) sbeta[tid] = tid < n ? ld(beta, (t0 + tid) * H + h) : 0.f;
+    // the chunk's gate, staged in one coalesced pass (rows past the end as 0)
+    for (int idx = tid; idx < C * DK; idx += kBwdThreads) {
+        const int t = idx / DK, c = idx % DK;
+        sB[idx] = t < n ? (HG ? ld(g, (t0 + t) * H + h) : ld(g, ((t0 + t) * H + h) * DK + c)) : 0.f;
+    }
     __syncthreads();
-    if (tid < DK) {
-        const int c = tid;
-        const int m = (n - 1) / 2;
-        auto gate = [&](int t) -> float {
-            return HG ? ld(g, (t0 + t) * H + h) : ld(g, ((t0 + t) * H + h) * DK + c);
-        };
-        // pass 1: the reference (middle row) and the last prefix sum
-        float b = 0.f, r = 0.f;
-        for (int t = 0; t < n; ++t) {
-            b += gate(t);
-            if (t == m) r = b;
-        }
-        const float bl = b;
-        w.Gn[(size_t)slot * DK + c] = gate_exp<E>(bl);
-        // pass 2: the same sums again, and every decayed operand
-        b = 0.f;
+    // prefix sums per channel, in place (rows past the end keep the last sum)
+    for (int c = tid; c < DK; c += kBwdThreads) {
+        float b = 0.f;
         for (int t = 0; t < C; ++t) {
-            float qv = 0.f, kv = 0.f;
-            if (t < n) {
-                b += gate(t);
-                qv = ld(q, ((t0 + t) * H + h) * DK + c);
-                kv = ld(k, ((t0 + t) * H + h) * DK + c);
-            }
-            const float e = gate_exp<E>(b), er = gate_exp<E>(b - r), eir = gate_exp<E>(r - b),
-                        ed = gate_exp<E>(bl - b);
-            const size_t i = oCK + (size_t)t * DK + c;
-            w.B[i] = b;
-            w.QG[i] = qv * e;
-            w.KG[i] = kv * e;
-            w.Kd[i] = kv * ed;
-            w.Qr[i] = qv * er;
-            w.Kr[i] = kv * er;
-            w.Ki[i] = kv * eir;
-            w.KiT[oCK + (size_t)c * C + t] = kv * eir;
-            w.XwT[oCK + (size_t)c * C + t] = sbeta[t] * kv * e;
+            b += sB[t * DK + c];
+            sB[t * DK + c] = b;
         }
+        w.Gn[(size_t)slot * DK + c] = gate_exp<E>(b);
+    }
+    __syncthreads();
+    // every decayed operand; r is the middle row's prefix sum
+    const int m = (n - 1) / 2;
+    for (int idx = tid; idx < C * DK; idx += kBwdThreads) {
+        const int t = idx / DK, c = idx % DK;
+        const float b = sB[idx], r = sB[m * DK + c], bl = sB[(n - 1) * DK + c];
+        float qv = 0.f, kv = 0.f;
+        if (t < n) {
+            qv = ld(q, ((t0 + t) * H + h) * DK + c);
+            kv = ld(k, ((t0 + t) * H + h) * DK + c);
+        }
+        const float e = gate_exp<E>(b), er = gate_exp<E>(b - r), eir = gate_exp<E>(r - b), ed = gate_exp<E>(bl - b);
+        const size_t i = oCK + idx;
+        w.B[i] = b;
+        w.QG[i] = qv * e;
+        w.KG[i] = kv * e;
+        w.Kd[i] = kv * ed;
+        w.Qr[i] = qv * er;
+        w.Kr[i] = kv * er;
+        w.Ki[i] = kv * eir;
+        w.KiT[oCK + (size_t)c * C + t] = kv * eir;
+        w.XwT[oCK + (size_t)c * C + t] = sbeta[t] * kv * e;
     }
     for (int idx = tid; idx < C * DV; idx += kBwdThreads) {
         const int t = idx / DV, c = idx % DV;

@@ -159,3 +159,17 @@ def test_bwd_varlen_gated_deltanet_full_size_prefix_support():
         e = rel_err(gv, rv)
         print(f"bwd gdn varlen prefix {n_}={e:.2e}", flush=True)
         assert e <= TOL["bf16"], (n_, e)
+
+
+def test_bwd_no_tokens_passes_state_cotangent():
+    """T = 0 (every sequence empty): dS0 = dS_T exactly, nothing else to do."""
+    H, dk, dv, N = 2, 64, 128, 3
+    rng = np.random.default_rng(77)
+    dST = rng.standard_normal((N, H, dk, dv)).astype(np.float32)
+    e = torch.empty((0, H, dk), dtype=torch.bfloat16, device="cuda")
+    ev = torch.empty((0, H, dv), dtype=torch.bfloat16, device="cuda")
+    eb = torch.empty((0, H), dtype=torch.bfloat16, device="cuda")
+    got = kda.chunk_bwd(e, e, ev, e, eb, ev, dS_T=torch.from_numpy(dST).cuda(),
+                        cu_seqlens=torch.zeros(N + 1, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert np.array_equal(got[5].cpu().numpy(), dST)
