@@ -280,7 +280,9 @@ def chunk_bwd(q, k, v, g, beta, dO, *, S0=None, dS_T=None, cu_seqlens=None, N=No
     and the cotangents dO ([T, H, dv], q's dtype) and dS_T (fp32
     [N, H, dk, dv] or None = zeros).  Returns (dq, dk, dv, dg, dbeta, dS0):
     the first five with the shapes and dtype of q, k, v, g, beta; dS0 fp32
-    [N, H, dk, dv] (None when ``need_dS0`` is False).
+    [N, H, dk, dv] (None when ``need_dS0`` is False).  ``workspace`` may be
+    smaller than ``chunk_bwd_workspace_size`` for all heads (at least the size
+    for one head): the heads are then processed in groups that fit.
     """
     if q.dim() != 3 or v.dim() != 3:
         raise ValueError("q, k, v must be [T, H, d]")

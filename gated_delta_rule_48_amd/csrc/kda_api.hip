@@ -137,7 +137,7 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
         (cu_seqlens && !aligned(cu_seqlens, 4)))
         return KDA_ERR_INVALID_ARG;
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERR_WORKSPACE;
-    if (workspace_bytes < kda::bwd_workspace_bytes(T_total, N, H, d_k, d_v)) return KDA_ERR_WORKSPACE;
+    if (kda::bwd_head_group(T_total, N, H, d_k, d_v, workspace_bytes) < 1) return KDA_ERR_WORKSPACE;
 
     kda::BwdArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
@@ -147,7 +147,7 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
     a.max_chunks = kda::max_chunks_for(T_total, N);
     a.bf16 = dt == KDA_BF16;
     a.head_gate = gk == KDA_GATE_PER_HEAD;
-    return kda::launch_chunk_bwd(a, workspace, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    return kda::launch_chunk_bwd(a, workspace, workspace_bytes, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 namespace {

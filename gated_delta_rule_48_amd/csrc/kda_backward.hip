@@ -42,6 +42,8 @@
 // product tiled through LDS with 4 x N/16 register tiles.
 #include "kda_internal.h"
 
+#include <type_traits>
+
 namespace kda {
 
 namespace {
@@ -49,7 +51,10 @@ namespace {
 constexpr int kBwdThreads = 256;
 constexpr int C = kChunk;
 
-// Per-(chunk, head) arrays, fp32; slot = chunk * H + head.
+// Per-(chunk, head) arrays, fp32; slot = chunk * H + head, where H counts the
+// heads of the group being processed.  Token and state tensors are indexed
+// with the full head count Hs (their row stride); the host offsets their
+// pointers to the group's first head.
 struct BwdWs {
     WsHeader* header;
     int32_t* cu;
@@ -175,7 +180,7 @@ __device__ __forceinline__ void gemm64(Acc<N>& acc, LA la, LB lb, float* lds) {
 template <typename E, int DK, int DV, bool HG>
 __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const E* __restrict__ q, const E* __restrict__ k,
                                                                const E* __restrict__ v, const E* __restrict__ g,
-                                                               const E* __restrict__ beta, int32_t H, BwdWs w) {
+                                                               const E* __restrict__ beta, int32_t H, int32_t Hs, BwdWs w) {
     // sA | sT for the solve; before that, the chunk's prefix sums b [C][DK]
     __shared__ float sAT[2 * C * (C + 1)];
     __shared__ float sbeta[C];
@@ -193,11 +198,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const E* __restri
     const int n = ct.y;
     const int tid = threadIdx.x;
     const size_t oCK = (size_t)slot * C * DK, oCV = (size_t)slot * C * DV, oCC = (size_t)slot * C * C;
-    if (tid < C) sbeta[tid] = tid < n ? ld(beta, (t0 + tid) * H + h) : 0.f;
+    if (tid < C) sbeta[tid] = tid < n ? ld(beta, (t0 + tid) * Hs + h) : 0.f;
     // the chunk's gate, staged in one coalesced pass (rows past the end as 0)
     for (int idx = tid; idx < C * DK; idx += kBwdThreads) {
         const int t = idx / DK, c = idx % DK;
-        sB[idx] = t < n ? (HG ? ld(g, (t0 + t) * H + h) : ld(g, ((t0 + t) * H + h) * DK + c)) : 0.f;
+        sB[idx] = t < n ? (HG ? ld(g, (t0 + t) * Hs + h) : ld(g, ((t0 + t) * Hs + h) * DK + c)) : 0.f;
     }
     __syncthreads();
     // prefix sums per channel, in place (rows past the end keep the last sum)
@@ -217,8 +222,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const E* __restri
         const float b = sB[idx], r = sB[m * DK + c], bl = sB[(n - 1) * DK + c];
         float qv = 0.f, kv = 0.f;
         if (t < n) {
-            qv = ld(q, ((t0 + t) * H + h) * DK + c);
-            kv = ld(k, ((t0 + t) * H + h) * DK + c);
+            qv = ld(q, ((t0 + t) * Hs + h) * DK + c);
+            kv = ld(k, ((t0 + t) * Hs + h) * DK + c);
         }
         const float e = gate_exp<E>(b), er = gate_exp<E>(b - r), eir = gate_exp<E>(r - b), ed = gate_exp<E>(bl - b);
         const size_t i = oCK + idx;
@@ -234,7 +239,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const E* __restri
     }
     for (int idx = tid; idx < C * DV; idx += kBwdThreads) {
         const int t = idx / DV, c = idx % DV;
-        const float vv = t < n ? ld(v, ((t0 + t) * H + h) * DV + c) : 0.f;
+        const float vv = t < n ? ld(v, ((t0 + t) * Hs + h) * DV + c) : 0.f;
         w.XuT[oCV + (size_t)c * C + t] = sbeta[t] * vv;
     }
     __syncthreads();
@@ -384,7 +389,7 @@ struct StateWalkLds {
 // One workgroup of four waves per CU at most (LDS), so a wave may use the
 // whole register file: the next chunk's operands are held in registers.
 template <int DK, int DV>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_state_walk_kernel(int32_t H, const float* __restrict__ S0,
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_state_walk_kernel(int32_t H, int32_t Hs, const float* __restrict__ S0,
                                                                      BwdWs w) {
     using L = StateWalkLds<DK, DV>;
     constexpr int NS = DV / 16, SK = L::SK, RS = DK / 16;  // rows of S per thread
@@ -405,7 +410,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
     float S[RS];
 #pragma unroll
     for (int i = 0; i < RS; ++i)
-        S[i] = S0 ? S0[(((size_t)seq * H + h) * DK + rg * RS + i) * DV + col] : 0.f;
+        S[i] = S0 ? S0[(((size_t)seq * Hs + h) * DK + rg * RS + i) * DV + col] : 0.f;
     f32x4 rW[block_regs<DK>()], rK[block_regs<DK>()];
     if (c0 < c1) {
         const size_t slot = (size_t)c0 * H + h;
@@ -475,7 +480,7 @@ struct DStateWalkLds {
 };
 
 template <typename E, int DK, int DV>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dstate_walk_kernel(int32_t H, const E* __restrict__ dO,
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dstate_walk_kernel(int32_t H, int32_t Hs, const E* __restrict__ dO,
                                                                       const float* __restrict__ dST,
                                                                       float* __restrict__ dS0, BwdWs w) {
     using L = DStateWalkLds<DK, DV>;
@@ -499,14 +504,14 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
     float dS[RS];
 #pragma unroll
     for (int i = 0; i < RS; ++i)
-        dS[i] = dST ? dST[(((size_t)seq * H + h) * DK + rg * RS + i) * DV + col] : 0.f;
+        dS[i] = dST ? dST[(((size_t)seq * Hs + h) * DK + rg * RS + i) * DV + col] : 0.f;
     // dO of a chunk for this thread's 4 rows of column `col`
     auto load_dO = [&](int ch, float (&r)[4]) {
         const int2 ct = w.chunk_tab[ch];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = rg * 4 + i;
-            r[i] = t < ct.y ? ld(dO, (((int64_t)ct.x + t) * H + h) * DV + col) : 0.f;
+            r[i] = t < ct.y ? ld(dO, (((int64_t)ct.x + t) * Hs + h) * DV + col) : 0.f;
         }
     };
     f32x4 rP[block_regs<C>()], rK[block_regs<DK>()], rQ[block_regs<DK>()], rW[block_regs<DK>()];
@@ -589,7 +594,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
     }
     if (dS0) {
 #pragma unroll
-        for (int i = 0; i < RS; ++i) dS0[(((size_t)seq * H + h) * DK + rg * RS + i) * DV + col] = dS[i];
+        for (int i = 0; i < RS; ++i) dS0[(((size_t)seq * Hs + h) * DK + rg * RS + i) * DV + col] = dS[i];
     }
 }
 
@@ -600,7 +605,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
 // barriers to kernel boundaries; each launch holds far fewer registers.
 template <typename E, int DK, int DV, bool HG, int PH>
 __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restrict__ v, const E* __restrict__ beta,
-                                                                const E* __restrict__ dO, int32_t H, BwdWs w,
+                                                                const E* __restrict__ dO, int32_t H, int32_t Hs, BwdWs w,
                                                                 E* __restrict__ dq, E* __restrict__ dk,
                                                                 E* __restrict__ dv, E* __restrict__ dg,
                                                                 E* __restrict__ dbeta) {
@@ -618,7 +623,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
     const int tid = threadIdx.x;
     const size_t oCK = (size_t)slot * C * DK, oCV = (size_t)slot * C * DV, oCC = (size_t)slot * C * C;
     const size_t oK = (size_t)slot * DK, oKV = (size_t)slot * DK * DV;
-    if (tid < C) sbeta[tid] = tid < n ? ld(beta, (t0 + tid) * H + h) : 0.f;
+    if (tid < C) sbeta[tid] = tid < n ? ld(beta, (t0 + tid) * Hs + h) : 0.f;
     if (tid < DK) {
         sr[tid] = w.B[oCK + (size_t)((n - 1) / 2) * DK + tid];
         sbl[tid] = w.B[oCK + (size_t)(n - 1) * DK + tid];
@@ -628,7 +633,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
     const float* Um = w.U + oCV;
     const float* dUm = w.dU + oCV;
     const float* TT = w.TT + oCC;
-    auto dOat = [&](int t, int x) -> float { return t < n ? ld(dO, ((t0 + t) * H + h) * DV + x) : 0.f; };
+    auto dOat = [&](int t, int x) -> float { return t < n ? ld(dO, ((t0 + t) * Hs + h) * DV + x) : 0.f; };
     // store a 64 x N accumulator tile (times s) to dst (row stride N), rows >= n as zero
     auto put = [&](auto& acc, float* dst, int N, float s) {
         constexpr int NT = sizeof(acc.v[0]) / sizeof(float);
@@ -784,7 +789,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
                 const float bb = w.B[j], r = sr[c], bl = sbl[c];
                 const float e = gate_exp<E>(bb), er = gate_exp<E>(bb - r), eir = gate_exp<E>(r - bb),
                             ed = gate_exp<E>(bl - bb);
-                const int64_t o = ((t0 + t) * H + h) * DK + c;
+                const int64_t o = ((t0 + t) * Hs + h) * DK + c;
                 dq[o] = Elt<E>::from(dQG * e + dQr * er);
                 dk[o] = Elt<E>::from(dKG * e + dKr * er + dKi * eir + dKd * ed);
                 w.dW[j] = dQG * w.QG[j] + dQr * w.Qr[j] + dKG * w.KG[j] + dKr * w.Kr[j] - dKi * w.Ki[j] -
@@ -802,15 +807,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
             for (int c = q; c < DK; c += 4) s += w.dXw[oCK + (size_t)t * DK + c] * w.KG[oCK + (size_t)t * DK + c];
 #pragma unroll 8
             for (int x = q; x < DV; x += 4)
-                s += w.dXu[oCV + (size_t)t * DV + x] * ld(v, ((t0 + t) * H + h) * DV + x);
+                s += w.dXu[oCV + (size_t)t * DV + x] * ld(v, ((t0 + t) * Hs + h) * DV + x);
         }
         s += __shfl_xor(s, 1, 64);
         s += __shfl_xor(s, 2, 64);
-        if (t < n && q == 0) dbeta[(t0 + t) * H + h] = Elt<E>::from(s);
+        if (t < n && q == 0) dbeta[(t0 + t) * Hs + h] = Elt<E>::from(s);
     }
     for (int idx = tid; idx < C * DV; idx += kBwdThreads) {
         const int t = idx / DV, x = idx % DV;
-        if (t < n) dv[((t0 + t) * H + h) * DV + x] = Elt<E>::from(sbeta[t] * w.dXu[oCV + idx]);
+        if (t < n) dv[((t0 + t) * Hs + h) * DV + x] = Elt<E>::from(sbeta[t] * w.dXu[oCV + idx]);
     }
     __syncthreads();
 
@@ -826,7 +831,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
             if (HG)
                 w.dQG[oCK + (size_t)t * DK + c] = acc;
             else
-                dg[((t0 + t) * H + h) * DK + c] = Elt<E>::from(acc);
+                dg[((t0 + t) * Hs + h) * DK + c] = Elt<E>::from(acc);
         }
     }
     if (HG) {
@@ -835,7 +840,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
             float s = 0.f;
 #pragma unroll 8
             for (int c = 0; c < DK; ++c) s += w.dQG[oCK + (size_t)t * DK + c];
-            dg[(t0 + t) * H + h] = Elt<E>::from(s);
+            dg[(t0 + t) * Hs + h] = Elt<E>::from(s);
         }
     }
     }  // PH == 2
@@ -890,53 +895,64 @@ hipError_t lds_attr(const void* kern, size_t bytes) {
     return hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
+// One head group: a.H heads starting at the pointers given (already offset),
+// token and state tensors with a row stride of Hs heads.
 template <typename E, int DK, int DV, bool HG>
-hipError_t launch_bwd_t(const BwdArgs& a, const BwdWs& w, hipStream_t stream) {
+hipError_t launch_bwd_t(const BwdArgs& a, int32_t Hs, const BwdWs& w, hipStream_t stream) {
     const unsigned slots = (unsigned)(a.max_chunks * a.H);
     const unsigned walks = (unsigned)((int64_t)a.N * a.H * (DV / 16));
     hipError_t e = hipSuccess;
     if (a.T > 0) {
         hipLaunchKernelGGL((bwd_prep_kernel<E, DK, DV, HG>), dim3(slots), dim3(kBwdThreads), 0, stream,
-                           (const E*)a.q, (const E*)a.k, (const E*)a.v, (const E*)a.g, (const E*)a.beta, a.H, w);
+                           (const E*)a.q, (const E*)a.k, (const E*)a.v, (const E*)a.g, (const E*)a.beta, a.H, Hs,
+                           w);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         auto sw = bwd_state_walk_kernel<DK, DV>;
         constexpr size_t sw_lds = StateWalkLds<DK, DV>::bytes;
         if ((e = lds_attr(reinterpret_cast<const void*>(sw), sw_lds)) != hipSuccess) return e;
-        hipLaunchKernelGGL(sw, dim3(walks), dim3(kBwdThreads), sw_lds, stream, a.H, a.S0, w);
+        hipLaunchKernelGGL(sw, dim3(walks), dim3(kBwdThreads), sw_lds, stream, a.H, Hs, a.S0, w);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     auto dw = bwd_dstate_walk_kernel<E, DK, DV>;
     constexpr size_t dw_lds = DStateWalkLds<DK, DV>::bytes;
     if ((e = lds_attr(reinterpret_cast<const void*>(dw), dw_lds)) != hipSuccess) return e;
-    hipLaunchKernelGGL(dw, dim3(walks), dim3(kBwdThreads), dw_lds, stream, a.H, (const E*)a.dO, a.dS_T, a.dS0, w);
+    hipLaunchKernelGGL(dw, dim3(walks), dim3(kBwdThreads), dw_lds, stream, a.H, Hs, (const E*)a.dO, a.dS_T, a.dS0,
+                       w);
     e = hipGetLastError();
     if (e != hipSuccess || a.T == 0) return e;
     hipLaunchKernelGGL((bwd_local_kernel<E, DK, DV, HG, 0>), dim3(slots), dim3(kBwdThreads), 0, stream,
-                       (const E*)a.v, (const E*)a.beta, (const E*)a.dO, a.H, w, (E*)a.dq, (E*)a.dk, (E*)a.dv,
+                       (const E*)a.v, (const E*)a.beta, (const E*)a.dO, a.H, Hs, w, (E*)a.dq, (E*)a.dk, (E*)a.dv,
                        (E*)a.dg, (E*)a.dbeta);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_local_kernel<E, DK, DV, HG, 1>), dim3(slots), dim3(kBwdThreads), 0, stream,
-                       (const E*)a.v, (const E*)a.beta, (const E*)a.dO, a.H, w, (E*)a.dq, (E*)a.dk, (E*)a.dv,
+                       (const E*)a.v, (const E*)a.beta, (const E*)a.dO, a.H, Hs, w, (E*)a.dq, (E*)a.dk, (E*)a.dv,
                        (E*)a.dg, (E*)a.dbeta);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_local_kernel<E, DK, DV, HG, 2>), dim3(slots), dim3(kBwdThreads), 0, stream,
-                       (const E*)a.v, (const E*)a.beta, (const E*)a.dO, a.H, w, (E*)a.dq, (E*)a.dk, (E*)a.dv,
+                       (const E*)a.v, (const E*)a.beta, (const E*)a.dO, a.H, Hs, w, (E*)a.dq, (E*)a.dk, (E*)a.dv,
                        (E*)a.dg, (E*)a.dbeta);
     return hipGetLastError();
 }
 
 template <typename E, int DK, int DV>
-hipError_t launch_bwd_g(const BwdArgs& a, const BwdWs& w, hipStream_t s) {
-    return a.head_gate ? launch_bwd_t<E, DK, DV, true>(a, w, s) : launch_bwd_t<E, DK, DV, false>(a, w, s);
+hipError_t launch_bwd_g(const BwdArgs& a, int32_t Hs, const BwdWs& w, hipStream_t s) {
+    return a.head_gate ? launch_bwd_t<E, DK, DV, true>(a, Hs, w, s) : launch_bwd_t<E, DK, DV, false>(a, Hs, w, s);
 }
 
 template <typename E>
-hipError_t launch_bwd_e(const BwdArgs& a, const BwdWs& w, hipStream_t s) {
-    if (a.dk_ == 64 && a.dv_ == 64) return launch_bwd_g<E, 64, 64>(a, w, s);
-    if (a.dk_ == 64 && a.dv_ == 128) return launch_bwd_g<E, 64, 128>(a, w, s);
-    if (a.dk_ == 128 && a.dv_ == 64) return launch_bwd_g<E, 128, 64>(a, w, s);
-    return launch_bwd_g<E, 128, 128>(a, w, s);
+hipError_t launch_bwd_e(const BwdArgs& a, int32_t Hs, const BwdWs& w, hipStream_t s) {
+    if (a.dk_ == 64 && a.dv_ == 64) return launch_bwd_g<E, 64, 64>(a, Hs, w, s);
+    if (a.dk_ == 64 && a.dv_ == 128) return launch_bwd_g<E, 64, 128>(a, Hs, w, s);
+    if (a.dk_ == 128 && a.dv_ == 64) return launch_bwd_g<E, 128, 64>(a, Hs, w, s);
+    return launch_bwd_g<E, 128, 128>(a, Hs, w, s);
+}
+
+// p advanced by `elems` elements of `esz` bytes (null stays null)
+template <typename P>
+P* at(P* p, size_t elems, size_t esz) {
+    using B = typename std::conditional<std::is_const<P>::value, const char, char>::type;
+    return p ? reinterpret_cast<P*>(reinterpret_cast<B*>(p) + elems * esz) : nullptr;
 }
 
 }  // namespace
@@ -945,11 +961,34 @@ size_t bwd_workspace_bytes(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t 
     return bwd_sizes(T, N, H, dk, dv).total;
 }
 
-hipError_t launch_chunk_bwd(const BwdArgs& a, void* workspace, hipStream_t stream) {
-    const BwdWs w = carve_bwd(workspace, a.T, a.N, a.H, a.dk_, a.dv_);
+int32_t bwd_head_group(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, size_t workspace_bytes) {
+    int32_t g = H;
+    while (g > 0 && bwd_sizes(T, N, g, dk, dv).total > workspace_bytes) --g;
+    return g;
+}
+
+hipError_t launch_chunk_bwd(const BwdArgs& a, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    // heads are independent: process them in the largest groups whose
+    // intermediates fit the workspace, one group after another on the stream
+    const int32_t G = bwd_head_group(a.T, a.N, a.H, a.dk_, a.dv_, workspace_bytes);
+    const BwdWs w = carve_bwd(workspace, a.T, a.N, G, a.dk_, a.dv_);
     hipError_t e = launch_chunk_map(a.cu_seqlens, a.N, a.T, w.header, w.cu, w.chunk_off, w.chunk_tab, stream);
     if (e != hipSuccess) return e;
-    return a.bf16 ? launch_bwd_e<bf16_t>(a, w, stream) : launch_bwd_e<float>(a, w, stream);
+    const size_t esz = a.bf16 ? 2 : 4;
+    for (int32_t h0 = 0; h0 < a.H; h0 += G) {
+        BwdArgs b = a;
+        b.H = a.H - h0 < G ? a.H - h0 : G;
+        const size_t hk = (size_t)h0 * a.dk_, hv = (size_t)h0 * a.dv_, hs = (size_t)h0 * a.dk_ * a.dv_;
+        const size_t hgk = a.head_gate ? (size_t)h0 : hk;
+        b.q = at(a.q, hk, esz); b.k = at(a.k, hk, esz); b.v = at(a.v, hv, esz); b.g = at(a.g, hgk, esz);
+        b.beta = at(a.beta, h0, esz); b.dO = at(a.dO, hv, esz);
+        b.dq = at(a.dq, hk, esz); b.dk = at(a.dk, hk, esz); b.dv = at(a.dv, hv, esz); b.dg = at(a.dg, hgk, esz);
+        b.dbeta = at(a.dbeta, h0, esz);
+        b.S0 = at(a.S0, hs, 4); b.dS_T = at(a.dS_T, hs, 4); b.dS0 = at(a.dS0, hs, 4);
+        e = a.bf16 ? launch_bwd_e<bf16_t>(b, a.H, w, stream) : launch_bwd_e<float>(b, a.H, w, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace kda

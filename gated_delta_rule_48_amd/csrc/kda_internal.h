@@ -93,6 +93,8 @@ struct BwdArgs {
 };
 
 size_t bwd_workspace_bytes(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv);
-hipError_t launch_chunk_bwd(const BwdArgs& a, void* workspace, hipStream_t stream);
+// The largest number of heads whose intermediates fit in workspace_bytes (0: not even one).
+int32_t bwd_head_group(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, size_t workspace_bytes);
+hipError_t launch_chunk_bwd(const BwdArgs& a, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 }  // namespace kda

@@ -224,9 +224,10 @@ kda_status kda_recurrent_step_raw(const void *q_raw, const void *k_raw,
                                   hipStream_t stream);
 
 /*
- * Bytes of device workspace kda_chunk_bwd needs for these sizes (0 if the
- * sizes are invalid or unsupported).  About 900 KB per (chunk, head) at
- * d_k = d_v = 128: every intermediate of a chunk is kept in fp32.
+ * Bytes of device workspace kda_chunk_bwd needs to process all H heads at
+ * once (0 if the sizes are invalid or unsupported).  About 900 KB per (chunk,
+ * head) at d_k = d_v = 128: every intermediate of a chunk is kept in fp32.
+ * The value for H = 1 is the least kda_chunk_bwd accepts.
  */
 size_t kda_chunk_bwd_workspace_size(int64_t T_total, int32_t N, int32_t H,
                                     int32_t d_k, int32_t d_v, kda_dtype dt,
@@ -256,9 +257,13 @@ size_t kda_chunk_bwd_workspace_size(int64_t T_total, int32_t N, int32_t H,
  *   dv                [T_total, H, d_v], type dt;  dbeta [T_total, H], type dt
  *   dS0               fp32 [N, H, d_k, d_v] or NULL (not written); an empty
  *                     sequence gives dS0 = dS_T
- *   workspace         >= kda_chunk_bwd_workspace_size() bytes, 256-byte
- *                     aligned, clobbered; kda_chunk_fwd_check accepts it too
- *                     and reports rejected cu_seqlens the same way
+ *   workspace         256-byte aligned, clobbered; at least
+ *                     kda_chunk_bwd_workspace_size(..., H = 1, ...) bytes.
+ *                     With less than the size for all H heads, the heads are
+ *                     processed in the largest groups that fit, one group
+ *                     after another on `stream` (same results, more time).
+ *                     kda_chunk_fwd_check accepts it too and reports rejected
+ *                     cu_seqlens the same way
  *
  * Alignment: every pointer to its element size.  Errors as for
  * kda_chunk_fwd.  Numerics: all arithmetic in fp32, gradients rounded once

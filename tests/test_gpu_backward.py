@@ -173,3 +173,56 @@ def test_bwd_no_tokens_passes_state_cotangent():
                         cu_seqlens=torch.zeros(N + 1, dtype=torch.int32, device="cuda"))
     torch.cuda.synchronize()
     assert np.array_equal(got[5].cpu().numpy(), dST)
+
+
+@pytest.mark.parametrize("dtype,gate", [("bf16", "channel"), ("f32", "head")])
+def test_bwd_head_groups_bit_identical(dtype, gate):
+    """A workspace for two heads processes five heads in groups of 2, 2, 1;
+    the results equal those of one pass over all heads bit for bit."""
+    d, dO, dST = _case(5, 128, 128, dtype, gate, [150, 70], seed=13)
+    full = _run(d, dtype, gate, dO, dST)
+    T = int(d["cu_seqlens"][-1])
+    small = kda.chunk_bwd_workspace_size(T, 2, 2, 128, 128, torch.bfloat16 if dtype == "bf16" else torch.float32)
+    assert small < kda.chunk_bwd_workspace_size(T, 2, 5, 128, 128)
+    x = {n: to_dev(d[n], dtype) for n in ("q", "k", "v", "g", "beta")}
+    got = kda.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], to_dev(dO, dtype),
+                        S0=torch.from_numpy(d["S0"]).cuda(), dS_T=torch.from_numpy(dST).cuda(),
+                        cu_seqlens=torch.from_numpy(d["cu_seqlens"].astype(np.int32)).cuda(),
+                        per_head_gate=(gate == "head"),
+                        workspace=torch.empty(small, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    for a, b in zip(full, got):
+        assert np.array_equal(a, to_np64(b))
+
+
+def test_bwd_1m_tokens_in_head_groups_prefix_support():
+    """The 1M-token workload (T = 1,048,576, H = 16, d = 128, bf16) through a
+    workspace for four heads (four groups of four).  dO is zero after the
+    first 256 tokens and dS_T = 0: those tokens' gradients and dS0 are the
+    256-token problem's, and every later gradient is exactly zero."""
+    cfg = synth.CONFIGS["kda_1m_bf16"]
+    T, H, dk, dv = cfg.T, cfg.H, cfg.dk, cfg.dv
+    shapes = {"q": (T, H, dk), "k": (T, H, dk), "v": (T, H, dv), "g": (T, H, dk), "beta": (T, H)}
+    dev = {n: torch.empty(s, dtype=torch.bfloat16, device="cuda") for n, s in shapes.items()}
+    first = None
+    for b, start, blk in synth.iter_token_blocks(cfg, workers=8):
+        rows = blk["q"].shape[0]
+        for n in shapes:
+            dev[n][start:start + rows].copy_(torch.from_numpy(blk[n].view(np.int16)).view(torch.bfloat16))
+        if start == 0:
+            first = blk
+    P = 256
+    dO = torch.zeros((T, H, dv), dtype=torch.bfloat16, device="cuda")
+    dO_head = synth.bf16_bits(np.random.default_rng(4040).standard_normal((P, H, dv), dtype=np.float32))
+    dO[:P].copy_(torch.from_numpy(dO_head.view(np.int16)).view(torch.bfloat16))
+    ws = torch.empty(kda.chunk_bwd_workspace_size(T, 1, 4, dk, dv), dtype=torch.uint8, device="cuda")
+    got = kda.chunk_bwd(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], dO, workspace=ws)
+    torch.cuda.synchronize()
+    for gv in got[:5]:
+        assert int(torch.count_nonzero(gv[P:])) == 0, "gradient beyond the support of dO"
+    ref = recurrence_grad(first["q"][:P], first["k"][:P], first["v"][:P], first["g"][:P], first["beta"][:P],
+                          dO_head)
+    for n_, gv, rv in zip(NAMES, [to_np64(g[:P]) for g in got[:5]] + [to_np64(got[5])], ref):
+        e = rel_err(gv, rv)
+        print(f"bwd 1m prefix {n_}={e:.2e}", flush=True)
+        assert e <= TOL["bf16"], (n_, e)
