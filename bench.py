@@ -15,7 +15,8 @@ on a bounded prefix of the same workload as `cpu_baseline`.  After the timed
 steps, the chunked backward pass (kda_chunk_bwd) over the same prefill inputs
 is timed on its own and reported under `backward`, and the pre-path
 transforms (kda_prepare_inputs on the prefill inputs, and the decode step with
-them fused in) under `prepath`.
+them fused in) under `prepath`, and the d = 64 variant of the prefill at the
+same model width (H = 64) under `variant_d64`.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-backward]
 """
@@ -189,6 +190,31 @@ def time_prepath(kda, torch, hip, x, T, H, dk, stream, S_dec, toks, steps=10):
     }
 
 
+def time_d64_variant(kda, torch, hip, stream, T=32768, H=64, steps=5):
+    """The d_k = d_v = 64 variant at the same model width (H = 64 heads of 64
+    channels, T = 32768, bf16, per-channel gate, seeded inputs of the 32K
+    recipe) through kda_chunk_fwd, timed with HIP events; reported beside the
+    d = 128 workload, not part of `value`."""
+    import synth
+    cfg = synth.small_chunk_config(H=H, dk=64, dv=64, dtype="bf16", gate="channel", gate_mu=-1.0, s0_sigma=0.0,
+                                   seed=303)
+    d = synth.chunk_inputs(cfg, lengths=[T])
+    x = {n: _to_dev(d[n], torch) for n in ("q", "k", "v", "g", "beta")}
+    o = torch.empty((T, H, 64), dtype=torch.bfloat16, device="cuda")
+    S_T = torch.empty((1, H, 64, 64), dtype=torch.float32, device="cuda")
+    ws = torch.empty(kda.chunk_fwd_workspace_size(T, 1, H, 64, 64), dtype=torch.uint8, device="cuda")
+    ev = Events(hip, steps + 1)
+    for _ in range(2):
+        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], out=o, S_T=S_T, workspace=ws)
+    ev.record(0, stream)
+    for i in range(steps):
+        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], out=o, S_T=S_T, workspace=ws)
+        ev.record(i + 1, stream)
+    torch.cuda.synchronize()
+    t = float(np.median([ev.ms(i, i + 1) for i in range(steps)]))
+    return {"what": f"kda_chunk_fwd, T={T}, H={H}, d_k=d_v=64, bf16", "ms": t, "tokens_per_s": T / (t * 1e-3)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -197,6 +223,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-prefix", type=int, default=32768)
     ap.add_argument("--no-backward", action="store_true", help="skip timing the chunked backward pass")
+    ap.add_argument("--no-variants", action="store_true", help="skip timing the d = 64 variant")
     ap.add_argument("--backward-steps", type=int, default=5)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one device-to-device copy of exactly 1 GiB before the timed steps, so that a "
@@ -286,6 +313,7 @@ def main():
     t_b2b = float(np.median([ev_b2b.ms(i, i + 1) for i in range(n_b2b)]))
 
     prepath = time_prepath(kda, torch, hip, x, T, H, dk, stream, S_dec, toks)
+    d64 = None if args.no_variants else time_d64_variant(kda, torch, hip, stream)
     bwd = None if args.no_backward else time_backward(kda, torch, hip, x, d, T, H, dk, dv, stream,
                                                       steps=args.backward_steps)
 
@@ -344,6 +372,8 @@ def main():
                           "TFLOP_per_s": path_tflops, "frac_bf16_mfma_peak": path_tflops / BF16_MFMA_PEAK_TFLOPS},
     }
     res["prepath"] = prepath
+    if d64 is not None:
+        res["variant_d64"] = d64
     if bwd is not None:
         res["backward"] = bwd
     if not args.no_cpu_baseline:

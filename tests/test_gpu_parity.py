@@ -314,6 +314,18 @@ def test_config_32k_bf16():
     print("32k errs", _assert_close("o", o, o_ref, 1e-2), _assert_close("S_T", S, S_ref, 1e-2))
 
 
+def test_variant_d64_32k_full_width():
+    """The d = 64 variant at the same model width as the 32K workload:
+    T=32768, H=64, d_k=d_v=64, bf16, per-channel gate from N(-1,1), S0 = 0."""
+    _announce("variant d64 32k x 64 heads")
+    cfg = synth.small_chunk_config(H=64, dk=64, dv=64, dtype="bf16", gate="channel", gate_mu=-1.0, s0_sigma=0.0,
+                                   seed=303)
+    d = synth.chunk_inputs(cfg, lengths=[32768])
+    o, S = _run_chunk(d, "bf16", "channel")
+    o_ref, S_ref = _oracle_chunk(d, "channel")
+    print("d64 errs", _assert_close("o", o, o_ref, 1e-2), _assert_close("S_T", S, S_ref, 1e-2))
+
+
 def test_config_1m_bf16():
     """B=1, T=1,048,576, H=16, d=128, per-channel gate from N(-1,1): o at 4096
     seeded positions and the full S_T.  The inputs are drawn block by block
