@@ -84,24 +84,25 @@ __device__ __forceinline__ float ld(const E* p, int64_t i) {
 //   acc(m, n) += sum_k a(m, k) b(k, n),   m < 64, n < N, k < K.
 // a and b are element loaders; A_KFAST / B_NFAST say which index is the
 // contiguous one in memory, so that the staging loads are coalesced.  Tiles
-// of 16 k-steps pass through LDS (k-major); thread (ty, tx) = (tid / 16,
-// tid % 16) owns rows 4ty..4ty+3 and columns tx*N/16 .. tx*N/16 + N/16 - 1.
-// The next tile is fetched into registers while the current one is
-// multiplied.  Every thread of the workgroup must call it (it contains
+// of 16 k-steps pass through LDS (k-major) and are multiplied on the fp32
+// matrix cores (16 x 16 x 4 per instruction): wave w owns rows 16w..16w+15,
+// and lane (g, r) = (lane / 16, lane % 16) holds rows 16w + 4g + i (i < 4) of
+// column 16j + r of every 16-column tile j.  The next tile is fetched into
+// registers while the current one is multiplied.  Every thread of the workgroup must call it (it contains
 // barriers); whatever the loaders read must be complete before the call.
 constexpr int kGemmLds = 16 * (64 + 4) + 16 * (128 + 4);  // floats
 
 template <int N>
 struct Acc {
-    float v[4][N / 16];
+    f32x4 t[N / 16];  // t[j][i]: row row(i), column col(j)
     __device__ __forceinline__ void zero() {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < N / 16; ++j) v[i][j] = 0.f;
+        for (int j = 0; j < N / 16; ++j) t[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    __device__ __forceinline__ static int row(int i) { return (threadIdx.x / 16) * 4 + i; }
-    __device__ __forceinline__ static int col(int j) { return (threadIdx.x % 16) * (N / 16) + j; }
+    __device__ __forceinline__ static int row(int i) {
+        return 16 * (threadIdx.x / 64) + 4 * ((threadIdx.x % 64) / 16) + i;
+    }
+    __device__ __forceinline__ static int col(int j) { return 16 * j + threadIdx.x % 16; }
 };
 
 template <int N, int K, bool A_KFAST, bool B_NFAST, typename LA, typename LB>
@@ -110,7 +111,7 @@ __device__ __forceinline__ void gemm64(Acc<N>& acc, LA la, LB lb, float* lds) {
     constexpr int RA = M * KT / kBwdThreads, RB = N * KT / kBwdThreads;
     float* sA = lds;
     float* sB = lds + KT * SA;
-    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+    const int tid = threadIdx.x, wv = tid / 64, lg = (tid % 64) / 16, lr = tid % 16;
     // element r of this thread's share of a tile
     auto a_mk = [&](int r, int& m, int& kk) {
         const int idx = tid + r * kBwdThreads;
@@ -155,20 +156,14 @@ __device__ __forceinline__ void gemm64(Acc<N>& acc, LA la, LB lb, float* lds) {
         // stay in flight across these barriers
         lds_barrier();
         if (k0 + KT < K) fetch(k0 + KT);
-#pragma unroll 4
-        for (int kk = 0; kk < KT; ++kk) {
-            const float4 a = *reinterpret_cast<const float4*>(sA + kk * SA + ty * 4);
-            float b[NT];
 #pragma unroll
-            for (int j = 0; j < NT; j += 4) {
-                const float4 x = *reinterpret_cast<const float4*>(sB + kk * SB + tx * NT + j);
-                b[j] = x.x; b[j + 1] = x.y; b[j + 2] = x.z; b[j + 3] = x.w;
+        for (int ks = 0; ks < KT; ks += 4) {
+            const float a = sA[(ks + lg) * SA + 16 * wv + lr];
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                const float b = sB[(ks + lg) * SB + 16 * j + lr];
+                acc.t[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc.t[j], 0, 0, 0);
             }
-            const float av[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < NT; ++j) acc.v[i][j] += av[i] * b[j];
         }
         lds_barrier();
     }
@@ -260,9 +255,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const E* __restri
 #pragma unroll
             for (int b = 0; b < C / 16; ++b) {
                 const int t = Acc<C>::row(a), i = Acc<C>::col(b);
-                const float mv = (i < t && t < n) ? am.v[a][b] : 0.f;
+                const float mv = (i < t && t < n) ? am.t[b][a] : 0.f;
                 w.M[oCC + (size_t)t * C + i] = mv;
-                w.P[oCC + (size_t)t * C + i] = (i <= t && t < n) ? ap.v[a][b] : 0.f;
+                w.P[oCC + (size_t)t * C + i] = (i <= t && t < n) ? ap.t[b][a] : 0.f;
                 sA[t][i] = sbeta[t] * mv;
             }
     }
@@ -302,7 +297,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const E* __restri
         for (int a = 0; a < 4; ++a)
 #pragma unroll
             for (int b = 0; b < DK / 16; ++b)
-                w.W[oCK + (size_t)Acc<DK>::row(a) * DK + Acc<DK>::col(b)] = aw.v[a][b];
+                w.W[oCK + (size_t)Acc<DK>::row(a) * DK + Acc<DK>::col(b)] = aw.t[b][a];
         Acc<DV> au;
         au.zero();
         gemm64<DV, C, true, false>(au, [&](int t, int i) { return sT[t][i]; },
@@ -311,7 +306,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const E* __restri
         for (int a = 0; a < 4; ++a)
 #pragma unroll
             for (int b = 0; b < DV / 16; ++b)
-                w.Up[oCV + (size_t)Acc<DV>::row(a) * DV + Acc<DV>::col(b)] = au.v[a][b];
+                w.Up[oCV + (size_t)Acc<DV>::row(a) * DV + Acc<DV>::col(b)] = au.t[b][a];
     }
 }
 
@@ -636,13 +631,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
     auto dOat = [&](int t, int x) -> float { return t < n ? ld(dO, ((t0 + t) * Hs + h) * DV + x) : 0.f; };
     // store a 64 x N accumulator tile (times s) to dst (row stride N), rows >= n as zero
     auto put = [&](auto& acc, float* dst, int N, float s) {
-        constexpr int NT = sizeof(acc.v[0]) / sizeof(float);
+        constexpr int NT = sizeof(acc.t) / sizeof(acc.t[0]);
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
             for (int b = 0; b < NT; ++b) {
-                const int t = (tid / 16) * 4 + a, c = (tid % 16) * NT + b;
-                dst[(size_t)t * N + c] = t < n ? s * acc.v[a][b] : 0.f;
+                const int t = 16 * (tid / 64) + 4 * ((tid % 64) / 16) + a, c = 16 * b + tid % 16;
+                dst[(size_t)t * N + c] = t < n ? s * acc.t[b][a] : 0.f;
             }
     };
 
@@ -669,7 +664,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
 #pragma unroll
             for (int b = 0; b < C / 16; ++b) {
                 const int t = Acc<C>::row(a), i = Acc<C>::col(b);
-                w.dP[oCC + (size_t)t * C + i] = (i <= t && t < n) ? ap.v[a][b] : 0.f;
+                w.dP[oCC + (size_t)t * C + i] = (i <= t && t < n) ? ap.t[b][a] : 0.f;
             }
     }
     for (int c = tid; c < DK; c += kBwdThreads) {
@@ -697,7 +692,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
 #pragma unroll
             for (int b = 0; b < C / 16; ++b) {
                 const int t = Acc<C>::row(a), i = Acc<C>::col(b);
-                w.dT[oCC + (size_t)t * C + i] = (i < t && t < n) ? at.v[a][b] : 0.f;
+                w.dT[oCC + (size_t)t * C + i] = (i < t && t < n) ? at.t[b][a] : 0.f;
             }
         Acc<DK> ax;
         ax.zero();
@@ -724,7 +719,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
 #pragma unroll
             for (int b = 0; b < C / 16; ++b) {
                 const int r = Acc<C>::row(a), i = Acc<C>::col(b);
-                w.Y[oCC + (size_t)r * C + i] = (i < r && r < n) ? ay.v[a][b] : 0.f;
+                w.Y[oCC + (size_t)r * C + i] = (i < r && r < n) ? ay.t[b][a] : 0.f;
             }
     }
     __syncthreads();
@@ -741,7 +736,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
 #pragma unroll
             for (int b = 0; b < C / 16; ++b) {
                 const int t = Acc<C>::row(a), i = Acc<C>::col(b);
-                w.dA[oCC + (size_t)t * C + i] = (i < t && t < n) ? -aa.v[a][b] : 0.f;
+                w.dA[oCC + (size_t)t * C + i] = (i < t && t < n) ? -aa.t[b][a] : 0.f;
             }
     }
     }  // PH == 1
@@ -783,7 +778,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
                 if (t >= n) continue;
                 const size_t j = oCK + (size_t)t * DK + c;
                 const size_t jt = (size_t)t * DK + c;
-                const float dKr = sbeta[t] * dKr_s[jt], dKi = acc.v[a][b], dQr = dQr_s[jt];
+                const float dKr = sbeta[t] * dKr_s[jt], dKi = acc.t[b][a], dQr = dQr_s[jt];
                 const float dKG = sbeta[t] * w.dXw[j];
                 const float dQG = w.dQG[j], dKd = w.dKd[j];
                 const float bb = w.B[j], r = sr[c], bl = sbl[c];
