@@ -62,10 +62,10 @@ struct BwdWs {
     int2* chunk_tab;
     // [C][DK]
     float *B, *QG, *KG, *Kd, *Qr, *Kr, *Ki, *W, *dW, *dQG, *dKd, *dXw;
-    // [DK][C]
-    float *KiT, *XwT;
-    // [C][DV] (XuT is stored [DV][C])
-    float *Up, *U, *dU, *dXu, *XuT;
+    // [C][DK] scratch of the last local phase (dKr, dQr)
+    float *dKr, *dQr;
+    // [C][DV]
+    float *Up, *U, *dU, *dXu;
     // [C][C]
     float *M, *P, *T, *TT, *dP, *dT, *Y, *dA;
     // [DK]
@@ -229,27 +229,22 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const E* __restri
         w.Qr[i] = qv * er;
         w.Kr[i] = kv * er;
         w.Ki[i] = kv * eir;
-        w.KiT[oCK + (size_t)c * C + t] = kv * eir;
-        w.XwT[oCK + (size_t)c * C + t] = sbeta[t] * kv * e;
-    }
-    for (int idx = tid; idx < C * DV; idx += kBwdThreads) {
-        const int t = idx / DV, c = idx % DV;
-        const float vv = t < n ? ld(v, ((t0 + t) * Hs + h) * DV + c) : 0.f;
-        w.XuT[oCV + (size_t)c * C + t] = sbeta[t] * vv;
     }
     __syncthreads();
+    // v of row i scaled by beta_i (zero past the chunk's end)
+    auto xu = [&](int i, int x) -> float { return i < n ? sbeta[i] * ld(v, ((t0 + i) * Hs + h) * DV + x) : 0.f; };
     // M = strict_tril(Kr Ki^T) and P = tril(Qr Ki^T)
     {
         const float* Kr = w.Kr + oCK;
         const float* Qr = w.Qr + oCK;
-        const float* KiT = w.KiT + oCK;
+        const float* Ki = w.Ki + oCK;
         Acc<C> am, ap;
         am.zero();
         ap.zero();
-        gemm64<C, DK, true, true>(am, [&](int t, int c) { return Kr[(size_t)t * DK + c]; },
-                                  [&](int c, int i) { return KiT[(size_t)c * C + i]; }, lds);
-        gemm64<C, DK, true, true>(ap, [&](int t, int c) { return Qr[(size_t)t * DK + c]; },
-                                  [&](int c, int i) { return KiT[(size_t)c * C + i]; }, lds);
+        gemm64<C, DK, true, false>(am, [&](int t, int c) { return Kr[(size_t)t * DK + c]; },
+                                   [&](int c, int i) { return Ki[(size_t)i * DK + c]; }, lds);
+        gemm64<C, DK, true, false>(ap, [&](int t, int c) { return Qr[(size_t)t * DK + c]; },
+                                   [&](int c, int i) { return Ki[(size_t)i * DK + c]; }, lds);
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -287,12 +282,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const E* __restri
     }
     // W = T Xw (Xw = diag(beta) KG),  U' = T Xu (Xu = diag(beta) V)
     {
-        const float* XwT = w.XwT + oCK;
-        const float* XuT = w.XuT + oCV;
+        const float* KG = w.KG + oCK;
         Acc<DK> aw;
         aw.zero();
-        gemm64<DK, C, true, false>(aw, [&](int t, int i) { return sT[t][i]; },
-                                   [&](int i, int c) { return XwT[(size_t)c * C + i]; }, lds);
+        gemm64<DK, C, true, true>(aw, [&](int t, int i) { return sT[t][i]; },
+                                  [&](int i, int c) { return sbeta[i] * KG[(size_t)i * DK + c]; }, lds);
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -300,8 +294,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const E* __restri
                 w.W[oCK + (size_t)Acc<DK>::row(a) * DK + Acc<DK>::col(b)] = aw.t[b][a];
         Acc<DV> au;
         au.zero();
-        gemm64<DV, C, true, false>(au, [&](int t, int i) { return sT[t][i]; },
-                                   [&](int i, int c) { return XuT[(size_t)c * C + i]; }, lds);
+        gemm64<DV, C, true, true>(au, [&](int t, int i) { return sT[t][i]; }, xu, lds);
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -623,6 +616,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
         sr[tid] = w.B[oCK + (size_t)((n - 1) / 2) * DK + tid];
         sbl[tid] = w.B[oCK + (size_t)(n - 1) * DK + tid];
     }
+    __syncthreads();  // sbeta, sr, sbl are read by every thread (also inside block-product loaders)
     const float* Sm = w.S + oKV;
     const float* dSn = w.dSn + oKV;
     const float* Um = w.U + oCV;
@@ -679,14 +673,16 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
     // phase 2: dT = strict_tril(dW Xw^T + dU Xu^T), dXw = T^T dW, dXu = T^T dU
     {
         const float* dW = w.dW + oCK;
-        const float* XwT = w.XwT + oCK;
-        const float* XuT = w.XuT + oCV;
+        const float* KG = w.KG + oCK;
         Acc<C> at;
         at.zero();
-        gemm64<C, DK, true, true>(at, [&](int t, int c) { return dW[(size_t)t * DK + c]; },
-                                  [&](int c, int i) { return XwT[(size_t)c * C + i]; }, lds);
-        gemm64<C, DV, true, true>(at, [&](int t, int x) { return dUm[(size_t)t * DV + x]; },
-                                  [&](int x, int i) { return XuT[(size_t)x * C + i]; }, lds);
+        gemm64<C, DK, true, false>(at, [&](int t, int c) { return dW[(size_t)t * DK + c]; },
+                                   [&](int c, int i) { return sbeta[i] * KG[(size_t)i * DK + c]; }, lds);
+        gemm64<C, DV, true, false>(at, [&](int t, int x) { return dUm[(size_t)t * DV + x]; },
+                                   [&](int x, int i) {
+                                       return i < n ? sbeta[i] * ld(v, ((t0 + i) * Hs + h) * DV + x) : 0.f;
+                                   },
+                                   lds);
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -751,10 +747,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
         const float* Ki = w.Ki + oCK;
         const float* Kr = w.Kr + oCK;
         const float* Qr = w.Qr + oCK;
-        // one accumulator tile at a time: dKr and dQr are parked in KiT and XwT
-        // (neither is read again by this chunk)
-        float* dKr_s = w.KiT + oCK;
-        float* dQr_s = w.XwT + oCK;
+        // one accumulator tile at a time: dKr and dQr are parked in the workspace
+        float* dKr_s = w.dKr + oCK;
+        float* dQr_s = w.dQr + oCK;
         Acc<DK> acc;
         acc.zero();
         gemm64<DK, C, true, true>(acc, [&](int t, int i) { return dA[(size_t)t * C + i]; },
@@ -858,7 +853,7 @@ BwdSizes bwd_sizes(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv) {
     s.cc = al256(slots * C * C * 4);
     s.k = al256(slots * dk * 4);
     s.kv = al256(slots * dk * dv * 4);
-    s.total = s.head + 14 * s.ck + 5 * s.cv + 8 * s.cc + 2 * s.k + 2 * s.kv;
+    s.total = s.head + 14 * s.ck + 4 * s.cv + 8 * s.cc + 2 * s.k + 2 * s.kv;
     return s;
 }
 
@@ -872,9 +867,9 @@ BwdWs carve_bwd(void* base, int64_t T, int32_t N, int32_t H, int32_t dk, int32_t
     w.chunk_tab = reinterpret_cast<int2*>(p); p += al256((size_t)max_chunks_for(T, N) * sizeof(int2));
     auto take = [&](size_t bytes) { float* f = reinterpret_cast<float*>(p); p += bytes; return f; };
     float** ck[] = {&w.B, &w.QG, &w.KG, &w.Kd, &w.Qr, &w.Kr, &w.Ki, &w.W, &w.dW, &w.dQG, &w.dKd, &w.dXw,
-                    &w.KiT, &w.XwT};
+                    &w.dKr, &w.dQr};
     for (float** f : ck) *f = take(s.ck);
-    float** cv[] = {&w.Up, &w.U, &w.dU, &w.dXu, &w.XuT};
+    float** cv[] = {&w.Up, &w.U, &w.dU, &w.dXu};
     for (float** f : cv) *f = take(s.cv);
     float** cc[] = {&w.M, &w.P, &w.T, &w.TT, &w.dP, &w.dT, &w.Y, &w.dA};
     for (float** f : cc) *f = take(s.cc);
