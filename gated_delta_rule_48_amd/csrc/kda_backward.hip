@@ -305,11 +305,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const E* __restri
 
 // ---------------------------------------------------------------------------
 // The two walks run one workgroup per (sequence, head, 16-column slice of
-// d_v).  Threads own register tiles: (rg, v) = (tid / 16, tid % 16) computes
-// rows R*rg .. R*rg + R-1 of column v.  A chunk's operands sit in LDS
-// (rows padded by 4 floats); the next ones are loaded into registers while the
-// current chunk is computed and written to LDS afterwards.  The waves share
-// only LDS, so the barriers order LDS alone and leave those loads in flight.
+// d_v); their products run on the fp32 matrix cores (layout at mfma_tile).
+// A chunk's operands sit in LDS (rows padded by 4 floats); the next ones are
+// loaded into registers while the current chunk is computed and written to
+// LDS afterwards.  The waves share only LDS, so the barriers order LDS alone
+// and leave those loads in flight.
 
 // Load a C x WIDTH fp32 block (row-major, 16-byte aligned) into registers:
 // this thread's share, C * WIDTH / 1024 float4; then write it to LDS rows of
@@ -333,35 +333,16 @@ __device__ __forceinline__ void block_store(const f32x4 (&r)[block_regs<WIDTH>()
     }
 }
 
-// out[t] (t = 4 rows of this thread) += sum_k X[t][k] y[k], X rows in LDS
-// (stride SX), y a column of a [K][16] LDS block.
-template <int K, int SX>
-__device__ __forceinline__ void rows4_dot(float (&out)[4], const float* X, int t0, const float* y, int v) {
+// Matrix-core layout of the walks (v_mfma_f32_16x16x4f32): wave wv owns
+// 16-row tiles and lane (lg, lr) = (lane / 16, lane % 16) holds rows 4 lg + i
+// (i < 4) of a tile in column lr.  acc += sum over k < K of A(r, k) B(k, lr),
+// where a(k) reads A at the lane's row r = lr of the tile and b(k) reads
+// B(k, lr); each instruction takes k = k0 + lg.
+template <int K, typename FA, typename FB>
+__device__ __forceinline__ f32x4 mfma_tile(f32x4 acc, FA a, FB b, int lg) {
 #pragma unroll 4
-    for (int k = 0; k < K; k += 4) {
-        const float y0 = y[(k + 0) * 16 + v], y1 = y[(k + 1) * 16 + v], y2 = y[(k + 2) * 16 + v],
-                    y3 = y[(k + 3) * 16 + v];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float4 x = *reinterpret_cast<const float4*>(X + (t0 + i) * SX + k);
-            out[i] += x.x * y0 + x.y * y1 + x.z * y2 + x.w * y3;
-        }
-    }
-}
-
-// out[i] += sum_t X[t][c0 + i] y[t], i < 8: X columns in LDS (stride SX), y a
-// column of a [C][16] LDS block; s scales X.
-template <int SX>
-__device__ __forceinline__ void cols8_dot(float (&out)[8], const float* X, int c0, const float* y, int v,
-                                          float s) {
-#pragma unroll 4
-    for (int t = 0; t < C; ++t) {
-        const float yt = s * y[t * 16 + v];
-        const float4 a = *reinterpret_cast<const float4*>(X + t * SX + c0);
-        const float4 b = *reinterpret_cast<const float4*>(X + t * SX + c0 + 4);
-        out[0] += a.x * yt; out[1] += a.y * yt; out[2] += a.z * yt; out[3] += a.w * yt;
-        out[4] += b.x * yt; out[5] += b.y * yt; out[6] += b.z * yt; out[7] += b.w * yt;
-    }
+    for (int k0 = 0; k0 < K; k0 += 4) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a(k0 + lg), b(k0 + lg), acc, 0, 0, 0);
+    return acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -380,7 +361,7 @@ template <int DK, int DV>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_state_walk_kernel(int32_t H, int32_t Hs, const float* __restrict__ S0,
                                                                      BwdWs w) {
     using L = StateWalkLds<DK, DV>;
-    constexpr int NS = DV / 16, SK = L::SK, RS = DK / 16;  // rows of S per thread
+    constexpr int NS = DV / 16, SK = L::SK, TPW = DK / 64, RS = 4 * TPW;  // 16-row tiles of S per wave
     extern __shared__ __align__(16) float smem[];
     float* sW = smem + L::W;    // [C][SK]
     float* sKd = smem + L::Kd;  // [C][SK]
@@ -391,14 +372,15 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
     const int h = nh % H;
     const int seq = nh / H;
     if (w.header->bad_seqlens) return;
-    const int tid = threadIdx.x, rg = tid / 16, v = tid % 16;
-    const int col = sl * 16 + v;
+    const int tid = threadIdx.x, wv = tid / 64, lg = (tid % 64) / 16, lr = tid % 16;
+    const int col = sl * 16 + lr;
+    const int t0 = 16 * wv + 4 * lg;  // this lane's rows of U: t0 .. t0 + 3
+    auto srow = [&](int i) { return 16 * (wv * TPW + i / 4) + 4 * lg + i % 4; };  // rows of S
     const int c0 = w.chunk_off[seq], c1 = w.chunk_off[seq + 1];
-    // this thread's rows of S stay in registers; sS mirrors them for the U step
+    // this lane's rows of S stay in registers; sS mirrors them for the U step
     float S[RS];
 #pragma unroll
-    for (int i = 0; i < RS; ++i)
-        S[i] = S0 ? S0[(((size_t)seq * Hs + h) * DK + rg * RS + i) * DV + col] : 0.f;
+    for (int i = 0; i < RS; ++i) S[i] = S0 ? S0[(((size_t)seq * Hs + h) * DK + srow(i)) * DV + col] : 0.f;
     f32x4 rW[block_regs<DK>()], rK[block_regs<DK>()];
     if (c0 < c1) {
         const size_t slot = (size_t)c0 * H + h;
@@ -412,46 +394,42 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
         block_store<DK>(rK, sKd, SK);
 #pragma unroll
         for (int i = 0; i < RS; ++i) {
-            sS[(rg * RS + i) * 16 + v] = S[i];
-            w.S[oKV + (size_t)(rg * RS + i) * DV + col] = S[i];
+            sS[srow(i) * 16 + lr] = S[i];
+            w.S[oKV + (size_t)srow(i) * DV + col] = S[i];
         }
         float gn[RS];
 #pragma unroll
-        for (int i = 0; i < RS; ++i) gn[i] = w.Gn[slot * DK + rg * RS + i];
+        for (int i = 0; i < RS; ++i) gn[i] = w.Gn[slot * DK + srow(i)];
         float up[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) up[i] = w.Up[oCV + (size_t)(rg * 4 + i) * DV + col];
+        for (int i = 0; i < 4; ++i) up[i] = w.Up[oCV + (size_t)(t0 + i) * DV + col];
         lds_barrier();
         if (ch + 1 < c1) {  // next chunk's operands, in flight during this one
             const size_t nslot = slot + H;
             block_load<DK>(rW, w.W + nslot * C * DK);
             block_load<DK>(rK, w.Kd + nslot * C * DK);
         }
-        // U = U' - W S (rows 4rg..4rg+3)
-        float u[4] = {0.f, 0.f, 0.f, 0.f};
-        rows4_dot<DK, SK>(u, sW, rg * 4, sS, v);
+        // U = U' - W S (this wave's 16 rows)
+        const f32x4 ws = mfma_tile<DK>(f32x4{0.f, 0.f, 0.f, 0.f},
+                                       [&](int k) { return sW[(16 * wv + lr) * SK + k]; },
+                                       [&](int k) { return sS[k * 16 + lr]; }, lg);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float x = up[i] - u[i];
-            sU[(rg * 4 + i) * 16 + v] = x;
-            w.U[oCV + (size_t)(rg * 4 + i) * DV + col] = x;
+            const float x = up[i] - ws[i];
+            sU[(t0 + i) * 16 + lr] = x;
+            w.U[oCV + (size_t)(t0 + i) * DV + col] = x;
         }
         lds_barrier();
-        // S <- Diag(Gn) S + Kd^T U (rows RS*rg ..)
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if constexpr (RS == 8) {
-            cols8_dot<SK>(acc, sKd, rg * 8, sU, v, 1.f);
-        } else {
-            // d_k = 64: four rows per thread, read as the first half of eight
-#pragma unroll 4
-            for (int t = 0; t < C; ++t) {
-                const float yt = sU[t * 16 + v];
-                const float4 a = *reinterpret_cast<const float4*>(sKd + t * SK + rg * 4);
-                acc[0] += a.x * yt; acc[1] += a.y * yt; acc[2] += a.z * yt; acc[3] += a.w * yt;
-            }
-        }
+        // S <- Diag(Gn) S + Kd^T U (this wave's TPW tiles of rows)
 #pragma unroll
-        for (int i = 0; i < RS; ++i) S[i] = gn[i] * S[i] + acc[i];
+        for (int tt = 0; tt < TPW; ++tt) {
+            const int m0 = 16 * (wv * TPW + tt);
+            const f32x4 a = mfma_tile<C>(f32x4{0.f, 0.f, 0.f, 0.f},
+                                         [&](int k) { return sKd[k * SK + m0 + lr]; },
+                                         [&](int k) { return sU[k * 16 + lr]; }, lg);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[4 * tt + i] = gn[4 * tt + i] * S[4 * tt + i] + a[i];
+        }
         lds_barrier();
     }
 }
@@ -472,7 +450,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
                                                                       const float* __restrict__ dST,
                                                                       float* __restrict__ dS0, BwdWs w) {
     using L = DStateWalkLds<DK, DV>;
-    constexpr int NS = DV / 16, SK = L::SK, SC = L::SC, RS = DK / 16;
+    constexpr int NS = DV / 16, SK = L::SK, SC = L::SC, TPW = DK / 64, RS = 4 * TPW;
     extern __shared__ __align__(16) float smem[];
     float* sP = smem + L::P;    // [C][SC]
     float* sKd = smem + L::Kd;  // [C][SK]
@@ -486,19 +464,20 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
     const int h = nh % H;
     const int seq = nh / H;
     if (w.header->bad_seqlens) return;
-    const int tid = threadIdx.x, rg = tid / 16, v = tid % 16;
-    const int col = sl * 16 + v;
+    const int tid = threadIdx.x, wv = tid / 64, lg = (tid % 64) / 16, lr = tid % 16;
+    const int col = sl * 16 + lr;
+    const int t0 = 16 * wv + 4 * lg;  // this lane's rows of dU (and of dO it loads)
+    auto srow = [&](int i) { return 16 * (wv * TPW + i / 4) + 4 * lg + i % 4; };  // rows of dS
     const int c0 = w.chunk_off[seq], c1 = w.chunk_off[seq + 1];
     float dS[RS];
 #pragma unroll
-    for (int i = 0; i < RS; ++i)
-        dS[i] = dST ? dST[(((size_t)seq * Hs + h) * DK + rg * RS + i) * DV + col] : 0.f;
-    // dO of a chunk for this thread's 4 rows of column `col`
+    for (int i = 0; i < RS; ++i) dS[i] = dST ? dST[(((size_t)seq * Hs + h) * DK + srow(i)) * DV + col] : 0.f;
+    // dO of a chunk for this lane's 4 rows of column `col`
     auto load_dO = [&](int ch, float (&r)[4]) {
         const int2 ct = w.chunk_tab[ch];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int t = rg * 4 + i;
+            const int t = t0 + i;
             r[i] = t < ct.y ? ld(dO, (((int64_t)ct.x + t) * Hs + h) * DV + col) : 0.f;
         }
     };
@@ -513,36 +492,33 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
         block_store<C>(rP, sP, SC);
         block_store<DK>(rK, sKd, SK);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sdO[(rg * 4 + i) * 16 + v] = rO[i];
+        for (int i = 0; i < 4; ++i) sdO[(t0 + i) * 16 + lr] = rO[i];
     }
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     for (int ch = c1 - 1; ch >= c0; --ch) {
         const size_t slot = (size_t)ch * H + h;
         const size_t oCK = slot * C * DK, oCV = slot * C * DV, oKV = slot * DK * DV;
         float* dOc = sdO + buf * C * 16;
 #pragma unroll
         for (int i = 0; i < RS; ++i) {
-            sdS[(rg * RS + i) * 16 + v] = dS[i];
-            w.dSn[oKV + (size_t)(rg * RS + i) * DV + col] = dS[i];
+            sdS[srow(i) * 16 + lr] = dS[i];
+            w.dSn[oKV + (size_t)srow(i) * DV + col] = dS[i];
         }
         float gn[RS];
 #pragma unroll
-        for (int i = 0; i < RS; ++i) gn[i] = w.Gn[slot * DK + rg * RS + i];
+        for (int i = 0; i < RS; ++i) gn[i] = w.Gn[slot * DK + srow(i)];
         lds_barrier();
         block_load<DK>(rQ, w.QG + oCK);  // this chunk's QG and W, in flight during dU
         block_load<DK>(rW, w.W + oCK);
-        // dU = P^T dO + Kd dS_next (rows 4rg..4rg+3)
-        float du[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-        for (int i = 0; i < C; ++i) {
-            const float y = dOc[i * 16 + v];
-            const float4 p = *reinterpret_cast<const float4*>(sP + i * SC + rg * 4);  // P[i][t..t+3]
-            du[0] += p.x * y; du[1] += p.y * y; du[2] += p.z * y; du[3] += p.w * y;
-        }
-        rows4_dot<DK, SK>(du, sKd, rg * 4, sdS, v);
+        // dU = P^T dO + Kd dS_next (this wave's 16 rows)
+        f32x4 du = mfma_tile<C>(zero, [&](int k) { return sP[k * SC + 16 * wv + lr]; },
+                                [&](int k) { return dOc[k * 16 + lr]; }, lg);
+        du = mfma_tile<DK>(du, [&](int k) { return sKd[(16 * wv + lr) * SK + k]; },
+                           [&](int k) { return sdS[k * 16 + lr]; }, lg);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            sdU[(rg * 4 + i) * 16 + v] = du[i];
-            w.dU[oCV + (size_t)(rg * 4 + i) * DV + col] = du[i];
+            sdU[(t0 + i) * 16 + lr] = du[i];
+            w.dU[oCV + (size_t)(t0 + i) * DV + col] = du[i];
         }
         block_store<DK>(rQ, sQG, SK);
         block_store<DK>(rW, sW, SK);
@@ -553,36 +529,30 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
             block_load<DK>(rK, w.Kd + pslot * C * DK);
             load_dO(ch - 1, rO);
         }
-        // dS = Diag(Gn) dS_next + QG^T dO - W^T dU (rows RS*rg ..)
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if constexpr (RS == 8) {
-            cols8_dot<SK>(acc, sQG, rg * 8, dOc, v, 1.f);
-            cols8_dot<SK>(acc, sW, rg * 8, sdU, v, -1.f);
-        } else {
-#pragma unroll 4
-            for (int t = 0; t < C; ++t) {
-                const float yo = dOc[t * 16 + v], yu = sdU[t * 16 + v];
-                const float4 a = *reinterpret_cast<const float4*>(sQG + t * SK + rg * 4);
-                const float4 b = *reinterpret_cast<const float4*>(sW + t * SK + rg * 4);
-                acc[0] += a.x * yo - b.x * yu; acc[1] += a.y * yo - b.y * yu;
-                acc[2] += a.z * yo - b.z * yu; acc[3] += a.w * yo - b.w * yu;
-            }
-        }
+        // dS = Diag(Gn) dS_next + QG^T dO - W^T dU (this wave's TPW tiles of rows)
 #pragma unroll
-        for (int i = 0; i < RS; ++i) dS[i] = gn[i] * dS[i] + acc[i];
+        for (int tt = 0; tt < TPW; ++tt) {
+            const int m0 = 16 * (wv * TPW + tt);
+            f32x4 a = mfma_tile<C>(zero, [&](int k) { return sQG[k * SK + m0 + lr]; },
+                                   [&](int k) { return dOc[k * 16 + lr]; }, lg);
+            a = mfma_tile<C>(a, [&](int k) { return -sW[k * SK + m0 + lr]; },
+                             [&](int k) { return sdU[k * 16 + lr]; }, lg);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dS[4 * tt + i] = gn[4 * tt + i] * dS[4 * tt + i] + a[i];
+        }
         if (ch > c0) {
             block_store<C>(rP, sP, SC);
             block_store<DK>(rK, sKd, SK);
             float* dOn = sdO + (buf ^ 1) * C * 16;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dOn[(rg * 4 + i) * 16 + v] = rO[i];
+            for (int i = 0; i < 4; ++i) dOn[(t0 + i) * 16 + lr] = rO[i];
         }
         buf ^= 1;
         lds_barrier();
     }
     if (dS0) {
 #pragma unroll
-        for (int i = 0; i < RS; ++i) dS0[(((size_t)seq * Hs + h) * DK + rg * RS + i) * DV + col] = dS[i];
+        for (int i = 0; i < RS; ++i) dS0[(((size_t)seq * Hs + h) * DK + srow(i)) * DV + col] = dS[i];
     }
 }
 
