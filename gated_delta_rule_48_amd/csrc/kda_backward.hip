@@ -67,7 +67,7 @@ struct BwdWs {
     // [C][DV]
     float *Up, *U, *dU, *dXu;
     // [C][C]
-    float *M, *P, *T, *TT, *dP, *dT, *Y, *dA;
+    float *M, *P, *T, *dP, *dT, *Y, *dA;
     // [DK]
     float *Gn, *dGn;
     // [DK][DV]: chunk start state and the state cotangent after the chunk
@@ -278,7 +278,6 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const E* __restri
     for (int idx = tid; idx < C * C; idx += kBwdThreads) {
         const int t = idx / C, i = idx % C;
         w.T[oCC + idx] = sT[t][i];
-        w.TT[oCC + idx] = sT[i][t];
     }
     // W = T Xw (Xw = diag(beta) KG),  U' = T Xu (Xu = diag(beta) V)
     {
@@ -591,7 +590,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
     const float* dSn = w.dSn + oKV;
     const float* Um = w.U + oCV;
     const float* dUm = w.dU + oCV;
-    const float* TT = w.TT + oCC;
+    const float* Tm = w.T + oCC;  // T[a][i] at Tm[a * C + i]
     auto dOat = [&](int t, int x) -> float { return t < n ? ld(dO, ((t0 + t) * Hs + h) * DV + x) : 0.f; };
     // store a 64 x N accumulator tile (times s) to dst (row stride N), rows >= n as zero
     auto put = [&](auto& acc, float* dst, int N, float s) {
@@ -662,12 +661,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
             }
         Acc<DK> ax;
         ax.zero();
-        gemm64<DK, C, true, true>(ax, [&](int t, int a) { return TT[(size_t)t * C + a]; },
+        gemm64<DK, C, false, true>(ax, [&](int t, int a) { return Tm[(size_t)a * C + t]; },
                                   [&](int a, int c) { return dW[(size_t)a * DK + c]; }, lds);
         put(ax, w.dXw + oCK, DK, 1.f);
         Acc<DV> au;
         au.zero();
-        gemm64<DV, C, true, true>(au, [&](int t, int a) { return TT[(size_t)t * C + a]; },
+        gemm64<DV, C, false, true>(au, [&](int t, int a) { return Tm[(size_t)a * C + t]; },
                                   [&](int a, int x) { return dUm[(size_t)a * DV + x]; }, lds);
         put(au, w.dXu + oCV, DV, 1.f);
     }
@@ -678,8 +677,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
         const float* dT = w.dT + oCC;
         Acc<C> ay;
         ay.zero();
-        gemm64<C, C, true, true>(ay, [&](int a, int b) { return dT[(size_t)a * C + b]; },
-                                 [&](int b, int i) { return TT[(size_t)b * C + i]; }, lds);
+        gemm64<C, C, true, false>(ay, [&](int a, int b) { return dT[(size_t)a * C + b]; },
+                                  [&](int b, int i) { return Tm[(size_t)i * C + b]; }, lds);
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -695,7 +694,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
         const float* Y = w.Y + oCC;
         Acc<C> aa;
         aa.zero();
-        gemm64<C, C, true, true>(aa, [&](int t, int a) { return TT[(size_t)t * C + a]; },
+        gemm64<C, C, false, true>(aa, [&](int t, int a) { return Tm[(size_t)a * C + t]; },
                                  [&](int a, int i) { return Y[(size_t)a * C + i]; }, lds);
 #pragma unroll
         for (int a = 0; a < 4; ++a)
@@ -823,7 +822,7 @@ BwdSizes bwd_sizes(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv) {
     s.cc = al256(slots * C * C * 4);
     s.k = al256(slots * dk * 4);
     s.kv = al256(slots * dk * dv * 4);
-    s.total = s.head + 14 * s.ck + 4 * s.cv + 8 * s.cc + 2 * s.k + 2 * s.kv;
+    s.total = s.head + 14 * s.ck + 4 * s.cv + 7 * s.cc + 2 * s.k + 2 * s.kv;
     return s;
 }
 
@@ -841,7 +840,7 @@ BwdWs carve_bwd(void* base, int64_t T, int32_t N, int32_t H, int32_t dk, int32_t
     for (float** f : ck) *f = take(s.ck);
     float** cv[] = {&w.Up, &w.U, &w.dU, &w.dXu};
     for (float** f : cv) *f = take(s.cv);
-    float** cc[] = {&w.M, &w.P, &w.T, &w.TT, &w.dP, &w.dT, &w.Y, &w.dA};
+    float** cc[] = {&w.M, &w.P, &w.T, &w.dP, &w.dT, &w.Y, &w.dA};
     for (float** f : cc) *f = take(s.cc);
     w.Gn = take(s.k);
     w.dGn = take(s.k);
