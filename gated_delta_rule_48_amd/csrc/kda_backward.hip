@@ -336,12 +336,18 @@ __device__ __forceinline__ void block_store(const f32x4 (&r)[block_regs<WIDTH>()
 // 16-row tiles and lane (lg, lr) = (lane / 16, lane % 16) holds rows 4 lg + i
 // (i < 4) of a tile in column lr.  acc += sum over k < K of A(r, k) B(k, lr),
 // where a(k) reads A at the lane's row r = lr of the tile and b(k) reads
-// B(k, lr); each instruction takes k = k0 + lg.
+// B(k, lr); each instruction takes k = k0 + lg.  Even and odd steps of four
+// accumulate separately, so two independent instructions are in flight.
 template <int K, typename FA, typename FB>
 __device__ __forceinline__ f32x4 mfma_tile(f32x4 acc, FA a, FB b, int lg) {
+    static_assert(K % 8 == 0, "two accumulators");
+    f32x4 odd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-    for (int k0 = 0; k0 < K; k0 += 4) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a(k0 + lg), b(k0 + lg), acc, 0, 0, 0);
-    return acc;
+    for (int k0 = 0; k0 < K; k0 += 8) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a(k0 + lg), b(k0 + lg), acc, 0, 0, 0);
+        odd = __builtin_amdgcn_mfma_f32_16x16x4f32(a(k0 + 4 + lg), b(k0 + 4 + lg), odd, 0, 0, 0);
+    }
+    return acc + odd;
 }
 
 // ---------------------------------------------------------------------------
