@@ -350,6 +350,24 @@ __device__ __forceinline__ f32x4 mfma_tile(f32x4 acc, FA a, FB b, int lg) {
     return acc + odd;
 }
 
+// The (sequence, head) pair and 16-column slice of a walk workgroup.  Blocks
+// are dispatched to the eight XCDs in turn (block b to XCD b mod 8); when the
+// pairs fill whole rounds of eight, the NS slices of a pair are all placed on
+// one XCD, so its L2 fetches the pair's per-chunk operands once instead of
+// once per slice.
+__device__ __forceinline__ void walk_item(int NS, int& slice, int& pair) {
+    const int64_t NH = (int64_t)(gridDim.x / NS);
+    const int64_t bid = blockIdx.x;
+    if (NH % 8 == 0) {
+        const int64_t idx = bid >> 3;
+        pair = (int)((idx / NS) * 8 + (bid & 7));
+        slice = (int)(idx % NS);
+    } else {
+        pair = (int)(bid / NS);
+        slice = (int)(bid % NS);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Forward state walk: saves the start state S of every chunk and
 // U = U' - W S, then S <- Diag(Gn) S + Kd^T U.
@@ -372,8 +390,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
     float* sKd = smem + L::Kd;  // [C][SK]
     float* sS = smem + L::S;    // [DK][16]
     float* sU = smem + L::U;    // [C][16]
-    const int sl = blockIdx.x % NS;
-    const int nh = blockIdx.x / NS;
+    int sl, nh;
+    walk_item(NS, sl, nh);
     const int h = nh % H;
     const int seq = nh / H;
     if (w.header->bad_seqlens) return;
@@ -464,8 +482,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
     float* sdS = smem + L::dS;  // [DK][16]
     float* sdU = smem + L::dU;  // [C][16]
     float* sdO = smem + L::dO;  // two [C][16] buffers
-    const int sl = blockIdx.x % NS;
-    const int nh = blockIdx.x / NS;
+    int sl, nh;
+    walk_item(NS, sl, nh);
     const int h = nh % H;
     const int seq = nh / H;
     if (w.header->bad_seqlens) return;
