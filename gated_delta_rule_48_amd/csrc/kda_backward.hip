@@ -585,7 +585,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
 // phases exchange everything through the workspace, so the split only moves
 // barriers to kernel boundaries; each launch holds far fewer registers.
 template <typename E, int DK, int DV, bool HG, int PH>
-__global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restrict__ v, const E* __restrict__ beta,
+__global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restrict__ q, const E* __restrict__ k,
+                                                                const E* __restrict__ v, const E* __restrict__ beta,
                                                                 const E* __restrict__ dO, int32_t H, int32_t Hs, BwdWs w,
                                                                 E* __restrict__ dq, E* __restrict__ dk,
                                                                 E* __restrict__ dv, E* __restrict__ dg,
@@ -773,10 +774,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
                 const float e = gate_exp<E>(bb), er = gate_exp<E>(bb - r), eir = gate_exp<E>(r - bb),
                             ed = gate_exp<E>(bl - bb);
                 const int64_t o = ((t0 + t) * Hs + h) * DK + c;
-                dq[o] = Elt<E>::from(dQG * e + dQr * er);
-                dk[o] = Elt<E>::from(dKG * e + dKr * er + dKi * eir + dKd * ed);
-                w.dW[j] = dQG * w.QG[j] + dQr * w.Qr[j] + dKG * w.KG[j] + dKr * w.Kr[j] - dKi * w.Ki[j] -
-                          dKd * w.Kd[j];
+                // the decayed operands are q or k times these factors, so the
+                // gate's gradient needs q and k themselves, not the six arrays
+                const float gq = dQG * e + dQr * er;    // dq
+                const float gk_up = dKG * e + dKr * er;  // factors that grow with b
+                const float gk_dn = dKi * eir + dKd * ed;
+                dq[o] = Elt<E>::from(gq);
+                dk[o] = Elt<E>::from(gk_up + gk_dn);
+                w.dW[j] = ld(q, o) * gq + ld(k, o) * (gk_up - gk_dn);
             }
     }
     // dbeta: four adjacent lanes per row, each a quarter of the row's sums
@@ -905,15 +910,18 @@ hipError_t launch_bwd_t(const BwdArgs& a, int32_t Hs, const BwdWs& w, hipStream_
     e = hipGetLastError();
     if (e != hipSuccess || a.T == 0) return e;
     hipLaunchKernelGGL((bwd_local_kernel<E, DK, DV, HG, 0>), dim3(slots), dim3(kBwdThreads), 0, stream,
-                       (const E*)a.v, (const E*)a.beta, (const E*)a.dO, a.H, Hs, w, (E*)a.dq, (E*)a.dk, (E*)a.dv,
+                       (const E*)a.q, (const E*)a.k, (const E*)a.v, (const E*)a.beta, (const E*)a.dO, a.H, Hs, w,
+                       (E*)a.dq, (E*)a.dk, (E*)a.dv,
                        (E*)a.dg, (E*)a.dbeta);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_local_kernel<E, DK, DV, HG, 1>), dim3(slots), dim3(kBwdThreads), 0, stream,
-                       (const E*)a.v, (const E*)a.beta, (const E*)a.dO, a.H, Hs, w, (E*)a.dq, (E*)a.dk, (E*)a.dv,
+                       (const E*)a.q, (const E*)a.k, (const E*)a.v, (const E*)a.beta, (const E*)a.dO, a.H, Hs, w,
+                       (E*)a.dq, (E*)a.dk, (E*)a.dv,
                        (E*)a.dg, (E*)a.dbeta);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_local_kernel<E, DK, DV, HG, 2>), dim3(slots), dim3(kBwdThreads), 0, stream,
-                       (const E*)a.v, (const E*)a.beta, (const E*)a.dO, a.H, Hs, w, (E*)a.dq, (E*)a.dk, (E*)a.dv,
+                       (const E*)a.q, (const E*)a.k, (const E*)a.v, (const E*)a.beta, (const E*)a.dO, a.H, Hs, w,
+                       (E*)a.dq, (E*)a.dk, (E*)a.dv,
                        (E*)a.dg, (E*)a.dbeta);
     return hipGetLastError();
 }
