@@ -257,22 +257,31 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const E* __restri
             }
     }
     __syncthreads();
-    // T = (I + A)^{-1}: column j by forward substitution (one thread per column)
+    // T = (I + A)^{-1}: column j by forward substitution, one thread per
+    // column, the column in registers.  With T[i][j] = 0 above the diagonal
+    // the sums need no per-lane bounds: T[t][j] = -sum_{i<t} A[t][i] T[i][j]
+    // for t != j, and 1 on the diagonal.  A[t][i] is the same for every lane
+    // (broadcast LDS reads, independent of T); four partial sums shorten the
+    // chain of dependent additions.
     if (tid < C) {
         const int j = tid;
+        float Tc[C];
+#pragma unroll
         for (int t = 0; t < C; ++t) {
-            float val;
-            if (t < j) {
-                val = 0.f;
-            } else if (t == j) {
-                val = 1.f;
-            } else {
-                float s = 0.f;
-                for (int i = j; i < t; ++i) s += sA[t][i] * sT[i][j];
-                val = -s;
+            float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+            for (int i = 0; i + 3 < t; i += 4) {
+                s0 += sA[t][i] * Tc[i];
+                s1 += sA[t][i + 1] * Tc[i + 1];
+                s2 += sA[t][i + 2] * Tc[i + 2];
+                s3 += sA[t][i + 3] * Tc[i + 3];
             }
-            sT[t][j] = val;
+#pragma unroll
+            for (int i = t & ~3; i < t; ++i) s0 += sA[t][i] * Tc[i];
+            Tc[t] = t == j ? 1.f : -((s0 + s1) + (s2 + s3));
         }
+#pragma unroll
+        for (int t = 0; t < C; ++t) sT[t][j] = Tc[t];
     }
     __syncthreads();
     for (int idx = tid; idx < C * C; idx += kBwdThreads) {
