@@ -603,6 +603,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
     __shared__ float sbeta[C];
     __shared__ float sr[DK];
     __shared__ float sbl[DK];
+    __shared__ float sRowKG[C];       // sum_c dXw[t][c] KG[t][c], per row
+    __shared__ float sColKd[4 * DK];  // sum_t dKd[t][c] Kd[t][c], per wave and column
     __shared__ __align__(16) float lds[kGemmLds];
     const int64_t slot = blockIdx.x;
     const int64_t chunk = slot / H;
@@ -767,7 +769,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
                                    [&](int a, int c) { return Kr[(size_t)a * DK + c]; }, lds);
         gemm64<DK, C, false, true>(acc, [&](int t, int a) { return dP[(size_t)a * C + t]; },
                                    [&](int a, int c) { return Qr[(size_t)a * DK + c]; }, lds);
-        // the parked tiles were written by this thread: same (t, c) positions
+        // the parked tiles were written by this thread: same (t, c) positions.
+        // The same pass forms the row sums of dXw * KG (for dbeta) and the
+        // column sums of dKd * Kd (for the last row of the gate's prefix sum),
+        // with KG = k e^b and Kd = k e^{b_last - b} from factors at hand.
+        float rowp[4] = {0.f, 0.f, 0.f, 0.f};
+        float colp[DK / 16];
+#pragma unroll
+        for (int b = 0; b < DK / 16; ++b) colp[b] = 0.f;
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -777,7 +786,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
                 const size_t j = oCK + (size_t)t * DK + c;
                 const size_t jt = (size_t)t * DK + c;
                 const float dKr = sbeta[t] * dKr_s[jt], dKi = acc.t[b][a], dQr = dQr_s[jt];
-                const float dKG = sbeta[t] * w.dXw[j];
+                const float dXw = w.dXw[j];
+                const float dKG = sbeta[t] * dXw;
                 const float dQG = w.dQG[j], dKd = w.dKd[j];
                 const float bb = w.B[j], r = sr[c], bl = sbl[c];
                 const float e = gate_exp<E>(bb), er = gate_exp<E>(bb - r), eir = gate_exp<E>(r - bb),
@@ -788,27 +798,47 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
                 const float gq = dQG * e + dQr * er;    // dq
                 const float gk_up = dKG * e + dKr * er;  // factors that grow with b
                 const float gk_dn = dKi * eir + dKd * ed;
+                const float kv = ld(k, o);
                 dq[o] = Elt<E>::from(gq);
                 dk[o] = Elt<E>::from(gk_up + gk_dn);
-                w.dW[j] = ld(q, o) * gq + ld(k, o) * (gk_up - gk_dn);
+                w.dW[j] = ld(q, o) * gq + kv * (gk_up - gk_dn);
+                rowp[a] += dXw * kv * e;
+                colp[b] += dKd * kv * ed;
             }
+        // rows: the 16 lanes of a lane group; columns: the four lane groups of a
+        // wave, then the four waves in a fixed order (no atomics: deterministic)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            float x = rowp[a];
+            x += __shfl_xor(x, 1, 64);
+            x += __shfl_xor(x, 2, 64);
+            x += __shfl_xor(x, 4, 64);
+            x += __shfl_xor(x, 8, 64);
+            if ((tid & 15) == 0) sRowKG[Acc<DK>::row(a)] = x;
+        }
+#pragma unroll
+        for (int b = 0; b < DK / 16; ++b) {
+            float x = colp[b];
+            x += __shfl_xor(x, 16, 64);
+            x += __shfl_xor(x, 32, 64);
+            if ((tid & 63) < 16) sColKd[(tid / 64) * DK + Acc<DK>::col(b)] = x;
+        }
     }
+    __syncthreads();
     // dbeta: four adjacent lanes per row, each a quarter of the row's sums
     {
-        const int t = tid / 4, q = tid % 4;
+        const int t = tid / 4, part = tid % 4;
         float s = 0.f;
         if (t < n) {
 #pragma unroll 4
-            for (int i = q; i < t; i += 4) s += w.dA[oCC + (size_t)t * C + i] * w.M[oCC + (size_t)t * C + i];
+            for (int i = part; i < t; i += 4) s += w.dA[oCC + (size_t)t * C + i] * w.M[oCC + (size_t)t * C + i];
 #pragma unroll 8
-            for (int c = q; c < DK; c += 4) s += w.dXw[oCK + (size_t)t * DK + c] * w.KG[oCK + (size_t)t * DK + c];
-#pragma unroll 8
-            for (int x = q; x < DV; x += 4)
+            for (int x = part; x < DV; x += 4)
                 s += w.dXu[oCV + (size_t)t * DV + x] * ld(v, ((t0 + t) * Hs + h) * DV + x);
         }
         s += __shfl_xor(s, 1, 64);
         s += __shfl_xor(s, 2, 64);
-        if (t < n && q == 0) dbeta[(t0 + t) * Hs + h] = Elt<E>::from(s);
+        if (t < n && part == 0) dbeta[(t0 + t) * Hs + h] = Elt<E>::from(s + sRowKG[t]);
     }
     for (int idx = tid; idx < C * DV; idx += kBwdThreads) {
         const int t = idx / DV, x = idx % DV;
@@ -819,9 +849,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
     // phase 6: dg = reverse cumulative sum of db; the last row's prefix sum
     // also carries e^{b_last} (Gn) and the e^{b_last} factor of Kd
     for (int c = tid; c < DK; c += kBwdThreads) {
-        float acc = w.dGn[oK + c] * w.Gn[oK + c];
-#pragma unroll 8
-        for (int t = 0; t < n; ++t) acc += w.dKd[oCK + (size_t)t * DK + c] * w.Kd[oCK + (size_t)t * DK + c];
+        float acc = w.dGn[oK + c] * w.Gn[oK + c] + ((sColKd[c] + sColKd[DK + c]) + (sColKd[2 * DK + c] + sColKd[3 * DK + c]));
 #pragma unroll 8
         for (int t = n - 1; t >= 0; --t) {
             acc += w.dW[oCK + (size_t)t * DK + c];
