@@ -521,6 +521,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
         block_load<C>(rP, w.P + slot * C * C);
         block_load<DK>(rK, w.Kd + slot * C * DK);
         load_dO(c1 - 1, rO);
+        block_load<DK>(rQ, w.QG + slot * C * DK);
+        block_load<DK>(rW, w.W + slot * C * DK);
         block_store<C>(rP, sP, SC);
         block_store<DK>(rK, sKd, SK);
 #pragma unroll
@@ -529,7 +531,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     for (int ch = c1 - 1; ch >= c0; --ch) {
         const size_t slot = (size_t)ch * H + h;
-        const size_t oCK = slot * C * DK, oCV = slot * C * DV, oKV = slot * DK * DV;
+        const size_t oCV = slot * C * DV, oKV = slot * DK * DV;
         float* dOc = sdO + buf * C * 16;
 #pragma unroll
         for (int i = 0; i < RS; ++i) {
@@ -540,8 +542,6 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
 #pragma unroll
         for (int i = 0; i < RS; ++i) gn[i] = w.Gn[slot * DK + srow(i)];
         lds_barrier();
-        block_load<DK>(rQ, w.QG + oCK);  // this chunk's QG and W, in flight during dU
-        block_load<DK>(rW, w.W + oCK);
         // dU = P^T dO + Kd dS_next (this wave's 16 rows)
         f32x4 du = mfma_tile<C>(zero, [&](int k) { return sP[k * SC + 16 * wv + lr]; },
                                 [&](int k) { return dOc[k * 16 + lr]; }, lg);
@@ -555,11 +555,14 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
         block_store<DK>(rQ, sQG, SK);
         block_store<DK>(rW, sW, SK);
         lds_barrier();
-        if (ch > c0) {  // the previous chunk's P, Kd and dO, in flight during dS
+        if (ch > c0) {  // the previous chunk's operands: P, Kd and dO in flight during
+                        // dS, QG and W during dS and the next dU
             const size_t pslot = slot - H;
             block_load<C>(rP, w.P + pslot * C * C);
             block_load<DK>(rK, w.Kd + pslot * C * DK);
             load_dO(ch - 1, rO);
+            block_load<DK>(rQ, w.QG + pslot * C * DK);
+            block_load<DK>(rW, w.W + pslot * C * DK);
         }
         // dS = Diag(Gn) dS_next + QG^T dO - W^T dU (this wave's TPW tiles of rows)
 #pragma unroll
