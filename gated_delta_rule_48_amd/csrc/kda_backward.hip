@@ -332,6 +332,18 @@ __device__ __forceinline__ void block_load(f32x4 (&r)[block_regs<WIDTH>()], cons
     for (int i = 0; i < block_regs<WIDTH>(); ++i) r[i] = s4[i * kBwdThreads];
 }
 
+// block_load with the loads issued in index order wherever it is inlined, so
+// that a wait for one register of r is computed alike on every path.
+template <int WIDTH>
+__device__ __forceinline__ void block_load_ordered(f32x4 (&r)[block_regs<WIDTH>()], const float* src) {
+    const f32x4* s4 = reinterpret_cast<const f32x4*>(src) + threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < block_regs<WIDTH>(); ++i) {
+        r[i] = s4[i * kBwdThreads];
+        asm volatile("" ::: "memory");
+    }
+}
+
 template <int WIDTH>
 __device__ __forceinline__ void block_store(const f32x4 (&r)[block_regs<WIDTH>()], float* dst, int stride) {
 #pragma unroll
@@ -351,7 +363,7 @@ template <int K, typename FA, typename FB>
 __device__ __forceinline__ f32x4 mfma_tile(f32x4 acc, FA a, FB b, int lg) {
     static_assert(K % 8 == 0, "two accumulators");
     f32x4 odd = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
+#pragma unroll
     for (int k0 = 0; k0 < K; k0 += 8) {
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a(k0 + lg), b(k0 + lg), acc, 0, 0, 0);
         odd = __builtin_amdgcn_mfma_f32_16x16x4f32(a(k0 + 4 + lg), b(k0 + 4 + lg), odd, 0, 0, 0);
@@ -388,7 +400,7 @@ struct StateWalkLds {
 };
 
 // One workgroup of four waves per CU at most (LDS), so a wave may use the
-// whole register file: the next chunk's operands are held in registers.
+// whole register file: the next two chunks' operands are held in registers.
 template <int DK, int DV>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_state_walk_kernel(int32_t H, int32_t Hs, const float* __restrict__ S0,
                                                                      BwdWs w) {
@@ -413,45 +425,53 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
     float S[RS];
 #pragma unroll
     for (int i = 0; i < RS; ++i) S[i] = S0 ? S0[(((size_t)seq * Hs + h) * DK + srow(i)) * DV + col] : 0.f;
-    f32x4 rW[block_regs<DK>()], rK[block_regs<DK>()];
-    if (c0 < c1) {
-        const size_t slot = (size_t)c0 * H + h;
-        block_load<DK>(rW, w.W + slot * C * DK);
-        block_load<DK>(rK, w.Kd + slot * C * DK);
-    }
-    for (int ch = c0; ch < c1; ++ch) {
+    // Two chunks' operands in flight: buffer a holds even steps, b odd ones.
+    // A wait for a load also waits for every load issued before it, so no
+    // load needed sooner is issued after one needed later: a step fetches
+    // W and Kd two chunks ahead once they are in LDS, and that chunk's Gn
+    // and U' at its end, after their last use.  Past the sequence's last
+    // chunk the fetches re-read that chunk (unused), so that every path
+    // issues the same loads and the compiler's waits stay exact.
+    constexpr int NR = block_regs<DK>();
+    f32x4 rWa[NR], rKa[NR], rWb[NR], rKb[NR];
+    float gna[RS], upa[4], gnb[RS], upb[4];
+    auto fetch_wk = [&](int ch, f32x4 (&rW)[NR], f32x4 (&rK)[NR]) {
+        const size_t slot = (size_t)ch * H + h;
+        block_load_ordered<DK>(rW, w.W + slot * C * DK);
+        block_load_ordered<DK>(rK, w.Kd + slot * C * DK);
+    };
+    auto fetch_gu = [&](int ch, float (&gn)[RS], float (&up)[4]) {
+        const size_t slot = (size_t)ch * H + h;
+#pragma unroll
+        for (int i = 0; i < RS; ++i) gn[i] = w.Gn[slot * DK + srow(i)];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) up[i] = w.Up[slot * C * DV + (size_t)(t0 + i) * DV + col];
+    };
+    auto step = [&](int ch, f32x4 (&rW)[NR], f32x4 (&rK)[NR], float (&gn)[RS], float (&up)[4]) {
         const size_t slot = (size_t)ch * H + h;
         const size_t oCV = slot * C * DV, oKV = slot * DK * DV;
         block_store<DK>(rW, sW, SK);
         block_store<DK>(rK, sKd, SK);
 #pragma unroll
-        for (int i = 0; i < RS; ++i) {
-            sS[srow(i) * 16 + lr] = S[i];
-            w.S[oKV + (size_t)srow(i) * DV + col] = S[i];
-        }
-        float gn[RS];
-#pragma unroll
-        for (int i = 0; i < RS; ++i) gn[i] = w.Gn[slot * DK + srow(i)];
-        float up[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) up[i] = w.Up[oCV + (size_t)(t0 + i) * DV + col];
+        for (int i = 0; i < RS; ++i) sS[srow(i) * 16 + lr] = S[i];
         lds_barrier();
-        if (ch + 1 < c1) {  // next chunk's operands, in flight during this one
-            const size_t nslot = slot + H;
-            block_load<DK>(rW, w.W + nslot * C * DK);
-            block_load<DK>(rK, w.Kd + nslot * C * DK);
-        }
+        // operands two chunks ahead, in flight during this and the next chunk
+        fetch_wk(min(ch + 2, c1 - 1), rW, rK);
+        // the saved S as 16-byte stores from its LDS copy (four lanes per row)
+#pragma unroll
+        for (int i = tid; i < DK * 4; i += kBwdThreads)
+            *reinterpret_cast<f32x4*>(w.S + oKV + (size_t)(i / 4) * DV + sl * 16 + 4 * (i % 4)) =
+                *reinterpret_cast<const f32x4*>(sS + 4 * i);
         // U = U' - W S (this wave's 16 rows)
         const f32x4 ws = mfma_tile<DK>(f32x4{0.f, 0.f, 0.f, 0.f},
                                        [&](int k) { return sW[(16 * wv + lr) * SK + k]; },
                                        [&](int k) { return sS[k * 16 + lr]; }, lg);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float x = up[i] - ws[i];
-            sU[(t0 + i) * 16 + lr] = x;
-            w.U[oCV + (size_t)(t0 + i) * DV + col] = x;
-        }
+        for (int i = 0; i < 4; ++i) sU[(t0 + i) * 16 + lr] = up[i] - ws[i];
         lds_barrier();
+        // U as 16-byte stores from its LDS copy: one per thread
+        *reinterpret_cast<f32x4*>(w.U + oCV + (size_t)(tid / 4) * DV + sl * 16 + 4 * (tid % 4)) =
+            *reinterpret_cast<const f32x4*>(sU + 4 * tid);
         // S <- Diag(Gn) S + Kd^T U (this wave's TPW tiles of rows)
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
@@ -462,7 +482,18 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
 #pragma unroll
             for (int i = 0; i < 4; ++i) S[4 * tt + i] = gn[4 * tt + i] * S[4 * tt + i] + a[i];
         }
+        fetch_gu(min(ch + 2, c1 - 1), gn, up);
         lds_barrier();
+    };
+    if (c0 >= c1) return;
+    fetch_wk(c0, rWa, rKa);
+    fetch_gu(c0, gna, upa);
+    asm volatile("" ::: "memory");  // buffer a's loads all issue before buffer b's
+    fetch_wk(min(c0 + 1, c1 - 1), rWb, rKb);
+    fetch_gu(min(c0 + 1, c1 - 1), gnb, upb);
+    for (int ch = c0; ch < c1; ch += 2) {
+        step(ch, rWa, rKa, gna, upa);
+        if (ch + 1 < c1) step(ch + 1, rWb, rKb, gnb, upb);
     }
 }
 
@@ -504,86 +535,107 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
     float dS[RS];
 #pragma unroll
     for (int i = 0; i < RS; ++i) dS[i] = dST ? dST[(((size_t)seq * Hs + h) * DK + srow(i)) * DV + col] : 0.f;
-    // dO of a chunk for this lane's 4 rows of column `col`
-    auto load_dO = [&](int ch, float (&r)[4]) {
-        const int2 ct = w.chunk_tab[ch];
+    if (c0 >= c1) {
+        if (dS0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = t0 + i;
-            r[i] = t < ct.y ? ld(dO, (((int64_t)ct.x + t) * Hs + h) * DV + col) : 0.f;
+            for (int i = 0; i < RS; ++i) dS0[(((size_t)seq * Hs + h) * DK + srow(i)) * DV + col] = dS[i];
         }
-    };
-    f32x4 rP[block_regs<C>()], rK[block_regs<DK>()], rQ[block_regs<DK>()], rW[block_regs<DK>()];
-    float rO[4];
-    int buf = 0;
-    if (c0 < c1) {
-        const size_t slot = (size_t)(c1 - 1) * H + h;
-        block_load<C>(rP, w.P + slot * C * C);
-        block_load<DK>(rK, w.Kd + slot * C * DK);
-        load_dO(c1 - 1, rO);
-        block_load<DK>(rQ, w.QG + slot * C * DK);
-        block_load<DK>(rW, w.W + slot * C * DK);
-        block_store<C>(rP, sP, SC);
-        block_store<DK>(rK, sKd, SK);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sdO[(t0 + i) * 16 + lr] = rO[i];
+        return;
     }
+    // A wait for a load also waits for every load issued before it.  So no
+    // load's address depends on another load inside the loop (a chunk's
+    // tokens follow from the sequence's offsets), no load sits in a branch,
+    // and each chunk's loads are issued in the order they are needed:
+    // dO, P, Kd at the end of the step that fetches them, then Gn, QG, W
+    // one step later.
+    const int tok0 = w.cu[seq], tok1 = w.cu[seq + 1];
+    // dO of a chunk for this lane's 4 rows of column `col`, as stored; rows
+    // past the chunk's end re-read its last row and are zeroed when staged
+    auto rows_of = [&](int ch) { return min(C, tok1 - (tok0 + (ch - c0) * C)); };
+    auto load_dO = [&](int ch, E (&r)[4]) {
+        const int first = tok0 + (ch - c0) * C, n = rows_of(ch);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = dO[(((int64_t)first + min(t0 + i, n - 1)) * Hs + h) * DV + col];
+    };
+    auto stage_dO = [&](int ch, const E (&r)[4], float* dst) {
+        const int n = rows_of(ch);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(t0 + i) * 16 + lr] = t0 + i < n ? Elt<E>::to(r[i]) : 0.f;
+    };
+    constexpr int NP = block_regs<C>(), NK = block_regs<DK>();
+    f32x4 rP[NP], rK[NK], rQ[NK], rW[NK];
+    E rO[4];
+    float gn[RS], gnn[RS];
+    auto fetch = [&](int ch) {
+        const size_t slot = (size_t)ch * H + h;
+        load_dO(ch, rO);
+        block_load_ordered<C>(rP, w.P + slot * C * C);
+        block_load_ordered<DK>(rK, w.Kd + slot * C * DK);
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < RS; ++i) gnn[i] = w.Gn[slot * DK + srow(i)];
+        asm volatile("" ::: "memory");
+        block_load_ordered<DK>(rQ, w.QG + slot * C * DK);
+        block_load_ordered<DK>(rW, w.W + slot * C * DK);
+    };
+    int buf = 0;
+    fetch(c1 - 1);
+    block_store<C>(rP, sP, SC);
+    block_store<DK>(rK, sKd, SK);
+    stage_dO(c1 - 1, rO, sdO);
+#pragma unroll
+    for (int i = 0; i < RS; ++i) gn[i] = gnn[i];
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     for (int ch = c1 - 1; ch >= c0; --ch) {
         const size_t slot = (size_t)ch * H + h;
         const size_t oCV = slot * C * DV, oKV = slot * DK * DV;
         float* dOc = sdO + buf * C * 16;
 #pragma unroll
-        for (int i = 0; i < RS; ++i) {
-            sdS[srow(i) * 16 + lr] = dS[i];
-            w.dSn[oKV + (size_t)srow(i) * DV + col] = dS[i];
-        }
-        float gn[RS];
-#pragma unroll
-        for (int i = 0; i < RS; ++i) gn[i] = w.Gn[slot * DK + srow(i)];
+        for (int i = 0; i < RS; ++i) sdS[srow(i) * 16 + lr] = dS[i];
         lds_barrier();
+        // the saved dS_next as 16-byte stores from its LDS copy (four lanes per row)
+#pragma unroll
+        for (int i = tid; i < DK * 4; i += kBwdThreads)
+            *reinterpret_cast<f32x4*>(w.dSn + oKV + (size_t)(i / 4) * DV + sl * 16 + 4 * (i % 4)) =
+                *reinterpret_cast<const f32x4*>(sdS + 4 * i);
         // dU = P^T dO + Kd dS_next (this wave's 16 rows)
         f32x4 du = mfma_tile<C>(zero, [&](int k) { return sP[k * SC + 16 * wv + lr]; },
                                 [&](int k) { return dOc[k * 16 + lr]; }, lg);
         du = mfma_tile<DK>(du, [&](int k) { return sKd[(16 * wv + lr) * SK + k]; },
                            [&](int k) { return sdS[k * 16 + lr]; }, lg);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sdU[(t0 + i) * 16 + lr] = du[i];
-            w.dU[oCV + (size_t)(t0 + i) * DV + col] = du[i];
-        }
+        for (int i = 0; i < 4; ++i) sdU[(t0 + i) * 16 + lr] = du[i];
+        // no work that waits for the loads in flight is scheduled into the products
+        __builtin_amdgcn_sched_barrier(0);
         block_store<DK>(rQ, sQG, SK);
-        block_store<DK>(rW, sW, SK);
+#pragma unroll
+        for (int i = 0; i < NK; ++i) rW[i] = -rW[i];
+        block_store<DK>(rW, sW, SK);  // sW holds -W
         lds_barrier();
-        if (ch > c0) {  // the previous chunk's operands: P, Kd and dO in flight during
-                        // dS, QG and W during dS and the next dU
-            const size_t pslot = slot - H;
-            block_load<C>(rP, w.P + pslot * C * C);
-            block_load<DK>(rK, w.Kd + pslot * C * DK);
-            load_dO(ch - 1, rO);
-            block_load<DK>(rQ, w.QG + pslot * C * DK);
-            block_load<DK>(rW, w.W + pslot * C * DK);
-        }
+        *reinterpret_cast<f32x4*>(w.dU + oCV + (size_t)(tid / 4) * DV + sl * 16 + 4 * (tid % 4)) =
+            *reinterpret_cast<const f32x4*>(sdU + 4 * tid);
+        // the previous chunk's operands (past the first chunk: this one's, unused)
+        fetch(max(ch - 1, c0));
         // dS = Diag(Gn) dS_next + QG^T dO - W^T dU (this wave's TPW tiles of rows)
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
             const int m0 = 16 * (wv * TPW + tt);
             f32x4 a = mfma_tile<C>(zero, [&](int k) { return sQG[k * SK + m0 + lr]; },
                                    [&](int k) { return dOc[k * 16 + lr]; }, lg);
-            a = mfma_tile<C>(a, [&](int k) { return -sW[k * SK + m0 + lr]; },
+            a = mfma_tile<C>(a, [&](int k) { return sW[k * SK + m0 + lr]; },
                              [&](int k) { return sdU[k * 16 + lr]; }, lg);
 #pragma unroll
             for (int i = 0; i < 4; ++i) dS[4 * tt + i] = gn[4 * tt + i] * dS[4 * tt + i] + a[i];
         }
-        if (ch > c0) {
-            block_store<C>(rP, sP, SC);
-            block_store<DK>(rK, sKd, SK);
-            float* dOn = sdO + (buf ^ 1) * C * 16;
+        __builtin_amdgcn_sched_barrier(0);  // the staging below stays after the products
+        // sP and sKd were last read before the second barrier, the other dO
+        // buffer a step ago; the next step's first barrier publishes these
+        block_store<C>(rP, sP, SC);
+        block_store<DK>(rK, sKd, SK);
+        stage_dO(max(ch - 1, c0), rO, sdO + (buf ^ 1) * C * 16);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dOn[(t0 + i) * 16 + lr] = rO[i];
-        }
+        for (int i = 0; i < RS; ++i) gn[i] = gnn[i];
         buf ^= 1;
-        lds_barrier();
     }
     if (dS0) {
 #pragma unroll
