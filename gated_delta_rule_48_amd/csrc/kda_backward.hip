@@ -649,7 +649,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
 // phases exchange everything through the workspace, so the split only moves
 // barriers to kernel boundaries; each launch holds far fewer registers.
 template <typename E, int DK, int DV, bool HG, int PH>
-__global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restrict__ q, const E* __restrict__ k,
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH == 0 ? 2 : 1))) void bwd_local_kernel(const E* __restrict__ q, const E* __restrict__ k,
                                                                 const E* __restrict__ v, const E* __restrict__ beta,
                                                                 const E* __restrict__ dO, int32_t H, int32_t Hs, BwdWs w,
                                                                 E* __restrict__ dq, E* __restrict__ dk,
@@ -660,7 +660,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
     __shared__ float sbl[DK];
     __shared__ float sRowKG[C];       // sum_c dXw[t][c] KG[t][c], per row
     __shared__ float sColKd[4 * DK];  // sum_t dKd[t][c] Kd[t][c], per wave and column
-    __shared__ __align__(16) float lds[kGemmLds];
+    // phase 1 stages five operand tiles at once; the later phases use gemm64's two
+    constexpr int kLdsFloats = PH == 0 ? 16 * (3 * (C + 4) + 2 * (DK + 4)) : kGemmLds;
+    __shared__ __align__(16) float lds[kLdsFloats];
     const int64_t slot = blockIdx.x;
     const int64_t chunk = slot / H;
     const int h = (int)(slot % H);
@@ -696,36 +698,97 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(const E* __restr
     };
 
     if constexpr (PH == 0) {
-    // phase 1: dW = -dU S^T, dQG = dO S^T, dKd = U dS_next^T, dP = tril(dO U^T), dGn
+    // phase 1 as one pass over the value index x in tiles of 16: dW = -dU S^T,
+    // dQG = dO S^T, dKd = U dS_next^T, dP = tril(dO U^T) and dGn[c] = sum_x
+    // S[c][x] dS_next[c][x].  Each operand tile is read from memory once and
+    // serves every product that uses it (U is the left operand of dKd and the
+    // right one of dP, with the same LDS layout).
     {
-        Acc<DK> acc;
-        acc.zero();
-        gemm64<DK, DV, true, false>(acc, [&](int t, int x) { return dUm[(size_t)t * DV + x]; },
-                                    [&](int x, int c) { return Sm[(size_t)c * DV + x]; }, lds);
-        put(acc, w.dW + oCK, DK, -1.f);
-        acc.zero();
-        gemm64<DK, DV, true, false>(acc, dOat, [&](int x, int c) { return Sm[(size_t)c * DV + x]; }, lds);
-        put(acc, w.dQG + oCK, DK, 1.f);
-        acc.zero();
-        gemm64<DK, DV, true, false>(acc, [&](int t, int x) { return Um[(size_t)t * DV + x]; },
-                                    [&](int x, int c) { return dSn[(size_t)c * DV + x]; }, lds);
-        put(acc, w.dKd + oCK, DK, 1.f);
-        Acc<C> ap;
-        ap.zero();
-        gemm64<C, DV, true, false>(ap, dOat, [&](int x, int i) { return Um[(size_t)i * DV + x]; }, lds);
+        constexpr int KT = 16, SA = C + 4, SB = DK + 4, NT = DK / 16;
+        constexpr int RA = C * KT / kBwdThreads, RB = DK * KT / kBwdThreads;
+        static_assert(KT * (3 * SA + 2 * SB) <= kLdsFloats, "phase-1 tiles fit");
+        float* tdU = lds;
+        float* tdO = tdU + KT * SA;
+        float* tU = tdO + KT * SA;
+        float* tS = tU + KT * SA;
+        float* tD = tS + KT * SB;
+        const int wv = tid / 64, lg = (tid % 64) / 16, lr = tid % 16;
+        Acc<DK> aW, aQ, aK;
+        Acc<C> aP;
+        aW.zero();
+        aQ.zero();
+        aK.zero();
+        aP.zero();
+        float gn = 0.f;
+        float rdU[RA], rdO[RA], rU[RA], rS[RB], rD[RB];
+        // thread's share of a tile: element idx = tid + r * threads at row idx / KT, x0 + idx % KT
+        auto fetch = [&](int x0) {
+#pragma unroll
+            for (int r = 0; r < RA; ++r) {
+                const int idx = tid + r * kBwdThreads, m = idx / KT, x = x0 + idx % KT;
+                rdU[r] = dUm[(size_t)m * DV + x];
+                rdO[r] = dOat(m, x);
+                rU[r] = Um[(size_t)m * DV + x];
+            }
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                const int idx = tid + r * kBwdThreads, c = idx / KT, x = x0 + idx % KT;
+                rS[r] = Sm[(size_t)c * DV + x];
+                rD[r] = dSn[(size_t)c * DV + x];
+            }
+        };
+        fetch(0);
+        for (int x0 = 0; x0 < DV; x0 += KT) {
+#pragma unroll
+            for (int r = 0; r < RA; ++r) {
+                const int idx = tid + r * kBwdThreads, m = idx / KT, kk = idx % KT;
+                tdU[kk * SA + m] = rdU[r];
+                tdO[kk * SA + m] = rdO[r];
+                tU[kk * SA + m] = rU[r];
+            }
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                const int idx = tid + r * kBwdThreads, c = idx / KT, kk = idx % KT;
+                tS[kk * SB + c] = rS[r];
+                tD[kk * SB + c] = rD[r];
+            }
+            lds_barrier();
+            if (x0 + KT < DV) fetch(x0 + KT);
+            if (tid < DK) {
+#pragma unroll
+                for (int kk = 0; kk < KT; ++kk) gn += tS[kk * SB + tid] * tD[kk * SB + tid];
+            }
+#pragma unroll
+            for (int ks = 0; ks < KT; ks += 4) {
+                const int kr = ks + lg;
+                const float a_dU = tdU[kr * SA + 16 * wv + lr], a_dO = tdO[kr * SA + 16 * wv + lr],
+                            a_U = tU[kr * SA + 16 * wv + lr];
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const float bS = tS[kr * SB + 16 * j + lr], bD = tD[kr * SB + 16 * j + lr];
+                    aW.t[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_dU, bS, aW.t[j], 0, 0, 0);
+                    aQ.t[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_dO, bS, aQ.t[j], 0, 0, 0);
+                    aK.t[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_U, bD, aK.t[j], 0, 0, 0);
+                }
+#pragma unroll
+                for (int j = 0; j < C / 16; ++j) {
+                    const float bU = tU[kr * SA + 16 * j + lr];
+                    aP.t[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_dO, bU, aP.t[j], 0, 0, 0);
+                }
+            }
+            lds_barrier();
+        }
+        put(aW, w.dW + oCK, DK, -1.f);
+        put(aQ, w.dQG + oCK, DK, 1.f);
+        put(aK, w.dKd + oCK, DK, 1.f);
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
             for (int b = 0; b < C / 16; ++b) {
                 const int t = Acc<C>::row(a), i = Acc<C>::col(b);
-                w.dP[oCC + (size_t)t * C + i] = (i <= t && t < n) ? ap.t[b][a] : 0.f;
+                w.dP[oCC + (size_t)t * C + i] = (i <= t && t < n) ? aP.t[b][a] : 0.f;
             }
-    }
-    for (int c = tid; c < DK; c += kBwdThreads) {
-        float s = 0.f;
-#pragma unroll 8
-        for (int x = 0; x < DV; ++x) s += Sm[(size_t)c * DV + x] * dSn[(size_t)c * DV + x];
-        w.dGn[oK + c] = s;
+        if (tid < DK) w.dGn[oK + tid] = gn;
     }
     }  // PH == 0
 
