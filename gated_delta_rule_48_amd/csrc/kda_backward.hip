@@ -649,7 +649,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
 // phases exchange everything through the workspace, so the split only moves
 // barriers to kernel boundaries; each launch holds far fewer registers.
 template <typename E, int DK, int DV, bool HG, int PH>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH == 0 ? 2 : 1))) void bwd_local_kernel(const E* __restrict__ q, const E* __restrict__ k,
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH == 1 ? 1 : 2))) void bwd_local_kernel(const E* __restrict__ q, const E* __restrict__ k,
                                                                 const E* __restrict__ v, const E* __restrict__ beta,
                                                                 const E* __restrict__ dO, int32_t H, int32_t Hs, BwdWs w,
                                                                 E* __restrict__ dq, E* __restrict__ dk,
@@ -660,8 +660,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
     __shared__ float sbl[DK];
     __shared__ float sRowKG[C];       // sum_c dXw[t][c] KG[t][c], per row
     __shared__ float sColKd[4 * DK];  // sum_t dKd[t][c] Kd[t][c], per wave and column
-    // phase 1 stages five operand tiles at once; the later phases use gemm64's two
-    constexpr int kLdsFloats = PH == 0 ? 16 * (3 * (C + 4) + 2 * (DK + 4)) : kGemmLds;
+    // phases 1 and 5 stage five and seven operand tiles at once; phases 2-4 use gemm64's two
+    constexpr int kLdsFloats = PH == 0   ? 16 * (3 * (C + 4) + 2 * (DK + 4))
+                               : PH == 2 ? 16 * (4 * (C + 4) + 3 * (DK + 4))
+                                         : kGemmLds;
     __shared__ __align__(16) float lds[kLdsFloats];
     const int64_t slot = blockIdx.x;
     const int64_t chunk = slot / H;
@@ -870,24 +872,84 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
         const float* Ki = w.Ki + oCK;
         const float* Kr = w.Kr + oCK;
         const float* Qr = w.Qr + oCK;
-        // one accumulator tile at a time: dKr and dQr are parked in the workspace
-        float* dKr_s = w.dKr + oCK;
-        float* dQr_s = w.dQr + oCK;
-        Acc<DK> acc;
+        // One pass over the chunk-row index in tiles of 16, all three results
+        // in registers: dKr and dQr take dA's and dP's column blocks against
+        // Ki's rows; dKi takes dA's and dP's row blocks (transposed use)
+        // against Kr's and Qr's rows.  Ki is read once, nothing is parked.
+        constexpr int KT = 16, SA = C + 4, SB = DK + 4, NT = DK / 16;
+        constexpr int RA = C * KT / kBwdThreads, RB = DK * KT / kBwdThreads;
+        static_assert(KT * (4 * SA + 3 * SB) <= kLdsFloats, "phase-5 tiles fit");
+        float* tAc = lds;            // [kk][t] = dA[t][k0 + kk]
+        float* tPc = tAc + KT * SA;  // [kk][t] = dP[t][k0 + kk]
+        float* tAr = tPc + KT * SA;  // [kk][t] = beta[k0 + kk] dA[k0 + kk][t]
+        float* tPr = tAr + KT * SA;  // [kk][t] = dP[k0 + kk][t]
+        float* tKi = tPr + KT * SA;  // [kk][c] = Ki[k0 + kk][c]
+        float* tKr = tKi + KT * SB;
+        float* tQr = tKr + KT * SB;
+        const int wv = tid / 64, lg = (tid % 64) / 16, lr = tid % 16;
+        Acc<DK> aKr, aQr, acc;  // acc: dKi
+        aKr.zero();
+        aQr.zero();
         acc.zero();
-        gemm64<DK, C, true, true>(acc, [&](int t, int i) { return dA[(size_t)t * C + i]; },
-                                  [&](int i, int c) { return Ki[(size_t)i * DK + c]; }, lds);
-        put(acc, dKr_s, DK, 1.f);
-        acc.zero();
-        gemm64<DK, C, true, true>(acc, [&](int t, int i) { return dP[(size_t)t * C + i]; },
-                                  [&](int i, int c) { return Ki[(size_t)i * DK + c]; }, lds);
-        put(acc, dQr_s, DK, 1.f);
-        acc.zero();
-        gemm64<DK, C, false, true>(acc, [&](int t, int a) { return sbeta[a] * dA[(size_t)a * C + t]; },
-                                   [&](int a, int c) { return Kr[(size_t)a * DK + c]; }, lds);
-        gemm64<DK, C, false, true>(acc, [&](int t, int a) { return dP[(size_t)a * C + t]; },
-                                   [&](int a, int c) { return Qr[(size_t)a * DK + c]; }, lds);
-        // the parked tiles were written by this thread: same (t, c) positions.
+        float rAc[RA], rPc[RA], rAr[RA], rPr[RA], rKi[RB], rKr[RB], rQr[RB];
+        auto fetch = [&](int k0) {
+#pragma unroll
+            for (int r = 0; r < RA; ++r) {
+                const int idx = tid + r * kBwdThreads;
+                const int m = idx / KT, kc = k0 + idx % KT;  // column blocks: 16 per row
+                rAc[r] = dA[(size_t)m * C + kc];
+                rPc[r] = dP[(size_t)m * C + kc];
+                const int kr = k0 + idx / C, t = idx % C;    // row blocks: whole rows
+                rAr[r] = sbeta[kr] * dA[(size_t)kr * C + t];
+                rPr[r] = dP[(size_t)kr * C + t];
+            }
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                const int idx = tid + r * kBwdThreads;
+                const size_t o = (size_t)(k0 + idx / DK) * DK + idx % DK;
+                rKi[r] = Ki[o];
+                rKr[r] = Kr[o];
+                rQr[r] = Qr[o];
+            }
+        };
+        fetch(0);
+        for (int k0 = 0; k0 < C; k0 += KT) {
+#pragma unroll
+            for (int r = 0; r < RA; ++r) {
+                const int idx = tid + r * kBwdThreads;
+                const int m = idx / KT, kk = idx % KT;
+                tAc[kk * SA + m] = rAc[r];
+                tPc[kk * SA + m] = rPc[r];
+                tAr[(idx / C) * SA + idx % C] = rAr[r];
+                tPr[(idx / C) * SA + idx % C] = rPr[r];
+            }
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                const int idx = tid + r * kBwdThreads;
+                const int j = (idx / DK) * SB + idx % DK;
+                tKi[j] = rKi[r];
+                tKr[j] = rKr[r];
+                tQr[j] = rQr[r];
+            }
+            lds_barrier();
+            if (k0 + KT < C) fetch(k0 + KT);
+#pragma unroll
+            for (int ks = 0; ks < KT; ks += 4) {
+                const int kr = ks + lg, ar = kr * SA + 16 * wv + lr;
+                const float a_Ac = tAc[ar], a_Pc = tPc[ar], a_Ar = tAr[ar], a_Pr = tPr[ar];
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const int br = kr * SB + 16 * j + lr;
+                    const float bKi = tKi[br], bKr = tKr[br], bQr = tQr[br];
+                    aKr.t[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_Ac, bKi, aKr.t[j], 0, 0, 0);
+                    aQr.t[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_Pc, bKi, aQr.t[j], 0, 0, 0);
+                    acc.t[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_Ar, bKr, acc.t[j], 0, 0, 0);
+                    acc.t[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_Pr, bQr, acc.t[j], 0, 0, 0);
+                }
+            }
+            lds_barrier();
+        }
+        // dKr, dQr and dKi share the accumulator layout: same (t, c) positions.
         // The same pass forms the row sums of dXw * KG (for dbeta) and the
         // column sums of dKd * Kd (for the last row of the gate's prefix sum),
         // with KG = k e^b and Kd = k e^{b_last - b} from factors at hand.
@@ -902,8 +964,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
                 const int t = Acc<DK>::row(a), c = Acc<DK>::col(b);
                 if (t >= n) continue;
                 const size_t j = oCK + (size_t)t * DK + c;
-                const size_t jt = (size_t)t * DK + c;
-                const float dKr = sbeta[t] * dKr_s[jt], dKi = acc.t[b][a], dQr = dQr_s[jt];
+                const float dKr = sbeta[t] * aKr.t[b][a], dKi = acc.t[b][a], dQr = aQr.t[b][a];
                 const float dXw = w.dXw[j];
                 const float dKG = sbeta[t] * dXw;
                 const float dQG = w.dQG[j], dKd = w.dKd[j];
