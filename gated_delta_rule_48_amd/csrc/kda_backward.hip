@@ -62,8 +62,6 @@ struct BwdWs {
     int2* chunk_tab;
     // [C][DK]
     float *B, *QG, *KG, *Kd, *Qr, *Kr, *Ki, *W, *dW, *dQG, *dKd, *dXw;
-    // [C][DK] scratch of the last local phase (dKr, dQr)
-    float *dKr, *dQr;
     // [C][DV]
     float *Up, *U, *dU, *dXu;
     // [C][C]
@@ -1067,7 +1065,7 @@ BwdSizes bwd_sizes(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv) {
     s.cc = al256(slots * C * C * 4);
     s.k = al256(slots * dk * 4);
     s.kv = al256(slots * dk * dv * 4);
-    s.total = s.head + 14 * s.ck + 4 * s.cv + 7 * s.cc + 2 * s.k + 2 * s.kv;
+    s.total = s.head + 12 * s.ck + 4 * s.cv + 7 * s.cc + 2 * s.k + 2 * s.kv;
     return s;
 }
 
@@ -1080,8 +1078,7 @@ BwdWs carve_bwd(void* base, int64_t T, int32_t N, int32_t H, int32_t dk, int32_t
     w.chunk_off = reinterpret_cast<int32_t*>(p); p += al256((size_t)(N + 1) * 4);
     w.chunk_tab = reinterpret_cast<int2*>(p); p += al256((size_t)max_chunks_for(T, N) * sizeof(int2));
     auto take = [&](size_t bytes) { float* f = reinterpret_cast<float*>(p); p += bytes; return f; };
-    float** ck[] = {&w.B, &w.QG, &w.KG, &w.Kd, &w.Qr, &w.Kr, &w.Ki, &w.W, &w.dW, &w.dQG, &w.dKd, &w.dXw,
-                    &w.dKr, &w.dQr};
+    float** ck[] = {&w.B, &w.QG, &w.KG, &w.Kd, &w.Qr, &w.Kr, &w.Ki, &w.W, &w.dW, &w.dQG, &w.dKd, &w.dXw};
     for (float** f : ck) *f = take(s.ck);
     float** cv[] = {&w.Up, &w.U, &w.dU, &w.dXu};
     for (float** f : cv) *f = take(s.cv);
