@@ -65,7 +65,7 @@ struct BwdWs {
     // [C][DV]
     float *Up, *U, *dU, *dXu;
     // [C][C]
-    float *M, *P, *T, *dP, *dT, *Y, *dA;
+    float *M, *P, *T, *dP, *dA;
     // [DK]
     float *Gn, *dGn;
     // [DK][DV]: chunk start state and the state cotangent after the chunk
@@ -793,6 +793,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
     }  // PH == 0
 
     if constexpr (PH == 1) {
+    // dT and Y are used only inside this launch: they stay in LDS
+    __shared__ float sdT[C][C + 1];
+    __shared__ float sY[C][C + 1];
     // phase 2: dT = strict_tril(dW Xw^T + dU Xu^T), dXw = T^T dW, dXu = T^T dU
     {
         const float* dW = w.dW + oCK;
@@ -811,7 +814,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
 #pragma unroll
             for (int b = 0; b < C / 16; ++b) {
                 const int t = Acc<C>::row(a), i = Acc<C>::col(b);
-                w.dT[oCC + (size_t)t * C + i] = (i < t && t < n) ? at.t[b][a] : 0.f;
+                sdT[t][i] = (i < t && t < n) ? at.t[b][a] : 0.f;
             }
         Acc<DK> ax;
         ax.zero();
@@ -828,28 +831,26 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
 
     // phase 3: Y = dT T^T (kept where column < row)
     {
-        const float* dT = w.dT + oCC;
         Acc<C> ay;
         ay.zero();
-        gemm64<C, C, true, false>(ay, [&](int a, int b) { return dT[(size_t)a * C + b]; },
+        gemm64<C, C, true, false>(ay, [&](int a, int b) { return sdT[a][b]; },
                                   [&](int b, int i) { return Tm[(size_t)i * C + b]; }, lds);
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
             for (int b = 0; b < C / 16; ++b) {
                 const int r = Acc<C>::row(a), i = Acc<C>::col(b);
-                w.Y[oCC + (size_t)r * C + i] = (i < r && r < n) ? ay.t[b][a] : 0.f;
+                sY[r][i] = (i < r && r < n) ? ay.t[b][a] : 0.f;
             }
     }
     __syncthreads();
 
     // phase 4: dA = strict_tril(-T^T Y)
     {
-        const float* Y = w.Y + oCC;
         Acc<C> aa;
         aa.zero();
         gemm64<C, C, false, true>(aa, [&](int t, int a) { return Tm[(size_t)a * C + t]; },
-                                 [&](int a, int i) { return Y[(size_t)a * C + i]; }, lds);
+                                 [&](int a, int i) { return sY[a][i]; }, lds);
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -1065,7 +1066,7 @@ BwdSizes bwd_sizes(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv) {
     s.cc = al256(slots * C * C * 4);
     s.k = al256(slots * dk * 4);
     s.kv = al256(slots * dk * dv * 4);
-    s.total = s.head + 12 * s.ck + 4 * s.cv + 7 * s.cc + 2 * s.k + 2 * s.kv;
+    s.total = s.head + 12 * s.ck + 4 * s.cv + 5 * s.cc + 2 * s.k + 2 * s.kv;
     return s;
 }
 
@@ -1082,7 +1083,7 @@ BwdWs carve_bwd(void* base, int64_t T, int32_t N, int32_t H, int32_t dk, int32_t
     for (float** f : ck) *f = take(s.ck);
     float** cv[] = {&w.Up, &w.U, &w.dU, &w.dXu};
     for (float** f : cv) *f = take(s.cv);
-    float** cc[] = {&w.M, &w.P, &w.T, &w.dP, &w.dT, &w.Y, &w.dA};
+    float** cc[] = {&w.M, &w.P, &w.T, &w.dP, &w.dA};
     for (float** f : cc) *f = take(s.cc);
     w.Gn = take(s.k);
     w.dGn = take(s.k);
