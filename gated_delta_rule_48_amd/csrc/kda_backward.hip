@@ -543,9 +543,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
     // A wait for a load also waits for every load issued before it.  So no
     // load's address depends on another load inside the loop (a chunk's
     // tokens follow from the sequence's offsets), no load sits in a branch,
-    // and each chunk's loads are issued in the order they are needed:
-    // dO, P, Kd at the end of the step that fetches them, then Gn, QG, W
-    // one step later.
+    // and each chunk's loads are issued in the order they are needed: a
+    // step starts by fetching the previous chunk's dO, P, Kd (staged at its
+    // end) and, after its second barrier, that chunk's Gn, QG, W (Gn for its
+    // end, QG and W for the middle of the next step).
     const int tok0 = w.cu[seq], tok1 = w.cu[seq + 1];
     // dO of a chunk for this lane's 4 rows of column `col`, as stored; rows
     // past the chunk's end re-read its last row and are zeroed when staged
@@ -564,12 +565,15 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
     f32x4 rP[NP], rK[NK], rQ[NK], rW[NK];
     E rO[4];
     float gn[RS], gnn[RS];
-    auto fetch = [&](int ch) {
+    auto fetch_far = [&](int ch) {  // P, Kd, dO: staged at the end of the step that fetches them
         const size_t slot = (size_t)ch * H + h;
         load_dO(ch, rO);
         block_load_ordered<C>(rP, w.P + slot * C * C);
         block_load_ordered<DK>(rK, w.Kd + slot * C * DK);
         asm volatile("" ::: "memory");
+    };
+    auto fetch_near = [&](int ch) {  // Gn, QG, W: used at the end of this step and in the next one
+        const size_t slot = (size_t)ch * H + h;
 #pragma unroll
         for (int i = 0; i < RS; ++i) gnn[i] = w.Gn[slot * DK + srow(i)];
         asm volatile("" ::: "memory");
@@ -577,7 +581,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
         block_load_ordered<DK>(rW, w.W + slot * C * DK);
     };
     int buf = 0;
-    fetch(c1 - 1);
+    fetch_far(c1 - 1);
+    fetch_near(c1 - 1);
     block_store<C>(rP, sP, SC);
     block_store<DK>(rK, sKd, SK);
     stage_dO(c1 - 1, rO, sdO);
@@ -588,6 +593,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
         const size_t slot = (size_t)ch * H + h;
         const size_t oCV = slot * C * DV, oKV = slot * DK * DV;
         float* dOc = sdO + buf * C * 16;
+        // this chunk's P and Kd are in LDS already: the previous chunk's are
+        // fetched now, in flight during both product phases (past the first
+        // chunk this re-reads it, unused)
+        fetch_far(max(ch - 1, c0));
 #pragma unroll
         for (int i = 0; i < RS; ++i) sdS[srow(i) * 16 + lr] = dS[i];
         lds_barrier();
@@ -612,8 +621,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
         lds_barrier();
         *reinterpret_cast<f32x4*>(w.dU + oCV + (size_t)(tid / 4) * DV + sl * 16 + 4 * (tid % 4)) =
             *reinterpret_cast<const f32x4*>(sdU + 4 * tid);
-        // the previous chunk's operands (past the first chunk: this one's, unused)
-        fetch(max(ch - 1, c0));
+        fetch_near(max(ch - 1, c0));
         // dS = Diag(Gn) dS_next + QG^T dO - W^T dU (this wave's TPW tiles of rows)
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
