@@ -175,7 +175,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const E* __restri
                                                                const E* __restrict__ v, const E* __restrict__ g,
                                                                const E* __restrict__ beta, int32_t H, int32_t Hs, BwdWs w) {
     // sA | sT for the solve; before that, the chunk's prefix sums b [C][DK]
-    __shared__ float sAT[2 * C * (C + 1)];
+    __shared__ __align__(16) float sAT[2 * C * (C + 1)];
     __shared__ float sbeta[C];
     __shared__ __align__(16) float lds[kGemmLds];
     static_assert(C * DK <= 2 * C * (C + 1), "prefix sums fit in the solve's LDS");
@@ -208,25 +208,40 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const E* __restri
         w.Gn[(size_t)slot * DK + c] = gate_exp<E>(b);
     }
     __syncthreads();
-    // every decayed operand; r is the middle row's prefix sum
+    // every decayed operand; r is the middle row's prefix sum.  Four
+    // consecutive channels per thread, so each array is written with 16-byte stores.
     const int m = (n - 1) / 2;
-    for (int idx = tid; idx < C * DK; idx += kBwdThreads) {
+    for (int idx = 4 * tid; idx < C * DK; idx += 4 * kBwdThreads) {
         const int t = idx / DK, c = idx % DK;
-        const float b = sB[idx], r = sB[m * DK + c], bl = sB[(n - 1) * DK + c];
-        float qv = 0.f, kv = 0.f;
-        if (t < n) {
-            qv = ld(q, ((t0 + t) * Hs + h) * DK + c);
-            kv = ld(k, ((t0 + t) * Hs + h) * DK + c);
+        const f32x4 b4 = *reinterpret_cast<const f32x4*>(sB + idx);
+        const f32x4 r4 = *reinterpret_cast<const f32x4*>(sB + m * DK + c);
+        const f32x4 bl4 = *reinterpret_cast<const f32x4*>(sB + (n - 1) * DK + c);
+        f32x4 oQG, oKG, oKd, oQr, oKr, oKi;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float qv = 0.f, kv = 0.f;
+            if (t < n) {
+                qv = ld(q, ((t0 + t) * Hs + h) * DK + c + j);
+                kv = ld(k, ((t0 + t) * Hs + h) * DK + c + j);
+            }
+            const float b = b4[j], r = r4[j], bl = bl4[j];
+            const float e = gate_exp<E>(b), er = gate_exp<E>(b - r), eir = gate_exp<E>(r - b),
+                        ed = gate_exp<E>(bl - b);
+            oQG[j] = qv * e;
+            oKG[j] = kv * e;
+            oKd[j] = kv * ed;
+            oQr[j] = qv * er;
+            oKr[j] = kv * er;
+            oKi[j] = kv * eir;
         }
-        const float e = gate_exp<E>(b), er = gate_exp<E>(b - r), eir = gate_exp<E>(r - b), ed = gate_exp<E>(bl - b);
         const size_t i = oCK + idx;
-        w.B[i] = b;
-        w.QG[i] = qv * e;
-        w.KG[i] = kv * e;
-        w.Kd[i] = kv * ed;
-        w.Qr[i] = qv * er;
-        w.Kr[i] = kv * er;
-        w.Ki[i] = kv * eir;
+        *reinterpret_cast<f32x4*>(w.B + i) = b4;
+        *reinterpret_cast<f32x4*>(w.QG + i) = oQG;
+        *reinterpret_cast<f32x4*>(w.KG + i) = oKG;
+        *reinterpret_cast<f32x4*>(w.Kd + i) = oKd;
+        *reinterpret_cast<f32x4*>(w.Qr + i) = oQr;
+        *reinterpret_cast<f32x4*>(w.Kr + i) = oKr;
+        *reinterpret_cast<f32x4*>(w.Ki + i) = oKi;
     }
     __syncthreads();
     // v of row i scaled by beta_i (zero past the chunk's end)
