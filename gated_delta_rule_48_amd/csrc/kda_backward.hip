@@ -121,8 +121,10 @@ __device__ __forceinline__ void gemm64(Acc<N>& acc, LA la, LB lb, float* lds) {
         n = B_NFAST ? idx % N : idx / KT;
         kk = B_NFAST ? idx / N : idx % KT;
     };
-    float ra[RA], rb[RB];
-    auto fetch = [&](int k0) {
+    // two tiles in flight: buffer 0 holds even tiles, buffer 1 odd ones
+    static_assert(K % (2 * KT) == 0, "tiles in pairs");
+    float ra0[RA], rb0[RB], ra1[RA], rb1[RB];
+    auto fetch = [&](float (&ra)[RA], float (&rb)[RB], int k0) {
 #pragma unroll
         for (int r = 0; r < RA; ++r) {
             int m, kk;
@@ -136,8 +138,7 @@ __device__ __forceinline__ void gemm64(Acc<N>& acc, LA la, LB lb, float* lds) {
             rb[r] = lb(k0 + kk, n);
         }
     };
-    fetch(0);
-    for (int k0 = 0; k0 < K; k0 += KT) {
+    auto tile = [&](float (&ra)[RA], float (&rb)[RB], int k0) {
 #pragma unroll
         for (int r = 0; r < RA; ++r) {
             int m, kk;
@@ -150,10 +151,10 @@ __device__ __forceinline__ void gemm64(Acc<N>& acc, LA la, LB lb, float* lds) {
             b_kn(r, kk, n);
             sB[kk * SB + n] = rb[r];
         }
-        // the tiles are shared through LDS only: the next tile's global loads
+        // the tiles are shared through LDS only: the later tiles' global loads
         // stay in flight across these barriers
         lds_barrier();
-        if (k0 + KT < K) fetch(k0 + KT);
+        if (k0 + 2 * KT < K) fetch(ra, rb, k0 + 2 * KT);
 #pragma unroll
         for (int ks = 0; ks < KT; ks += 4) {
             const float a = sA[(ks + lg) * SA + 16 * wv + lr];
@@ -164,6 +165,13 @@ __device__ __forceinline__ void gemm64(Acc<N>& acc, LA la, LB lb, float* lds) {
             }
         }
         lds_barrier();
+    };
+    fetch(ra0, rb0, 0);
+    fetch(ra1, rb1, KT);
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 2 * KT) {
+        tile(ra0, rb0, k0);
+        tile(ra1, rb1, k0 + KT);
     }
 }
 
