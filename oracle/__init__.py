@@ -229,11 +229,25 @@ def dense_dplr(q, k, v, g, beta, *, S0=None, cu_seqlens=None, per_head_gate=Fals
 
 
 def rel_err(got, ref):
-    """max |got - ref| / max |ref| over the whole tensor (the parity metric)."""
+    """max |got - ref| / max |ref| over the whole tensor (the parity metric).
+
+    The largest absolute deviation anywhere in the tensor, divided by the
+    largest magnitude of the reference (not of ``got``, and not a mean), so a
+    single wrong element is enough to fail a bound.  ``got`` and ``ref`` must
+    have the same shape (no broadcasting).  Any NaN or infinity in ``got`` or
+    ``ref`` gives +inf.  Two empty tensors give 0; an all-zero reference gives
+    the plain max |got - ref|.
+    """
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
-    den = np.max(np.abs(ref))
-    num = np.max(np.abs(got - ref)) if got.size else 0.0
+    if got.shape != ref.shape:
+        raise ValueError(f"rel_err: shapes differ, got {got.shape} vs ref {ref.shape}")
+    if got.size == 0:
+        return 0.0
+    if not (np.all(np.isfinite(got)) and np.all(np.isfinite(ref))):
+        return float("inf")
+    num = float(np.max(np.abs(got - ref)))
+    den = float(np.max(np.abs(ref)))
     if den == 0.0:
-        return float(num)
-    return float(num / den)
+        return num
+    return num / den

@@ -325,3 +325,39 @@ def test_bf16_rounding_is_round_to_nearest_even():
     got = synth.bf16_to_f32(synth.bf16_bits(x))
     np.testing.assert_array_equal(got, np.array([1.0, 1.0, 1.0 + 2.0 ** -6, 1.0 + 2.0 ** -7, -2.5],
                                                 dtype=np.float32))
+
+
+# ------------------------------------------------------------ parity metric
+# rel_err is the metric every GPU parity bound is stated in: the largest
+# absolute deviation over the whole tensor divided by the largest magnitude of
+# the reference.  Hand values, chosen so that a mean instead of a max, a
+# denominator taken from `got`, an absolute error, a silently broadcast shape
+# or a swallowed NaN each give a different number.
+def test_rel_err_hand_values():
+    # one element off by 2 against max|ref| = 4: 0.5 (a mean of |diff| would
+    # give 1.0 / 4 = 0.25 or 1.0; dividing by max|got| = 2 would give 1.0)
+    assert oracle.rel_err([1.0, 2.0], [1.0, 4.0]) == 0.5
+    # the deviation is absolute: a sign flip of the largest element counts 2x
+    assert oracle.rel_err([-3.0, 1.0], [3.0, 1.0]) == 2.0
+    # max over every element, not the first or the last
+    assert oracle.rel_err([[0.0, 0.0, 0.5], [2.0, 0.0, 0.0]],
+                          [[0.0, 0.0, 0.0], [2.0, 0.0, 0.0]]) == 0.25
+    # an all-zero reference falls back to the absolute max deviation
+    assert oracle.rel_err([0.0, -0.125], [0.0, 0.0]) == 0.125
+    # identical tensors and two empty tensors give exactly 0
+    assert oracle.rel_err([1.5, -2.5], [1.5, -2.5]) == 0.0
+    assert oracle.rel_err(np.zeros((0, 3)), np.zeros((0, 3))) == 0.0
+    # the denominator is the reference's: scaling both by 10 changes nothing,
+    # scaling only `got` does
+    assert oracle.rel_err([10.0, 20.0], [10.0, 40.0]) == 0.5
+    assert oracle.rel_err([2.0, 8.0], [1.0, 4.0]) == 1.0
+
+
+def test_rel_err_rejects_shape_mismatch_and_non_finite():
+    with pytest.raises(ValueError):
+        oracle.rel_err(np.zeros(3), np.zeros((1, 3)))
+    with pytest.raises(ValueError):
+        oracle.rel_err(np.zeros(0), np.ones(2))
+    assert oracle.rel_err([np.nan, 1.0], [1.0, 1.0]) == math.inf
+    assert oracle.rel_err([np.inf, 1.0], [1.0, 1.0]) == math.inf
+    assert oracle.rel_err([1.0, 1.0], [1.0, np.nan]) == math.inf
