@@ -10,14 +10,17 @@
 // chunk algebra of the forward kernels.
 //
 // Forward algebra of one chunk (start state S, local rows t < n <= C):
-//   b_t  = g_0 + ... + g_t (per key channel),  r = b at the middle row
+//   b_t  = g_0 + ... + g_t (per key channel),  r_t = b at the middle row of
+//          t's 16-row tile
 //   QG = Q e^b, KG = K e^b, Kd = K e^{b_last - b}, Gn = e^{b_last}
 //   Qr = Q e^{b - r}, Kr = K e^{b - r}, Ki = K e^{r - b}
-//   M  = strict_tril(Kr Ki^T),  A = diag(beta) M,  T = (I + A)^{-1}
-//   P  = tril(Qr Ki^T),  W = T diag(beta) KG,  U' = T diag(beta) V
+//   M  = strict_tril(K K^T with decay),  A = diag(beta) M,  T = (I + A)^{-1}
+//   P  = tril(Q K^T with decay),  W = T diag(beta) KG,  U' = T diag(beta) V
 //   U  = U' - W S,  O = QG S + P U,  S_next = Diag(Gn) S + Kd^T U
-// (Qr Ki^T and Kr Ki^T equal the decayed products Q K^T and K K^T: the
-// reference r cancels; it only keeps the factors in range.)
+// (Inside one tile the decayed products are Qr Ki^T and Kr Ki^T; between two
+// tiles the decay is rebuilt from factors <= 1, see the tile factors below.
+// The references only keep the factors in range: the exact values do not
+// depend on them.)
 //
 // Backward, per chunk in reverse order (reverse state walk):
 //   dU = P^T dO + Kd dS_next
@@ -29,14 +32,16 @@
 //   dXw = T^T dW, dXu = T^T dU,  dA = strict_tril(-T^T dT T^T)
 //   dbeta = rowsum(dA * M) + rowsum(dXw * KG) + rowsum(dXu * V)
 //   dKr = diag(beta) dA Ki, dKi = (diag(beta) dA)^T Kr + dP^T Qr, dQr = dP Ki
+//        (tile by tile, with the same factors between tiles as M and P)
 //   dq = dQG e^b + dQr e^{b-r},  dk = beta dXw e^b + dKr e^{b-r} + dKi e^{r-b} + dKd e^{b_last-b}
 //   db = dQG QG + dQr Qr + beta dXw KG + dKr Kr - dKi Ki - dKd Kd
 //        (+ sum_t dKd_t Kd_t + dGn Gn on the last row),  dv = beta dXu
 //   dg = reverse cumulative sum of db over the chunk (summed over channels
 //        for a per-head gate).
 //
-// All arithmetic is fp32 on the vector units.  Every intermediate of a chunk
-// is kept in the workspace.  The two walks run one workgroup per (sequence,
+// All arithmetic is fp32; every matrix product runs on the fp32 matrix cores
+// (v_mfma_f32_16x16x4f32).  Every intermediate of a chunk is kept in the
+// workspace.  The two walks run one workgroup per (sequence,
 // head, 16-column slice) with register tiles and the next chunk's operands in
 // flight; every product of the per-chunk kernels runs as a 64 x N block
 // product tiled through LDS with 4 x N/16 register tiles.
@@ -176,6 +181,138 @@ __device__ __forceinline__ void gemm64(Acc<N>& acc, LA la, LB lb, float* lds) {
 }
 
 // ---------------------------------------------------------------------------
+// Decay references of the four 16-row tiles of a chunk.  Tile a covers rows
+// 16a..16a+15, with start row s(a) = 16a, middle row m(a) = 16a + 8 and end
+// row e(a) = 16a + 15.  Every stored decayed operand of row t is referred to
+// the middle row of t's own tile (Qr = Q e^{b - b_m}, Kr = K e^{b - b_m},
+// Ki = K e^{b_m - b}), so each of its factors spans at most eight tokens of
+// decay.  The decay between rows of two different tiles a > bb is rebuilt
+// from factors that are each <= 1 (the prefix sums do not increase along the
+// rows), applied one after another, so that no large intermediate value ever
+// meets a small later factor:
+//   fs[a]      e^{b_m(a) - b_s(a)}   takes a row operand of tile a to s(a)
+//   fe[bb]     e^{b_e(bb) - b_m(bb)} takes a column operand of tile bb to e(bb)
+//   fx[a,bb]   e^{b_s(a) - b_e(bb)}  from e(bb) on to s(a)   (M and P)
+//   f1[a,bb]   e^{b_m(a) - b_e(bb)}  from e(bb) on to m(a)   (row-side gradients)
+//   f2[a,bb]   e^{b_s(a) - b_m(bb)}  from s(a) on to m(bb)   (column-side gradients)
+// for the six pairs a > bb, pair index a (a - 1) / 2 + bb.  Every exponent is
+// capped at 80 nats, so that a gate outside the supported range still gives
+// finite values.  f1 spans up to nine tokens, so inside the supported range
+// it can fall below the smallest normal float (e^-87); the row-side results
+// later multiply it by a row factor of up to e^80.  The table is therefore
+// computed with the library expf, which returns subnormal results, for
+// either input type (the hardware exp of the bf16 path flushes them to
+// zero); the products with it keep subnormals as well.
+constexpr int kTiles = C / 16;
+constexpr int kPairs = kTiles * (kTiles - 1) / 2;
+constexpr float kCapNats = 80.f;
+__device__ __forceinline__ int pair_of(int a, int bb) { return a * (a - 1) / 2 + bb; }
+__device__ __forceinline__ int tile_mid_row(int a) { return 16 * a + 8; }
+
+template <typename E>
+__device__ __forceinline__ float capped_exp(float x) { return gate_exp<E>(fminf(x, kCapNats)); }
+
+// Rows of the factor table (each DK floats).
+constexpr int kTfBm = 0;                    // b_m(a), the reference of tile a
+constexpr int kTfFs = kTfBm + kTiles;       // fs[a]
+constexpr int kTfFe = kTfFs + kTiles;       // fe[bb]
+constexpr int kTfFx = kTfFe + kTiles;       // fx[a,bb]
+constexpr int kTfF1 = kTfFx + kPairs;       // f1[a,bb]
+constexpr int kTfF2 = kTfF1 + kPairs;       // f2[a,bb]
+constexpr int kTfRows = kTfF2 + kPairs;
+
+// Fill the factor table from the chunk's prefix sums; b(row, c) reads the
+// prefix sum of row `row` (rows past the chunk's end hold the last sum).
+// Every thread of the workgroup calls it; the caller publishes the table with
+// a barrier.
+__device__ __forceinline__ float table_exp(float x) { return expf(fminf(x, kCapNats)); }
+
+template <typename E, int DK, typename BF>
+__device__ __forceinline__ void fill_tile_factors(float* tf, BF b) {
+    for (int idx = threadIdx.x; idx < kTfRows * DK; idx += kBwdThreads) {
+        const int row = idx / DK, c = idx % DK;
+        float v;
+        if (row < kTfFs) {
+            v = b(tile_mid_row(row - kTfBm), c);
+        } else if (row < kTfFe) {
+            const int a = row - kTfFs;
+            v = table_exp(b(tile_mid_row(a), c) - b(16 * a, c));
+        } else if (row < kTfFx) {
+            const int bb = row - kTfFe;
+            v = table_exp(b(16 * bb + 15, c) - b(tile_mid_row(bb), c));
+        } else {
+            const int kind = (row - kTfFx) / kPairs, p = (row - kTfFx) % kPairs;
+            const int a = p >= 3 ? 3 : (p >= 1 ? 2 : 1), bb = p - pair_of(a, 0);
+            const int ra = kind == 1 ? tile_mid_row(a) : 16 * a;           // fx, f2: s(a); f1: m(a)
+            const int rb = kind == 2 ? tile_mid_row(bb) : 16 * bb + 15;     // fx, f1: e(bb); f2: m(bb)
+            v = table_exp(b(ra, c) - b(rb, c));
+        }
+        tf[idx] = v;
+    }
+}
+
+// M = strict_tril(K K^T with decay) and P = tril(Q K^T with decay) of one
+// chunk from the stored Kr, Qr, Ki, by 16 x 16 tiles: wave a computes the
+// tiles (a, bb), bb <= a, of its row tile.  A diagonal tile multiplies the
+// stored operands (both referred to m(a)); below the diagonal the row operand
+// is taken to s(a) (times fs[a]) and the column operand to e(bb) (times
+// fe[bb]) and on to s(a) (times fx[a,bb]).  Channels pass through LDS in tiles
+// of 16, the next tile in registers while the current one is multiplied.
+// acc[bb][i] holds row 16a + 4 (lane / 16) + i, column 16bb + lane % 16.
+template <int DK>
+__device__ __forceinline__ void decayed_mp(const float* Kr, const float* Qr, const float* Ki, const float* tf,
+                                           float* lds, f32x4 (&accM)[kTiles], f32x4 (&accP)[kTiles]) {
+    constexpr int KT = 16, SA = C + 4, R = C * KT / kBwdThreads;
+    float* tKr = lds;
+    float* tQr = tKr + KT * SA;
+    float* tKi = tQr + KT * SA;
+    const int tid = threadIdx.x, lg = (tid % 64) / 16, lr = tid % 16;
+    const int a = __builtin_amdgcn_readfirstlane(tid / 64);
+#pragma unroll
+    for (int bb = 0; bb < kTiles; ++bb) accM[bb] = accP[bb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float rKr[R], rQr[R], rKi[R];
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int idx = tid + r * kBwdThreads;
+            const size_t o = (size_t)(idx / KT) * DK + k0 + idx % KT;
+            rKr[r] = Kr[o];
+            rQr[r] = Qr[o];
+            rKi[r] = Ki[o];
+        }
+    };
+    fetch(0);
+    for (int k0 = 0; k0 < DK; k0 += KT) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int idx = tid + r * kBwdThreads, j = (idx % KT) * SA + idx / KT;
+            tKr[j] = rKr[r];
+            tQr[j] = rQr[r];
+            tKi[j] = rKi[r];
+        }
+        lds_barrier();
+        if (k0 + KT < DK) fetch(k0 + KT);
+#pragma unroll
+        for (int ks = 0; ks < KT; ks += 4) {
+            const int kr = ks + lg, c = k0 + kr;
+            const float ar = tKr[kr * SA + 16 * a + lr], aq = tQr[kr * SA + 16 * a + lr];
+            const float fsa = tf[(kTfFs + a) * DK + c];
+            const float ars = ar * fsa, aqs = aq * fsa;
+#pragma unroll
+            for (int bb = 0; bb < kTiles; ++bb) {
+                if (bb > a) continue;
+                float bi = tKi[kr * SA + 16 * bb + lr];
+                const bool off = bb < a;
+                if (off) bi = (bi * tf[(kTfFe + bb) * DK + c]) * tf[(kTfFx + pair_of(a, bb)) * DK + c];
+                accM[bb] = __builtin_amdgcn_mfma_f32_16x16x4f32(off ? ars : ar, bi, accM[bb], 0, 0, 0);
+                accP[bb] = __builtin_amdgcn_mfma_f32_16x16x4f32(off ? aqs : aq, bi, accP[bb], 0, 0, 0);
+            }
+        }
+        lds_barrier();
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Per (chunk, head): prefix sums, decayed operands, M, P, T = (I + A)^{-1},
 // W and U'.
 template <typename E, int DK, int DV, bool HG>
@@ -185,7 +322,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const E* __restri
     // sA | sT for the solve; before that, the chunk's prefix sums b [C][DK]
     __shared__ __align__(16) float sAT[2 * C * (C + 1)];
     __shared__ float sbeta[C];
-    __shared__ __align__(16) float lds[kGemmLds];
+    __shared__ float sTf[kTfRows * DK];  // tile decay factors
+    constexpr int kLdsFloats = kGemmLds > 3 * 16 * (C + 4) ? kGemmLds : 3 * 16 * (C + 4);
+    __shared__ __align__(16) float lds[kLdsFloats];
     static_assert(C * DK <= 2 * C * (C + 1), "prefix sums fit in the solve's LDS");
     float (*sA)[C + 1] = reinterpret_cast<float (*)[C + 1]>(sAT);
     float (*sT)[C + 1] = reinterpret_cast<float (*)[C + 1]>(sAT + C * (C + 1));
@@ -216,13 +355,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const E* __restri
         w.Gn[(size_t)slot * DK + c] = gate_exp<E>(b);
     }
     __syncthreads();
-    // every decayed operand; r is the middle row's prefix sum.  Four
-    // consecutive channels per thread, so each array is written with 16-byte stores.
-    const int m = (n - 1) / 2;
+    fill_tile_factors<E, DK>(sTf, [&](int row, int c) { return sB[row * DK + c]; });
+    // every decayed operand; r is the prefix sum at the middle row of the
+    // row's own 16-row tile.  Four consecutive channels per thread, so each
+    // array is written with 16-byte stores.
     for (int idx = 4 * tid; idx < C * DK; idx += 4 * kBwdThreads) {
         const int t = idx / DK, c = idx % DK;
         const f32x4 b4 = *reinterpret_cast<const f32x4*>(sB + idx);
-        const f32x4 r4 = *reinterpret_cast<const f32x4*>(sB + m * DK + c);
+        const f32x4 r4 = *reinterpret_cast<const f32x4*>(sB + tile_mid_row(t / 16) * DK + c);
         const f32x4 bl4 = *reinterpret_cast<const f32x4*>(sB + (n - 1) * DK + c);
         f32x4 oQG, oKG, oKd, oQr, oKr, oKi;
 #pragma unroll
@@ -233,7 +373,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const E* __restri
                 kv = ld(k, ((t0 + t) * Hs + h) * DK + c + j);
             }
             const float b = b4[j], r = r4[j], bl = bl4[j];
-            const float e = gate_exp<E>(b), er = gate_exp<E>(b - r), eir = gate_exp<E>(r - b),
+            const float e = gate_exp<E>(b), er = capped_exp<E>(b - r), eir = capped_exp<E>(r - b),
                         ed = gate_exp<E>(bl - b);
             oQG[j] = qv * e;
             oKG[j] = kv * e;
@@ -254,27 +394,20 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const E* __restri
     __syncthreads();
     // v of row i scaled by beta_i (zero past the chunk's end)
     auto xu = [&](int i, int x) -> float { return i < n ? sbeta[i] * ld(v, ((t0 + i) * Hs + h) * DV + x) : 0.f; };
-    // M = strict_tril(Kr Ki^T) and P = tril(Qr Ki^T)
+    // M = strict_tril(K K^T with decay) and P = tril(Q K^T with decay), by
+    // tiles with the decay rebuilt from factors <= 1 below the diagonal
     {
-        const float* Kr = w.Kr + oCK;
-        const float* Qr = w.Qr + oCK;
-        const float* Ki = w.Ki + oCK;
-        Acc<C> am, ap;
-        am.zero();
-        ap.zero();
-        gemm64<C, DK, true, false>(am, [&](int t, int c) { return Kr[(size_t)t * DK + c]; },
-                                   [&](int c, int i) { return Ki[(size_t)i * DK + c]; }, lds);
-        gemm64<C, DK, true, false>(ap, [&](int t, int c) { return Qr[(size_t)t * DK + c]; },
-                                   [&](int c, int i) { return Ki[(size_t)i * DK + c]; }, lds);
+        f32x4 am[kTiles], ap[kTiles];
+        decayed_mp<DK>(w.Kr + oCK, w.Qr + oCK, w.Ki + oCK, sTf, lds, am, ap);
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
             for (int b = 0; b < C / 16; ++b) {
                 const int t = Acc<C>::row(a), i = Acc<C>::col(b);
-                const float mv = (i < t && t < n) ? am.t[b][a] : 0.f;
+                const float mv = (i < t && t < n) ? am[b][a] : 0.f;
                 w.M[oCC + (size_t)t * C + i] = mv;
-                w.P[oCC + (size_t)t * C + i] = (i <= t && t < n) ? ap.t[b][a] : 0.f;
-                sA[t][i] = sbeta[t] * mv;
+                w.P[oCC + (size_t)t * C + i] = (i <= t && t < n) ? ap[b][a] : 0.f;
+                lds_put(&sA[t][i], sbeta[t] * mv);
             }
     }
     __syncthreads();
@@ -685,7 +818,6 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
                                                                 E* __restrict__ dv, E* __restrict__ dg,
                                                                 E* __restrict__ dbeta) {
     __shared__ float sbeta[C];
-    __shared__ float sr[DK];
     __shared__ float sbl[DK];
     __shared__ float sRowKG[C];       // sum_c dXw[t][c] KG[t][c], per row
     __shared__ float sColKd[4 * DK];  // sum_t dKd[t][c] Kd[t][c], per wave and column
@@ -705,11 +837,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
     const size_t oCK = (size_t)slot * C * DK, oCV = (size_t)slot * C * DV, oCC = (size_t)slot * C * C;
     const size_t oK = (size_t)slot * DK, oKV = (size_t)slot * DK * DV;
     if (tid < C) sbeta[tid] = tid < n ? ld(beta, (t0 + tid) * Hs + h) : 0.f;
-    if (tid < DK) {
-        sr[tid] = w.B[oCK + (size_t)((n - 1) / 2) * DK + tid];
-        sbl[tid] = w.B[oCK + (size_t)(n - 1) * DK + tid];
-    }
-    __syncthreads();  // sbeta, sr, sbl are read by every thread (also inside block-product loaders)
+    if (tid < DK) sbl[tid] = w.B[oCK + (size_t)(n - 1) * DK + tid];
+    __syncthreads();  // sbeta, sbl are read by every thread (also inside block-product loaders)
     const float* Sm = w.S + oKV;
     const float* dSn = w.dSn + oKV;
     const float* Um = w.U + oCV;
@@ -845,7 +974,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
 #pragma unroll
             for (int b = 0; b < C / 16; ++b) {
                 const int t = Acc<C>::row(a), i = Acc<C>::col(b);
-                sdT[t][i] = (i < t && t < n) ? at.t[b][a] : 0.f;
+                lds_put(&sdT[t][i], (i < t && t < n) ? at.t[b][a] : 0.f);
             }
         Acc<DK> ax;
         ax.zero();
@@ -871,7 +1000,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
 #pragma unroll
             for (int b = 0; b < C / 16; ++b) {
                 const int r = Acc<C>::row(a), i = Acc<C>::col(b);
-                sY[r][i] = (i < r && r < n) ? ay.t[b][a] : 0.f;
+                lds_put(&sY[r][i], (i < r && r < n) ? ay.t[b][a] : 0.f);
             }
     }
     __syncthreads();
@@ -893,9 +1022,18 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
     }  // PH == 1
 
     if constexpr (PH == 2) {
+    __shared__ float sTf[kTfRows * DK];  // tile decay factors and references
+    fill_tile_factors<E, DK>(sTf, [&](int row, int c) { return w.B[oCK + (size_t)row * DK + c]; });
+    __syncthreads();
 
     // phase 5: dKr = diag(beta) dA Ki, dKi = (diag(beta) dA)^T Kr + dP^T Qr,
-    // dQr = dP Ki; then dq, dk and db (kept in dW's slot), dbeta, dv
+    // dQr = dP Ki; then dq, dk and db (kept in dW's slot), dbeta, dv.
+    // Tile by tile: row-side results (dKr, dQr) of row tile a are referred to
+    // m(a), column-side ones (dKi) of column tile bb to m(bb), i.e. every
+    // result of a row is referred to the middle row of its own tile, like the
+    // stored operands.  Between two tiles the stored operand is first taken
+    // to its own tile's end (fe) or start (fs) and then on to the other
+    // tile's middle (f1, f2), factors <= 1 one after another.
     {
         const float* dA = w.dA + oCC;
         const float* dP = w.dP + oCC;
@@ -916,7 +1054,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
         float* tKi = tPr + KT * SA;  // [kk][c] = Ki[k0 + kk][c]
         float* tKr = tKi + KT * SB;
         float* tQr = tKr + KT * SB;
-        const int wv = tid / 64, lg = (tid % 64) / 16, lr = tid % 16;
+        const int wv = __builtin_amdgcn_readfirstlane(tid / 64), lg = (tid % 64) / 16, lr = tid % 16;
         Acc<DK> aKr, aQr, acc;  // acc: dKi
         aKr.zero();
         aQr.zero();
@@ -928,10 +1066,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
                 const int idx = tid + r * kBwdThreads;
                 const int m = idx / KT, kc = k0 + idx % KT;  // column blocks: 16 per row
                 rAc[r] = dA[(size_t)m * C + kc];
-                rPc[r] = dP[(size_t)m * C + kc];
+                rPc[r] = m == kc ? 0.f : dP[(size_t)m * C + kc];  // diagonal: see the epilogue
                 const int kr = k0 + idx / C, t = idx % C;    // row blocks: whole rows
                 rAr[r] = sbeta[kr] * dA[(size_t)kr * C + t];
-                rPr[r] = dP[(size_t)kr * C + t];
+                rPr[r] = kr == t ? 0.f : dP[(size_t)kr * C + t];
             }
 #pragma unroll
             for (int r = 0; r < RB; ++r) {
@@ -963,6 +1101,14 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
             }
             lds_barrier();
             if (k0 + KT < C) fetch(k0 + KT);
+            // kt: the tile of the summed token index.  Row side: dA and dP
+            // are zero above the diagonal (kt > wv); below it Ki goes to
+            // e(kt), then to m(wv).  Column side: nothing for kt < wv; for
+            // kt > wv, Kr and Qr go to s(kt), then to m(wv).
+            const int kt = k0 / KT;
+            const bool row_side = kt <= wv, col_side = kt >= wv;
+            const float* fu = sTf + (kt < wv ? kTfFe + kt : kTfFs + kt) * DK;
+            const float* fv = sTf + (kt < wv ? kTfF1 + pair_of(wv, kt) : kTfF2 + pair_of(kt > wv ? kt : 1, kt > wv ? wv : 0)) * DK;
 #pragma unroll
             for (int ks = 0; ks < KT; ks += 4) {
                 const int kr = ks + lg, ar = kr * SA + 16 * wv + lr;
@@ -970,11 +1116,22 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
 #pragma unroll
                 for (int j = 0; j < NT; ++j) {
                     const int br = kr * SB + 16 * j + lr;
-                    const float bKi = tKi[br], bKr = tKr[br], bQr = tQr[br];
-                    aKr.t[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_Ac, bKi, aKr.t[j], 0, 0, 0);
-                    aQr.t[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_Pc, bKi, aQr.t[j], 0, 0, 0);
-                    acc.t[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_Ar, bKr, acc.t[j], 0, 0, 0);
-                    acc.t[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_Pr, bQr, acc.t[j], 0, 0, 0);
+                    float bKi = tKi[br], bKr = tKr[br], bQr = tQr[br];
+                    if (kt < wv) {
+                        bKi = (bKi * fu[16 * j + lr]) * fv[16 * j + lr];
+                    } else if (kt > wv) {
+                        const float u = fu[16 * j + lr], x = fv[16 * j + lr];
+                        bKr = (bKr * u) * x;
+                        bQr = (bQr * u) * x;
+                    }
+                    if (row_side) {
+                        aKr.t[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_Ac, bKi, aKr.t[j], 0, 0, 0);
+                        aQr.t[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_Pc, bKi, aQr.t[j], 0, 0, 0);
+                    }
+                    if (col_side) {
+                        acc.t[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_Ar, bKr, acc.t[j], 0, 0, 0);
+                        acc.t[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_Pr, bQr, acc.t[j], 0, 0, 0);
+                    }
                 }
             }
             lds_barrier();
@@ -983,6 +1140,12 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
         // The same pass forms the row sums of dXw * KG (for dbeta) and the
         // column sums of dKd * Kd (for the last row of the gate's prefix sum),
         // with KG = k e^b and Kd = k e^{b_last - b} from factors at hand.
+        // Two pairs of terms cancel exactly in the gate's gradient and are
+        // left out of it, so that their rounding does not swamp a gradient
+        // that strong decay makes small: P's diagonal (P_tt = q_t . k_t
+        // carries no decay; it was left out of the products above and enters
+        // dq and dk here directly), and the last row's own Kd term against
+        // its share of the last-row column sum (Kd = k there).
         float rowp[4] = {0.f, 0.f, 0.f, 0.f};
         float colp[DK / 16];
 #pragma unroll
@@ -998,21 +1161,21 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
                 const float dXw = w.dXw[j];
                 const float dKG = sbeta[t] * dXw;
                 const float dQG = w.dQG[j], dKd = w.dKd[j];
-                const float bb = w.B[j], r = sr[c], bl = sbl[c];
-                const float e = gate_exp<E>(bb), er = gate_exp<E>(bb - r), eir = gate_exp<E>(r - bb),
+                const float bb = w.B[j], r = sTf[(kTfBm + wv) * DK + c], bl = sbl[c];
+                const float e = gate_exp<E>(bb), er = capped_exp<E>(bb - r), eir = capped_exp<E>(r - bb),
                             ed = gate_exp<E>(bl - bb);
                 const int64_t o = ((t0 + t) * Hs + h) * DK + c;
                 // the decayed operands are q or k times these factors, so the
                 // gate's gradient needs q and k themselves, not the six arrays
-                const float gq = dQG * e + dQr * er;    // dq
+                const float gq = dQG * e + dQr * er;    // dq without P's diagonal
                 const float gk_up = dKG * e + dKr * er;  // factors that grow with b
-                const float gk_dn = dKi * eir + dKd * ed;
-                const float kv = ld(k, o);
-                dq[o] = Elt<E>::from(gq);
-                dk[o] = Elt<E>::from(gk_up + gk_dn);
-                w.dW[j] = ld(q, o) * gq + kv * (gk_up - gk_dn);
+                const float gk_dd = dKi * eir, gk_kd = t == n - 1 ? 0.f : dKd * ed;
+                const float kv = ld(k, o), qv = ld(q, o), dPd = w.dP[oCC + (size_t)t * C + t];
+                dq[o] = Elt<E>::from(gq + dPd * kv);
+                dk[o] = Elt<E>::from(gk_up + gk_dd + dKd * ed + dPd * qv);
+                w.dW[j] = qv * gq + kv * (gk_up - (gk_dd + gk_kd));
                 rowp[a] += dXw * kv * e;
-                colp[b] += dKd * kv * ed;
+                colp[b] += gk_kd * kv;
             }
         // rows: the 16 lanes of a lane group; columns: the four lane groups of a
         // wave, then the four waves in a fixed order (no atomics: deterministic)

@@ -267,9 +267,11 @@ size_t kda_chunk_bwd_workspace_size(int64_t T_total, int32_t N, int32_t H,
  *
  * Alignment: every pointer to its element size.  Errors as for
  * kda_chunk_fwd.  Numerics: all arithmetic in fp32, gradients rounded once
- * to dt.  Domain: besides the forward's, the decay accumulated over any 32
- * consecutive tokens of a chunk must stay above e^-80 (e.g. every g >= -2.5),
- * since the operands are referred to the chunk's middle row.
+ * to dt.  Domain: the forward's.  Every decayed operand is referred to the
+ * middle row of its own 16-token tile and the decay between tiles is rebuilt
+ * from factors <= 1, so the gradients are exact (up to rounding) while the
+ * decay accumulated over any eight consecutive tokens stays above e^-80 (e.g.
+ * every g >= -10); stronger decay stays finite but loses accuracy.
  */
 kda_status kda_chunk_bwd(const void *q, const void *k, const void *v,
                          const void *g, const void *beta, const float *S0,

@@ -83,11 +83,68 @@ def test_bwd_without_s0_and_state_cotangent():
     _compare(got, _ref(d, "channel", dO, dST, with_s0=False, with_dst=False), TOL["f32"], "bwd no S0/dS_T")
 
 
-def test_bwd_gate_at_domain_edge():
-    """g = -2.5 on every channel: 32 tokens of decay reach e^-80."""
+def _set_gate(d, dtype, g32):
+    """Replace the log-gate by the float32 values g32 (rounded to the case's dtype)."""
+    g32 = np.asarray(g32, dtype=np.float32)
+    d["g"] = synth.bf16_bits(g32) if dtype == "bf16" else g32
+
+
+def test_bwd_moderate_gate():
+    """g = -2.5 on every channel: 32 tokens of decay reach e^-80 (the limit
+    of a single reference row per chunk)."""
     d, dO, dST = _case(2, 64, 64, "f32", "channel", [128, 100], seed=10)
-    d["g"] = np.full_like(d["g"], -2.5)
+    _set_gate(d, "f32", np.full(d["g"].shape, -2.5))
     _compare(_run(d, "f32", "channel", dO, dST), _ref(d, "channel", dO, dST), TOL["f32"], "bwd g=-2.5")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_gate_minus_ten(dtype):
+    """g = -10 on every channel: eight tokens of decay reach e^-80, the edge
+    of the supported range; a whole chunk decays by e^-640."""
+    d, dO, dST = _case(2, 128, 128, dtype, "channel", [150, 64, 37], seed=20)
+    _set_gate(d, dtype, np.full(d["g"].shape, -10.0))
+    _compare(_run(d, dtype, "channel", dO, dST), _ref(d, "channel", dO, dST), TOL[dtype], f"bwd g=-10 {dtype}")
+
+
+def _mixed_gate(shape, seed, fast):
+    """Per-channel gates: a third of the (head, channel) pairs forget fast
+    (g = `fast` at every token), a third slowly (g = -0.1), the rest draw g
+    uniformly from [-10, 0] at every token."""
+    T, H, dk = shape
+    rng = np.random.default_rng(seed)
+    kind = rng.integers(0, 3, size=(1, H, dk))
+    g = np.where(kind == 0, fast, np.where(kind == 1, -0.1, rng.uniform(-10.0, 0.0, size=(T, H, dk))))
+    return np.ascontiguousarray(np.broadcast_to(g, (T, H, dk)), dtype=np.float32)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_mixed_fast_and_slow_channels(dtype):
+    """Fast channels at the edge of the range (g = -10), slow ones (g = -0.1)
+    and channels uniform in [-10, 0], side by side."""
+    d, dO, dST = _case(2, 128, 128, dtype, "channel", [200, 90], seed=21)
+    _set_gate(d, dtype, _mixed_gate(d["g"].shape, 2121, -10.0))
+    _compare(_run(d, dtype, "channel", dO, dST), _ref(d, "channel", dO, dST), TOL[dtype], f"bwd mixed {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_beyond_range_stays_finite(dtype):
+    """Channels at g = -30 (beyond the exact range: eight tokens decay by
+    e^-240) next to slow ones: every gradient stays finite."""
+    d, dO, dST = _case(2, 128, 128, dtype, "channel", [200, 90], seed=24)
+    _set_gate(d, dtype, _mixed_gate(d["g"].shape, 2424, -30.0))
+    got = _run(d, dtype, "channel", dO, dST)
+    errs = {n: rel_err(np.nan_to_num(gv, nan=0.0, posinf=0.0, neginf=0.0), rv)
+            for n, gv, rv in zip(NAMES, got, _ref(d, "channel", dO, dST))}
+    print(f"bwd beyond range {dtype}", " ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
+    for n, gv in zip(NAMES, got):
+        assert np.all(np.isfinite(gv)), n
+
+
+def test_bwd_strong_per_head_gate():
+    """The Gated DeltaNet special case at g = -8 per (token, head)."""
+    d, dO, dST = _case(2, 128, 128, "f32", "head", [129, 64], seed=22)
+    _set_gate(d, "f32", np.full(d["g"].shape, -8.0))
+    _compare(_run(d, "f32", "head", dO, dST), _ref(d, "head", dO, dST), TOL["f32"], "bwd head g=-8")
 
 
 def test_bwd_longer_bench_distribution():

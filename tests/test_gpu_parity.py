@@ -202,6 +202,45 @@ def test_chunk_deterministic_and_s0_none_equals_zeros():
         assert torch.equal(o, runs[0][0]) and torch.equal(S, runs[0][1])
 
 
+def _mixed_gate(shape, seed, fast):
+    """Per-channel gates: a third of the (head, channel) pairs forget fast
+    (g = `fast` at every token), a third slowly (g = -0.1), the rest draw g
+    uniformly from [-10, 0] at every token."""
+    T, H, dk = shape
+    rng = np.random.default_rng(seed)
+    kind = rng.integers(0, 3, size=(1, H, dk))
+    g = np.where(kind == 0, fast, np.where(kind == 1, -0.1, rng.uniform(-10.0, 0.0, size=(T, H, dk))))
+    return np.ascontiguousarray(np.broadcast_to(g, (T, H, dk)), dtype=np.float32)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunk_mixed_fast_and_slow_channels(dtype):
+    """Fast channels at the edge of the exact range (g = -10), slow ones
+    (g = -0.1) and channels uniform in [-10, 0], side by side."""
+    _announce(f"mixed fast/slow gates {dtype}")
+    d = chunk_case(2, 128, 128, dtype, "channel", [200, 90], seed=23)
+    g = _mixed_gate(d["g"].shape, 2323, -10.0)
+    d["g"] = synth.bf16_bits(g) if dtype == "bf16" else g
+    o, S = _run_chunk(d, dtype, "channel")
+    o_ref, S_ref = _oracle_chunk(d, "channel")
+    _assert_close("o", o, o_ref, TOL[dtype])
+    _assert_close("S_T", S, S_ref, TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunk_beyond_range_stays_finite(dtype):
+    """Channels at g = -30 (beyond the exact range) next to slow ones: o and
+    S_T stay finite."""
+    _announce(f"beyond-range gates {dtype}")
+    d = chunk_case(2, 128, 128, dtype, "channel", [200, 90], seed=25)
+    g = _mixed_gate(d["g"].shape, 2525, -30.0)
+    d["g"] = synth.bf16_bits(g) if dtype == "bf16" else g
+    o, S = _run_chunk(d, dtype, "channel")
+    o_ref, S_ref = _oracle_chunk(d, "channel")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
+    print(f"beyond range {dtype}: o {oracle.rel_err(o, o_ref):.2e} S_T {oracle.rel_err(S, S_ref):.2e}", flush=True)
+
+
 def test_chunk_batched_equals_packed():
     _announce("batched [B,T,H,d] == packed")
     d = chunk_case(2, 64, 64, "bf16", "channel", [96, 96], seed=10)
