@@ -42,9 +42,9 @@ BF16, F32, F64 = 0, 1, 2
 
 
 def build(force: bool = True) -> str:
-    """Compile the C oracle with gcc (plain -O2, no fast-math) into oracle/."""
+    """Compile the C oracle with gcc (-O3, no fast-math: IEEE fp64 throughout) into oracle/."""
     if force or not os.path.exists(_LIB):
-        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+        cmd = ["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-std=c11",
                "-Wall", "-Wextra", "-o", _LIB + ".tmp", _SRC, "-lm"]
         subprocess.check_call(cmd)
         os.replace(_LIB + ".tmp", _LIB)

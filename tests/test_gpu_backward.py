@@ -4,18 +4,24 @@ gradient oracle (autograd of the sequential recurrence).
 Every gradient (dq, dk, dv, dg, dbeta, dS0) is compared element by element:
 max|gpu - oracle| / max|oracle| <= 1e-4 for fp32 inputs and <= 1e-2 for bf16
 inputs (fp32 state and fp32 arithmetic inside), the bounds stated for the
-forward path.  The full-size case (T = 32768, H = 32, d = 128) uses a
-property that holds at any length: with dO zero after the first P tokens and
-dS_T = 0, the gradients of those P tokens are those of the P-token problem
-(causality) and every later gradient is exactly zero.
+forward path.  Small cases use the autograd oracle; the benchmark workloads
+(T = 32768 x 32 heads, the packed 8-sequence Gated DeltaNet batch, and
+T = 1,048,576 x 16 heads) use the hand-written fp64 C adjoint with dense
+cotangents dO and dS_T, so that the reverse state walk carries a nonzero
+cotangent through every chunk.  A causality property is checked as well: with
+dO zero after the first P tokens and dS_T = 0, the gradients of those P tokens
+are those of the P-token problem and every later gradient is exactly zero.
 """
+import os
+import sys
+
 import numpy as np
 import pytest
 import torch
 
 import synth
 from oracle import rel_err
-from oracle.grad import recurrence_grad
+from oracle.grad import adjoint, recurrence_grad
 
 from _kda_cases import TOL, chunk_case, to_dev, to_np64
 
@@ -283,3 +289,93 @@ def test_bwd_1m_tokens_in_head_groups_prefix_support():
         e = rel_err(gv, rv)
         print(f"bwd 1m prefix {n_}={e:.2e}", flush=True)
         assert e <= TOL["bf16"], (n_, e)
+
+
+def _threads():
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _say(msg):
+    sys.stdout.write(f"\n[case] {msg}\n")
+    sys.stdout.flush()
+
+
+def _dense_cotangents(seed, T, N, H, dk, dv, block=1 << 16):
+    """dO ~ N(0, 1) as bf16 bits, drawn in blocks of rows; dS_T ~ N(0, 1) fp32."""
+    rng = np.random.default_rng(seed)
+    dO = np.empty((T, H, dv), dtype=np.uint16)
+    for s0 in range(0, T, block):
+        e = min(T, s0 + block)
+        dO[s0:e] = synth.bf16_bits(rng.standard_normal((e - s0, H, dv), dtype=np.float32))
+    dST = rng.standard_normal((N, H, dk, dv), dtype=np.float32)
+    return dO, dST
+
+
+def test_bwd_full_size_dense():
+    """T = 32768, H = 32, d = 128, bf16 (the prefill benchmark workload) with
+    dense dO and dS_T: every gradient, every element, against the C adjoint."""
+    _say("bwd 32k x 32 dense")
+    cfg = synth.CONFIGS["kda_32k_bf16"]
+    d = synth.chunk_inputs(cfg)
+    T, H, dk, dv = cfg.T, cfg.H, cfg.dk, cfg.dv
+    dO, dST = _dense_cotangents(3032, T, 1, H, dk, dv)
+    x = {n: to_dev(d[n], "bf16") for n in ("q", "k", "v", "g", "beta")}
+    got = kda.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], to_dev(dO, "bf16"),
+                        dS_T=torch.from_numpy(dST).cuda())
+    torch.cuda.synchronize()
+    got = [to_np64(t) for t in got]
+    _say("bwd 32k x 32 dense: oracle")
+    ref = adjoint(d["q"], d["k"], d["v"], d["g"], d["beta"], dO, dS_T=dST, threads=_threads())
+    _compare(got, ref, TOL["bf16"], "bwd 32k dense")
+
+
+def test_bwd_varlen_gated_deltanet_dense():
+    """The packed 8-sequence Gated DeltaNet workload (per-head gate, S0 given,
+    H = 16, d = 128, bf16) with dense dO and dS_T, against the C adjoint."""
+    _say("bwd gdn varlen dense")
+    cfg = synth.CONFIGS["gdn_varlen_bf16"]
+    d = synth.chunk_inputs(cfg)
+    cu = d["cu_seqlens"].astype(np.int64)
+    T, H, dk, dv, N = int(cu[-1]), cfg.H, cfg.dk, cfg.dv, len(cu) - 1
+    dO, dST = _dense_cotangents(2022, T, N, H, dk, dv)
+    x = {n: to_dev(d[n], "bf16") for n in ("q", "k", "v", "g", "beta")}
+    got = kda.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], to_dev(dO, "bf16"),
+                        S0=torch.from_numpy(d["S0"]).cuda(), dS_T=torch.from_numpy(dST).cuda(),
+                        cu_seqlens=torch.from_numpy(cu.astype(np.int32)).cuda(), per_head_gate=True)
+    torch.cuda.synchronize()
+    got = [to_np64(t) for t in got]
+    ref = adjoint(d["q"], d["k"], d["v"], d["g"], d["beta"], dO, S0=d["S0"], dS_T=dST, cu_seqlens=cu,
+                  per_head_gate=True, threads=_threads())
+    _compare(got, ref, TOL["bf16"], "bwd gdn varlen dense")
+
+
+def test_bwd_1m_dense_sampled_in_head_groups():
+    """The 1M-token workload (T = 1,048,576, H = 16, d = 128, bf16) with dense
+    dO and dS_T, through a workspace for four heads: the gradients at 4096
+    seeded positions and the full dS0, against the C adjoint (which walks all
+    16,384 chunks of every head in fp64)."""
+    _say("bwd 1m x 16 dense: inputs")
+    cfg = synth.CONFIGS["kda_1m_bf16"]
+    T, H, dk, dv = cfg.T, cfg.H, cfg.dk, cfg.dv
+    shapes = {"q": (T, H, dk), "k": (T, H, dk), "v": (T, H, dv), "g": (T, H, dk), "beta": (T, H)}
+    host = {n: np.empty(s, dtype=np.uint16) for n, s in shapes.items()}
+    dev = {n: torch.empty(s, dtype=torch.bfloat16, device="cuda") for n, s in shapes.items()}
+    for b, start, blk in synth.iter_token_blocks(cfg, workers=8):
+        rows = blk["q"].shape[0]
+        for n in shapes:
+            host[n][start:start + rows] = blk[n]
+            dev[n][start:start + rows].copy_(torch.from_numpy(blk[n].view(np.int16)).view(torch.bfloat16))
+    dO, dST = _dense_cotangents(4041, T, 1, H, dk, dv)
+    pos = synth.sample_positions(T, 4096, seed=4042)
+    _say("bwd 1m x 16 dense: gpu")
+    ws = torch.empty(kda.chunk_bwd_workspace_size(T, 1, 4, dk, dv), dtype=torch.uint8, device="cuda")
+    got = kda.chunk_bwd(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], to_dev(dO, "bf16"),
+                        dS_T=torch.from_numpy(dST).cuda(), workspace=ws)
+    idx = torch.from_numpy(pos).cuda()
+    got = [to_np64(t[idx]) for t in got[:5]] + [to_np64(got[5])]
+    torch.cuda.synchronize()
+    del dev, ws
+    _say("bwd 1m x 16 dense: oracle")
+    ref = adjoint(host["q"], host["k"], host["v"], host["g"], host["beta"], dO, dS_T=dST, positions=pos,
+                  threads=_threads())
+    _compare(got, ref, TOL["bf16"], "bwd 1m dense")

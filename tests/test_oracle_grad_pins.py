@@ -1,7 +1,8 @@
-"""Pins for the gradient oracle (``oracle.grad.recurrence_grad``).
+"""Pins for the gradient oracles (``oracle.grad.recurrence_grad``, autograd of
+the sequential recurrence, and ``oracle.grad.adjoint``, the hand-written fp64
+C adjoint).
 
-The gradient oracle differentiates the sequential recurrence with autograd.
-These tests tie it to things that do not come from that tape:
+These tests tie both to things that do not come from either:
 
 * a one-token closed form, derived by hand from the transition
   S_1 = (I - beta k k^T) Diag(a) S_0 + beta k v^T, o = S_1^T q, with
@@ -9,7 +10,13 @@ These tests tie it to things that do not come from that tape:
 * central finite differences of the C forward oracle (a separate program) in
   every input element, for per-channel and per-head gates and two packed
   sequences;
-* linearity of a vector-Jacobian product in its cotangents.
+* linearity of a vector-Jacobian product in its cotangents;
+* for the adjoint at lengths autograd cannot reach (thousands of tokens,
+  several checkpoint stretches), exact identities of the loss: L is linear in
+  q (o_t = S_t^T q_t and the state does not depend on q) and jointly linear in
+  (v, S0) (the state is), so L(x + d) - L(x) = <dL/dx, d> up to rounding, with
+  L evaluated by the C forward oracle;
+* the two implementations against each other on varied packed batches.
 
 A dropped term, a wrong sign, a transposed operand or a gate applied after
 the read in the oracle's update fails the finite-difference test; a mistake
@@ -19,7 +26,9 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle.grad import recurrence_grad
+from oracle.grad import adjoint, recurrence_grad
+
+GRADS = {"autograd": recurrence_grad, "adjoint": adjoint}
 
 
 def _inputs(rng, T, H, dk, dv, N=1, per_head=False):
@@ -33,7 +42,8 @@ def _inputs(rng, T, H, dk, dv, N=1, per_head=False):
     return q, k, v, g, beta, S0
 
 
-def test_one_token_closed_form():
+@pytest.mark.parametrize("impl", sorted(GRADS))
+def test_one_token_closed_form(impl):
     """T = 1 per sequence: every gradient written out by hand."""
     rng = np.random.default_rng(11)
     H, dk, dv = 3, 5, 4
@@ -42,7 +52,7 @@ def test_one_token_closed_form():
     q, k, v, g, beta, S0 = _inputs(rng, T, H, dk, dv, N=len(lengths))
     dO = rng.standard_normal((T, H, dv))
     dST = rng.standard_normal((len(lengths), H, dk, dv))
-    got = recurrence_grad(q, k, v, g, beta, dO, S0=S0, dS_T=dST, cu_seqlens=[0, 1, 2])
+    got = GRADS[impl](q, k, v, g, beta, dO, S0=S0, dS_T=dST, cu_seqlens=[0, 1, 2])
     for n in range(len(lengths)):
         for h in range(H):
             t = n
@@ -72,8 +82,9 @@ def _loss(x, dO, dST, cu, per_head):
     return float((o * dO).sum() + (S_T * dST).sum())
 
 
+@pytest.mark.parametrize("impl", sorted(GRADS))
 @pytest.mark.parametrize("per_head", [False, True])
-def test_finite_differences_of_forward_oracle(per_head):
+def test_finite_differences_of_forward_oracle(per_head, impl):
     """Every element of every input: central differences of the C oracle."""
     rng = np.random.default_rng(12 + per_head)
     cu = [0, 4, 9]
@@ -81,7 +92,7 @@ def test_finite_differences_of_forward_oracle(per_head):
     x = list(_inputs(rng, T, H, dk, dv, N=2, per_head=per_head))
     dO = rng.standard_normal((T, H, dv))
     dST = rng.standard_normal((2, H, dk, dv))
-    grads = recurrence_grad(*x[:5], dO, S0=x[5], dS_T=dST, cu_seqlens=cu, per_head_gate=per_head)
+    grads = GRADS[impl](*x[:5], dO, S0=x[5], dS_T=dST, cu_seqlens=cu, per_head_gate=per_head)
     eps = 1e-6
     for i, (xi, gi) in enumerate(zip(x, grads)):
         assert gi.shape == xi.shape
@@ -121,3 +132,62 @@ def test_zero_length_sequence_passes_state_gradient_through():
     dST = rng.standard_normal((2, H, dk, dv))
     got = recurrence_grad(q, k, v, g, beta, dO, S0=S0, dS_T=dST, cu_seqlens=[0, 0, 5])
     assert np.array_equal(got[5][0], dST[0])
+
+
+@pytest.mark.parametrize("per_head", [False, True])
+def test_adjoint_matches_autograd(per_head):
+    """Packed sequences of assorted lengths (empty, one token, several
+    checkpoint stretches, a ragged tail), with and without S0 and dS_T."""
+    rng = np.random.default_rng(15 + per_head)
+    lengths = [0, 1, 37, 300, 17]
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    T, H, dk, dv = int(cu[-1]), 2, 6, 5
+    q, k, v, g, beta, S0 = _inputs(rng, T, H, dk, dv, N=len(lengths), per_head=per_head)
+    dO = rng.standard_normal((T, H, dv))
+    dST = rng.standard_normal((len(lengths), H, dk, dv))
+    for s0, dst in ((S0, dST), (None, None)):
+        a = adjoint(q, k, v, g, beta, dO, S0=s0, dS_T=dst, cu_seqlens=cu, per_head_gate=per_head)
+        b = recurrence_grad(q, k, v, g, beta, dO, S0=s0, dS_T=dst, cu_seqlens=cu, per_head_gate=per_head)
+        for x, y in zip(a, b):
+            assert x.shape == y.shape
+            assert oracle.rel_err(x, y) < 1e-12
+
+
+def test_adjoint_exact_identities_at_length():
+    """T = 3000 (about 55 checkpoint stretches): L is linear in q and jointly
+    linear in (v, S0), so a finite step of any size changes L by exactly the
+    inner product of the gradient with the step (up to fp64 rounding)."""
+    rng = np.random.default_rng(16)
+    T, H, dk, dv = 3000, 2, 8, 6
+    q, k, v, g, beta, S0 = _inputs(rng, T, H, dk, dv)
+    dO = rng.standard_normal((T, H, dv))
+    dST = rng.standard_normal((1, H, dk, dv))
+    dq, _, dv_, _, _, dS0 = adjoint(q, k, v, g, beta, dO, S0=S0, dS_T=dST)
+    L0 = _loss([q, k, v, g, beta, S0], dO, dST, [0, T], False)
+    Dq = rng.standard_normal(q.shape)
+    Lq = _loss([q + Dq, k, v, g, beta, S0], dO, dST, [0, T], False)
+    assert abs((Lq - L0) - (dq * Dq).sum()) <= 1e-9 * max(1.0, abs(Lq - L0))
+    Dv, DS = rng.standard_normal(v.shape), rng.standard_normal(S0.shape)
+    Lv = _loss([q, k, v + Dv, g, beta, S0 + DS], dO, dST, [0, T], False)
+    want = (dv_ * Dv).sum() + (dS0 * DS).sum()
+    assert abs((Lv - L0) - want) <= 1e-9 * max(1.0, abs(Lv - L0))
+
+
+def test_adjoint_selected_rows_and_bf16_bits():
+    """Gradients of selected tokens only, and bf16-bit inputs and cotangents,
+    give the same values as the full computation on the widened inputs."""
+    import synth
+    rng = np.random.default_rng(17)
+    T, H, dk, dv = 400, 2, 8, 8
+    q, k, v, g, beta, S0 = _inputs(rng, T, H, dk, dv)
+    bits = [synth.bf16_bits(x.astype(np.float32)) for x in (q, k, v, g, beta)]
+    dO = synth.bf16_bits(rng.standard_normal((T, H, dv)).astype(np.float32))
+    full = adjoint(*bits, dO, S0=S0)
+    wide = adjoint(*(oracle.widen(b) for b in bits), oracle.widen(dO), S0=S0)
+    for x, y in zip(full, wide):
+        assert np.array_equal(x, y)
+    pos = np.array([0, 5, 63, 64, 399])
+    part = adjoint(*bits, dO, S0=S0, positions=pos)
+    for x, y in zip(part[:5], full[:5]):
+        assert np.array_equal(x, y[pos])
+    assert np.array_equal(part[5], full[5])
