@@ -8,12 +8,19 @@ One step = one pass of the whole hot path over one batch of synthetic input:
     state (kda_recurrent_step).
 Inputs are generated once (seeded, synth.CONFIGS / DECODE_CONFIGS) and are
 resident in HBM before the timed region.  `value` is prefill tokens/s over
-the chunked-forward time of the timed steps; `decode` reports the decode step
-in GB/s of its algorithmic bytes.  Each kernel is timed with HIP events
-recorded on the stream it runs on.  The oracle (fp64, host cores) is timed
-on a bounded prefix of the same workload as `cpu_baseline`.  After the timed
-steps, the chunked backward pass (kda_chunk_bwd) over the same prefill inputs
-is timed on its own and reported under `backward`, and the pre-path
+the chunked-forward time of the timed steps.  `roofline` prices the dominant
+kernel of the step against HBM with the method's own minimum bytes (bf16 q,
+k, v, g, o and beta: 1282 B per head-token); `path_roofline` does the same
+for the whole kda_chunk_fwd call, next to its fraction of the bf16 MFMA peak
+at the algorithmic FLOP count; `kernels_intermediate` gives each prefill
+kernel's rate over the bytes it actually moves (its inputs plus the
+intermediates it reads or writes).  Each kernel is timed with HIP events
+recorded on the stream it runs on.  `decode` reports 64 decode steps launched
+back to back, each timed, in GB/s of the step's algorithmic bytes.  The
+oracle (fp64, host cores) is timed on a bounded prefix of the same workload as
+`cpu_baseline`.  After the timed steps, the 1M-token prefill (T = 1,048,576,
+H = 16) is timed under `long_context`, the chunked backward pass
+(kda_chunk_bwd) over the 32K prefill inputs under `backward`, the pre-path
 transforms (kda_prepare_inputs on the prefill inputs, and the decode step with
 them fused in) under `prepath`, and the d = 64 variant of the prefill at the
 same model width (H = 64) under `variant_d64`.
@@ -111,6 +118,26 @@ def _to_dev(a, torch):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
 
 
+def cpu_model():
+    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.strip().startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(d, prefix_tokens):
     import oracle
     oracle.build(force=False)
@@ -121,7 +148,7 @@ def cpu_baseline(d, prefix_tokens):
     oracle.recurrence(sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["g"]), sl(d["beta"]), cu_seqlens=[0, T],
                       threads=threads)
     dt = time.perf_counter() - t0
-    return {"value": T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": T / dt, "unit": "tokens/s", "cores": threads, "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"first {T} tokens of the 32K x 32-head prefill workload (all heads; the whole "
                       f"workload when {T} = 32768), fp64 sequential recurrence, {dt:.2f} s"}
 
@@ -190,6 +217,46 @@ def time_prepath(kda, torch, hip, x, T, H, dk, stream, S_dec, toks, steps=10):
     }
 
 
+def time_long_context(kda, torch, hip, stream, steps=3):
+    """The 1M-token prefill (kda_1m_bf16: B=1, T=1,048,576, H=16, d=128,
+    bf16, per-channel gate from N(-1,1)) through kda_chunk_fwd, inputs drawn
+    block by block (the recipe of the parity test) and resident in HBM before
+    the timed calls; each call timed with HIP events on its stream."""
+    import synth
+    cfg = synth.CONFIGS["kda_1m_bf16"]
+    T, H, dk, dv = cfg.T, cfg.H, cfg.dk, cfg.dv
+    shapes = {"q": (T, H, dk), "k": (T, H, dk), "v": (T, H, dv), "g": (T, H, dk), "beta": (T, H)}
+    dev = {n: torch.empty(s, dtype=torch.bfloat16, device="cuda") for n, s in shapes.items()}
+    for _, start, blk in synth.iter_token_blocks(cfg, workers=8):
+        rows = blk["q"].shape[0]
+        for n in shapes:
+            dev[n][start:start + rows].copy_(torch.from_numpy(blk[n].view(np.int16)).view(torch.bfloat16))
+    o = torch.empty((T, H, dv), dtype=torch.bfloat16, device="cuda")
+    S_T = torch.empty((1, H, dk, dv), dtype=torch.float32, device="cuda")
+    ws = torch.empty(kda.chunk_fwd_workspace_size(T, 1, H, dk, dv), dtype=torch.uint8, device="cuda")
+    ev = Events(hip, steps + 1)
+
+    def run():
+        kda.chunk_fwd(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], out=o, S_T=S_T, workspace=ws)
+
+    run()
+    ev.record(0, stream)
+    for i in range(steps):
+        run()
+        ev.record(i + 1, stream)
+    torch.cuda.synchronize()
+    ms = [ev.ms(i, i + 1) for i in range(steps)]
+    t = float(np.median(ms))
+    ht = T * H
+    gbs = PATH_MIN_BYTES_PER_HT * ht / (t * 1e-3) / 1e9
+    res = {"what": f"kda_chunk_fwd, kda_1m_bf16: T={T}, H={H}, d_k=d_v={dk}, bf16", "ms_median": t,
+           "ms_min": float(np.min(ms)), "tokens_per_s": T / (t * 1e-3), "method_GB_per_s": gbs,
+           "frac_hbm_peak": gbs / HBM_PEAK_GBS}
+    del dev, o, S_T, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def time_d64_variant(kda, torch, hip, stream, T=32768, H=64, steps=5):
     """The d_k = d_v = 64 variant at the same model width (H = 64 heads of 64
     channels, T = 32768, bf16, per-channel gate, seeded inputs of the 32K
@@ -224,6 +291,7 @@ def main():
     ap.add_argument("--cpu-prefix", type=int, default=32768)
     ap.add_argument("--no-backward", action="store_true", help="skip timing the chunked backward pass")
     ap.add_argument("--no-variants", action="store_true", help="skip timing the d = 64 variant")
+    ap.add_argument("--no-long-context", action="store_true", help="skip timing the 1M-token prefill")
     ap.add_argument("--backward-steps", type=int, default=5)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one device-to-device copy of exactly 1 GiB before the timed steps, so that a "
@@ -297,9 +365,10 @@ def main():
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / K
 
-    # decode steps back to back on one state (the serving pattern), after the
-    # timed region: the step above follows a prefill, these follow each other
-    n_b2b = 20
+    # 64 decode steps back to back on one state (the serving pattern), each
+    # timed, after the timed region: the step above follows a prefill, these
+    # follow each other
+    n_b2b = 64
     ev_b2b = Events(hip, n_b2b + 1)
     for i in range(3):
         tk = toks[i % n_tok]
@@ -310,10 +379,12 @@ def main():
         kda.recurrent_step(tk["q"], tk["k"], tk["v"], tk["g"], tk["beta"], S_dec, out=o_dec)
         ev_b2b.record(i + 1, stream)
     torch.cuda.synchronize()
-    t_b2b = float(np.median([ev_b2b.ms(i, i + 1) for i in range(n_b2b)]))
+    b2b_ms = [ev_b2b.ms(i, i + 1) for i in range(n_b2b)]
+    t_b2b = float(np.median(b2b_ms))
 
     prepath = time_prepath(kda, torch, hip, x, T, H, dk, stream, S_dec, toks)
     d64 = None if args.no_variants else time_d64_variant(kda, torch, hip, stream)
+    longc = None if args.no_long_context else time_long_context(kda, torch, hip, stream)
     bwd = None if args.no_backward else time_backward(kda, torch, hip, x, d, T, H, dk, dv, stream,
                                                       steps=args.backward_steps)
 
@@ -325,14 +396,20 @@ def main():
     ht = T * H
     tokens_per_s = T / (t_fwd * 1e-3)
 
+    # the method's minimum bytes per launch: a prefill kernel is priced with
+    # the whole path's 1282 B per head-token, the decode step with its own
     kern = {
-        "kda::intra_chunk_kernel": (t_intra, INTRA_BYTES_PER_HT * ht),
-        "kda::chunk_walk_kernel": (t_walk, WALK_BYTES_PER_HT * ht),
+        "kda::intra_chunk_kernel": (t_intra, PATH_MIN_BYTES_PER_HT * ht),
+        "kda::chunk_walk_kernel": (t_walk, PATH_MIN_BYTES_PER_HT * ht),
         "kda::decode_step_kernel": (t_dec, DECODE_BYTES_PER_STEP),
     }
     dom = max(kern, key=lambda k: kern[k][0])
     dom_ms, dom_bytes = kern[dom]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    inter = {"intra_chunk": {"ms": t_intra, "bytes": INTRA_BYTES_PER_HT * ht,
+                             "GB_per_s": INTRA_BYTES_PER_HT * ht / (t_intra * 1e-3) / 1e9},
+             "chunk_walk": {"ms": t_walk, "bytes": WALK_BYTES_PER_HT * ht,
+                            "GB_per_s": WALK_BYTES_PER_HT * ht / (t_walk * 1e-3) / 1e9}}
     dec_gbs = DECODE_BYTES_PER_STEP / (t_dec * 1e-3) / 1e9
     path_gbs = PATH_MIN_BYTES_PER_HT * ht / (t_fwd * 1e-3) / 1e9
     path_tflops = PATH_FLOP_PER_HT * ht / (t_fwd * 1e-3) / 1e12
@@ -361,17 +438,25 @@ def main():
         "decode": {"us_per_step": t_dec * 1e3, "GB_per_s": dec_gbs, "frac_hbm_peak": dec_gbs / HBM_PEAK_GBS,
                    "tokens_per_s": dcfg.N / (t_dec * 1e-3), "bytes_per_step": DECODE_BYTES_PER_STEP,
                    "back_to_back": {"steps": n_b2b, "us_per_step_median": t_b2b * 1e3,
+                                    "us_per_step_min": float(np.min(b2b_ms)) * 1e3,
                                     "GB_per_s": DECODE_BYTES_PER_STEP / (t_b2b * 1e-3) / 1e9,
-                                    "frac_hbm_peak": DECODE_BYTES_PER_STEP / (t_b2b * 1e-3) / 1e9 / HBM_PEAK_GBS}},
+                                    "frac_hbm_peak": DECODE_BYTES_PER_STEP / (t_b2b * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                    "tokens_per_s": dcfg.N / (t_b2b * 1e-3)}},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(dom),
-                     "algorithmic_bytes": dom_bytes},
+                     "algorithmic_bytes": dom_bytes,
+                     "what": "the method's minimum bytes per launch (1282 B per head-token for a prefill "
+                             "kernel, the decode step's state and token bytes) over the dominant kernel's "
+                             "HIP-event time"},
+        "kernels_intermediate": inter,
         "path_roofline": {"what": "whole kda_chunk_fwd call vs the method's minimum bytes (1282 B/head-token) "
                                   "and algorithmic FLOPs (139136 /head-token)",
                           "GB_per_s": path_gbs, "frac_hbm_peak": path_gbs / HBM_PEAK_GBS,
                           "TFLOP_per_s": path_tflops, "frac_bf16_mfma_peak": path_tflops / BF16_MFMA_PEAK_TFLOPS},
     }
     res["prepath"] = prepath
+    if longc is not None:
+        res["long_context"] = longc
     if d64 is not None:
         res["variant_d64"] = d64
     if bwd is not None:

@@ -36,6 +36,8 @@
 //                      d_v): walks the chunks in order with its fp32 slice of
 //                      S in registers; U = U' - W S, O = QG S + P U,
 //                      S <- Diag(Gn) S + KdT U, all on MFMA
+#include <atomic>
+
 #include "kda_internal.h"
 
 namespace kda {
@@ -1400,17 +1402,29 @@ ChunkWorkspace carve_chunk_workspace(void* base, int64_t T, int32_t N, int32_t H
     return w;
 }
 
+// Allow a kernel more than the default dynamic LDS, once per (kernel, device):
+// `done` holds one bit per device, set once the call has succeeded there.
+// Setting the attribute twice (two threads racing on a first call) is
+// harmless.
+static hipError_t ensure_lds_attr(const void* kern, int bytes, std::atomic<uint64_t>& done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t{1} << dev) : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
+
 template <typename E, int DK, int DV, bool HG>
 static hipError_t launch_intra(const ChunkArgs& a, const ChunkWorkspace& ws, hipStream_t stream) {
     using L = IntraLayout<E, DK, DV>;
     auto kern = intra_chunk_kernel<E, DK, DV, HG>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> attr_done{0};
+    if (hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(kern), (int)L::bytes, attr_done);
+        e != hipSuccess)
+        return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)(a.max_chunks * a.H)), dim3(kIntraThreads), L::bytes, stream,
                        (const E*)a.q, (const E*)a.k, (const E*)a.v, (const E*)a.g, (const E*)a.beta, ws.header,
                        ws.chunk_tab, a.H, (E*)ws.W, (E*)ws.QG, (E*)ws.KdT, (E*)ws.Up, (E*)ws.P, ws.Gn);
@@ -1421,13 +1435,10 @@ template <typename E, int DK, int DV>
 static hipError_t launch_walk(const ChunkArgs& a, const ChunkWorkspace& ws, int64_t blocks, hipStream_t stream) {
     using L = WalkLayout<E, DK, DV>;
     auto kern = chunk_walk_kernel<E, DK, DV>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> attr_done{0};
+    if (hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(kern), (int)L::bytes, attr_done);
+        e != hipSuccess)
+        return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kWalkThreads), L::bytes, stream, ws.header, ws.cu,
                        ws.chunk_off, a.N, a.H, (const E*)ws.W, (const E*)ws.QG, (const E*)ws.KdT, (const E*)ws.Up,
                        (const E*)ws.P, (const float*)ws.Gn, a.S0, a.S_T, (E*)a.o);
