@@ -5,6 +5,8 @@ Thin Python binding over the C ABI of ``libkda.so`` (declared in
 in the library's HIP kernels.  PyTorch provides device memory and streams.
 
     chunk_fwd(q, k, v, g, beta, S0=..., cu_seqlens=...) -> (o, S_T)
+    chunk_fwd_noalloc(q, k, v, g, beta, out=o, S_T=..., ...) -> (o, S_T)
+        (the same, with the library's static scratch instead of a workspace)
     recurrent_step(q, k, v, g, beta, S) -> o            (S updated in place)
     chunk_bwd(q, k, v, g, beta, dO, S0=..., dS_T=..., cu_seqlens=...)
         -> (dq, dk, dv, dg, dbeta, dS0)                  (gradients of the forward)
@@ -22,14 +24,14 @@ import os
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_fwd_workspace_size", "chunk_fwd_check", "recurrent_step",
+__all__ = ["chunk_fwd", "chunk_fwd_workspace_size", "chunk_fwd_check", "chunk_fwd_noalloc", "recurrent_step",
            "chunk_bwd", "chunk_bwd_workspace_size", "prepare_inputs", "recurrent_step_raw",
            "KDAError", "LIB_PATH", "load_library", "STATUS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "KDA_ERR_WORKSPACE",
-          4: "KDA_ERR_HIP", 5: "KDA_ERR_BAD_SEQLENS", 6: "KDA_ERR_TIMEOUT"}
+          4: "KDA_ERR_HIP", 5: "KDA_ERR_BAD_SEQLENS", 6: "KDA_ERR_TIMEOUT", 7: "KDA_ERR_TOO_LARGE"}
 _BF16, _F32 = 0, 1
 _PER_CHANNEL, _PER_HEAD = 0, 1
 
@@ -60,6 +62,9 @@ def load_library():
                                       ctypes.c_int, vp, vp, vp, sz, vp]
         lib.kda_chunk_fwd_instrumented.restype = ctypes.c_int
         lib.kda_chunk_fwd_instrumented.argtypes = lib.kda_chunk_fwd.argtypes + [vp]
+        lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
+        lib.kda_chunk_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, ctypes.c_int,
+                                              ctypes.c_int, vp, vp, vp]
         lib.kda_chunk_fwd_check.restype = ctypes.c_int
         lib.kda_chunk_fwd_check.argtypes = [vp, vp]
         lib.kda_chunk_bwd_workspace_size.restype = sz
@@ -197,6 +202,37 @@ def chunk_fwd(q, k, v, g, beta, *, S0=None, cu_seqlens=None, N=None, per_head_ga
     if batched:
         o = o.reshape(N, T_total // N, H, dv)
     return o, S_T
+
+
+def chunk_fwd_noalloc(q, k, v, g, beta, *, out, S_T=None, S0=None, cu_seqlens=None, N=None,
+                      per_head_gate=False, stream=None):
+    """``chunk_fwd`` through kda_chunk_fwd_noalloc: no workspace, the library's
+    static scratch instead (at most KDA_NOALLOC_SCRATCH_BYTES of workspace,
+    else KDAError KDA_ERR_TOO_LARGE).  Packed [T, H, d] inputs only; the
+    caller passes the outputs (``out`` [T, H, dv]; ``S_T`` fp32 [N, H, dk, dv]
+    or None), and nothing is allocated here either.  Calls that overlap on one
+    GPU race on the shared scratch.  Returns (out, S_T)."""
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be packed [T, H, d]")
+    T_total, H, dk = q.shape
+    dv = v.shape[2]
+    _shapes(k=(k, (T_total, H, dk)), v=(v, (T_total, H, dv)), beta=(beta, (T_total, H)),
+            g=(g, (T_total, H) if per_head_gate else (T_total, H, dk)), out=(out, (T_total, H, dv)))
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("out", out)):
+        _dev_contig(name, t, q.dtype)
+    if cu_seqlens is not None:
+        _dev_contig("cu_seqlens", cu_seqlens, torch.int32)
+        N = cu_seqlens.numel() - 1
+    elif N is None:
+        N = 1
+    for name, t in (("S0", S0), ("S_T", S_T)):
+        if t is not None:
+            _dev_contig(name, t, torch.float32)
+            _shapes(**{name: (t, (N, H, dk, dv))})
+    _check(load_library().kda_chunk_fwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(cu_seqlens), N, T_total, H, dk, dv,
+        _dt(q), _PER_HEAD if per_head_gate else _PER_CHANNEL, _ptr(out), _ptr(S_T), _stream(stream)))
+    return out, S_T
 
 
 def chunk_fwd_check(workspace, stream=None):

@@ -34,6 +34,9 @@ const char* kda_status_string(kda_status status) {
         case KDA_ERR_HIP: return "KDA_ERR_HIP: a HIP runtime call or kernel launch failed";
         case KDA_ERR_BAD_SEQLENS: return "KDA_ERR_BAD_SEQLENS: device cu_seqlens rejected";
         case KDA_ERR_TIMEOUT: return "KDA_ERR_TIMEOUT: an internal wait between waves gave up; results unspecified";
+        case KDA_ERR_TOO_LARGE:
+            return "KDA_ERR_TOO_LARGE: the problem needs more than the static scratch of kda_chunk_fwd_noalloc "
+                   "(KDA_NOALLOC_SCRATCH_BYTES); use kda_chunk_fwd with a workspace";
     }
     return "KDA_ERR_UNKNOWN";
 }
@@ -99,6 +102,21 @@ kda_status kda_chunk_fwd_instrumented(const void* q, const void* k, const void* 
     if (!events) return KDA_ERR_INVALID_ARG;
     return chunk_fwd_impl(q, k, v, g, beta, S0, cu_seqlens, N, T_total, H, d_k, d_v, dt, gk, o, S_T, workspace,
                           workspace_bytes, stream, events);
+}
+
+kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                 const float* S0, const int32_t* cu_seqlens, int32_t N, int64_t T_total, int32_t H,
+                                 int32_t d_k, int32_t d_v, kda_dtype dt, kda_gate gk, void* o, float* S_T,
+                                 hipStream_t stream) {
+    const kda_status st = check_common(H, d_k, d_v, dt, gk);
+    if (st != KDA_OK) return st;
+    if (N <= 0 || T_total < 0 || T_total > INT32_MAX) return KDA_ERR_INVALID_ARG;
+    if (kda::chunk_workspace_bytes(T_total, N, H, d_k, d_v, dt == KDA_BF16) > KDA_NOALLOC_SCRATCH_BYTES)
+        return KDA_ERR_TOO_LARGE;
+    void* scratch = nullptr;
+    if (kda::noalloc_scratch(&scratch) != hipSuccess) return KDA_ERR_HIP;
+    return chunk_fwd_impl(q, k, v, g, beta, S0, cu_seqlens, N, T_total, H, d_k, d_v, dt, gk, o, S_T, scratch,
+                          KDA_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 kda_status kda_chunk_fwd_check(const void* workspace, hipStream_t stream) {

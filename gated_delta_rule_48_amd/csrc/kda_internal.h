@@ -74,6 +74,11 @@ hipError_t launch_chunk_map(const int32_t* cu_seqlens, int32_t N, int64_t T, WsH
                             int32_t* chunk_off, int2* chunk_tab, hipStream_t stream);
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+// Device address, on the current GPU, of the static scratch array of the
+// allocation-free chunked forward (KDA_NOALLOC_SCRATCH_BYTES bytes, 256-byte
+// aligned); looked up once per device.
+hipError_t noalloc_scratch(void** out);
 // events: null, or four events recorded before map / intra / walk and after walk.
 hipError_t launch_chunk_fwd(const ChunkArgs& a, const ChunkWorkspace& ws, hipStream_t stream,
                             hipEvent_t* events = nullptr);

@@ -32,7 +32,8 @@
  *    q, k, v and a per-channel g to two elements; in kda_recurrent_step S
  *    to 16 bytes; the workspace to 256 bytes.  The caller allocates and owns every buffer, including
  *    the workspace, and keeps it alive until the work on `stream` completes.
- *    The library allocates nothing and keeps no per-call state.
+ *    The library allocates nothing and keeps no per-call state (the static
+ *    scratch of kda_chunk_fwd_noalloc aside, which the library holds).
  *  - Calls are asynchronous on `stream` (0 = the null stream) and never
  *    synchronise the host.
  *  - Token tensors: q, k, g are [T, H, d_k]; v, o are [T, H, d_v]; beta is
@@ -74,7 +75,8 @@ typedef enum {
     KDA_ERR_WORKSPACE = 3,
     KDA_ERR_HIP = 4,
     KDA_ERR_BAD_SEQLENS = 5,
-    KDA_ERR_TIMEOUT = 6
+    KDA_ERR_TIMEOUT = 6,
+    KDA_ERR_TOO_LARGE = 7
 } kda_status;
 
 typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
@@ -153,6 +155,37 @@ kda_status kda_chunk_fwd_instrumented(const void *q, const void *k, const void *
                                       kda_gate gk, void *o, float *S_T, void *workspace,
                                       size_t workspace_bytes, hipStream_t stream,
                                       hipEvent_t *events);
+
+/*
+ * kda_chunk_fwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It allocates nothing and frees nothing.
+ * Its scratch is a static device array of KDA_NOALLOC_SCRATCH_BYTES inside
+ * the library, one copy on every GPU the library runs on, held until the
+ * process ends; its address on a device is looked up once, on the first call
+ * with that device current.
+ *
+ *   Arguments, layouts, numerics and results as for kda_chunk_fwd (bit-
+ *   identical to it for the same arguments); the caller still allocates the
+ *   inputs and the outputs o and S_T.
+ *   Limit: problems whose kda_chunk_fwd_workspace_size exceeds
+ *   KDA_NOALLOC_SCRATCH_BYTES (128 MiB: about 1,800 (chunk, head) pairs at
+ *   d_k = d_v = 128 in bf16, e.g. T = 3,500 tokens over 32 heads) return
+ *   KDA_ERR_TOO_LARGE before anything is launched.
+ *   Every call on one GPU shares that GPU's array, which keeps the last
+ *   call's contents: calls that overlap on one GPU (on different streams, or
+ *   from different host threads without ordering) race and give unspecified
+ *   results.  Calls on one stream are ordered and safe.  Device-side
+ *   rejection of cu_seqlens leaves o and S_T unwritten, as for kda_chunk_fwd;
+ *   there is no status query for it.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+kda_status kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
+                                 const void *g, const void *beta, const float *S0,
+                                 const int32_t *cu_seqlens, int32_t N,
+                                 int64_t T_total, int32_t H, int32_t d_k,
+                                 int32_t d_v, kda_dtype dt, kda_gate gk, void *o,
+                                 float *S_T, hipStream_t stream);
 
 /*
  * Wait for `stream` and report how the last kda_chunk_fwd that used this

@@ -176,10 +176,27 @@ def test_recurrent_step_raw_rejects_bad_arguments(lib):
     assert f(P, P, P, P, P, P + 4, 4, 2, 64, 64, 0, 0, P, None) == INVALID
 
 
+def test_chunk_fwd_noalloc_rejects_before_any_device_call(lib):
+    """Unsupported sizes, bad counts and problems beyond the static scratch
+    are refused on the host, before the scratch is looked up or anything is
+    launched (so this runs without a GPU)."""
+    f = lib.kda_chunk_fwd_noalloc
+    f.restype = ctypes.c_int
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    f.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, ctypes.c_int, ctypes.c_int, vp, vp, vp]
+    P = 1 << 20
+    assert f(P, P, P, P, P, None, None, 1, 128, 2, 48, 64, 0, 0, P, None, None) == UNSUPPORTED
+    assert f(P, P, P, P, P, None, None, 1, 128, 0, 64, 64, 0, 0, P, None, None) == INVALID
+    assert f(P, P, P, P, P, None, None, 0, 128, 2, 64, 64, 0, 0, P, None, None) == INVALID
+    assert f(P, P, P, P, P, None, None, 1, -1, 2, 64, 64, 0, 0, P, None, None) == INVALID
+    # 8192 tokens x 32 heads at d = 128 need ~580 MB of workspace: beyond the 128 MiB scratch
+    assert f(P, P, P, P, P, None, None, 1, 8192, 32, 128, 128, 0, 0, P, None, None) == 7
+
+
 def test_status_strings(lib):
     f = lib.kda_status_string
     f.restype = ctypes.c_char_p
     f.argtypes = [ctypes.c_int]
-    for code in range(7):
+    for code in range(8):
         assert f(code).startswith(b"KDA_")
     assert f(99) == b"KDA_ERR_UNKNOWN"
