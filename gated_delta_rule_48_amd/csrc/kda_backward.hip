@@ -1371,7 +1371,8 @@ hipError_t launch_chunk_bwd(const BwdArgs& a, void* workspace, size_t workspace_
     // intermediates fit the workspace, one group after another on the stream
     const int32_t G = bwd_head_group(a.T, a.N, a.H, a.dk_, a.dv_, workspace_bytes);
     const BwdWs w = carve_bwd(workspace, a.T, a.N, G, a.dk_, a.dv_);
-    hipError_t e = launch_chunk_map(a.cu_seqlens, a.N, a.T, w.header, w.cu, w.chunk_off, w.chunk_tab, stream);
+    hipError_t e = launch_chunk_map(a.cu_seqlens, a.N, a.T, w.header, w.cu, w.chunk_off, w.chunk_tab, nullptr, 0,
+                                    stream);
     if (e != hipSuccess) return e;
     const size_t esz = a.bf16 ? 2 : 4;
     for (int32_t h0 = 0; h0 < a.H; h0 += G) {

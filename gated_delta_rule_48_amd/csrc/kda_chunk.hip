@@ -36,7 +36,9 @@
 //                      d_v): walks the chunks in order with its fp32 slice of
 //                      S in registers; U = U' - W S, O = QG S + P U,
 //                      S <- Diag(Gn) S + KdT U, all on MFMA
+#include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "kda_internal.h"
 
@@ -51,7 +53,8 @@ __global__ __launch_bounds__(256) void chunk_map_kernel(const int32_t* __restric
                                                         int64_t T, WsHeader* __restrict__ hdr,
                                                         int32_t* __restrict__ cu,
                                                         int32_t* __restrict__ chunk_off,
-                                                        int2* __restrict__ chunk_tab) {
+                                                        int2* __restrict__ chunk_tab,
+                                                        int32_t* __restrict__ seg_flags, int64_t n_flags) {
     __shared__ int bad;
     __shared__ int carry;
     __shared__ int scan[256];
@@ -92,7 +95,9 @@ __global__ __launch_bounds__(256) void chunk_map_kernel(const int32_t* __restric
         hdr->total_chunks = isbad ? 0 : carry;
         hdr->bad_seqlens = isbad;
         hdr->wait_timeout = 0;
+        hdr->seg_ticket = 0;
     }
+    for (int64_t i = tid; i < n_flags; i += 256) seg_flags[i] = 0;
     __syncthreads();  // chunk_off of every sequence is written
     const int total = isbad ? 0 : carry;
     for (int cid = tid; cid < total; cid += 256) {
@@ -1239,6 +1244,9 @@ __global__ __launch_bounds__(kWalkThreads) void chunk_walk_kernel(
             for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                 for (int t = 0; t < TT; ++t) X[t] = mma(fW[t][ks], sf[ks], X[t]);
+            // every product is issued before the wave can stall on a counter
+            // or an LDS read below: the matrix cores work through the wait
+            __builtin_amdgcn_sched_barrier(0);
             acquire_ops(nxt, seen);
             load_w(nxt);
             Frag<E> uf[KB];
@@ -1257,6 +1265,7 @@ __global__ __launch_bounds__(kWalkThreads) void chunk_walk_kernel(
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int m = 0; m < MT; ++m) Sreg[m] = mma(fK[m][kb], uf[kb], Sreg[m]);
+            __builtin_amdgcn_sched_barrier(0);
             // every operand of chunk c has been read (its registers are in
             // use above), and S, U of chunk c are in the ring
             lds_release();
@@ -1345,10 +1354,404 @@ __global__ __launch_bounds__(kWalkThreads) void chunk_walk_kernel(
 }
 
 // ----------------------------------------------------------------------------
+// Segmented walk (bf16 operands, d_k = d_v = 128): the two-level form of the
+// chunk chain, for prefills with few (sequence, head) pairs.  The chunks of
+// every pair are cut into G segments of consecutive chunks, one workgroup per
+// segment, each owning all d_v columns of the state (eight waves, one
+// 16-column slice each), so that a chunk's operands are fetched once per head
+// rather than once per slice.  The chunk step S <- A_c S + KdT U' with
+// A_c = Diag(Gn) - KdT W is affine in S, so a segment maps its start state to
+// its end state by S_end = M S_start + B, M the product of its A_c ("Kimi
+// Linear architecture", section on the chunkwise form).  Per segment j:
+//   pass 1  walk the segment without outputs: B from S = 0 with the inputs,
+//           M from the identity without them (U' taken as 0), both with the
+//           same W, KdT and Gn.  Segment 0 knows its start state and walks S
+//           from S0 instead (B is then its end state; no M).
+//   chain   once S_start(j) is published by segment j - 1:
+//           S_start(j + 1) = M S_start(j) + B (one 128 x 128 x 128 product,
+//           each operand split into two bf16 parts so that the product keeps
+//           about 16 bits), published in turn.
+//   pass 3  walk the segment again from S_start(j), with outputs; the last
+//           segment writes S_T and has no pass 1.
+// Workgroups take (segment, pair) from an atomic ticket in segment-major
+// order, so a workgroup only ever waits for a segment with a lower ticket,
+// which was taken by a workgroup that is resident or done and that itself
+// waits only for lower tickets.  Every wait is bounded: on timeout the
+// header's wait_timeout is set and the results are unspecified.
+// Per chunk, the operands go to LDS by 16-byte LDS-DMA loads spread over the
+// eight waves, double-buffered (the next chunk's while this one is
+// computed), with two workgroup barriers per chunk; the O tile of a chunk is
+// staged in LDS and stored by all waves during the next chunk.  The two
+// operand slots are distinct LDS objects and the loops are unrolled by two,
+// so that the compiler can tell that the matrix-core operand reads of one
+// slot do not depend on the loads in flight into the other.
+constexpr int kSegWaves = 8;
+constexpr int kSegThreads = 64 * kSegWaves;
+constexpr int kSegTarget = 256;          // workgroups wanted: one per compute unit
+constexpr int kSegMaxGroups = 64;        // most segments per pair
+constexpr int kSegMinChunks = 8;         // fewest chunks per segment (on average)
+constexpr int kSegSpinLimit = 1 << 24;   // polls of about 128 clocks: several seconds
+
+struct SegLayout {
+    static constexpr int C = kChunk, DK = 128, DV = 128, KS = DK / 32, KB = C / 32;
+    static constexpr int W_B = C * DK * 2, K_B = DK * C * 2, U_B = C * DV * 2, Q_B = C * DK * 2;
+    static constexpr int P_B = 6 * 1024, G_B = DK * 4;  // P: its 6 nonzero 1 KB fragment blocks
+    static constexpr int off_W = 0, off_K = W_B, off_U = off_K + K_B, off_G = off_U + U_B, off_Q = off_G + G_B,
+                         off_P = off_Q + Q_B;
+    static constexpr int SLOT = off_P + P_B;  // 72,192 B
+    static constexpr int LDO = DV + 8;        // O tile row (bf16), padded
+    static constexpr int LDM = DK + 8;        // M tile row (bf16), padded; two tiles in the second slot
+    static constexpr int M_B = DK * LDM * 2;
+    // 1 KB LDS-DMA pieces per chunk: W, KdT, U', Gn (half a piece) in pass 1;
+    // then QG and the P blocks in pass 3
+    static constexpr int PIECES1 = W_B / 1024 + K_B / 1024 + U_B / 1024 + 1;
+    static constexpr int PIECES3 = PIECES1 + Q_B / 1024 + P_B / 1024;
+    static constexpr int bytes = 2 * SLOT + C * LDO * 2 + 16;
+    static_assert(bytes <= kLdsBytes, "LDS budget");
+    static_assert(2 * M_B <= SLOT, "both M tiles fit in the second slot");
+};
+
+// Index of the nonzero fragment block (t, kb) of P among the six kept.
+__device__ __forceinline__ int p_block_index(int t, int kb) { return t < 2 ? t : 2 + 2 * (t - 2) + kb; }
+
+// x split into a bf16 part and the bf16 of the remainder: hi + lo carries
+// about 16 significant bits.
+__device__ __forceinline__ void split_frag(f32x4 a, f32x4 b, Frag<bf16_t>& hi, Frag<bf16_t>& lo) {
+    hi = acc_to_frag(bf16_t{}, a, b);
+    const u16x8 hv = hi.v;
+    f32x4 ra, rb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        ra[i] = a[i] - bf16_to_f32(hv[i]);
+        rb[i] = b[i] - bf16_to_f32(hv[4 + i]);
+    }
+    lo = acc_to_frag(bf16_t{}, ra, rb);
+}
+
+__global__ __launch_bounds__(kSegThreads) void seg_walk_kernel(
+    WsHeader* __restrict__ hdr, int* __restrict__ seg_flags, float* __restrict__ seg_state,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off, int32_t N, int32_t H, int32_t G,
+    const bf16_t* __restrict__ Wi, const bf16_t* __restrict__ QGi, const bf16_t* __restrict__ KdTi,
+    const bf16_t* __restrict__ UpTi, const bf16_t* __restrict__ Pi, const float* __restrict__ Gni,
+    const float* __restrict__ S0, float* __restrict__ S_T, bf16_t* __restrict__ o) {
+    using L = SegLayout;
+    using E = bf16_t;
+    constexpr int C = kChunk, DK = L::DK, DV = L::DV, KS = L::KS, KB = L::KB;
+    constexpr int MT = DK / 16, TT = C / 16;
+    __shared__ __align__(16) char slotA[L::SLOT];
+    __shared__ __align__(16) char slotB[L::SLOT];
+    __shared__ __align__(16) E sO[C * L::LDO];
+    __shared__ int sticket;
+
+    if (hdr->bad_seqlens) return;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
+    const int lr = lane & 15, lg = lane >> 4;
+    if (tid == 0) sticket = atomicAdd(&hdr->seg_ticket, 1);
+    __syncthreads();
+    const int64_t NP = (int64_t)N * H;
+    const int64_t ticket = __builtin_amdgcn_readfirstlane(sticket);  // uniform: scalar addressing below
+    const int j = (int)(ticket / NP);
+    const int64_t pair = ticket % NP;
+    const int n = (int)(pair / H), h = (int)(pair % H);
+    const int cbeg = chunk_off[n], cend = chunk_off[n + 1];
+    const int64_t seq0 = cu[n], seqend = cu[n + 1];
+    const int seglen = (cend - cbeg + G - 1) / G;
+    const int s0 = min(cend, cbeg + j * seglen), s1 = min(cend, s0 + seglen);
+    const int col0 = 16 * w;  // this wave's value columns
+    const bool first = j == 0, last = j == G - 1;
+    // S_start(i) for 1 <= i < G lives at seg_state[pair][i - 1]; its flag is
+    // seg_flags[pair][i]
+    auto start_state = [&](int i) { return seg_state + (pair * (G - 1) + i - 1) * DK * DV; };
+
+    // this wave's share of the LDS-DMA pieces of chunk c into slot sb
+    auto dma_chunk = [&](int c, char* sb, bool pass3) __attribute__((always_inline)) {
+        // (chunk, head) index through readfirstlane: opaque to the loop
+        // optimiser, which would otherwise keep every piece's address as a
+        // 64-bit induction variable in vector registers
+        const int64_t ch = (int64_t)__builtin_amdgcn_readfirstlane(c) * H + h;
+        const int np = pass3 ? L::PIECES3 : L::PIECES1;
+#pragma unroll
+        for (int k = 0; k < (L::PIECES3 + kSegWaves - 1) / kSegWaves; ++k) {
+            const int p = w + kSegWaves * k;
+            if (p >= np) break;
+            const char* src;
+            int dst;
+            if (p < 16) {
+                src = (const char*)(Wi + ch * C * DK) + 1024 * p;
+                dst = L::off_W + 1024 * p;
+            } else if (p < 32) {
+                src = (const char*)(KdTi + ch * DK * C) + 1024 * (p - 16);
+                dst = L::off_K + 1024 * (p - 16);
+            } else if (p < 48) {
+                src = (const char*)(UpTi + ch * DV * C) + 1024 * (p - 32);
+                dst = L::off_U + 1024 * (p - 32);
+            } else if (p == 48) {
+                if (lane < L::G_B / 16) lds_dma16((const char*)(Gni + ch * DK) + 16 * lane, sb + L::off_G);
+                continue;
+            } else if (p < 49 + 16) {
+                src = (const char*)(QGi + ch * C * DK) + 1024 * (p - 49);
+                dst = L::off_Q + 1024 * (p - 49);
+            } else {
+                const int b = p - 65;  // b-th kept block of P, (t, kb) in p_block_index order
+                const int t = b < 2 ? b : 2 + (b - 2) / 2, kb = b < 2 ? 0 : (b - 2) % 2;
+                src = (const char*)(Pi + ch * C * C) + 1024 * (t * KB + kb);
+                dst = L::off_P + 1024 * b;
+            }
+            lds_dma16(src + 16 * lane, sb + dst);
+        }
+    };
+    auto frag_at = [&](const char* sb, int off, int blk) __attribute__((always_inline)) {
+        return ld_frag(reinterpret_cast<const E*>(sb + off) + (blk * 64 + lane) * 8);
+    };
+    // state slices in accumulator layout: lane holds rows 16 m + 4 lg + i of
+    // column col0 + lr
+    auto load_state = [&](f32x4 (&S)[MT], const float* src) {
+        if (src) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[m][i] = src[(16 * m + 4 * lg + i) * DV + col0 + lr];
+        } else {
+#pragma unroll
+            for (int m = 0; m < MT; ++m) S[m] = zero4();
+        }
+    };
+    auto store_state = [&](const f32x4 (&S)[MT], float* dst) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[(16 * m + 4 * lg + i) * DV + col0 + lr] = S[m][i];
+    };
+    // The start states pass between workgroups on any of the chip's L2
+    // caches, so they are written and read with device-scope accesses, which
+    // are coherent at the device level by themselves; a release/acquire pair
+    // around plain accesses would instead write back and invalidate a whole
+    // L2 at every hand-over.  Ordering: every lane waits for its stores'
+    // completion before the barrier that precedes the flag store, and the
+    // loads are issued after the flag was seen.
+    auto publish_state = [&](const f32x4 (&S)[MT], float* dst) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                __hip_atomic_store(&dst[(16 * m + 4 * lg + i) * DV + col0 + lr], S[m][i], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    };
+    auto fetch_state = [&](f32x4 (&S)[MT], const float* src) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                S[m][i] = __hip_atomic_load(&src[(16 * m + 4 * lg + i) * DV + col0 + lr], __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+    };
+    // one chunk step of Y (accumulator layout) with the operands in sb:
+    // X = W Y;  Y <- Diag(Gn) Y + KdT (in - X), in = U' (with_u) or 0.
+    // yf, uf: the fragments of Y before the step and of in - X.
+    auto chain_step = [&](f32x4 (&Y)[MT], const char* sb, bool with_u, Frag<E> (&yf)[KS], Frag<E> (&uf)[KB])
+                          __attribute__((always_inline)) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) yf[ks] = acc_to_frag(E{}, Y[2 * ks], Y[2 * ks + 1]);
+        f32x4 X[TT];
+#pragma unroll
+        for (int t = 0; t < TT; ++t) X[t] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int t = 0; t < TT; ++t) X[t] = mma(frag_at(sb, L::off_W, t * KS + ks), yf[ks], X[t]);
+        const float* gn = reinterpret_cast<const float*>(sb + L::off_G);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) Y[m] = *reinterpret_cast<const f32x4*>(gn + 16 * m + 4 * lg) * Y[m];
+        f32x4 up[TT];
+        if (with_u) {
+            const E* Up = reinterpret_cast<const E*>(sb + L::off_U) + (w * 64 + lane) * 16;
+#pragma unroll
+            for (int t = 0; t < TT; ++t) up[t] = Raw4<E>::widen(Raw4<E>::load(Up + 4 * t));
+        } else {
+#pragma unroll
+            for (int t = 0; t < TT; ++t) up[t] = zero4();
+        }
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+            uf[kb] = acc_to_frag(E{}, up[2 * kb] - X[2 * kb], up[2 * kb + 1] - X[2 * kb + 1]);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) Y[m] = mma(frag_at(sb, L::off_K, m * KB + kb), uf[kb], Y[m]);
+    };
+    // wait until S_start(i) is published (one lane polls; the others wait at
+    // the barrier)
+    auto wait_start = [&](int i) {
+        if (tid == 0) {
+            for (int spins = 0;
+                 __hip_atomic_load(&seg_flags[pair * G + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0;
+                 ++spins) {
+                if (spins >= kSegSpinLimit) {
+                    hdr->wait_timeout = 1;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
+        __syncthreads();
+    };
+
+    // ------------------------------------------------------------ pass 1
+    if (!last) {
+        f32x4 B[MT], M[MT];
+        load_state(B, first ? (S0 ? S0 + pair * DK * DV : nullptr) : nullptr);
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) M[m][i] = (16 * m + 4 * lg + i == col0 + lr) ? 1.f : 0.f;
+        // chunk c from slot cur, the next chunk's operands loading into nxt
+        auto step1 = [&](int c, const char* cur, char* nxt) __attribute__((always_inline)) {
+            if (c + 1 < s1) dma_chunk(c + 1, nxt, false);
+            Frag<E> yf[KS], uf[KB];
+            chain_step(B, cur, true, yf, uf);
+            if (!first) chain_step(M, cur, false, yf, uf);
+            wait_vmcnt<0>();
+            lds_barrier();
+        };
+        if (s0 < s1) {
+            dma_chunk(s0, slotA, false);
+            wait_vmcnt<0>();
+            lds_barrier();
+        }
+        for (int c = s0; c < s1; c += 2) {
+            step1(c, slotA, slotB);
+            if (c + 1 < s1) step1(c + 1, slotB, slotA);
+        }
+        // ---- chain: S_start(j + 1) = M S_start(j) + B (segment 0: B itself)
+        if (!first) {
+            // M to LDS as two bf16 tiles (row-major, columns in fragment
+            // order) for the A operand, in the second slot (free: the walk
+            // ended at a barrier)
+            E* sMh = reinterpret_cast<E*>(slotB);
+            E* sMl = sMh + DK * L::LDM;
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int at = (16 * m + 4 * lg + i) * L::LDM + frag_pos(col0 + lr);
+                    const E hi = Elt<E>::from(M[m][i]);
+                    lds_put(&sMh[at], hi);
+                    lds_put(&sMl[at], Elt<E>::from(M[m][i] - Elt<E>::to(hi)));
+                }
+            wait_start(j);
+            f32x4 Sj[MT];
+            fetch_state(Sj, start_state(j));
+            if (s0 < s1) {
+                Frag<E> sh[KS], sl[KS];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) split_frag(Sj[2 * ks], Sj[2 * ks + 1], sh[ks], sl[ks]);
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const int at = (16 * m + lr) * L::LDM + 32 * ks + 8 * lg;
+                        const Frag<E> mh = ld_frag(sMh + at), ml = ld_frag(sMl + at);
+                        B[m] = mma(mh, sh[ks], B[m]);
+                        B[m] = mma(mh, sl[ks], B[m]);
+                        B[m] = mma(ml, sh[ks], B[m]);
+                    }
+            } else {
+                // empty segment: the map is the identity
+#pragma unroll
+                for (int m = 0; m < MT; ++m) B[m] = Sj[m];
+            }
+        }
+        publish_state(B, start_state(j + 1));
+        wait_vmcnt<0>();  // this lane's part has reached the device level
+        __syncthreads();  // every wave's part (and the M tiles are read)
+        if (tid == 0) __hip_atomic_store(&seg_flags[pair * G + j + 1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // ------------------------------------------------------------ pass 3
+    if (s0 < s1) dma_chunk(s0, slotA, true);  // in flight during the wait below
+    f32x4 S[MT];
+    if (first) {
+        load_state(S, S0 ? S0 + pair * DK * DV : nullptr);
+    } else {
+        if (last) wait_start(j);
+        fetch_state(S, start_state(j));
+    }
+    // store the O rows of chunk c from the O tile: 16 KB as 1 KB pieces of
+    // four token rows, two pieces per wave
+    auto store_o = [&](int c) __attribute__((always_inline)) {
+        const int64_t t0 = seq0 + (int64_t)(c - cbeg) * C;
+#pragma unroll
+        for (int k = 0; k < C * DV * 2 / 1024 / kSegWaves; ++k) {
+            const int piece = w + kSegWaves * k;
+            const int row = 4 * piece + (lane >> 4), c8 = 8 * (lane & 15);
+            const uint4 v = *reinterpret_cast<const uint4*>(sO + row * L::LDO + c8);
+            const int64_t tok = t0 + row;
+            if (tok < seqend) *reinterpret_cast<uint4*>(o + (tok * H + h) * DV + c8) = v;
+        }
+    };
+    auto step3 = [&](int c, const char* cur, char* nxt) __attribute__((always_inline)) {
+        if (c > s0) store_o(c - 1);
+        if (c + 1 < s1) dma_chunk(c + 1, nxt, true);
+        Frag<E> sf[KS], uf[KB];
+        chain_step(S, cur, true, sf, uf);
+        f32x4 O[TT];
+#pragma unroll
+        for (int t = 0; t < TT; ++t) O[t] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int t = 0; t < TT; ++t) O[t] = mma(frag_at(cur, L::off_Q, t * KS + ks), sf[ks], O[t]);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int t = 0; t < TT; ++t)
+                if (!p_block_zero(t, kb)) O[t] = mma(frag_at(cur, L::off_P, p_block_index(t, kb)), uf[kb], O[t]);
+        // every wave has read the previous chunk's rows out of the O tile
+        // (the reads were waited for here; no fence, which would also wait
+        // for the loads in flight into the other slot)
+        lds_release();
+        __builtin_amdgcn_s_barrier();
+        lds_acquire();
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                lds_put(&sO[(16 * t + 4 * lg + i) * L::LDO + col0 + lr], Elt<E>::from(O[t][i]));
+        wait_vmcnt<0>();
+        lds_barrier();
+    };
+    if (s0 < s1) {
+        wait_vmcnt<0>();
+        lds_barrier();
+    }
+    for (int c = s0; c < s1; c += 2) {
+        step3(c, slotA, slotB);
+        if (c + 1 < s1) step3(c + 1, slotB, slotA);
+    }
+    if (s0 < s1) store_o(s1 - 1);
+    if (last && S_T) store_state(S, S_T + pair * DK * DV);
+}
+
+// ----------------------------------------------------------------------------
 // Host side.
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int64_t max_chunks_for(int64_t T, int32_t N) { return (T + kChunk - 1) / kChunk + N; }
+
+// Segments per (sequence, head) of the segmented walk, or 0 where the
+// per-slice walk runs (fp32 operands, other head sizes).  Enough segments
+// for about one workgroup per compute unit, but on average at least
+// kSegMinChunks chunks per segment (shorter ones spend more on the extra
+// pass and the chain than they gain).
+int32_t seg_groups_for(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, bool bf16) {
+    if (!bf16 || dk != 128 || dv != 128 || N <= 0 || H <= 0) return 0;
+    const int64_t np = (int64_t)N * H;
+    int64_t g = np >= kSegTarget ? 1 : kSegTarget / np;
+    const int64_t per_seq = (T + (int64_t)N * kChunk - 1) / ((int64_t)N * kChunk);  // mean chunks per sequence
+    g = std::min<int64_t>(g, std::max<int64_t>(1, per_seq / kSegMinChunks));
+    return (int32_t)std::min<int64_t>(g, kSegMaxGroups);
+}
 
 // The intra-chunk grid (one workgroup per chunk and head, in one dimension)
 // must stay within the 2^32 work-items a grid dimension can hold.
@@ -1358,7 +1761,8 @@ bool chunk_grid_fits(int64_t max_chunks, int32_t H) {
 
 namespace {
 struct WsSizes {
-    size_t header, cu, chunk_off, chunk_tab, W, QG, KdT, Up, P, Gn;
+    size_t header, cu, chunk_off, chunk_tab, W, QG, KdT, Up, P, Gn, seg_state, seg_flags;
+    int32_t seg_groups;
 };
 WsSizes ws_sizes(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, bool bf16) {
     const size_t esz = bf16 ? 2 : 4;
@@ -1375,13 +1779,18 @@ WsSizes ws_sizes(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, bool b
     s.Up = align256(mc * H * C * dv * esz);
     s.P = align256(mc * H * C * C * esz);
     s.Gn = align256(mc * H * dk * 4);
+    s.seg_groups = seg_groups_for(T, N, H, dk, dv, bf16);
+    const size_t np = (size_t)N * H, G = (size_t)s.seg_groups;
+    s.seg_state = G > 1 ? align256(np * (G - 1) * dk * dv * 4) : 0;
+    s.seg_flags = G > 1 ? align256(np * G * 4) : 0;
     return s;
 }
 }  // namespace
 
 size_t chunk_workspace_bytes(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, bool bf16) {
     const WsSizes s = ws_sizes(T, N, H, dk, dv, bf16);
-    return s.header + s.cu + s.chunk_off + s.chunk_tab + s.W + s.QG + s.KdT + s.Up + s.P + s.Gn;
+    return s.header + s.cu + s.chunk_off + s.chunk_tab + s.W + s.QG + s.KdT + s.Up + s.P + s.Gn + s.seg_state +
+           s.seg_flags;
 }
 
 ChunkWorkspace carve_chunk_workspace(void* base, int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv,
@@ -1398,7 +1807,10 @@ ChunkWorkspace carve_chunk_workspace(void* base, int64_t T, int32_t N, int32_t H
     w.KdT = p; p += s.KdT;
     w.Up = p; p += s.Up;
     w.P = p; p += s.P;
-    w.Gn = reinterpret_cast<float*>(p);
+    w.Gn = reinterpret_cast<float*>(p); p += s.Gn;
+    w.seg_groups = s.seg_groups;
+    w.seg_state = s.seg_state ? reinterpret_cast<float*>(p) : nullptr; p += s.seg_state;
+    w.seg_flags = s.seg_flags ? reinterpret_cast<int32_t*>(p) : nullptr;
     return w;
 }
 
@@ -1449,6 +1861,15 @@ static inline hipError_t mark(hipEvent_t* ev, int i, hipStream_t stream) {
     return ev ? hipEventRecord(ev[i], stream) : hipSuccess;
 }
 
+static hipError_t launch_seg_walk(const ChunkArgs& a, const ChunkWorkspace& ws, hipStream_t stream) {
+    const int64_t blocks = (int64_t)a.N * a.H * ws.seg_groups;
+    hipLaunchKernelGGL(seg_walk_kernel, dim3((unsigned)blocks), dim3(kSegThreads), 0, stream, ws.header,
+                       ws.seg_flags, ws.seg_state, ws.cu, ws.chunk_off, a.N, a.H, ws.seg_groups,
+                       (const bf16_t*)ws.W, (const bf16_t*)ws.QG, (const bf16_t*)ws.KdT, (const bf16_t*)ws.Up,
+                       (const bf16_t*)ws.P, (const float*)ws.Gn, a.S0, a.S_T, (bf16_t*)a.o);
+    return hipGetLastError();
+}
+
 template <typename E, int DK, int DV>
 static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkWorkspace& ws, hipStream_t stream,
                                  hipEvent_t* ev) {
@@ -1459,8 +1880,12 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkWorkspace& ws, h
         if (e != hipSuccess) return e;
     }
     if ((e = mark(ev, 2, stream)) != hipSuccess) return e;
-    const int64_t blocks = (int64_t)a.N * a.H * (DV / 16);
-    e = launch_walk<E, DK, DV>(a, ws, blocks, stream);
+    if constexpr (std::is_same<E, bf16_t>::value && DK == SegLayout::DK && DV == SegLayout::DV) {
+        if (ws.seg_groups > 0) e = launch_seg_walk(a, ws, stream);
+        else e = launch_walk<E, DK, DV>(a, ws, (int64_t)a.N * a.H * (DV / 16), stream);
+    } else {
+        e = launch_walk<E, DK, DV>(a, ws, (int64_t)a.N * a.H * (DV / 16), stream);
+    }
     if (e != hipSuccess) return e;
     return mark(ev, 3, stream);
 }
@@ -1474,16 +1899,19 @@ static hipError_t launch_chunk_e(const ChunkArgs& a, const ChunkWorkspace& ws, h
 }
 
 hipError_t launch_chunk_map(const int32_t* cu_seqlens, int32_t N, int64_t T, WsHeader* header, int32_t* cu,
-                            int32_t* chunk_off, int2* chunk_tab, hipStream_t stream) {
+                            int32_t* chunk_off, int2* chunk_tab, int32_t* seg_flags, int64_t n_flags,
+                            hipStream_t stream) {
     hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(256), 0, stream, cu_seqlens, N, T, header, cu, chunk_off,
-                       chunk_tab);
+                       chunk_tab, seg_flags, n_flags);
     return hipGetLastError();
 }
 
 hipError_t launch_chunk_fwd(const ChunkArgs& a, const ChunkWorkspace& ws, hipStream_t stream, hipEvent_t* ev) {
     hipError_t e = mark(ev, 0, stream);
     if (e != hipSuccess) return e;
-    e = launch_chunk_map(a.cu_seqlens, a.N, a.T, ws.header, ws.cu, ws.chunk_off, ws.chunk_tab, stream);
+    const int64_t n_flags = ws.seg_groups > 1 ? (int64_t)a.N * a.H * ws.seg_groups : 0;
+    e = launch_chunk_map(a.cu_seqlens, a.N, a.T, ws.header, ws.cu, ws.chunk_off, ws.chunk_tab, ws.seg_flags, n_flags,
+                         stream);
     if (e != hipSuccess) return e;
     return a.bf16 ? launch_chunk_e<bf16_t>(a, ws, stream, ev) : launch_chunk_e<float>(a, ws, stream, ev);
 }

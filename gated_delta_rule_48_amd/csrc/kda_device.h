@@ -170,7 +170,8 @@ __device__ __forceinline__ float sigmoid(float x) {
 struct WsHeader {
     int32_t bad_seqlens;   // nonzero: cu_seqlens rejected, every later kernel exits
     int32_t total_chunks;  // number of chunks over all sequences
-    int32_t wait_timeout;  // nonzero: a bounded inter-wave wait gave up
+    int32_t wait_timeout;  // nonzero: a bounded wait gave up
+    int32_t seg_ticket;    // next (segment, pair) ticket of the segmented walk
 };
 
 }  // namespace kda

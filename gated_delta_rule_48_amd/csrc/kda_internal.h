@@ -46,6 +46,12 @@ struct ChunkWorkspace {
     void* Up;             // dv x C values of T (beta V): [dv/16][64 lanes][16]
     void* P;              // C x C,   masked intra-chunk Q K^T with decay, fragment-major
     float* Gn;            // [max_chunks, H, dk]      exp(b_last)
+    // Segmented walk (null when the per-slice walk runs): segments per pair,
+    // the start state of every segment after the first, fp32
+    // [N*H][G-1][dk][dv], and one published flag per (pair, segment).
+    int32_t seg_groups;
+    float* seg_state;
+    int32_t* seg_flags;   // [N*H][G]
 };
 
 struct ChunkArgs {
@@ -65,13 +71,17 @@ size_t chunk_workspace_bytes(int64_t T, int32_t N, int32_t H, int32_t dk, int32_
 ChunkWorkspace carve_chunk_workspace(void* base, int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv,
                                      bool bf16);
 int64_t max_chunks_for(int64_t T, int32_t N);
+int32_t seg_groups_for(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, bool bf16);
 bool chunk_grid_fits(int64_t max_chunks, int32_t H);
 
 // Validate cu_seqlens (or synthesise N equal sequences when it is null) and
 // write the header, the sequence offsets, the first chunk of every sequence
 // and every chunk's first token and length.
+// seg_flags: the segmented walk's n_flags flags, cleared with the header
+// (null and 0 when it does not run).
 hipError_t launch_chunk_map(const int32_t* cu_seqlens, int32_t N, int64_t T, WsHeader* header, int32_t* cu,
-                            int32_t* chunk_off, int2* chunk_tab, hipStream_t stream);
+                            int32_t* chunk_off, int2* chunk_tab, int32_t* seg_flags, int64_t n_flags,
+                            hipStream_t stream);
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 

@@ -152,6 +152,53 @@ def test_chunk_many_ragged_sequences():
     _assert_close("S_T", S, S_ref, TOL["bf16"])
 
 
+@pytest.mark.parametrize("gate_kind", ["normal", "mixed"])
+def test_chunk_segmented_long_sequence(gate_kind):
+    """One 16384-token sequence, H = 2 (bf16, d = 128): few (sequence, head)
+    pairs, so the chunks of each pair are cut into many segments walked in
+    parallel and joined through their affine maps (about 32 segments of 8
+    chunks).  "mixed": fast (g = -10), slow (g = -0.1) and uniform channels
+    side by side, so the segment maps hold both near-identity and vanishing
+    columns."""
+    _announce(f"segmented walk, one long sequence, {gate_kind} gates")
+    d = chunk_case(2, 128, 128, "bf16", "channel", [16384], s0_sigma=0.1, seed=31)
+    if gate_kind == "mixed":
+        d["g"] = synth.bf16_bits(_mixed_gate(d["g"].shape, 3131, -10.0))
+    o, S = _run_chunk(d, "bf16", "channel")
+    o_ref, S_ref = _oracle_chunk(d, "channel")
+    print(f"segmented {gate_kind}: o {oracle.rel_err(o, o_ref):.2e} S_T {oracle.rel_err(S, S_ref):.2e}", flush=True)
+    _assert_close("o", o, o_ref, TOL["bf16"])
+    _assert_close("S_T", S, S_ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("lengths", [[8192, 100], [3000, 0, 1, 4097]], ids=["long_short", "with_empty"])
+def test_chunk_segmented_ragged(lengths):
+    """Segments of unequal sequences (bf16, d = 128, H = 2): the short and
+    empty sequences leave whole segments empty, whose map is the identity
+    (their start state is passed on unchanged), and the last segments end on
+    a ragged chunk."""
+    _announce(f"segmented walk, ragged {lengths}")
+    d = chunk_case(2, 128, 128, "bf16", "channel", lengths, s0_sigma=0.1, seed=32 + len(lengths))
+    o, S = _run_chunk(d, "bf16", "channel")
+    o_ref, S_ref = _oracle_chunk(d, "channel")
+    _assert_close("o", o, o_ref, TOL["bf16"])
+    _assert_close("S_T", S, S_ref, TOL["bf16"])
+    # an empty sequence passes S0 through unchanged, bit for bit
+    for n, L in enumerate(lengths):
+        if L == 0:
+            assert np.array_equal(S[n], np.asarray(d["S0"][n], dtype=np.float64))
+
+
+def test_chunk_segmented_deterministic():
+    """The segments finish in any order, but every one computes the same
+    values: two calls give bit-identical o and S_T."""
+    _announce("segmented walk determinism")
+    d = chunk_case(2, 128, 128, "bf16", "channel", [8192, 100], s0_sigma=0.1, seed=34)
+    a = _run_chunk(d, "bf16", "channel")
+    b = _run_chunk(d, "bf16", "channel")
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
 def test_chunk_head_gate_equals_broadcast_channel_gate():
     """A per-head gate gives bit-identical results to the per-channel gate
     filled with the same value on every channel (boundary semantics, no
