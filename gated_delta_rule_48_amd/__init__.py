@@ -62,6 +62,8 @@ def load_library():
                                       ctypes.c_int, vp, vp, vp, sz, vp]
         lib.kda_chunk_fwd_instrumented.restype = ctypes.c_int
         lib.kda_chunk_fwd_instrumented.argtypes = lib.kda_chunk_fwd.argtypes + [vp]
+        lib.kda_chunk_fwd_raw.restype = ctypes.c_int
+        lib.kda_chunk_fwd_raw.argtypes = lib.kda_chunk_fwd.argtypes
         lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
         lib.kda_chunk_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, ctypes.c_int,
                                               ctypes.c_int, vp, vp, vp]
@@ -133,7 +135,8 @@ def chunk_fwd_workspace_size(T_total, N, H, d_k, d_v, dtype=torch.bfloat16, per_
 
 
 def chunk_fwd(q, k, v, g, beta, *, S0=None, cu_seqlens=None, N=None, per_head_gate=False,
-              out=None, S_T=None, workspace=None, stream=None, output_final_state=True, events=None):
+              out=None, S_T=None, workspace=None, stream=None, output_final_state=True, events=None,
+              raw=False, check=True):
     """Chunked KDA forward (prefill).
 
     q, k: [T, H, dk] packed (with ``cu_seqlens`` int32 [N+1] on the device, or
@@ -144,8 +147,15 @@ def chunk_fwd(q, k, v, g, beta, *, S0=None, cu_seqlens=None, N=None, per_head_ga
     Returns (o with q's dtype and v's leading shape, S_T fp32 [N, H, dk, dv]
     or None).  ``events``: optional sequence of four raw hipEvent_t handles
     (ints) recorded before the chunk-map, intra-chunk and walk kernels and
-    after the walk kernel (kda_chunk_fwd_instrumented).
+    after the walk kernel (kda_chunk_fwd_instrumented).  ``raw``: q, k, g,
+    beta are raw projections and the pre-path transforms run inside the
+    intra-chunk kernel (kda_chunk_fwd_raw; no ``events``).  ``check``: wait
+    for the stream and raise KDAError if the device rejected the sequence
+    offsets or a bounded wait gave up (kda_chunk_fwd_check); pass False to
+    keep the call asynchronous and check the workspace later.
     """
+    if raw and events is not None:
+        raise ValueError("events are not recorded for raw inputs")
     batched = q.dim() == 4
     if batched:
         B, T = q.shape[0], q.shape[1]
@@ -193,15 +203,26 @@ def chunk_fwd(q, k, v, g, beta, *, S0=None, cu_seqlens=None, N=None, per_head_ga
             N, T_total, H, dk, dv, dt, gk, _ptr(o), _ptr(S_T), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(stream))
     if events is None:
-        _check(lib.kda_chunk_fwd(*args))
+        _check((lib.kda_chunk_fwd_raw if raw else lib.kda_chunk_fwd)(*args))
     else:
         if len(events) != 4:
             raise ValueError("events must hold four hipEvent_t handles")
         arr = (ctypes.c_void_p * 4)(*[int(e) for e in events])
         _check(lib.kda_chunk_fwd_instrumented(*args, arr))
+    if check:
+        chunk_fwd_check(workspace, stream=stream)
     if batched:
         o = o.reshape(N, T_total // N, H, dv)
     return o, S_T
+
+
+def chunk_fwd_raw(q_raw, k_raw, v, g_raw, beta_raw, **kw):
+    """``chunk_fwd`` from raw projections (kda_chunk_fwd_raw): q_raw, k_raw
+    are scaled to unit L2 norm over dk, g_raw goes through -softplus and
+    beta_raw through the logistic function inside the intra-chunk kernel,
+    each result rounded once to the input dtype.  Keyword arguments as for
+    ``chunk_fwd``."""
+    return chunk_fwd(q_raw, k_raw, v, g_raw, beta_raw, raw=True, **kw)
 
 
 def chunk_fwd_noalloc(q, k, v, g, beta, *, out, S_T=None, S0=None, cu_seqlens=None, N=None,
@@ -236,7 +257,8 @@ def chunk_fwd_noalloc(q, k, v, g, beta, *, out, S_T=None, S0=None, cu_seqlens=No
 
 
 def chunk_fwd_check(workspace, stream=None):
-    """Synchronise and raise KDAError if the last call's device cu_seqlens were rejected."""
+    """Synchronise and raise KDAError if the last call on this workspace had its
+    device cu_seqlens rejected or a bounded wait gave up."""
     _check(load_library().kda_chunk_fwd_check(_ptr(workspace), _stream(stream)))
 
 

@@ -54,7 +54,8 @@ namespace {
 kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const void* g, const void* beta,
                           const float* S0, const int32_t* cu_seqlens, int32_t N, int64_t T_total, int32_t H,
                           int32_t d_k, int32_t d_v, kda_dtype dt, kda_gate gk, void* o, float* S_T,
-                          void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* events) {
+                          void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
+                          bool raw = false) {
     const kda_status st = check_common(H, d_k, d_v, dt, gk);
     if (st != KDA_OK) return st;
     if (N <= 0 || T_total < 0 || T_total > INT32_MAX) return KDA_ERR_INVALID_ARG;
@@ -81,6 +82,7 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
     a.max_chunks = kda::max_chunks_for(T_total, N);
     a.bf16 = dt == KDA_BF16;
     a.head_gate = gk == KDA_GATE_PER_HEAD;
+    a.raw = raw;
     const kda::ChunkWorkspace ws = kda::carve_chunk_workspace(workspace, T_total, N, H, d_k, d_v, a.bf16);
     return kda::launch_chunk_fwd(a, ws, stream, events) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
@@ -92,6 +94,14 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
     return chunk_fwd_impl(q, k, v, g, beta, S0, cu_seqlens, N, T_total, H, d_k, d_v, dt, gk, o, S_T, workspace,
                           workspace_bytes, stream, nullptr);
+}
+
+kda_status kda_chunk_fwd_raw(const void* q_raw, const void* k_raw, const void* v, const void* g_raw,
+                             const void* beta_raw, const float* S0, const int32_t* cu_seqlens, int32_t N,
+                             int64_t T_total, int32_t H, int32_t d_k, int32_t d_v, kda_dtype dt, kda_gate gk,
+                             void* o, float* S_T, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return chunk_fwd_impl(q_raw, k_raw, v, g_raw, beta_raw, S0, cu_seqlens, N, T_total, H, d_k, d_v, dt, gk, o, S_T,
+                          workspace, workspace_bytes, stream, nullptr, true);
 }
 
 kda_status kda_chunk_fwd_instrumented(const void* q, const void* k, const void* v, const void* g, const void* beta,

@@ -158,13 +158,44 @@ template <> struct Pair2<bf16_t> {
     __device__ __forceinline__ void load(const bf16_t* p) { w = *reinterpret_cast<const uint32_t*>(p); }
     __device__ __forceinline__ float lo() const { return __uint_as_float(w << 16); }
     __device__ __forceinline__ float hi() const { return __uint_as_float(w & 0xffff0000u); }
+    __device__ __forceinline__ void set(float a, float b) { w = f32x2_to_bf16x2(a, b); }  // rounded
 };
 template <> struct Pair2<float> {
     float2 w;
     __device__ __forceinline__ void load(const float* p) { w = *reinterpret_cast<const float2*>(p); }
     __device__ __forceinline__ float lo() const { return w.x; }
     __device__ __forceinline__ float hi() const { return w.y; }
+    __device__ __forceinline__ void set(float a, float b) { w = make_float2(a, b); }
 };
+
+// Sum of x over aligned groups of LANES (32 or 64) lanes, in every lane of
+// the group, in one fixed order: within each 16-lane row by DPP (swap
+// neighbours, swap pairs, mirror halves, mirror the row), then the four row
+// sums read as scalars.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+template <int LANES>
+__device__ __forceinline__ float lane_group_sum(float x) {
+    static_assert(LANES == 32 || LANES == 64, "half or whole wave");
+    x += dpp_f32<0xb1>(x);   // quad_perm(1, 0, 3, 2)
+    x += dpp_f32<0x4e>(x);   // quad_perm(2, 3, 0, 1)
+    x += dpp_f32<0x141>(x);  // row_half_mirror
+    x += dpp_f32<0x140>(x);  // row_mirror
+    auto row = [&](int l) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l)); };
+    const float r0 = row(0), r1 = row(16), r2 = row(32), r3 = row(48);
+    if constexpr (LANES == 64) return (r0 + r1) + (r2 + r3);
+    else return (threadIdx.x & 32) ? r2 + r3 : r0 + r1;
+}
+
+// 1 / sqrt(x), 0 for x = 0: exact division of the rounded square root for
+// fp32 inputs, the hardware reciprocal square root (about one ulp) for bf16.
+template <typename E> __device__ __forceinline__ float inv_norm(float x);
+template <> __device__ __forceinline__ float inv_norm<float>(float x) { return x > 0.f ? 1.f / sqrtf(x) : 0.f; }
+template <> __device__ __forceinline__ float inv_norm<bf16_t>(float x) {
+    return x > 0.f ? __builtin_amdgcn_rsqf(x) : 0.f;
+}
 
 template <typename E> __device__ __forceinline__ void load2(const E* p, float& a, float& b);
 template <> __device__ __forceinline__ void load2<bf16_t>(const bf16_t* p, float& a, float& b) {
@@ -330,8 +361,17 @@ __device__ __forceinline__ Frag<float> scale_frag(Frag<float> f, const float* s)
     return f;
 }
 
-template <typename E, int DK, int DV, bool HG>
-__global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
+// RAW: q, k, g and beta are raw projections; the pre-path transforms
+// (q, k scaled to unit L2 norm over d_k per token and head, g <- -softplus(g),
+// beta <- sigmoid(beta); "Kimi Linear architecture", section "KDA: a memo that
+// erases and rewrites": one forget rate in (0, 1) per channel) are applied
+// here in fp32 as the values are loaded, each result rounded once to E.
+// bf16: two workgroups per compute unit fit the LDS, so the registers are
+// held to what two of them can have (the raw pre-path would otherwise take a
+// few more and halve the occupancy); fp32 fits one workgroup per unit.
+template <typename E, int DK, int DV, bool HG, bool RAW>
+__global__ __launch_bounds__(kIntraThreads) __attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 ? 4 : 1)))
+void intra_chunk_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v, const E* __restrict__ g,
     const E* __restrict__ beta, const WsHeader* __restrict__ hdr, const int2* __restrict__ chunk_tab,
     int32_t H, E* __restrict__ Wo, E* __restrict__ QGo,
@@ -401,8 +441,24 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
     for (int r = 0; r < RPTV; ++r) vraw[r].load(v + ((t0 + clamp_row(vpart * RPTV + r)) * H + h) * DV + j0);
     // beta of token `lane`, loaded by every wave (same 64 values) so that its
     // store into LDS needs no branch for the compiler to sink the load into
-    const float beta_raw = Elt<E>::load(beta + (t0 + clamp_row(lane)) * H + h);
+    float beta_raw = Elt<E>::load(beta + (t0 + clamp_row(lane)) * H + h);
     auto row_ok = [&](int r) { return part * RPT + r < len; };
+
+    // ---- 0b. raw projections: the pre-path transforms, in fp32, each result
+    // rounded once to E in place of the loaded value (the values
+    // kda_prepare_inputs writes, up to the order of the norm's sum):
+    // g <- -softplus(g) and beta <- sigmoid(beta) here, where only g's loads
+    // are waited for; q and k are scaled to unit L2 norm where step 2 first
+    // reads them, so that their loads stay in flight through step 1.
+    if constexpr (RAW) {
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            if (HG) gh[r] = Elt<E>::to(Elt<E>::from(neg_softplus<E>(gh[r])));
+            else graw[r].set(neg_softplus<E>(graw[r].lo()), neg_softplus<E>(graw[r].hi()));
+        }
+    }
+    // the log-gate of row r, channel c0 + i (per head: the row's value)
+    auto gate_of = [&](int r, int i) -> float { return HG ? gh[r] : (i ? graw[r].hi() : graw[r].lo()); };
 
     // ---- 1. chunk-local inclusive prefix sum of the log-gate ----------------
     // in base-2 units (b log2(e)), so that every decay factor below is a bare
@@ -412,8 +468,8 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
         float run0 = 0.f, run1 = 0.f;
 #pragma unroll
         for (int r = 0; r < RPT; ++r) {
-            run0 = fmaf(row_ok(r) ? (HG ? gh[r] : graw[r].lo()) : 0.f, kLog2e, run0);
-            run1 = fmaf(row_ok(r) ? (HG ? gh[r] : graw[r].hi()) : 0.f, kLog2e, run1);
+            run0 = fmaf(row_ok(r) ? gate_of(r, 0) : 0.f, kLog2e, run0);
+            run1 = fmaf(row_ok(r) ? gate_of(r, 1) : 0.f, kLog2e, run1);
             bb[r][0] = run0;
             bb[r][1] = run1;
         }
@@ -469,10 +525,10 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
     for (int r = 1; r < RPT; ++r) {
         const bool ok = row_ok(r);
         if (HG) {
-            eg[r][0] = eg[r][1] = gate_exp2<E>(ok ? gh[r] * kLog2e : 0.f);
+            eg[r][0] = eg[r][1] = gate_exp2<E>(ok ? gate_of(r, 0) * kLog2e : 0.f);
         } else {
-            eg[r][0] = gate_exp2<E>(ok ? graw[r].lo() * kLog2e : 0.f);
-            eg[r][1] = gate_exp2<E>(ok ? graw[r].hi() * kLog2e : 0.f);
+            eg[r][0] = gate_exp2<E>(ok ? gate_of(r, 0) * kLog2e : 0.f);
+            eg[r][1] = gate_exp2<E>(ok ? gate_of(r, 1) * kLog2e : 0.f);
         }
     }
     // e^{b_m - b} and e^{b_last - b}: from the last row back.  min(b_m - b, cap)
@@ -497,6 +553,17 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
     for (int r = 0; r < RPT; ++r) {
         const int row = part * RPT + r;
         const bool ok = row_ok(r);
+        if constexpr (RAW) {
+            // q and k of this row to unit L2 norm over d_k: the row's
+            // channels lie in DK / 2 consecutive lanes of one wave (two per
+            // lane; every lane takes part, rows past the end hold a copy of
+            // the last row); an all-zero row stays zero
+            const float rq0 = qraw[r].lo(), rq1 = qraw[r].hi(), rk0 = kraw[r].lo(), rk1 = kraw[r].hi();
+            const float iq = inv_norm<E>(lane_group_sum<DK / 2>(rq0 * rq0 + rq1 * rq1));
+            const float ik = inv_norm<E>(lane_group_sum<DK / 2>(rk0 * rk0 + rk1 * rk1));
+            qraw[r].set(rq0 * iq, rq1 * iq);
+            kraw[r].set(rk0 * ik, rk1 * ik);
+        }
         const float k0 = ok ? kraw[r].lo() : 0.f, k1 = ok ? kraw[r].hi() : 0.f;
         const float q0 = ok ? qraw[r].lo() : 0.f, q1 = ok ? qraw[r].hi() : 0.f;
         if (r > 0) {
@@ -554,6 +621,7 @@ __global__ __launch_bounds__(kIntraThreads) void intra_chunk_kernel(
         }
         sTileF[v * DK + c] = gate_exp2<E>(x);
     }
+    if constexpr (RAW) beta_raw = Elt<E>::to(Elt<E>::from(sigmoid<E>(beta_raw)));
     sBeta[lane] = lane < len ? beta_raw : 0.f;  // every wave writes the same values
     lds_barrier();
 
@@ -1829,10 +1897,10 @@ static hipError_t ensure_lds_attr(const void* kern, int bytes, std::atomic<uint6
     return e;
 }
 
-template <typename E, int DK, int DV, bool HG>
+template <typename E, int DK, int DV, bool HG, bool RAW>
 static hipError_t launch_intra(const ChunkArgs& a, const ChunkWorkspace& ws, hipStream_t stream) {
     using L = IntraLayout<E, DK, DV>;
-    auto kern = intra_chunk_kernel<E, DK, DV, HG>;
+    auto kern = intra_chunk_kernel<E, DK, DV, HG, RAW>;
     static std::atomic<uint64_t> attr_done{0};
     if (hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(kern), (int)L::bytes, attr_done);
         e != hipSuccess)
@@ -1876,7 +1944,12 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkWorkspace& ws, h
     hipError_t e = mark(ev, 1, stream);
     if (e != hipSuccess) return e;
     if (a.T > 0) {
-        e = a.head_gate ? launch_intra<E, DK, DV, true>(a, ws, stream) : launch_intra<E, DK, DV, false>(a, ws, stream);
+        if (a.raw)
+            e = a.head_gate ? launch_intra<E, DK, DV, true, true>(a, ws, stream)
+                            : launch_intra<E, DK, DV, false, true>(a, ws, stream);
+        else
+            e = a.head_gate ? launch_intra<E, DK, DV, true, false>(a, ws, stream)
+                            : launch_intra<E, DK, DV, false, false>(a, ws, stream);
         if (e != hipSuccess) return e;
     }
     if ((e = mark(ev, 2, stream)) != hipSuccess) return e;

@@ -64,6 +64,7 @@ struct ChunkArgs {
     int64_t T;
     int64_t max_chunks;
     bool bf16, head_gate;
+    bool raw;  // q, k, g, beta are raw projections (pre-path fused into the intra-chunk kernel)
 };
 
 // Workspace bytes and carving (host side, shared by size query and launch).

@@ -139,6 +139,30 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v,
                          size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * kda_chunk_fwd from raw projections: the pre-path transforms of
+ * kda_prepare_inputs (q, k scaled to unit L2 norm over d_k per token and
+ * head, an all-zero row staying zero; g <- -softplus(g); beta <-
+ * sigmoid(beta)) are applied inside the intra-chunk kernel as the inputs are
+ * read, in fp32, each result rounded once to dt: the values
+ * kda_prepare_inputs would write, up to the summation order of the norms.
+ * The separate pre-path pass and its round trip through HBM fall away.  "Kimi
+ * Linear architecture" (ttj.ttj.kr), section "KDA: a memo that erases and
+ * rewrites": one forget rate in (0, 1) per channel; "From GPT-2 to Kimi K3",
+ * section "Gated DeltaNet: now it can forget".  v is used as given.
+ * Arguments, layouts, workspace, alignment and status codes as for
+ * kda_chunk_fwd (q_raw, k_raw, g_raw, beta_raw in the places of q, k, g,
+ * beta; a raw gate may take any finite value).
+ */
+kda_status kda_chunk_fwd_raw(const void *q_raw, const void *k_raw,
+                             const void *v, const void *g_raw,
+                             const void *beta_raw, const float *S0,
+                             const int32_t *cu_seqlens, int32_t N,
+                             int64_t T_total, int32_t H, int32_t d_k,
+                             int32_t d_v, kda_dtype dt, kda_gate gk, void *o,
+                             float *S_T, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Same as kda_chunk_fwd, and also records the four caller-created HIP events
  * events[0..3] on `stream`: before the chunk-map kernel, before the
  * intra-chunk kernel, before the chunk-walk kernel and after it, so that

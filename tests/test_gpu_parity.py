@@ -324,11 +324,15 @@ def test_chunk_bad_seqlens_rejected_on_device():
     bad = torch.tensor([0, 100, 64], dtype=torch.int32, device="cuda")  # decreasing
     o = torch.full((128, 2, 64), 7.0, dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(kda.chunk_fwd_workspace_size(128, 2, 2, 64, 64), dtype=torch.uint8, device="cuda")
-    kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], cu_seqlens=bad, out=o, workspace=ws)
+    kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], cu_seqlens=bad, out=o, workspace=ws, check=False)
     with pytest.raises(kda.KDAError) as ei:
         kda.chunk_fwd_check(ws)
     assert ei.value.code == 5
     assert torch.all(o == 7.0)
+    # the binding's default checks the workspace itself
+    with pytest.raises(kda.KDAError) as ei:
+        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], cu_seqlens=bad, out=o, workspace=ws)
+    assert ei.value.code == 5
     kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], cu_seqlens=x["cu_seqlens"], out=o, workspace=ws)
     kda.chunk_fwd_check(ws)
 
