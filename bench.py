@@ -21,8 +21,9 @@ oracle (fp64, host cores) is timed on a bounded prefix of the same workload as
 `cpu_baseline`.  After the timed steps, the 1M-token prefill (T = 1,048,576,
 H = 16) is timed under `long_context`, the chunked backward pass
 (kda_chunk_bwd) over the 32K prefill inputs under `backward`, the pre-path
-transforms (kda_prepare_inputs on the prefill inputs, and the decode step with
-them fused in) under `prepath`, and the d = 64 variant of the prefill at the
+transforms (kda_prepare_inputs on the prefill inputs, the decode step with
+them fused in, and the prefill with them fused in, kda_chunk_fwd_raw) under
+`prepath`, and the d = 64 variant of the prefill at the
 same model width (H = 64) under `variant_d64`.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-backward]
@@ -49,6 +50,8 @@ PATH_FLOP_PER_HT = 139136              # 6 d^2 + (5C - 1) d
 INTRA_BYTES_PER_HT = 2154              # reads q,k,v,g,beta (1026); writes W,QG,KdT,U' (4 x 256), P (96: the 6 of
                                        # its 8 fragment blocks on or below the diagonal), Gn (8)
 WALK_BYTES_PER_HT = 1384               # reads W,QG,KdT,U' (4 x 256), P (96), Gn (8); writes o (256)
+SEG_PASS1_BYTES_PER_HT = 776           # the segmented walk's first pass re-reads W, KdT, U' (3 x 256), Gn (8)
+SEG_GROUPS_32K = 8                     # segments per (sequence, head) at 32K x 32 (one workgroup per CU)
 DECODE_BYTES_PER_STEP = 1084243968     # state read + write (2 x 536870912) + tokens in (8404992) + o (2097152)
 
 
@@ -419,16 +422,18 @@ def main():
     # the whole path's 1282 B per head-token, the decode step with its own
     kern = {
         "kda::intra_chunk_kernel": (t_intra, PATH_MIN_BYTES_PER_HT * ht),
-        "kda::chunk_walk_kernel": (t_walk, PATH_MIN_BYTES_PER_HT * ht),
+        "kda::seg_walk_kernel": (t_walk, PATH_MIN_BYTES_PER_HT * ht),
         "kda::decode_step_kernel": (t_dec, DECODE_BYTES_PER_STEP),
     }
     dom = max(kern, key=lambda k: kern[k][0])
     dom_ms, dom_bytes = kern[dom]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    walk_bytes = (WALK_BYTES_PER_HT + SEG_PASS1_BYTES_PER_HT * (SEG_GROUPS_32K - 1) / SEG_GROUPS_32K) * ht
     inter = {"intra_chunk": {"ms": t_intra, "bytes": INTRA_BYTES_PER_HT * ht,
                              "GB_per_s": INTRA_BYTES_PER_HT * ht / (t_intra * 1e-3) / 1e9},
-             "chunk_walk": {"ms": t_walk, "bytes": WALK_BYTES_PER_HT * ht,
-                            "GB_per_s": WALK_BYTES_PER_HT * ht / (t_walk * 1e-3) / 1e9}}
+             "chunk_walk": {"ms": t_walk, "bytes": walk_bytes, "GB_per_s": walk_bytes / (t_walk * 1e-3) / 1e9,
+                            "what": "segmented walk: pass 3 reads every chunk's operands and writes o, pass 1 "
+                                    "re-reads W, KdT, U', Gn of the chunks outside the last segment"}}
     dec_gbs = DECODE_BYTES_PER_STEP / (t_dec * 1e-3) / 1e9
     path_gbs = PATH_MIN_BYTES_PER_HT * ht / (t_fwd * 1e-3) / 1e9
     path_tflops = PATH_FLOP_PER_HT * ht / (t_fwd * 1e-3) / 1e12
