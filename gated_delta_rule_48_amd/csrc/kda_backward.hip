@@ -212,36 +212,42 @@ __device__ __forceinline__ int tile_mid_row(int a) { return 16 * a + 8; }
 template <typename E>
 __device__ __forceinline__ float capped_exp(float x) { return gate_exp<E>(fminf(x, kCapNats)); }
 
-// Rows of the factor table (each DK floats).
-constexpr int kTfBm = 0;                    // b_m(a), the reference of tile a
-constexpr int kTfFs = kTfBm + kTiles;       // fs[a]
+// Rows of the factor table (each DK floats).  Prep uses rows [0, kTfPrepRows)
+// and the last local launch rows [kTfLocalRow0, kTfRows), so each keeps only
+// its own part in LDS (prep then fits three workgroups per compute unit).
+constexpr int kTfFx = 0;                    // fx[a,bb]
+constexpr int kTfFs = kTfFx + kPairs;       // fs[a]
 constexpr int kTfFe = kTfFs + kTiles;       // fe[bb]
-constexpr int kTfFx = kTfFe + kTiles;       // fx[a,bb]
-constexpr int kTfF1 = kTfFx + kPairs;       // f1[a,bb]
+constexpr int kTfBm = kTfFe + kTiles;       // b_m(a), the reference of tile a
+constexpr int kTfF1 = kTfBm + kTiles;       // f1[a,bb]
 constexpr int kTfF2 = kTfF1 + kPairs;       // f2[a,bb]
 constexpr int kTfRows = kTfF2 + kPairs;
+constexpr int kTfPrepRows = kTfBm;          // fx, fs, fe
+constexpr int kTfLocalRow0 = kTfFs;         // fs, fe, b_m, f1, f2
 
-// Fill the factor table from the chunk's prefix sums; b(row, c) reads the
-// prefix sum of row `row` (rows past the chunk's end hold the last sum).
-// Every thread of the workgroup calls it; the caller publishes the table with
-// a barrier.
+// Fill rows [row0, row1) of the factor table from the chunk's prefix sums
+// into tf (row r at tf + (r - row0) DK); b(row, c) reads the prefix sum of
+// row `row` (rows past the chunk's end hold the last sum).  Every thread of
+// the workgroup calls it; the caller publishes the table with a barrier.
 __device__ __forceinline__ float table_exp(float x) { return expf(fminf(x, kCapNats)); }
 
-template <typename E, int DK, typename BF>
+template <typename E, int DK, int ROW0, int ROW1, typename BF>
 __device__ __forceinline__ void fill_tile_factors(float* tf, BF b) {
-    for (int idx = threadIdx.x; idx < kTfRows * DK; idx += kBwdThreads) {
-        const int row = idx / DK, c = idx % DK;
+    for (int idx = threadIdx.x; idx < (ROW1 - ROW0) * DK; idx += kBwdThreads) {
+        const int row = ROW0 + idx / DK, c = idx % DK;
         float v;
-        if (row < kTfFs) {
+        if (row >= kTfBm && row < kTfF1) {
             v = b(tile_mid_row(row - kTfBm), c);
-        } else if (row < kTfFe) {
+        } else if (row >= kTfFs && row < kTfFe) {
             const int a = row - kTfFs;
             v = table_exp(b(tile_mid_row(a), c) - b(16 * a, c));
-        } else if (row < kTfFx) {
+        } else if (row >= kTfFe && row < kTfBm) {
             const int bb = row - kTfFe;
             v = table_exp(b(16 * bb + 15, c) - b(tile_mid_row(bb), c));
         } else {
-            const int kind = (row - kTfFx) / kPairs, p = (row - kTfFx) % kPairs;
+            // fx (kind 0), f1 (kind 1), f2 (kind 2)
+            const int kind = row < kTfFs ? 0 : (row < kTfF2 ? 1 : 2);
+            const int p = row - (kind == 0 ? kTfFx : kind == 1 ? kTfF1 : kTfF2);
             const int a = p >= 3 ? 3 : (p >= 1 ? 2 : 1), bb = p - pair_of(a, 0);
             const int ra = kind == 1 ? tile_mid_row(a) : 16 * a;           // fx, f2: s(a); f1: m(a)
             const int rb = kind == 2 ? tile_mid_row(bb) : 16 * bb + 15;     // fx, f1: e(bb); f2: m(bb)
@@ -315,14 +321,16 @@ __device__ __forceinline__ void decayed_mp(const float* Kr, const float* Qr, con
 // ---------------------------------------------------------------------------
 // Per (chunk, head): prefix sums, decayed operands, M, P, T = (I + A)^{-1},
 // W and U'.
+// Three workgroups per compute unit: the registers are held to what three
+// can have (one over it otherwise), the LDS fits.
 template <typename E, int DK, int DV, bool HG>
-__global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const E* __restrict__ q, const E* __restrict__ k,
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))) void bwd_prep_kernel(const E* __restrict__ q, const E* __restrict__ k,
                                                                const E* __restrict__ v, const E* __restrict__ g,
                                                                const E* __restrict__ beta, int32_t H, int32_t Hs, BwdWs w) {
     // sA | sT for the solve; before that, the chunk's prefix sums b [C][DK]
     __shared__ __align__(16) float sAT[2 * C * (C + 1)];
     __shared__ float sbeta[C];
-    __shared__ float sTf[kTfRows * DK];  // tile decay factors
+    __shared__ float sTf[kTfPrepRows * DK];  // tile decay factors fx, fs, fe
     constexpr int kLdsFloats = kGemmLds > 3 * 16 * (C + 4) ? kGemmLds : 3 * 16 * (C + 4);
     __shared__ __align__(16) float lds[kLdsFloats];
     static_assert(C * DK <= 2 * C * (C + 1), "prefix sums fit in the solve's LDS");
@@ -355,7 +363,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(const E* __restri
         w.Gn[(size_t)slot * DK + c] = gate_exp<E>(b);
     }
     __syncthreads();
-    fill_tile_factors<E, DK>(sTf, [&](int row, int c) { return sB[row * DK + c]; });
+    fill_tile_factors<E, DK, 0, kTfPrepRows>(sTf, [&](int row, int c) { return sB[row * DK + c]; });
     // every decayed operand; r is the prefix sum at the middle row of the
     // row's own 16-row tile.  Four consecutive channels per thread, so each
     // array is written with 16-byte stores.
@@ -1022,8 +1030,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
     }  // PH == 1
 
     if constexpr (PH == 2) {
-    __shared__ float sTf[kTfRows * DK];  // tile decay factors and references
-    fill_tile_factors<E, DK>(sTf, [&](int row, int c) { return w.B[oCK + (size_t)row * DK + c]; });
+    __shared__ float sTf[(kTfRows - kTfLocalRow0) * DK];  // tile decay factors and references fs, fe, b_m, f1, f2
+    fill_tile_factors<E, DK, kTfLocalRow0, kTfRows>(sTf, [&](int row, int c) { return w.B[oCK + (size_t)row * DK + c]; });
+    auto tf_row = [&](int row) { return sTf + (row - kTfLocalRow0) * DK; };
     __syncthreads();
 
     // phase 5: dKr = diag(beta) dA Ki, dKi = (diag(beta) dA)^T Kr + dP^T Qr,
@@ -1107,8 +1116,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
             // kt > wv, Kr and Qr go to s(kt), then to m(wv).
             const int kt = k0 / KT;
             const bool row_side = kt <= wv, col_side = kt >= wv;
-            const float* fu = sTf + (kt < wv ? kTfFe + kt : kTfFs + kt) * DK;
-            const float* fv = sTf + (kt < wv ? kTfF1 + pair_of(wv, kt) : kTfF2 + pair_of(kt > wv ? kt : 1, kt > wv ? wv : 0)) * DK;
+            const float* fu = tf_row(kt < wv ? kTfFe + kt : kTfFs + kt);
+            const float* fv = tf_row(kt < wv ? kTfF1 + pair_of(wv, kt) : kTfF2 + pair_of(kt > wv ? kt : 1, kt > wv ? wv : 0));
 #pragma unroll
             for (int ks = 0; ks < KT; ks += 4) {
                 const int kr = ks + lg, ar = kr * SA + 16 * wv + lr;
@@ -1161,7 +1170,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
                 const float dXw = w.dXw[j];
                 const float dKG = sbeta[t] * dXw;
                 const float dQG = w.dQG[j], dKd = w.dKd[j];
-                const float bb = w.B[j], r = sTf[(kTfBm + wv) * DK + c], bl = sbl[c];
+                const float bb = w.B[j], r = tf_row(kTfBm + wv)[c], bl = sbl[c];
                 const float e = gate_exp<E>(bb), er = capped_exp<E>(bb - r), eir = capped_exp<E>(r - bb),
                             ed = gate_exp<E>(bl - bb);
                 const int64_t o = ((t0 + t) * Hs + h) * DK + c;
