@@ -246,6 +246,18 @@ def test_sequential_chunked_dplr_agree(T, dk, dv, chunk, per_head, seed):
         assert oracle.rel_err(s, s1) < 1e-11
 
 
+@pytest.mark.parametrize("per_head", [False, True])
+def test_chunked_c128_agrees(per_head):
+    """The chunk algebra at C = 128, the other chunk size the pages name
+    (three chunks, the last ragged), agrees with the sequential recurrence."""
+    rng = np.random.default_rng(128 + per_head)
+    q, k, v, g, beta, S0 = _rand(rng, 300, 2, 8, 6, per_head=per_head)
+    (o1, s1), (o2, s2), (o3, s3) = _all_forms(q, k, v, g, beta, S0=S0, chunk=128, per_head_gate=per_head)
+    for o, s in ((o2, s2), (o3, s3)):
+        assert oracle.rel_err(o, o1) < 1e-11
+        assert oracle.rel_err(s, s1) < 1e-11
+
+
 def test_varlen_equals_separate_sequences_and_empty():
     """Packed sequences never mix; an empty sequence returns S0 unchanged."""
     rng = np.random.default_rng(7)
