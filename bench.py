@@ -23,8 +23,10 @@ H = 16) is timed under `long_context`, the chunked backward pass
 (kda_chunk_bwd) over the 32K prefill inputs under `backward`, the pre-path
 transforms (kda_prepare_inputs on the prefill inputs, the decode step with
 them fused in, and the prefill with them fused in, kda_chunk_fwd_raw) under
-`prepath`, and the d = 64 variant of the prefill at the
-same model width (H = 64) under `variant_d64`.
+`prepath`, the d = 64 variant of the prefill at the same model width
+(H = 64) under `variant_d64`, and the 32K prefill with 128-token chunks
+(kda_chunk_fwd_c128) under `variant_c128` (the 1M prefill with them under
+`long_context.c128`).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-backward]
 """
@@ -57,7 +59,7 @@ DECODE_BYTES_PER_STEP = 1084243968     # state read + write (2 x 536870912) + to
 
 # The files the forward and decode kernels are compiled from (the backward
 # pass and the host-side ABI live elsewhere and do not change them).
-KERNEL_SOURCES = ("kda_chunk.hip", "kda_decode.hip", "kda_device.h")
+KERNEL_SOURCES = ("kda_chunk.hip", "kda_chunk_util.h", "kda_decode.hip", "kda_device.h")
 
 
 def kernel_sources_sha():
@@ -238,7 +240,34 @@ def time_prepath(kda, torch, hip, x, T, H, dk, stream, S_dec, toks, steps=10):
     }
 
 
-def time_long_context(kda, torch, hip, stream, steps=3):
+def time_c128(kda, torch, hip, x, T, H, dk, dv, stream, steps=10):
+    """The 32K x 32 prefill with 128-token chunks (kda_chunk_fwd_c128) on the
+    same resident inputs, each call's chunk map, intra-chunk kernel and walk
+    timed with HIP events on its stream; reported beside the 64-token path,
+    not part of `value`."""
+    o = torch.empty((T, H, dv), dtype=torch.bfloat16, device="cuda")
+    S_T = torch.empty((1, H, dk, dv), dtype=torch.float32, device="cuda")
+    ws = torch.empty(kda.chunk_fwd_workspace_size(T, 1, H, dk, dv, chunk=128), dtype=torch.uint8, device="cuda")
+    evs = [Events(hip, 4) for _ in range(steps)]
+    for _ in range(2):
+        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], out=o, S_T=S_T, workspace=ws, check=False,
+                      chunk=128)
+    for e in evs:
+        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], out=o, S_T=S_T, workspace=ws, check=False,
+                      chunk=128, events=e.ev)
+    torch.cuda.synchronize()
+    kda.chunk_fwd_check(ws)
+    med = lambda i, j: float(np.median([e.ms(i, j) for e in evs]))
+    t = med(0, 3)
+    ht = T * H
+    return {"what": f"kda_chunk_fwd_c128, T={T}, H={H}, d_k=d_v={dk}, bf16, C=128", "ms": t,
+            "tokens_per_s": T / (t * 1e-3),
+            "kernels_ms": {"chunk_map": med(0, 1), "intra_chunk": med(1, 2), "chunk_walk": med(2, 3)},
+            "method_GB_per_s": PATH_MIN_BYTES_PER_HT * ht / (t * 1e-3) / 1e9,
+            "TFLOP_per_s": PATH_FLOP_PER_HT * ht / (t * 1e-3) / 1e12}
+
+
+def time_long_context(kda, torch, hip, stream, steps=3, with_c128=True):
     """The 1M-token prefill (kda_1m_bf16: B=1, T=1,048,576, H=16, d=128,
     bf16, per-channel gate from N(-1,1)) through kda_chunk_fwd, inputs drawn
     block by block (the recipe of the parity test) and resident in HBM before
@@ -273,6 +302,27 @@ def time_long_context(kda, torch, hip, stream, steps=3):
     res = {"what": f"kda_chunk_fwd, kda_1m_bf16: T={T}, H={H}, d_k=d_v={dk}, bf16", "ms_median": t,
            "ms_min": float(np.min(ms)), "tokens_per_s": T / (t * 1e-3), "method_GB_per_s": gbs,
            "frac_hbm_peak": gbs / HBM_PEAK_GBS}
+    if with_c128:
+        # the same inputs with 128-token chunks (kda_chunk_fwd_c128)
+        del ws
+        ws = torch.empty(kda.chunk_fwd_workspace_size(T, 1, H, dk, dv, chunk=128), dtype=torch.uint8,
+                         device="cuda")
+        ev2 = Events(hip, steps + 1)
+
+        def run128():
+            kda.chunk_fwd(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], out=o, S_T=S_T, workspace=ws,
+                          check=False, chunk=128)
+
+        run128()
+        ev2.record(0, stream)
+        for i in range(steps):
+            run128()
+            ev2.record(i + 1, stream)
+        torch.cuda.synchronize()
+        kda.chunk_fwd_check(ws)
+        t2 = float(np.median([ev2.ms(i, i + 1) for i in range(steps)]))
+        res["c128"] = {"what": "kda_chunk_fwd_c128 on the same inputs (C = 128)", "ms_median": t2,
+                       "tokens_per_s": T / (t2 * 1e-3)}
     del dev, o, S_T, ws
     torch.cuda.empty_cache()
     return res
@@ -311,7 +361,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-prefix", type=int, default=32768)
     ap.add_argument("--no-backward", action="store_true", help="skip timing the chunked backward pass")
-    ap.add_argument("--no-variants", action="store_true", help="skip timing the d = 64 variant")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip timing the d = 64 and the 128-token-chunk variants")
     ap.add_argument("--no-long-context", action="store_true", help="skip timing the 1M-token prefill")
     ap.add_argument("--backward-steps", type=int, default=5)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -406,7 +457,9 @@ def main():
 
     prepath = time_prepath(kda, torch, hip, x, T, H, dk, stream, S_dec, toks)
     d64 = None if args.no_variants else time_d64_variant(kda, torch, hip, stream)
-    longc = None if args.no_long_context else time_long_context(kda, torch, hip, stream)
+    c128 = None if args.no_variants else time_c128(kda, torch, hip, x, T, H, dk, dv, stream)
+    longc = None if args.no_long_context else time_long_context(kda, torch, hip, stream,
+                                                                  with_c128=not args.no_variants)
     bwd = None if args.no_backward else time_backward(kda, torch, hip, x, d, T, H, dk, dv, stream,
                                                       steps=args.backward_steps)
 
@@ -483,6 +536,8 @@ def main():
         res["long_context"] = longc
     if d64 is not None:
         res["variant_d64"] = d64
+    if c128 is not None:
+        res["variant_c128"] = c128
     if bwd is not None:
         res["backward"] = bwd
     if not args.no_cpu_baseline:

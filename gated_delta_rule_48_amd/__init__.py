@@ -64,6 +64,10 @@ def load_library():
         lib.kda_chunk_fwd_instrumented.argtypes = lib.kda_chunk_fwd.argtypes + [vp]
         lib.kda_chunk_fwd_raw.restype = ctypes.c_int
         lib.kda_chunk_fwd_raw.argtypes = lib.kda_chunk_fwd.argtypes
+        lib.kda_chunk_fwd_c128_workspace_size.restype = sz
+        lib.kda_chunk_fwd_c128_workspace_size.argtypes = lib.kda_chunk_fwd_workspace_size.argtypes
+        lib.kda_chunk_fwd_c128.restype = ctypes.c_int
+        lib.kda_chunk_fwd_c128.argtypes = lib.kda_chunk_fwd.argtypes + [vp]
         lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
         lib.kda_chunk_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, ctypes.c_int,
                                               ctypes.c_int, vp, vp, vp]
@@ -127,16 +131,23 @@ def _shapes(**named):
             raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
-def chunk_fwd_workspace_size(T_total, N, H, d_k, d_v, dtype=torch.bfloat16, per_head_gate=False):
+def chunk_fwd_workspace_size(T_total, N, H, d_k, d_v, dtype=torch.bfloat16, per_head_gate=False, chunk=64):
     """Bytes of workspace ``chunk_fwd`` needs (0 for unsupported sizes)."""
     dt = _BF16 if dtype == torch.bfloat16 else _F32
-    return int(load_library().kda_chunk_fwd_workspace_size(
-        int(T_total), int(N), int(H), int(d_k), int(d_v), dt, _PER_HEAD if per_head_gate else _PER_CHANNEL))
+    lib = load_library()
+    fn = lib.kda_chunk_fwd_c128_workspace_size if _chunk_size(chunk) == 128 else lib.kda_chunk_fwd_workspace_size
+    return int(fn(int(T_total), int(N), int(H), int(d_k), int(d_v), dt, _PER_HEAD if per_head_gate else _PER_CHANNEL))
+
+
+def _chunk_size(chunk):
+    if chunk not in (64, 128):
+        raise ValueError(f"chunk must be 64 or 128, got {chunk}")
+    return chunk
 
 
 def chunk_fwd(q, k, v, g, beta, *, S0=None, cu_seqlens=None, N=None, per_head_gate=False,
               out=None, S_T=None, workspace=None, stream=None, output_final_state=True, events=None,
-              raw=False, check=True):
+              raw=False, check=True, chunk=64):
     """Chunked KDA forward (prefill).
 
     q, k: [T, H, dk] packed (with ``cu_seqlens`` int32 [N+1] on the device, or
@@ -152,10 +163,14 @@ def chunk_fwd(q, k, v, g, beta, *, S0=None, cu_seqlens=None, N=None, per_head_ga
     intra-chunk kernel (kda_chunk_fwd_raw; no ``events``).  ``check``: wait
     for the stream and raise KDAError if the device rejected the sequence
     offsets or a bounded wait gave up (kda_chunk_fwd_check); pass False to
-    keep the call asynchronous and check the workspace later.
+    keep the call asynchronous and check the workspace later.  ``chunk``:
+    tokens per chunk, 64 (kda_chunk_fwd) or 128 (kda_chunk_fwd_c128; not
+    with ``raw``).
     """
     if raw and events is not None:
         raise ValueError("events are not recorded for raw inputs")
+    if _chunk_size(chunk) == 128 and raw:
+        raise ValueError("raw inputs are taken with 64-token chunks only")
     batched = q.dim() == 4
     if batched:
         B, T = q.shape[0], q.shape[1]
@@ -193,7 +208,8 @@ def chunk_fwd(q, k, v, g, beta, *, S0=None, cu_seqlens=None, N=None, per_head_ga
         _dev_contig("S_T", S_T, torch.float32)
         _shapes(S_T=(S_T, (N, H, dk, dv)))
     lib = load_library()
-    need = int(lib.kda_chunk_fwd_workspace_size(T_total, N, H, dk, dv, dt, gk))
+    size_fn = lib.kda_chunk_fwd_c128_workspace_size if chunk == 128 else lib.kda_chunk_fwd_workspace_size
+    need = int(size_fn(T_total, N, H, dk, dv, dt, gk))
     if need == 0:
         raise KDAError(2, f"unsupported sizes T={T_total} N={N} H={H} dk={dk} dv={dv}")
     if workspace is None:
@@ -202,7 +218,14 @@ def chunk_fwd(q, k, v, g, beta, *, S0=None, cu_seqlens=None, N=None, per_head_ga
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(cu_seqlens),
             N, T_total, H, dk, dv, dt, gk, _ptr(o), _ptr(S_T), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(stream))
-    if events is None:
+    if chunk == 128:
+        arr = None
+        if events is not None:
+            if len(events) != 4:
+                raise ValueError("events must hold four hipEvent_t handles")
+            arr = (ctypes.c_void_p * 4)(*[int(e) for e in events])
+        _check(lib.kda_chunk_fwd_c128(*args, arr))
+    elif events is None:
         _check((lib.kda_chunk_fwd_raw if raw else lib.kda_chunk_fwd)(*args))
     else:
         if len(events) != 4:

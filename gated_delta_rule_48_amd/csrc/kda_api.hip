@@ -50,17 +50,26 @@ size_t kda_chunk_fwd_workspace_size(int64_t T_total, int32_t N, int32_t H, int32
     return kda::chunk_workspace_bytes(T_total, N, H, d_k, d_v, dt == KDA_BF16);
 }
 
+size_t kda_chunk_fwd_c128_workspace_size(int64_t T_total, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                                         kda_dtype dt, kda_gate gk) {
+    if (check_common(H, d_k, d_v, dt, gk) != KDA_OK) return 0;
+    if (!kda::chunk128_supported(d_k, d_v, dt == KDA_BF16)) return 0;
+    if (N <= 0 || T_total < 0 || T_total > INT32_MAX) return 0;
+    return kda::chunk_workspace_bytes(T_total, N, H, d_k, d_v, dt == KDA_BF16, 128);
+}
+
 namespace {
 kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const void* g, const void* beta,
                           const float* S0, const int32_t* cu_seqlens, int32_t N, int64_t T_total, int32_t H,
                           int32_t d_k, int32_t d_v, kda_dtype dt, kda_gate gk, void* o, float* S_T,
                           void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
-                          bool raw = false) {
+                          bool raw = false, int32_t chunk = kda::kChunk) {
     const kda_status st = check_common(H, d_k, d_v, dt, gk);
     if (st != KDA_OK) return st;
+    if (chunk == 128 && !kda::chunk128_supported(d_k, d_v, dt == KDA_BF16)) return KDA_ERR_UNSUPPORTED;
     if (N <= 0 || T_total < 0 || T_total > INT32_MAX) return KDA_ERR_INVALID_ARG;
     if (!cu_seqlens && T_total % N != 0) return KDA_ERR_INVALID_ARG;
-    if (!kda::chunk_grid_fits(kda::max_chunks_for(T_total, N), H)) return KDA_ERR_UNSUPPORTED;
+    if (!kda::chunk_grid_fits(kda::max_chunks_for(T_total, N, chunk), H, chunk)) return KDA_ERR_UNSUPPORTED;
     if (T_total > 0) {
         if (!q || !k || !v || !g || !beta || !o) return KDA_ERR_INVALID_ARG;
         // q, k, v and a per-channel g are read two elements at a time
@@ -72,18 +81,19 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
     if ((S0 && !aligned(S0, 4)) || (S_T && !aligned(S_T, 4)) || (cu_seqlens && !aligned(cu_seqlens, 4)))
         return KDA_ERR_INVALID_ARG;
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERR_WORKSPACE;
-    const size_t need = kda::chunk_workspace_bytes(T_total, N, H, d_k, d_v, dt == KDA_BF16);
+    const size_t need = kda::chunk_workspace_bytes(T_total, N, H, d_k, d_v, dt == KDA_BF16, chunk);
     if (workspace_bytes < need) return KDA_ERR_WORKSPACE;
 
     kda::ChunkArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
     a.S0 = S0; a.cu_seqlens = cu_seqlens; a.o = o; a.S_T = S_T;
     a.N = N; a.H = H; a.dk = d_k; a.dv = d_v; a.T = T_total;
-    a.max_chunks = kda::max_chunks_for(T_total, N);
+    a.max_chunks = kda::max_chunks_for(T_total, N, chunk);
     a.bf16 = dt == KDA_BF16;
     a.head_gate = gk == KDA_GATE_PER_HEAD;
     a.raw = raw;
-    const kda::ChunkWorkspace ws = kda::carve_chunk_workspace(workspace, T_total, N, H, d_k, d_v, a.bf16);
+    a.chunk = chunk;
+    const kda::ChunkWorkspace ws = kda::carve_chunk_workspace(workspace, T_total, N, H, d_k, d_v, a.bf16, chunk);
     return kda::launch_chunk_fwd(a, ws, stream, events) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 }  // namespace
@@ -102,6 +112,14 @@ kda_status kda_chunk_fwd_raw(const void* q_raw, const void* k_raw, const void* v
                              void* o, float* S_T, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     return chunk_fwd_impl(q_raw, k_raw, v, g_raw, beta_raw, S0, cu_seqlens, N, T_total, H, d_k, d_v, dt, gk, o, S_T,
                           workspace, workspace_bytes, stream, nullptr, true);
+}
+
+kda_status kda_chunk_fwd_c128(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                              const float* S0, const int32_t* cu_seqlens, int32_t N, int64_t T_total, int32_t H,
+                              int32_t d_k, int32_t d_v, kda_dtype dt, kda_gate gk, void* o, float* S_T,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* events) {
+    return chunk_fwd_impl(q, k, v, g, beta, S0, cu_seqlens, N, T_total, H, d_k, d_v, dt, gk, o, S_T, workspace,
+                          workspace_bytes, stream, events, false, 128);
 }
 
 kda_status kda_chunk_fwd_instrumented(const void* q, const void* k, const void* v, const void* g, const void* beta,

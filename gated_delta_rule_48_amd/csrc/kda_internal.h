@@ -43,7 +43,7 @@ struct ChunkWorkspace {
     void* W;              // C x dk,  T (beta K exp(b)), fragment-major
     void* QG;             // C x dk,  Q exp(b), fragment-major
     void* KdT;            // dk x C,  (K exp(b_last - b))^T, fragment-major
-    void* Up;             // dv x C values of T (beta V): [dv/16][64 lanes][16]
+    void* Up;             // dv x C values of T (beta V): [dv/16][64 lanes][C/4]
     void* P;              // C x C,   masked intra-chunk Q K^T with decay, fragment-major
     float* Gn;            // [max_chunks, H, dk]      exp(b_last)
     // Segmented walk (null when the per-slice walk runs): segments per pair,
@@ -65,15 +65,24 @@ struct ChunkArgs {
     int64_t max_chunks;
     bool bf16, head_gate;
     bool raw;  // q, k, g, beta are raw projections (pre-path fused into the intra-chunk kernel)
+    int32_t chunk = kChunk;  // tokens per chunk: 64, or 128 (kda_chunk128.hip)
 };
 
 // Workspace bytes and carving (host side, shared by size query and launch).
-size_t chunk_workspace_bytes(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, bool bf16);
+// `chunk` is the chunk size in tokens, 64 or 128.
+size_t chunk_workspace_bytes(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, bool bf16,
+                             int32_t chunk = kChunk);
 ChunkWorkspace carve_chunk_workspace(void* base, int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv,
-                                     bool bf16);
-int64_t max_chunks_for(int64_t T, int32_t N);
-int32_t seg_groups_for(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, bool bf16);
-bool chunk_grid_fits(int64_t max_chunks, int32_t H);
+                                     bool bf16, int32_t chunk = kChunk);
+int64_t max_chunks_for(int64_t T, int32_t N, int32_t chunk = kChunk);
+int32_t seg_groups_for(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, bool bf16, int32_t chunk = kChunk);
+bool chunk_grid_fits(int64_t max_chunks, int32_t H, int32_t chunk = kChunk);
+// Head sizes and element types the 128-token kernels support (bf16: d_k,
+// d_v in {64, 128}; fp32: d_k = d_v = 64, the LDS of one compute unit).
+bool chunk128_supported(int32_t dk, int32_t dv, bool bf16);
+// The intra-chunk kernel and walk for 128-token chunks, after the chunk map.
+hipError_t launch_chunk128_kernels(const ChunkArgs& a, const ChunkWorkspace& ws, hipStream_t stream,
+                                   hipEvent_t* events);
 
 // Validate cu_seqlens (or synthesise N equal sequences when it is null) and
 // write the header, the sequence offsets, the first chunk of every sequence
@@ -82,7 +91,7 @@ bool chunk_grid_fits(int64_t max_chunks, int32_t H);
 // (null and 0 when it does not run).
 hipError_t launch_chunk_map(const int32_t* cu_seqlens, int32_t N, int64_t T, WsHeader* header, int32_t* cu,
                             int32_t* chunk_off, int2* chunk_tab, int32_t* seg_flags, int64_t n_flags,
-                            hipStream_t stream);
+                            hipStream_t stream, int32_t chunk = kChunk);
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 

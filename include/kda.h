@@ -181,6 +181,36 @@ kda_status kda_chunk_fwd_instrumented(const void *q, const void *k, const void *
                                       hipEvent_t *events);
 
 /*
+ * kda_chunk_fwd with chunks of C = 128 tokens instead of 64.  "From GPT-2 to
+ * Kimi K3" (molayo1419.me), section "The parallelisation trick": chunks of 64
+ * or 128 tokens work best.  The chunk algebra is the same with C = 128: one
+ * 128 x 128 unit-lower-triangular solve per chunk, half as many steps of the
+ * state across chunk boundaries, each twice as long.
+ *
+ *   Arguments, layouts, numerics and status codes as for kda_chunk_fwd, with
+ *   the workspace sized by kda_chunk_fwd_c128_workspace_size (the status of
+ *   a call is read back with kda_chunk_fwd_check, as for kda_chunk_fwd).
+ *   Supported: KDA_BF16 with d_k, d_v in {64, 128}; KDA_F32 with
+ *   d_k = d_v = 64 only (the fp32 operand tiles of 128 rows at d = 128 do
+ *   not fit the 160 KB of LDS of a compute unit); KDA_ERR_UNSUPPORTED
+ *   otherwise.  Results agree with kda_chunk_fwd to rounding; they are not
+ *   bit-identical to it (the sums are grouped differently).
+ *   events: NULL, or four caller-created events recorded as for
+ *   kda_chunk_fwd_instrumented.
+ */
+size_t kda_chunk_fwd_c128_workspace_size(int64_t T_total, int32_t N, int32_t H,
+                                         int32_t d_k, int32_t d_v, kda_dtype dt,
+                                         kda_gate gk);
+kda_status kda_chunk_fwd_c128(const void *q, const void *k, const void *v,
+                              const void *g, const void *beta, const float *S0,
+                              const int32_t *cu_seqlens, int32_t N,
+                              int64_t T_total, int32_t H, int32_t d_k,
+                              int32_t d_v, kda_dtype dt, kda_gate gk, void *o,
+                              float *S_T, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream,
+                              hipEvent_t *events);
+
+/*
  * kda_chunk_fwd without a workspace argument, for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc.  It allocates nothing and frees nothing.

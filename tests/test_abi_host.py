@@ -30,7 +30,8 @@ def test_header_declares_expected_entry_points():
     names = _declared()
     for n in ("kda_chunk_fwd", "kda_recurrent_step", "kda_chunk_fwd_workspace_size",
               "kda_chunk_fwd_check", "kda_status_string", "kda_version", "kda_chunk_bwd",
-              "kda_chunk_bwd_workspace_size", "kda_prepare_inputs", "kda_recurrent_step_raw"):
+              "kda_chunk_bwd_workspace_size", "kda_prepare_inputs", "kda_recurrent_step_raw",
+              "kda_chunk_fwd_c128", "kda_chunk_fwd_c128_workspace_size"):
         assert n in names
 
 
@@ -101,6 +102,56 @@ def test_chunk_fwd_rejects_bad_arguments(lib):
     assert call(T=64 * (2**23 - 2), H=1, ws=None) == WORKSPACE   # 2^23 - 1 pairs: accepted
     assert call(T=64 * (2**23 - 1), H=1, ws=None) == UNSUPPORTED  # 2^23 pairs
     assert call(T=2**31 - 64, H=64) == UNSUPPORTED
+
+
+def _c128(lib):
+    f = lib.kda_chunk_fwd_c128
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    f.restype = ctypes.c_int
+    f.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, ctypes.c_int, ctypes.c_int, vp, vp, vp,
+                  ctypes.c_size_t, vp, vp]
+    s = lib.kda_chunk_fwd_c128_workspace_size
+    s.restype = ctypes.c_size_t
+    s.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_int, ctypes.c_int]
+    return f, s
+
+
+def test_chunk128_workspace_and_support(lib):
+    f, size = _c128(lib)
+    s64 = _sizes(lib)
+    for dk in (64, 128):
+        for dv in (64, 128):
+            assert size(32768, 1, 32, dk, dv, 0, 0) > 0          # bf16: every head size
+            assert size(32768, 1, 32, dk, dv, 0, 1) > 0
+    assert size(256, 1, 2, 64, 64, 1, 0) > 0                     # fp32: d = 64 only
+    assert size(256, 1, 2, 128, 128, 1, 0) == 0
+    assert size(256, 1, 2, 64, 128, 1, 0) == 0
+    assert size(256, 1, 2, 96, 64, 0, 0) == 0
+    assert size(256, 0, 2, 64, 64, 0, 0) == 0
+    # a 128-token chunk keeps a 128 x 128 block of P per chunk: more
+    # workspace than 64-token chunks at the same size
+    assert size(32768, 1, 32, 128, 128, 0, 0) > s64(32768, 1, 32, 128, 128, 0, 0)
+    P = FAKE
+    args = dict(q=P, k=P, v=P, g=P, beta=P, S0=None, cu=None, N=1, T=256, H=2, dk=64, dv=64, dt=1, gk=0,
+                o=P, S_T=None, ws=P, wsb=1 << 40, stream=None, ev=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["cu"], a["N"], a["T"], a["H"], a["dk"],
+                 a["dv"], a["dt"], a["gk"], a["o"], a["S_T"], a["ws"], a["wsb"], a["stream"], a["ev"])
+
+    assert call(dk=128, dv=128) == UNSUPPORTED    # fp32 at d = 128
+    assert call(dk=96, dt=0) == UNSUPPORTED
+    assert call(N=0) == INVALID
+    assert call(N=3) == INVALID                   # 256 % 3 != 0 without cu_seqlens
+    assert call(q=None) == INVALID
+    assert call(ws=None) == WORKSPACE
+    assert call(wsb=16) == WORKSPACE
+    # 1024 threads per (chunk, head) workgroup: ceil(T / 128) + N chunks
+    # times H must stay below 2^22
+    assert call(T=128 * (2**22 - 2), H=1, ws=None, dt=0) == WORKSPACE
+    assert call(T=128 * (2**22 - 1), H=1, ws=None, dt=0) == UNSUPPORTED
 
 
 def test_recurrent_step_rejects_bad_arguments(lib):
