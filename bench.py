@@ -59,7 +59,7 @@ DECODE_BYTES_PER_STEP = 1084243968     # state read + write (2 x 536870912) + to
 
 # The files the forward and decode kernels are compiled from (the backward
 # pass and the host-side ABI live elsewhere and do not change them).
-KERNEL_SOURCES = ("kda_chunk.hip", "kda_chunk_util.h", "kda_decode.hip", "kda_device.h")
+KERNEL_SOURCES = ("kda_chunk.hip", "kda_chunk128.hip", "kda_chunk_util.h", "kda_decode.hip", "kda_device.h")
 
 
 def kernel_sources_sha():

@@ -1353,6 +1353,51 @@ __global__ __launch_bounds__(kSegThreads) void seg_walk_kernel(
 #pragma unroll
             for (int m = 0; m < MT; ++m) Y[m] = mma(frag_at(sb, L::off_K, m * KB + kb), uf[kb], Y[m]);
     };
+    // the chunk steps of B (with U') and of M (without) at once: each W and
+    // KdT fragment is read from LDS once and feeds both products (each
+    // accumulates in the order chain_step uses)
+    auto chain_step2 = [&](f32x4 (&Y1)[MT], f32x4 (&Y2)[MT], const char* sb) __attribute__((always_inline)) {
+        Frag<E> yf1[KS], yf2[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            yf1[ks] = acc_to_frag(E{}, Y1[2 * ks], Y1[2 * ks + 1]);
+            yf2[ks] = acc_to_frag(E{}, Y2[2 * ks], Y2[2 * ks + 1]);
+        }
+        f32x4 X1[TT], X2[TT];
+#pragma unroll
+        for (int t = 0; t < TT; ++t) X1[t] = X2[t] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int t = 0; t < TT; ++t) {
+                const Frag<E> wf = frag_at(sb, L::off_W, t * KS + ks);
+                X1[t] = mma(wf, yf1[ks], X1[t]);
+                X2[t] = mma(wf, yf2[ks], X2[t]);
+            }
+        const float* gn = reinterpret_cast<const float*>(sb + L::off_G);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const f32x4 gm = *reinterpret_cast<const f32x4*>(gn + 16 * m + 4 * lg);
+            Y1[m] = gm * Y1[m];
+            Y2[m] = gm * Y2[m];
+        }
+        const E* Up = reinterpret_cast<const E*>(sb + L::off_U) + (w * 64 + lane) * 16;
+        Frag<E> uf1[KB], uf2[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            uf1[kb] = acc_to_frag(E{}, Raw4<E>::widen(Raw4<E>::load(Up + 8 * kb)) - X1[2 * kb],
+                                  Raw4<E>::widen(Raw4<E>::load(Up + 8 * kb + 4)) - X1[2 * kb + 1]);
+            uf2[kb] = acc_to_frag(E{}, zero4() - X2[2 * kb], zero4() - X2[2 * kb + 1]);
+        }
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const Frag<E> kf = frag_at(sb, L::off_K, m * KB + kb);
+                Y1[m] = mma(kf, uf1[kb], Y1[m]);
+                Y2[m] = mma(kf, uf2[kb], Y2[m]);
+            }
+    };
     // wait until S_start(i) is published (one lane polls; the others wait at
     // the barrier)
     auto wait_start = [&](int i) {
@@ -1381,9 +1426,12 @@ __global__ __launch_bounds__(kSegThreads) void seg_walk_kernel(
         // chunk c from slot cur, the next chunk's operands loading into nxt
         auto step1 = [&](int c, const char* cur, char* nxt) __attribute__((always_inline)) {
             if (c + 1 < s1) dma_chunk(c + 1, nxt, false);
-            Frag<E> yf[KS], uf[KB];
-            chain_step(B, cur, true, yf, uf);
-            if (!first) chain_step(M, cur, false, yf, uf);
+            if (first) {
+                Frag<E> yf[KS], uf[KB];
+                chain_step(B, cur, true, yf, uf);
+            } else {
+                chain_step2(B, M, cur);
+            }
             wait_vmcnt<0>();
             lds_barrier();
         };
