@@ -418,7 +418,7 @@ def test_variant_d64_32k_full_width():
 
 def test_config_1m_bf16():
     """B=1, T=1,048,576, H=16, d=128, per-channel gate from N(-1,1): o at 4096
-    seeded positions and the full S_T.  The inputs are drawn block by block
+    seeded positions and the full S_T, with 64- and with 128-token chunks.  The inputs are drawn block by block
     (16,384 rows each); every block goes to the device and through the oracle,
     whose state carries from block to block, so the host never holds the
     whole input."""
@@ -439,10 +439,15 @@ def test_config_1m_bf16():
         o_b, S_ref = oracle.recurrence(blk["q"], blk["k"], blk["v"], blk["g"], blk["beta"], S0=S_ref,
                                        o_positions=pos[sel] - start)
         o_ref[sel] = o_b
-    o, S_T = kda.chunk_fwd(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"])
-    o_s = to_np64(o[torch.from_numpy(pos).cuda()])
-    torch.cuda.synchronize()
-    print("1m errs", _assert_close("o", o_s, o_ref, 1e-2), _assert_close("S_T", to_np64(S_T), S_ref, 1e-2))
+    idx = torch.from_numpy(pos).cuda()
+    for chunk in (64, 128):  # both chunk sizes against the same oracle pass
+        o, S_T = kda.chunk_fwd(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], chunk=chunk)
+        o_s = to_np64(o[idx])
+        torch.cuda.synchronize()
+        print(f"1m errs (C = {chunk})", _assert_close("o", o_s, o_ref, 1e-2),
+              _assert_close("S_T", to_np64(S_T), S_ref, 1e-2), flush=True)
+        del o, S_T
+        torch.cuda.empty_cache()
 
 
 def test_config_decode_256x32_64_steps():
