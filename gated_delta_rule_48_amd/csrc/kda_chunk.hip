@@ -1355,14 +1355,22 @@ __global__ __launch_bounds__(kSegThreads) void seg_walk_kernel(
     };
     // the chunk steps of B (with U') and of M (without) at once: each W and
     // KdT fragment is read from LDS once and feeds both products (each
-    // accumulates in the order chain_step uses)
+    // accumulates in the order chain_step uses).  Each product's operand
+    // fragments are read together, ahead of its matrix-core instructions,
+    // with a scheduling barrier between the two groups: left to itself the
+    // compiler interleaves every read with the instruction that uses it and
+    // waits for each read in turn.
     auto chain_step2 = [&](f32x4 (&Y1)[MT], f32x4 (&Y2)[MT], const char* sb) __attribute__((always_inline)) {
+        Frag<E> wf[TT * KS];
+#pragma unroll
+        for (int i = 0; i < TT * KS; ++i) wf[i] = frag_at(sb, L::off_W, i);
         Frag<E> yf1[KS], yf2[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             yf1[ks] = acc_to_frag(E{}, Y1[2 * ks], Y1[2 * ks + 1]);
             yf2[ks] = acc_to_frag(E{}, Y2[2 * ks], Y2[2 * ks + 1]);
         }
+        __builtin_amdgcn_sched_barrier(0);
         f32x4 X1[TT], X2[TT];
 #pragma unroll
         for (int t = 0; t < TT; ++t) X1[t] = X2[t] = zero4();
@@ -1370,10 +1378,13 @@ __global__ __launch_bounds__(kSegThreads) void seg_walk_kernel(
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int t = 0; t < TT; ++t) {
-                const Frag<E> wf = frag_at(sb, L::off_W, t * KS + ks);
-                X1[t] = mma(wf, yf1[ks], X1[t]);
-                X2[t] = mma(wf, yf2[ks], X2[t]);
+                X1[t] = mma(wf[t * KS + ks], yf1[ks], X1[t]);
+                X2[t] = mma(wf[t * KS + ks], yf2[ks], X2[t]);
             }
+        __builtin_amdgcn_sched_barrier(0);
+        Frag<E> kf[MT * KB];
+#pragma unroll
+        for (int i = 0; i < MT * KB; ++i) kf[i] = frag_at(sb, L::off_K, i);
         const float* gn = reinterpret_cast<const float*>(sb + L::off_G);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
@@ -1389,13 +1400,13 @@ __global__ __launch_bounds__(kSegThreads) void seg_walk_kernel(
                                   Raw4<E>::widen(Raw4<E>::load(Up + 8 * kb + 4)) - X1[2 * kb + 1]);
             uf2[kb] = acc_to_frag(E{}, zero4() - X2[2 * kb], zero4() - X2[2 * kb + 1]);
         }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-                const Frag<E> kf = frag_at(sb, L::off_K, m * KB + kb);
-                Y1[m] = mma(kf, uf1[kb], Y1[m]);
-                Y2[m] = mma(kf, uf2[kb], Y2[m]);
+                Y1[m] = mma(kf[m * KB + kb], uf1[kb], Y1[m]);
+                Y2[m] = mma(kf[m * KB + kb], uf2[kb], Y2[m]);
             }
     };
     // wait until S_start(i) is published (one lane polls; the others wait at
@@ -1514,20 +1525,63 @@ __global__ __launch_bounds__(kSegThreads) void seg_walk_kernel(
     auto step3 = [&](int c, const char* cur, char* nxt) __attribute__((always_inline)) {
         if (c > s0) store_o(c - 1);
         if (c + 1 < s1) dma_chunk(c + 1, nxt, true);
+        // one group of fragment reads per product, as in chain_step:
+        // X = W S, then O = QG S, then S <- Diag(Gn) S + KdT U and O += P U
         Frag<E> sf[KS], uf[KB];
-        chain_step(S, cur, true, sf, uf);
-        f32x4 O[TT];
 #pragma unroll
-        for (int t = 0; t < TT; ++t) O[t] = zero4();
+        for (int ks = 0; ks < KS; ++ks) sf[ks] = acc_to_frag(E{}, S[2 * ks], S[2 * ks + 1]);
+        f32x4 X[TT], O[TT];
+        {
+            Frag<E> wf[TT * KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+            for (int i = 0; i < TT * KS; ++i) wf[i] = frag_at(cur, L::off_W, i);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int t = 0; t < TT; ++t) O[t] = mma(frag_at(cur, L::off_Q, t * KS + ks), sf[ks], O[t]);
+            for (int t = 0; t < TT; ++t) X[t] = zero4();
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+            for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int t = 0; t < TT; ++t)
-                if (!p_block_zero(t, kb)) O[t] = mma(frag_at(cur, L::off_P, p_block_index(t, kb)), uf[kb], O[t]);
+                for (int t = 0; t < TT; ++t) X[t] = mma(wf[t * KS + ks], sf[ks], X[t]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        {
+            Frag<E> qf[TT * KS];
+#pragma unroll
+            for (int i = 0; i < TT * KS; ++i) qf[i] = frag_at(cur, L::off_Q, i);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < TT; ++t) O[t] = zero4();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int t = 0; t < TT; ++t) O[t] = mma(qf[t * KS + ks], sf[ks], O[t]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        {
+            Frag<E> kf[MT * KB], pf[6];
+#pragma unroll
+            for (int i = 0; i < MT * KB; ++i) kf[i] = frag_at(cur, L::off_K, i);
+#pragma unroll
+            for (int i = 0; i < 6; ++i) pf[i] = frag_at(cur, L::off_P, i);
+            const float* gn = reinterpret_cast<const float*>(cur + L::off_G);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) S[m] = *reinterpret_cast<const f32x4*>(gn + 16 * m + 4 * lg) * S[m];
+            const E* Up = reinterpret_cast<const E*>(cur + L::off_U) + (w * 64 + lane) * 16;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+                uf[kb] = acc_to_frag(E{}, Raw4<E>::widen(Raw4<E>::load(Up + 8 * kb)) - X[2 * kb],
+                                     Raw4<E>::widen(Raw4<E>::load(Up + 8 * kb + 4)) - X[2 * kb + 1]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int m = 0; m < MT; ++m) S[m] = mma(kf[m * KB + kb], uf[kb], S[m]);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int t = 0; t < TT; ++t)
+                    if (!p_block_zero(t, kb)) O[t] = mma(pf[p_block_index(t, kb)], uf[kb], O[t]);
+        }
         // every wave has read the previous chunk's rows out of the O tile
         // (the reads were waited for here; no fence, which would also wait
         // for the loads in flight into the other slot)
