@@ -268,12 +268,16 @@ void intra_chunk_kernel(
     }
     lds_barrier();
     {
+        // every partial read at once (one wait), then summed in order
+        float2 pv[NPART - 1];
+#pragma unroll
+        for (int p = 0; p < NPART - 1; ++p) pv[p] = *reinterpret_cast<const float2*>(sPart + p * DK + c0);
         float off0 = 0.f, off1 = 0.f;
 #pragma unroll
         for (int p = 0; p < NPART - 1; ++p) {
             if (p < part) {
-                off0 += sPart[p * DK + c0];
-                off1 += sPart[p * DK + c0 + 1];
+                off0 += pv[p].x;
+                off1 += pv[p].y;
             }
         }
 #pragma unroll
@@ -467,10 +471,12 @@ void intra_chunk_kernel(
                 accA = mma(fa, fb, accA);
                 accP = mma(fq, fb, accP);
             }
+            // beta of the lane's four rows, one 16-byte read
+            const f32x4 bt4 = *reinterpret_cast<const f32x4*>(sBeta + 16 * ti + 4 * lg);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * ti + 4 * lg + i, col = 16 * tj + lr;
-                lds_put(&sA[row * LDA + col], (row > col) ? accA[i] * sBeta[row] : 0.f);
+                lds_put(&sA[row * LDA + col], (row > col) ? accA[i] * bt4[i] : 0.f);
                 accPt[pq][i] = (row >= col) ? accP[i] : 0.f;
             }
         }

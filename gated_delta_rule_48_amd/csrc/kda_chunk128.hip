@@ -164,12 +164,16 @@ __global__ __launch_bounds__(kIntra128Threads) void intra128_kernel(
     }
     lds_barrier();
     {
+        // every partial read at once (one wait), then summed in order
+        float2 pv[NPART - 1];
+#pragma unroll
+        for (int p = 0; p < NPART - 1; ++p) pv[p] = *reinterpret_cast<const float2*>(sPart + p * DK + c0);
         float off0 = 0.f, off1 = 0.f;
 #pragma unroll
         for (int p = 0; p < NPART - 1; ++p) {
             if (p < part) {
-                off0 += sPart[p * DK + c0];
-                off1 += sPart[p * DK + c0 + 1];
+                off0 += pv[p].x;
+                off1 += pv[p].y;
             }
         }
 #pragma unroll
@@ -338,10 +342,11 @@ __global__ __launch_bounds__(kIntra128Threads) void intra128_kernel(
     for (int s = 0; s < PPW; ++s) {
         if (wave + NWAVES * s < NPAIRS) {
             const int ti = pti[s], tj = ptj[s];
+            const f32x4 bt4 = *reinterpret_cast<const f32x4*>(sBeta + 16 * ti + 4 * lg);  // the lane's four rows
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * ti + 4 * lg + i, col = 16 * tj + lr;
-                lds_put(&sA[row * LDA + col], (row > col) ? accA[s][i] * sBeta[row] : 0.f);
+                lds_put(&sA[row * LDA + col], (row > col) ? accA[s][i] * bt4[i] : 0.f);
                 lds_put(&sPst[row * L::LDP + frag_pos(col)], Elt<E>::from((row >= col) ? accP[s][i] : 0.f));
             }
         }
