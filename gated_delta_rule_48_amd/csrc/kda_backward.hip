@@ -424,23 +424,31 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
     // the sums need no per-lane bounds: T[t][j] = -sum_{i<t} A[t][i] T[i][j]
     // for t != j, and 1 on the diagonal.  A[t][i] is the same for every lane
     // (broadcast LDS reads, independent of T); four partial sums shorten the
-    // chain of dependent additions.
+    // chain of dependent additions (term i goes to sum i % 4 below the last
+    // whole group of four, to sum 0 after it).  A row is read in groups of 16
+    // values, each group's reads together ahead of its products (a scheduling
+    // barrier keeps them apart): left to itself the compiler waited for every
+    // read in turn, about 900 LDS round trips on this one wave.
     if (tid < C) {
         const int j = tid;
         float Tc[C];
-#pragma unroll
+#pragma clang loop unroll(full)
         for (int t = 0; t < C; ++t) {
-            float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+            float s[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma clang loop unroll(full)
+            for (int i0 = 0; i0 < t; i0 += 16) {
+                float r[16];
 #pragma unroll
-            for (int i = 0; i + 3 < t; i += 4) {
-                s0 += sA[t][i] * Tc[i];
-                s1 += sA[t][i + 1] * Tc[i + 1];
-                s2 += sA[t][i + 2] * Tc[i + 2];
-                s3 += sA[t][i + 3] * Tc[i + 3];
+                for (int jj = 0; jj < 16; ++jj)
+                    if (i0 + jj < t) r[jj] = sA[t][i0 + jj];
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int jj = 0; jj < 16; ++jj) {
+                    const int i = i0 + jj;
+                    if (i < t) s[i < (t & ~3) ? (i & 3) : 0] += r[jj] * Tc[i];
+                }
             }
-#pragma unroll
-            for (int i = t & ~3; i < t; ++i) s0 += sA[t][i] * Tc[i];
-            Tc[t] = t == j ? 1.f : -((s0 + s1) + (s2 + s3));
+            Tc[t] = t == j ? 1.f : -((s[0] + s[1]) + (s[2] + s[3]));
         }
 #pragma unroll
         for (int t = 0; t < C; ++t) sT[t][j] = Tc[t];
@@ -521,14 +529,25 @@ __device__ __forceinline__ void block_store(const f32x4 (&r)[block_regs<WIDTH>()
 // where a(k) reads A at the lane's row r = lr of the tile and b(k) reads
 // B(k, lr); each instruction takes k = k0 + lg.  Even and odd steps of four
 // accumulate separately, so two independent instructions are in flight.
+// Every operand of the tile is read first and the instructions follow (a
+// scheduling barrier keeps the two groups apart): left to itself the compiler
+// placed each pair of reads right before its instruction, behind a wait of
+// its own, so that every step paid a whole LDS round trip.
 template <int K, typename FA, typename FB>
 __device__ __forceinline__ f32x4 mfma_tile(f32x4 acc, FA a, FB b, int lg) {
     static_assert(K % 8 == 0, "two accumulators");
+    float av[K / 4], bv[K / 4];
+#pragma unroll
+    for (int s = 0; s < K / 4; ++s) {
+        av[s] = a(4 * s + lg);
+        bv[s] = b(4 * s + lg);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     f32x4 odd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k0 = 0; k0 < K; k0 += 8) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a(k0 + lg), b(k0 + lg), acc, 0, 0, 0);
-        odd = __builtin_amdgcn_mfma_f32_16x16x4f32(a(k0 + 4 + lg), b(k0 + 4 + lg), odd, 0, 0, 0);
+    for (int s = 0; s < K / 4; s += 2) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], bv[s], acc, 0, 0, 0);
+        odd = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s + 1], bv[s + 1], odd, 0, 0, 0);
     }
     return acc + odd;
 }
