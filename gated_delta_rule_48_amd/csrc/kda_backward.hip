@@ -41,7 +41,8 @@
 //
 // All arithmetic is fp32; every matrix product runs on the fp32 matrix cores
 // (v_mfma_f32_16x16x4f32).  Every intermediate of a chunk is kept in the
-// workspace.  The two walks run one workgroup per (sequence,
+// workspace, except Qr, Kr and Ki: the two launches that multiply them form
+// them again from q, k and b as they stage them.  The two walks run one workgroup per (sequence,
 // head, 16-column slice) with register tiles and the next chunk's operands in
 // flight; every product of the per-chunk kernels runs as a 64 x N block
 // product tiled through LDS with 4 x N/16 register tiles.
@@ -66,7 +67,7 @@ struct BwdWs {
     int32_t* chunk_off;
     int2* chunk_tab;
     // [C][DK]
-    float *B, *QG, *KG, *Kd, *Qr, *Kr, *Ki, *W, *dW, *dQG, *dKd, *dXw;
+    float *B, *QG, *KG, *Kd, *W, *dW, *dQG, *dKd, *dXw;
     // [C][DV]
     float *Up, *U, *dU, *dXu;
     // [C][C]
@@ -258,16 +259,21 @@ __device__ __forceinline__ void fill_tile_factors(float* tf, BF b) {
 }
 
 // M = strict_tril(K K^T with decay) and P = tril(Q K^T with decay) of one
-// chunk from the stored Kr, Qr, Ki, by 16 x 16 tiles: wave a computes the
-// tiles (a, bb), bb <= a, of its row tile.  A diagonal tile multiplies the
-// stored operands (both referred to m(a)); below the diagonal the row operand
-// is taken to s(a) (times fs[a]) and the column operand to e(bb) (times
-// fe[bb]) and on to s(a) (times fx[a,bb]).  Channels pass through LDS in tiles
-// of 16, the next tile in registers while the current one is multiplied.
+// chunk, by 16 x 16 tiles: wave a computes the tiles (a, bb), bb <= a, of its
+// row tile.  The decayed operands are formed from q, k and the chunk's prefix
+// sums b ([C][DK] in LDS) as each tile is staged: Kr = k e^{b - r},
+// Qr = q e^{b - r}, Ki = k e^{r - b}, with r the b of the middle row of the
+// row's own 16-row tile (rows past the chunk's end are zero).  A diagonal
+// tile multiplies them as they are (both referred to m(a)); below the
+// diagonal the row operand is taken to s(a) (times fs[a]) and the column
+// operand to e(bb) (times fe[bb]) and on to s(a) (times fx[a,bb]).  Channels
+// pass through LDS in tiles of 16; the next tile's q and k are loaded into
+// registers while the current one is multiplied.
 // acc[bb][i] holds row 16a + 4 (lane / 16) + i, column 16bb + lane % 16.
-template <int DK>
-__device__ __forceinline__ void decayed_mp(const float* Kr, const float* Qr, const float* Ki, const float* tf,
-                                           float* lds, f32x4 (&accM)[kTiles], f32x4 (&accP)[kTiles]) {
+template <typename E, int DK>
+__device__ __forceinline__ void decayed_mp(const E* q, const E* k, int64_t t0, int n, int32_t Hs, int h,
+                                           const float* sB, const float* tf, float* lds, f32x4 (&accM)[kTiles],
+                                           f32x4 (&accP)[kTiles]) {
     constexpr int KT = 16, SA = C + 4, R = C * KT / kBwdThreads;
     float* tKr = lds;
     float* tQr = tKr + KT * SA;
@@ -276,25 +282,29 @@ __device__ __forceinline__ void decayed_mp(const float* Kr, const float* Qr, con
     const int a = __builtin_amdgcn_readfirstlane(tid / 64);
 #pragma unroll
     for (int bb = 0; bb < kTiles; ++bb) accM[bb] = accP[bb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float rKr[R], rQr[R], rKi[R];
+    // raw values in flight (converted when staged, so that nothing waits for
+    // the loads before the products); rows past the end load the last row
+    E rq[R], rk[R];
     auto fetch = [&](int k0) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int idx = tid + r * kBwdThreads;
-            const size_t o = (size_t)(idx / KT) * DK + k0 + idx % KT;
-            rKr[r] = Kr[o];
-            rQr[r] = Qr[o];
-            rKi[r] = Ki[o];
+            const int64_t o = ((t0 + min(idx / KT, n - 1)) * Hs + h) * DK + k0 + idx % KT;
+            rq[r] = q[o];
+            rk[r] = k[o];
         }
     };
     fetch(0);
     for (int k0 = 0; k0 < DK; k0 += KT) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int idx = tid + r * kBwdThreads, j = (idx % KT) * SA + idx / KT;
-            tKr[j] = rKr[r];
-            tQr[j] = rQr[r];
-            tKi[j] = rKi[r];
+            const int idx = tid + r * kBwdThreads, t = idx / KT, c = k0 + idx % KT, j = (idx % KT) * SA + t;
+            const float b = sB[t * DK + c], rm = sB[tile_mid_row(t / 16) * DK + c];
+            const float er = capped_exp<E>(b - rm), eir = capped_exp<E>(rm - b);
+            const float qv = t < n ? Elt<E>::to(rq[r]) : 0.f, kv = t < n ? Elt<E>::to(rk[r]) : 0.f;
+            tKr[j] = kv * er;
+            tQr[j] = qv * er;
+            tKi[j] = kv * eir;
         }
         lds_barrier();
         if (k0 + KT < DK) fetch(k0 + KT);
@@ -364,15 +374,15 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
     }
     __syncthreads();
     fill_tile_factors<E, DK, 0, kTfPrepRows>(sTf, [&](int row, int c) { return sB[row * DK + c]; });
-    // every decayed operand; r is the prefix sum at the middle row of the
-    // row's own 16-row tile.  Four consecutive channels per thread, so each
+    // the prefix sums and the decayed operands the later launches read (QG,
+    // KG, Kd; the tile-referred Kr, Qr, Ki are formed again from q, k and b
+    // wherever they are used).  Four consecutive channels per thread, so each
     // array is written with 16-byte stores.
     for (int idx = 4 * tid; idx < C * DK; idx += 4 * kBwdThreads) {
         const int t = idx / DK, c = idx % DK;
         const f32x4 b4 = *reinterpret_cast<const f32x4*>(sB + idx);
-        const f32x4 r4 = *reinterpret_cast<const f32x4*>(sB + tile_mid_row(t / 16) * DK + c);
         const f32x4 bl4 = *reinterpret_cast<const f32x4*>(sB + (n - 1) * DK + c);
-        f32x4 oQG, oKG, oKd, oQr, oKr, oKi;
+        f32x4 oQG, oKG, oKd;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             float qv = 0.f, kv = 0.f;
@@ -380,24 +390,17 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
                 qv = ld(q, ((t0 + t) * Hs + h) * DK + c + j);
                 kv = ld(k, ((t0 + t) * Hs + h) * DK + c + j);
             }
-            const float b = b4[j], r = r4[j], bl = bl4[j];
-            const float e = gate_exp<E>(b), er = capped_exp<E>(b - r), eir = capped_exp<E>(r - b),
-                        ed = gate_exp<E>(bl - b);
+            const float b = b4[j], bl = bl4[j];
+            const float e = gate_exp<E>(b), ed = gate_exp<E>(bl - b);
             oQG[j] = qv * e;
             oKG[j] = kv * e;
             oKd[j] = kv * ed;
-            oQr[j] = qv * er;
-            oKr[j] = kv * er;
-            oKi[j] = kv * eir;
         }
         const size_t i = oCK + idx;
         *reinterpret_cast<f32x4*>(w.B + i) = b4;
         *reinterpret_cast<f32x4*>(w.QG + i) = oQG;
         *reinterpret_cast<f32x4*>(w.KG + i) = oKG;
         *reinterpret_cast<f32x4*>(w.Kd + i) = oKd;
-        *reinterpret_cast<f32x4*>(w.Qr + i) = oQr;
-        *reinterpret_cast<f32x4*>(w.Kr + i) = oKr;
-        *reinterpret_cast<f32x4*>(w.Ki + i) = oKi;
     }
     __syncthreads();
     // v of row i scaled by beta_i (zero past the chunk's end)
@@ -406,7 +409,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
     // tiles with the decay rebuilt from factors <= 1 below the diagonal
     {
         f32x4 am[kTiles], ap[kTiles];
-        decayed_mp<DK>(w.Kr + oCK, w.Qr + oCK, w.Ki + oCK, sTf, lds, am, ap);
+        decayed_mp<E, DK>(q, k, t0, n, Hs, h, sB, sTf, lds, am, ap);
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -1065,13 +1068,13 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
     {
         const float* dA = w.dA + oCC;
         const float* dP = w.dP + oCC;
-        const float* Ki = w.Ki + oCK;
-        const float* Kr = w.Kr + oCK;
-        const float* Qr = w.Qr + oCK;
+        const float* Bm = w.B + oCK;
         // One pass over the chunk-row index in tiles of 16, all three results
         // in registers: dKr and dQr take dA's and dP's column blocks against
         // Ki's rows; dKi takes dA's and dP's row blocks (transposed use)
-        // against Kr's and Qr's rows.  Ki is read once, nothing is parked.
+        // against Kr's and Qr's rows.  Kr, Qr and Ki are formed from q, k
+        // and b as their rows are staged (the same values prep multiplied),
+        // nothing is parked.
         constexpr int KT = 16, SA = C + 4, SB = DK + 4, NT = DK / 16;
         constexpr int RA = C * KT / kBwdThreads, RB = DK * KT / kBwdThreads;
         static_assert(KT * (4 * SA + 3 * SB) <= kLdsFloats, "phase-5 tiles fit");
@@ -1087,7 +1090,22 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
         aKr.zero();
         aQr.zero();
         acc.zero();
-        float rAc[RA], rPc[RA], rAr[RA], rPr[RA], rKi[RB], rKr[RB], rQr[RB];
+        // q, k and b two adjacent channels at a time: raw values, converted
+        // when staged (rows past the end load the last row)
+        using E2 = typename std::conditional<std::is_same<E, float>::value, float2, uint32_t>::type;
+        constexpr int RB2 = RB / 2, DK2 = DK / 2;
+        float rAc[RA], rPc[RA], rAr[RA], rPr[RA];
+        float2 rb[RB2];
+        E2 rq[RB2], rk[RB2];
+        auto lo_hi = [](E2 x, float& lo, float& hi) {
+            if constexpr (std::is_same<E, float>::value) {
+                lo = x.x;
+                hi = x.y;
+            } else {
+                lo = __uint_as_float(x << 16);
+                hi = __uint_as_float(x & 0xffff0000u);
+            }
+        };
         auto fetch = [&](int k0) {
 #pragma unroll
             for (int r = 0; r < RA; ++r) {
@@ -1100,12 +1118,13 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
                 rPr[r] = kr == t ? 0.f : dP[(size_t)kr * C + t];
             }
 #pragma unroll
-            for (int r = 0; r < RB; ++r) {
+            for (int r = 0; r < RB2; ++r) {
                 const int idx = tid + r * kBwdThreads;
-                const size_t o = (size_t)(k0 + idx / DK) * DK + idx % DK;
-                rKi[r] = Ki[o];
-                rKr[r] = Kr[o];
-                rQr[r] = Qr[o];
+                const int t = k0 + idx / DK2, c = 2 * (idx % DK2);
+                const int64_t o = ((t0 + min(t, n - 1)) * Hs + h) * DK + c;
+                rq[r] = *reinterpret_cast<const E2*>(q + o);
+                rk[r] = *reinterpret_cast<const E2*>(k + o);
+                rb[r] = *reinterpret_cast<const float2*>(Bm + (size_t)t * DK + c);
             }
         };
         fetch(0);
@@ -1119,13 +1138,23 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
                 tAr[(idx / C) * SA + idx % C] = rAr[r];
                 tPr[(idx / C) * SA + idx % C] = rPr[r];
             }
+            // Kr = k e^{b - r}, Qr = q e^{b - r}, Ki = k e^{r - b}, r the b
+            // of the middle row of this row tile
+            const float* rmid = tf_row(kTfBm + k0 / KT);
 #pragma unroll
-            for (int r = 0; r < RB; ++r) {
+            for (int r = 0; r < RB2; ++r) {
                 const int idx = tid + r * kBwdThreads;
-                const int j = (idx / DK) * SB + idx % DK;
-                tKi[j] = rKi[r];
-                tKr[j] = rKr[r];
-                tQr[j] = rQr[r];
+                const int t = k0 + idx / DK2, c = 2 * (idx % DK2), j = (idx / DK2) * SB + c;
+                const float2 rm = *reinterpret_cast<const float2*>(rmid + c);
+                float q0, q1, k0v, k1v;
+                lo_hi(rq[r], q0, q1);
+                lo_hi(rk[r], k0v, k1v);
+                if (t >= n) q0 = q1 = k0v = k1v = 0.f;
+                const float er0 = capped_exp<E>(rb[r].x - rm.x), eir0 = capped_exp<E>(rm.x - rb[r].x);
+                const float er1 = capped_exp<E>(rb[r].y - rm.y), eir1 = capped_exp<E>(rm.y - rb[r].y);
+                *reinterpret_cast<float2*>(tKi + j) = float2{k0v * eir0, k1v * eir1};
+                *reinterpret_cast<float2*>(tKr + j) = float2{k0v * er0, k1v * er1};
+                *reinterpret_cast<float2*>(tQr + j) = float2{q0 * er0, q1 * er1};
             }
             lds_barrier();
             if (k0 + KT < C) fetch(k0 + KT);
@@ -1288,7 +1317,7 @@ BwdSizes bwd_sizes(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv) {
     s.cc = al256(slots * C * C * 4);
     s.k = al256(slots * dk * 4);
     s.kv = al256(slots * dk * dv * 4);
-    s.total = s.head + 12 * s.ck + 4 * s.cv + 5 * s.cc + 2 * s.k + 2 * s.kv;
+    s.total = s.head + 9 * s.ck + 4 * s.cv + 5 * s.cc + 2 * s.k + 2 * s.kv;
     return s;
 }
 
@@ -1301,7 +1330,7 @@ BwdWs carve_bwd(void* base, int64_t T, int32_t N, int32_t H, int32_t dk, int32_t
     w.chunk_off = reinterpret_cast<int32_t*>(p); p += al256((size_t)(N + 1) * 4);
     w.chunk_tab = reinterpret_cast<int2*>(p); p += al256((size_t)max_chunks_for(T, N) * sizeof(int2));
     auto take = [&](size_t bytes) { float* f = reinterpret_cast<float*>(p); p += bytes; return f; };
-    float** ck[] = {&w.B, &w.QG, &w.KG, &w.Kd, &w.Qr, &w.Kr, &w.Ki, &w.W, &w.dW, &w.dQG, &w.dKd, &w.dXw};
+    float** ck[] = {&w.B, &w.QG, &w.KG, &w.Kd, &w.W, &w.dW, &w.dQG, &w.dKd, &w.dXw};
     for (float** f : ck) *f = take(s.ck);
     float** cv[] = {&w.Up, &w.U, &w.dU, &w.dXu};
     for (float** f : cv) *f = take(s.cv);
