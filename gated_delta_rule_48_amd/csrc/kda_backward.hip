@@ -69,7 +69,9 @@ struct BwdWs {
     // [C][DK]
     float *B, *QG, *KG, *Kd, *W, *dW, *dQG, *dKd, *dXw;
     // [C][DV]
-    float *Up, *U, *dU, *dXu;
+    float *Up, *U, *dU;
+    // [C]: dbeta's row sums of dA * M and dXu * V
+    float* dBr;
     // [C][C]
     float *M, *P, *T, *dP, *dA;
     // [DK]
@@ -986,6 +988,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
     // dT and Y are used only inside this launch: they stay in LDS
     __shared__ float sdT[C][C + 1];
     __shared__ float sY[C][C + 1];
+    // this lane's rows' sums of dXu * V (for dbeta), complete in every lane
+    // of a lane group
+    float rsu[4];
     // phase 2: dT = strict_tril(dW Xw^T + dU Xu^T), dXw = T^T dW, dXu = T^T dU
     {
         const float* dW = w.dW + oCK;
@@ -1015,7 +1020,27 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
         au.zero();
         gemm64<DV, C, false, true>(au, [&](int t, int a) { return Tm[(size_t)a * C + t]; },
                                   [&](int a, int x) { return dUm[(size_t)a * DV + x]; }, lds);
-        put(au, w.dXu + oCV, DV, 1.f);
+        // dXu is used only here: dv = diag(beta) dXu, and the row sums of
+        // dXu * V for dbeta (in a fixed order: the lane's columns, then the
+        // 16 lanes of its group)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const int t = Acc<DV>::row(a);
+            float rs = 0.f;
+#pragma unroll
+            for (int b = 0; b < DV / 16; ++b) {
+                const int64_t o = ((t0 + t) * Hs + h) * DV + Acc<DV>::col(b);
+                if (t < n) {
+                    dv[o] = Elt<E>::from(sbeta[t] * au.t[b][a]);
+                    rs += au.t[b][a] * ld(v, o);
+                }
+            }
+            rs += __shfl_xor(rs, 1, 64);
+            rs += __shfl_xor(rs, 2, 64);
+            rs += __shfl_xor(rs, 4, 64);
+            rs += __shfl_xor(rs, 8, 64);
+            rsu[a] = rs;
+        }
     }
     __syncthreads();
 
@@ -1041,18 +1066,34 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
         aa.zero();
         gemm64<C, C, false, true>(aa, [&](int t, int a) { return Tm[(size_t)a * C + t]; },
                                  [&](int a, int i) { return sY[a][i]; }, lds);
+        // dA, and the row sums of dA * M plus those of dXu * V: dbeta less
+        // its dXw * KG part, which the last launch adds
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+        for (int a = 0; a < 4; ++a) {
+            const int t = Acc<C>::row(a);
+            float rs = 0.f;
 #pragma unroll
             for (int b = 0; b < C / 16; ++b) {
-                const int t = Acc<C>::row(a), i = Acc<C>::col(b);
-                w.dA[oCC + (size_t)t * C + i] = (i < t && t < n) ? -aa.t[b][a] : 0.f;
+                const int i = Acc<C>::col(b);
+                const float da = (i < t && t < n) ? -aa.t[b][a] : 0.f;
+                w.dA[oCC + (size_t)t * C + i] = da;
+                if (i < t && t < n) rs += da * w.M[oCC + (size_t)t * C + i];
             }
+            rs += __shfl_xor(rs, 1, 64);
+            rs += __shfl_xor(rs, 2, 64);
+            rs += __shfl_xor(rs, 4, 64);
+            rs += __shfl_xor(rs, 8, 64);
+            if (tid % 16 == 0 && t < n) w.dBr[(size_t)slot * C + t] = rs + rsu[a];
+        }
     }
     }  // PH == 1
 
     if constexpr (PH == 2) {
     __shared__ float sTf[(kTfRows - kTfLocalRow0) * DK];  // tile decay factors and references fs, fe, b_m, f1, f2
+    // db = the gate's gradient per row before its reverse prefix sum, [C][DK + 1],
+    // in the operand tiles' LDS once the pass over the chunk rows is done
+    float* sDb = lds;
+    static_assert(C * (DK + 1) <= kLdsFloats, "db fits in the operand tiles");
     fill_tile_factors<E, DK, kTfLocalRow0, kTfRows>(sTf, [&](int row, int c) { return w.B[oCK + (size_t)row * DK + c]; });
     auto tf_row = [&](int row) { return sTf + (row - kTfLocalRow0) * DK; };
     __syncthreads();
@@ -1230,7 +1271,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
                 const float kv = ld(k, o), qv = ld(q, o), dPd = w.dP[oCC + (size_t)t * C + t];
                 dq[o] = Elt<E>::from(gq + dPd * kv);
                 dk[o] = Elt<E>::from(gk_up + gk_dd + dKd * ed + dPd * qv);
-                w.dW[j] = qv * gq + kv * (gk_up - (gk_dd + gk_kd));
+                lds_put(&sDb[t * (DK + 1) + c], qv * gq + kv * (gk_up - (gk_dd + gk_kd)));
                 rowp[a] += dXw * kv * e;
                 colp[b] += gk_kd * kv;
             }
@@ -1254,36 +1295,20 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
         }
     }
     __syncthreads();
-    // dbeta: four adjacent lanes per row, each a quarter of the row's sums
-    {
-        const int t = tid / 4, part = tid % 4;
-        float s = 0.f;
-        if (t < n) {
-#pragma unroll 4
-            for (int i = part; i < t; i += 4) s += w.dA[oCC + (size_t)t * C + i] * w.M[oCC + (size_t)t * C + i];
-#pragma unroll 8
-            for (int x = part; x < DV; x += 4)
-                s += w.dXu[oCV + (size_t)t * DV + x] * ld(v, ((t0 + t) * Hs + h) * DV + x);
-        }
-        s += __shfl_xor(s, 1, 64);
-        s += __shfl_xor(s, 2, 64);
-        if (t < n && part == 0) dbeta[(t0 + t) * Hs + h] = Elt<E>::from(s + sRowKG[t]);
-    }
-    for (int idx = tid; idx < C * DV; idx += kBwdThreads) {
-        const int t = idx / DV, x = idx % DV;
-        if (t < n) dv[((t0 + t) * Hs + h) * DV + x] = Elt<E>::from(sbeta[t] * w.dXu[oCV + idx]);
-    }
-    __syncthreads();
+    // dbeta: the middle launch's row sums of dA * M and dXu * V, plus those of
+    // dXw * KG
+    for (int t = tid; t < n; t += kBwdThreads)
+        dbeta[(t0 + t) * Hs + h] = Elt<E>::from(w.dBr[(size_t)slot * C + t] + sRowKG[t]);
 
-    // phase 6: dg = reverse cumulative sum of db; the last row's prefix sum
-    // also carries e^{b_last} (Gn) and the e^{b_last} factor of Kd
+    // phase 6: dg = reverse cumulative sum of db (in LDS); the last row's
+    // prefix sum also carries e^{b_last} (Gn) and the e^{b_last} factor of Kd
     for (int c = tid; c < DK; c += kBwdThreads) {
         float acc = w.dGn[oK + c] * w.Gn[oK + c] + ((sColKd[c] + sColKd[DK + c]) + (sColKd[2 * DK + c] + sColKd[3 * DK + c]));
 #pragma unroll 8
         for (int t = n - 1; t >= 0; --t) {
-            acc += w.dW[oCK + (size_t)t * DK + c];
+            acc += sDb[t * (DK + 1) + c];
             if (HG)
-                w.dQG[oCK + (size_t)t * DK + c] = acc;
+                sDb[t * (DK + 1) + c] = acc;
             else
                 dg[((t0 + t) * Hs + h) * DK + c] = Elt<E>::from(acc);
         }
@@ -1293,7 +1318,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
         for (int t = tid; t < n; t += kBwdThreads) {
             float s = 0.f;
 #pragma unroll 8
-            for (int c = 0; c < DK; ++c) s += w.dQG[oCK + (size_t)t * DK + c];
+            for (int c = 0; c < DK; ++c) s += sDb[t * (DK + 1) + c];
             dg[(t0 + t) * Hs + h] = Elt<E>::from(s);
         }
     }
@@ -1305,7 +1330,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
 inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdSizes {
-    size_t head, ck, cv, cc, k, kv, total;
+    size_t head, ck, cv, cc, c, k, kv, total;
 };
 
 BwdSizes bwd_sizes(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv) {
@@ -1315,9 +1340,10 @@ BwdSizes bwd_sizes(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv) {
     s.ck = al256(slots * C * dk * 4);
     s.cv = al256(slots * C * dv * 4);
     s.cc = al256(slots * C * C * 4);
+    s.c = al256(slots * C * 4);
     s.k = al256(slots * dk * 4);
     s.kv = al256(slots * dk * dv * 4);
-    s.total = s.head + 9 * s.ck + 4 * s.cv + 5 * s.cc + 2 * s.k + 2 * s.kv;
+    s.total = s.head + 9 * s.ck + 3 * s.cv + 5 * s.cc + s.c + 2 * s.k + 2 * s.kv;
     return s;
 }
 
@@ -1332,10 +1358,11 @@ BwdWs carve_bwd(void* base, int64_t T, int32_t N, int32_t H, int32_t dk, int32_t
     auto take = [&](size_t bytes) { float* f = reinterpret_cast<float*>(p); p += bytes; return f; };
     float** ck[] = {&w.B, &w.QG, &w.KG, &w.Kd, &w.W, &w.dW, &w.dQG, &w.dKd, &w.dXw};
     for (float** f : ck) *f = take(s.ck);
-    float** cv[] = {&w.Up, &w.U, &w.dU, &w.dXu};
+    float** cv[] = {&w.Up, &w.U, &w.dU};
     for (float** f : cv) *f = take(s.cv);
     float** cc[] = {&w.M, &w.P, &w.T, &w.dP, &w.dA};
     for (float** f : cc) *f = take(s.cc);
+    w.dBr = take(s.c);
     w.Gn = take(s.k);
     w.dGn = take(s.k);
     w.S = take(s.kv);
