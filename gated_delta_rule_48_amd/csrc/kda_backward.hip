@@ -362,7 +362,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
     // the chunk's gate, staged in one coalesced pass (rows past the end as 0)
     for (int idx = tid; idx < C * DK; idx += kBwdThreads) {
         const int t = idx / DK, c = idx % DK;
-        sB[idx] = t < n ? (HG ? ld(g, (t0 + t) * Hs + h) : ld(g, ((t0 + t) * Hs + h) * DK + c)) : 0.f;
+        const int64_t tr = t0 + min(t, n - 1);
+        const float gv = HG ? ld(g, tr * Hs + h) : ld(g, (tr * Hs + h) * DK + c);
+        sB[idx] = t < n ? gv : 0.f;
     }
     __syncthreads();
     // prefix sums per channel, in place (rows past the end keep the last sum)
@@ -387,11 +389,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
         f32x4 oQG, oKG, oKd;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            float qv = 0.f, kv = 0.f;
-            if (t < n) {
-                qv = ld(q, ((t0 + t) * Hs + h) * DK + c + j);
-                kv = ld(k, ((t0 + t) * Hs + h) * DK + c + j);
-            }
+            const int64_t o = ((t0 + min(t, n - 1)) * Hs + h) * DK + c + j;
+            const float qr = ld(q, o), kr = ld(k, o);
+            const float qv = t < n ? qr : 0.f, kv = t < n ? kr : 0.f;
             const float b = b4[j], bl = bl4[j];
             const float e = gate_exp<E>(b), ed = gate_exp<E>(bl - b);
             oQG[j] = qv * e;
@@ -406,7 +406,12 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
     }
     __syncthreads();
     // v of row i scaled by beta_i (zero past the chunk's end)
-    auto xu = [&](int i, int x) -> float { return i < n ? sbeta[i] * ld(v, ((t0 + i) * Hs + h) * DV + x) : 0.f; };
+    // (loads are never under a condition, so that none has to be waited for
+    // where it is issued: rows past the end re-read the last row)
+    auto xu = [&](int i, int x) -> float {
+        const float vv = ld(v, ((t0 + min(i, n - 1)) * Hs + h) * DV + x);
+        return i < n ? sbeta[i] * vv : 0.f;
+    };
     // M = strict_tril(K K^T with decay) and P = tril(Q K^T with decay), by
     // tiles with the decay rebuilt from factors <= 1 below the diagonal
     {
@@ -843,7 +848,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
 // phases exchange everything through the workspace, so the split only moves
 // barriers to kernel boundaries; each launch holds far fewer registers.
 template <typename E, int DK, int DV, bool HG, int PH>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH == 1 ? 1 : 2))) void bwd_local_kernel(const E* __restrict__ q, const E* __restrict__ k,
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH == 1 ? 3 : 2))) void bwd_local_kernel(const E* __restrict__ q, const E* __restrict__ k,
                                                                 const E* __restrict__ v, const E* __restrict__ beta,
                                                                 const E* __restrict__ dO, int32_t H, int32_t Hs, BwdWs w,
                                                                 E* __restrict__ dq, E* __restrict__ dk,
@@ -876,7 +881,12 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
     const float* Um = w.U + oCV;
     const float* dUm = w.dU + oCV;
     const float* Tm = w.T + oCC;  // T[a][i] at Tm[a * C + i]
-    auto dOat = [&](int t, int x) -> float { return t < n ? ld(dO, ((t0 + t) * Hs + h) * DV + x) : 0.f; };
+    // dO of row t (zero past the chunk's end; the load itself is
+    // unconditional, so that the prefetch is not waited for where it is issued)
+    auto dOat = [&](int t, int x) -> float {
+        const float d = ld(dO, ((t0 + min(t, n - 1)) * Hs + h) * DV + x);
+        return t < n ? d : 0.f;
+    };
     // store a 64 x N accumulator tile (times s) to dst (row stride N), rows >= n as zero
     auto put = [&](auto& acc, float* dst, int N, float s) {
         constexpr int NT = sizeof(acc.t) / sizeof(acc.t[0]);
@@ -988,9 +998,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
     // dT and Y are used only inside this launch: they stay in LDS
     __shared__ float sdT[C][C + 1];
     __shared__ float sY[C][C + 1];
-    // this lane's rows' sums of dXu * V (for dbeta), complete in every lane
-    // of a lane group
-    float rsu[4];
+    __shared__ float sRsu[C];  // row sums of dXu * V (for dbeta)
     // phase 2: dT = strict_tril(dW Xw^T + dU Xu^T), dXw = T^T dW, dXu = T^T dU
     {
         const float* dW = w.dW + oCK;
@@ -1001,7 +1009,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
                                    [&](int c, int i) { return sbeta[i] * KG[(size_t)i * DK + c]; }, lds);
         gemm64<C, DV, true, false>(at, [&](int t, int x) { return dUm[(size_t)t * DV + x]; },
                                    [&](int x, int i) {
-                                       return i < n ? sbeta[i] * ld(v, ((t0 + i) * Hs + h) * DV + x) : 0.f;
+                                       const float vv = ld(v, ((t0 + min(i, n - 1)) * Hs + h) * DV + x);
+                                       return i < n ? sbeta[i] * vv : 0.f;
                                    },
                                    lds);
 #pragma unroll
@@ -1022,24 +1031,32 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
                                   [&](int a, int x) { return dUm[(size_t)a * DV + x]; }, lds);
         // dXu is used only here: dv = diag(beta) dXu, and the row sums of
         // dXu * V for dbeta (in a fixed order: the lane's columns, then the
-        // 16 lanes of its group)
+        // 16 lanes of its group).  A row's v is loaded before any of its
+        // stores, and loads are never under a condition (rows past the end
+        // re-read the last row): either would make every load wait in turn.
+        E vx[4][DV / 16];  // raw, all loaded before the first store
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < DV / 16; ++b)
+                vx[a][b] = v[((t0 + min(Acc<DV>::row(a), n - 1)) * Hs + h) * DV + Acc<DV>::col(b)];
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
             const int t = Acc<DV>::row(a);
+            const int64_t o0 = ((t0 + min(t, n - 1)) * Hs + h) * DV;
             float rs = 0.f;
 #pragma unroll
             for (int b = 0; b < DV / 16; ++b) {
-                const int64_t o = ((t0 + t) * Hs + h) * DV + Acc<DV>::col(b);
                 if (t < n) {
-                    dv[o] = Elt<E>::from(sbeta[t] * au.t[b][a]);
-                    rs += au.t[b][a] * ld(v, o);
+                    dv[o0 + Acc<DV>::col(b)] = Elt<E>::from(sbeta[t] * au.t[b][a]);
+                    rs += au.t[b][a] * Elt<E>::to(vx[a][b]);
                 }
             }
             rs += __shfl_xor(rs, 1, 64);
             rs += __shfl_xor(rs, 2, 64);
             rs += __shfl_xor(rs, 4, 64);
             rs += __shfl_xor(rs, 8, 64);
-            rsu[a] = rs;
+            if (tid % 16 == 0) sRsu[t] = rs;
         }
     }
     __syncthreads();
@@ -1068,6 +1085,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
                                  [&](int a, int i) { return sY[a][i]; }, lds);
         // dA, and the row sums of dA * M plus those of dXu * V: dbeta less
         // its dXw * KG part, which the last launch adds
+        float mv[4][C / 16];  // all loaded before the dA stores, which might alias M for the compiler
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < C / 16; ++b) mv[a][b] = w.M[oCC + (size_t)Acc<C>::row(a) * C + Acc<C>::col(b)];
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
             const int t = Acc<C>::row(a);
@@ -1077,13 +1099,13 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
                 const int i = Acc<C>::col(b);
                 const float da = (i < t && t < n) ? -aa.t[b][a] : 0.f;
                 w.dA[oCC + (size_t)t * C + i] = da;
-                if (i < t && t < n) rs += da * w.M[oCC + (size_t)t * C + i];
+                rs += da * mv[a][b];  // M is zero where dA is masked
             }
             rs += __shfl_xor(rs, 1, 64);
             rs += __shfl_xor(rs, 2, 64);
             rs += __shfl_xor(rs, 4, 64);
             rs += __shfl_xor(rs, 8, 64);
-            if (tid % 16 == 0 && t < n) w.dBr[(size_t)slot * C + t] = rs + rsu[a];
+            if (tid % 16 == 0 && t < n) w.dBr[(size_t)slot * C + t] = rs + sRsu[t];
         }
     }
     }  // PH == 1
