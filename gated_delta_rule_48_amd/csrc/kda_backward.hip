@@ -1270,33 +1270,59 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
         float colp[DK / 16];
 #pragma unroll
         for (int b = 0; b < DK / 16; ++b) colp[b] = 0.f;
+        // Row by row (eight elements per lane): every load of a row is issued
+        // before its first store, since a load is not moved above a store
+        // that might alias it and each would otherwise wait in turn; no load
+        // is under a condition (a load under a condition is waited for where
+        // it is issued).  Rows past the chunk's end are computed from what
+        // the workspace holds there (q and k re-read the last row) and are
+        // neither stored nor summed.
+        constexpr int NB = DK / 16;
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+        for (int a = 0; a < 4; ++a) {
+            const int t = Acc<DK>::row(a);
+            const bool live = t < n;
+            const size_t j0 = oCK + (size_t)t * DK;
+            const int64_t o0 = ((t0 + min(t, n - 1)) * Hs + h) * DK;
+            float xw[NB], xq[NB], xd[NB], xb[NB];
+            E rk[NB], rq[NB];
 #pragma unroll
-            for (int b = 0; b < DK / 16; ++b) {
-                const int t = Acc<DK>::row(a), c = Acc<DK>::col(b);
-                if (t >= n) continue;
-                const size_t j = oCK + (size_t)t * DK + c;
-                const float dKr = sbeta[t] * aKr.t[b][a], dKi = acc.t[b][a], dQr = aQr.t[b][a];
-                const float dXw = w.dXw[j];
-                const float dKG = sbeta[t] * dXw;
-                const float dQG = w.dQG[j], dKd = w.dKd[j];
-                const float bb = w.B[j], r = tf_row(kTfBm + wv)[c], bl = sbl[c];
+            for (int b = 0; b < NB; ++b) {
+                const int c = Acc<DK>::col(b);
+                xw[b] = w.dXw[j0 + c];
+                xq[b] = w.dQG[j0 + c];
+                xd[b] = w.dKd[j0 + c];
+                xb[b] = w.B[j0 + c];
+                rk[b] = k[o0 + c];
+                rq[b] = q[o0 + c];
+            }
+            const float dPd = w.dP[oCC + (size_t)t * C + t];
+            const float bt = sbeta[t];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const int c = Acc<DK>::col(b);
+                const float dKr = bt * aKr.t[b][a], dKi = acc.t[b][a], dQr = aQr.t[b][a];
+                const float dXw = xw[b];
+                const float dKG = bt * dXw;
+                const float dQG = xq[b], dKd = xd[b];
+                const float bb = xb[b], r = tf_row(kTfBm + wv)[c], bl = sbl[c];
                 const float e = gate_exp<E>(bb), er = capped_exp<E>(bb - r), eir = capped_exp<E>(r - bb),
                             ed = gate_exp<E>(bl - bb);
-                const int64_t o = ((t0 + t) * Hs + h) * DK + c;
                 // the decayed operands are q or k times these factors, so the
                 // gate's gradient needs q and k themselves, not the six arrays
                 const float gq = dQG * e + dQr * er;    // dq without P's diagonal
                 const float gk_up = dKG * e + dKr * er;  // factors that grow with b
                 const float gk_dd = dKi * eir, gk_kd = t == n - 1 ? 0.f : dKd * ed;
-                const float kv = ld(k, o), qv = ld(q, o), dPd = w.dP[oCC + (size_t)t * C + t];
-                dq[o] = Elt<E>::from(gq + dPd * kv);
-                dk[o] = Elt<E>::from(gk_up + gk_dd + dKd * ed + dPd * qv);
+                const float kv = Elt<E>::to(rk[b]), qv = Elt<E>::to(rq[b]);
+                if (live) {
+                    dq[o0 + c] = Elt<E>::from(gq + dPd * kv);
+                    dk[o0 + c] = Elt<E>::from(gk_up + gk_dd + dKd * ed + dPd * qv);
+                }
                 lds_put(&sDb[t * (DK + 1) + c], qv * gq + kv * (gk_up - (gk_dd + gk_kd)));
-                rowp[a] += dXw * kv * e;
-                colp[b] += gk_kd * kv;
+                rowp[a] += live ? dXw * kv * e : 0.f;
+                colp[b] += live ? gk_kd * kv : 0.f;
             }
+        }
         // rows: the 16 lanes of a lane group; columns: the four lane groups of a
         // wave, then the four waves in a fixed order (no atomics: deterministic)
 #pragma unroll
