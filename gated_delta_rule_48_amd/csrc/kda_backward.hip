@@ -359,6 +359,28 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
     const int tid = threadIdx.x;
     const size_t oCK = (size_t)slot * C * DK, oCV = (size_t)slot * C * DV, oCC = (size_t)slot * C * C;
     if (tid < C) sbeta[tid] = tid < n ? ld(beta, (t0 + tid) * Hs + h) : 0.f;
+    // q and k of this thread's elements of the decayed-operand pass below,
+    // four consecutive channels per load, issued first so that they arrive
+    // while the gate is staged and summed (rows past the end re-read the
+    // last row)
+    using QK4 = typename std::conditional<std::is_same<E, float>::value, f32x4, uint2>::type;
+    constexpr int NQ = C * DK / (4 * kBwdThreads);
+    QK4 rq4[NQ], rk4[NQ];
+#pragma unroll
+    for (int it = 0; it < NQ; ++it) {
+        const int idx = 4 * tid + it * 4 * kBwdThreads, t = idx / DK, c = idx % DK;
+        const int64_t o = ((t0 + min(t, n - 1)) * Hs + h) * DK + c;
+        rq4[it] = *reinterpret_cast<const QK4*>(q + o);
+        rk4[it] = *reinterpret_cast<const QK4*>(k + o);
+    }
+    auto elem4 = [](QK4 x, int j) -> float {
+        if constexpr (std::is_same<E, float>::value) {
+            return x[j];
+        } else {
+            const uint32_t u = j < 2 ? x.x : x.y;
+            return __uint_as_float((j & 1) ? (u & 0xffff0000u) : (u << 16));
+        }
+    };
     // the chunk's gate, staged in one coalesced pass (rows past the end as 0)
     for (int idx = tid; idx < C * DK; idx += kBwdThreads) {
         const int t = idx / DK, c = idx % DK;
@@ -370,6 +392,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
     // prefix sums per channel, in place (rows past the end keep the last sum)
     for (int c = tid; c < DK; c += kBwdThreads) {
         float b = 0.f;
+#pragma unroll
         for (int t = 0; t < C; ++t) {
             b += sB[t * DK + c];
             sB[t * DK + c] = b;
@@ -382,15 +405,15 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
     // KG, Kd; the tile-referred Kr, Qr, Ki are formed again from q, k and b
     // wherever they are used).  Four consecutive channels per thread, so each
     // array is written with 16-byte stores.
-    for (int idx = 4 * tid; idx < C * DK; idx += 4 * kBwdThreads) {
-        const int t = idx / DK, c = idx % DK;
+#pragma unroll
+    for (int it = 0; it < NQ; ++it) {
+        const int idx = 4 * tid + it * 4 * kBwdThreads, t = idx / DK, c = idx % DK;
         const f32x4 b4 = *reinterpret_cast<const f32x4*>(sB + idx);
         const f32x4 bl4 = *reinterpret_cast<const f32x4*>(sB + (n - 1) * DK + c);
         f32x4 oQG, oKG, oKd;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int64_t o = ((t0 + min(t, n - 1)) * Hs + h) * DK + c + j;
-            const float qr = ld(q, o), kr = ld(k, o);
+            const float qr = elem4(rq4[it], j), kr = elem4(rk4[it], j);
             const float qv = t < n ? qr : 0.f, kv = t < n ? kr : 0.f;
             const float b = b4[j], bl = bl4[j];
             const float e = gate_exp<E>(b), ed = gate_exp<E>(bl - b);
