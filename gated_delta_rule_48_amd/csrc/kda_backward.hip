@@ -183,6 +183,45 @@ __device__ __forceinline__ void gemm64(Acc<N>& acc, LA la, LB lb, float* lds) {
     }
 }
 
+// gemm64 for a B operand whose values are already in registers: lb(kt, r, k)
+// gives element r of this thread's share of k-tile kt (row k of B, column
+// (tid + r * threads) % N), so the tiles are staged without waiting for
+// memory; A is read through la as in gemm64.  Every thread must call it.
+template <int N, int K, bool A_KFAST, typename LA, typename LB>
+__device__ __forceinline__ void gemm64_regb(Acc<N>& acc, LA la, LB lb, float* lds) {
+    constexpr int KT = 16, M = 64, SA = M + 4, SB = N + 4, NT = N / 16;
+    constexpr int RA = M * KT / kBwdThreads, RB = N * KT / kBwdThreads;
+    float* sA = lds;
+    float* sB = lds + KT * SA;
+    const int tid = threadIdx.x, wv = tid / 64, lg = (tid % 64) / 16, lr = tid % 16;
+#pragma unroll
+    for (int kt = 0; kt < K / KT; ++kt) {
+        const int k0 = kt * KT;
+#pragma unroll
+        for (int r = 0; r < RA; ++r) {
+            const int idx = tid + r * kBwdThreads;
+            const int m = A_KFAST ? idx / KT : idx % M, kk = A_KFAST ? idx % KT : idx / M;
+            sA[kk * SA + m] = la(m, k0 + kk);
+        }
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            const int idx = tid + r * kBwdThreads;
+            sB[(idx / N) * SB + idx % N] = lb(kt, r, k0 + idx / N);
+        }
+        lds_barrier();
+#pragma unroll
+        for (int ks = 0; ks < KT; ks += 4) {
+            const float a = sA[(ks + lg) * SA + 16 * wv + lr];
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                const float b = sB[(ks + lg) * SB + 16 * j + lr];
+                acc.t[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc.t[j], 0, 0, 0);
+            }
+        }
+        lds_barrier();
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Decay references of the four 16-row tiles of a chunk.  Tile a covers rows
 // 16a..16a+15, with start row s(a) = 16a, middle row m(a) = 16a + 8 and end
@@ -359,10 +398,20 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
     const int tid = threadIdx.x;
     const size_t oCK = (size_t)slot * C * DK, oCV = (size_t)slot * C * DV, oCC = (size_t)slot * C * C;
     if (tid < C) sbeta[tid] = tid < n ? ld(beta, (t0 + tid) * Hs + h) : 0.f;
+    // the chunk's gate, loaded first (rows past the end re-read the last row)
+    constexpr int NG = C * DK / kBwdThreads;
+    E rg[NG];
+#pragma unroll
+    for (int r = 0; r < NG; ++r) {
+        const int idx = tid + r * kBwdThreads, t = idx / DK, c = idx % DK;
+        const int64_t tr = t0 + min(t, n - 1);
+        rg[r] = HG ? g[tr * Hs + h] : g[(tr * Hs + h) * DK + c];
+    }
+    asm volatile("" ::: "memory");  // the gate's loads go out before those of q and k
     // q and k of this thread's elements of the decayed-operand pass below,
-    // four consecutive channels per load, issued first so that they arrive
+    // four consecutive channels per load, issued next so that they arrive
     // while the gate is staged and summed (rows past the end re-read the
-    // last row)
+    // last row); waiting for the gate does not wait for them
     using QK4 = typename std::conditional<std::is_same<E, float>::value, f32x4, uint2>::type;
     constexpr int NQ = C * DK / (4 * kBwdThreads);
     QK4 rq4[NQ], rk4[NQ];
@@ -381,12 +430,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
             return __uint_as_float((j & 1) ? (u & 0xffff0000u) : (u << 16));
         }
     };
-    // the chunk's gate, staged in one coalesced pass (rows past the end as 0)
-    for (int idx = tid; idx < C * DK; idx += kBwdThreads) {
-        const int t = idx / DK, c = idx % DK;
-        const int64_t tr = t0 + min(t, n - 1);
-        const float gv = HG ? ld(g, tr * Hs + h) : ld(g, (tr * Hs + h) * DK + c);
-        sB[idx] = t < n ? gv : 0.f;
+    // the gate into LDS (rows past the end as 0)
+#pragma unroll
+    for (int r = 0; r < NG; ++r) {
+        const int idx = tid + r * kBwdThreads;
+        sB[idx] = idx / DK < n ? Elt<E>::to(rg[r]) : 0.f;
     }
     __syncthreads();
     // prefix sums per channel, in place (rows past the end keep the last sum)
@@ -428,13 +476,6 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
         *reinterpret_cast<f32x4*>(w.Kd + i) = oKd;
     }
     __syncthreads();
-    // v of row i scaled by beta_i (zero past the chunk's end)
-    // (loads are never under a condition, so that none has to be waited for
-    // where it is issued: rows past the end re-read the last row)
-    auto xu = [&](int i, int x) -> float {
-        const float vv = ld(v, ((t0 + min(i, n - 1)) * Hs + h) * DV + x);
-        return i < n ? sbeta[i] * vv : 0.f;
-    };
     // M = strict_tril(K K^T with decay) and P = tril(Q K^T with decay), by
     // tiles with the decay rebuilt from factors <= 1 below the diagonal
     {
@@ -505,7 +546,13 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
                 w.W[oCK + (size_t)Acc<DK>::row(a) * DK + Acc<DK>::col(b)] = aw.t[b][a];
         Acc<DV> au;
         au.zero();
-        gemm64<DV, C, true, true>(au, [&](int t, int i) { return sT[t][i]; }, xu, lds);
+        // beta_i is zero past the chunk's end, so the rows there (which re-read
+        // the last row of v) give zero; a select here would be turned into a
+        // branch around the load, which then waits where it is issued
+        gemm64<DV, C, true, true>(au, [&](int t, int i) { return sT[t][i]; },
+                                  [&](int i, int x) {
+                                      return sbeta[i] * ld(v, ((t0 + min(i, n - 1)) * Hs + h) * DV + x);
+                                  }, lds);
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -1031,9 +1078,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
         gemm64<C, DK, true, false>(at, [&](int t, int c) { return dW[(size_t)t * DK + c]; },
                                    [&](int c, int i) { return sbeta[i] * KG[(size_t)i * DK + c]; }, lds);
         gemm64<C, DV, true, false>(at, [&](int t, int x) { return dUm[(size_t)t * DV + x]; },
-                                   [&](int x, int i) {
-                                       const float vv = ld(v, ((t0 + min(i, n - 1)) * Hs + h) * DV + x);
-                                       return i < n ? sbeta[i] * vv : 0.f;
+                                   [&](int x, int i) {  // beta_i is zero past the end (no select: see prep)
+                                       return sbeta[i] * ld(v, ((t0 + min(i, n - 1)) * Hs + h) * DV + x);
                                    },
                                    lds);
 #pragma unroll
@@ -1139,7 +1185,24 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
     // in the operand tiles' LDS once the pass over the chunk rows is done
     float* sDb = lds;
     static_assert(C * (DK + 1) <= kLdsFloats, "db fits in the operand tiles");
-    fill_tile_factors<E, DK, kTfLocalRow0, kTfRows>(sTf, [&](int row, int c) { return w.B[oCK + (size_t)row * DK + c]; });
+    // the table needs the prefix sums of twelve rows (the start, middle and
+    // end row of each 16-row tile): loaded at once into the operand tiles'
+    // LDS, rather than one round trip per table entry
+    {
+        float* sBr = lds;  // [12][DK]: row 3 a + {0, 1, 2} = s(a), m(a), e(a)
+        static_assert(12 * DK % kBwdThreads == 0 && 12 * DK <= kLdsFloats, "table rows");
+#pragma unroll
+        for (int r = 0; r < 12 * DK / kBwdThreads; ++r) {
+            const int idx = tid + r * kBwdThreads, q3 = idx / DK, c = idx % DK;
+            const int row = 16 * (q3 / 3) + (q3 % 3 == 0 ? 0 : q3 % 3 == 1 ? 8 : 15);
+            sBr[idx] = w.B[oCK + (size_t)row * DK + c];
+        }
+        __syncthreads();
+        fill_tile_factors<E, DK, kTfLocalRow0, kTfRows>(sTf, [&](int row, int c) {
+            const int o = row % 16;
+            return sBr[(3 * (row / 16) + (o == 0 ? 0 : o == 8 ? 1 : 2)) * DK + c];
+        });
+    }
     auto tf_row = [&](int row) { return sTf + (row - kTfLocalRow0) * DK; };
     __syncthreads();
 
