@@ -1360,9 +1360,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
         // before its first store, since a load is not moved above a store
         // that might alias it and each would otherwise wait in turn; no load
         // is under a condition (a load under a condition is waited for where
-        // it is issued).  Rows past the chunk's end are computed from what
-        // the workspace holds there (q and k re-read the last row) and are
-        // neither stored nor summed.
+        // it is issued); the row's dq and dk are stored together after all
+        // its elements are computed (a store under a condition between two
+        // elements made the next element wait for it).  Rows past the
+        // chunk's end are computed from what the workspace holds there (q
+        // and k re-read the last row) and are neither stored nor summed.
         constexpr int NB = DK / 16;
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
@@ -1384,6 +1386,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
             }
             const float dPd = w.dP[oCC + (size_t)t * C + t];
             const float bt = sbeta[t];
+            float oq[NB], ok[NB];
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 const int c = Acc<DK>::col(b);
@@ -1400,13 +1403,18 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
                 const float gk_up = dKG * e + dKr * er;  // factors that grow with b
                 const float gk_dd = dKi * eir, gk_kd = t == n - 1 ? 0.f : dKd * ed;
                 const float kv = Elt<E>::to(rk[b]), qv = Elt<E>::to(rq[b]);
-                if (live) {
-                    dq[o0 + c] = Elt<E>::from(gq + dPd * kv);
-                    dk[o0 + c] = Elt<E>::from(gk_up + gk_dd + dKd * ed + dPd * qv);
-                }
+                oq[b] = gq + dPd * kv;
+                ok[b] = gk_up + gk_dd + dKd * ed + dPd * qv;
                 lds_put(&sDb[t * (DK + 1) + c], qv * gq + kv * (gk_up - (gk_dd + gk_kd)));
                 rowp[a] += live ? dXw * kv * e : 0.f;
                 colp[b] += live ? gk_kd * kv : 0.f;
+            }
+            if (live) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    dq[o0 + Acc<DK>::col(b)] = Elt<E>::from(oq[b]);
+                    dk[o0 + Acc<DK>::col(b)] = Elt<E>::from(ok[b]);
+                }
             }
         }
         // rows: the 16 lanes of a lane group; columns: the four lane groups of a
