@@ -308,8 +308,8 @@ __device__ __forceinline__ void fill_tile_factors(float* tf, BF b) {
 // tile multiplies them as they are (both referred to m(a)); below the
 // diagonal the row operand is taken to s(a) (times fs[a]) and the column
 // operand to e(bb) (times fe[bb]) and on to s(a) (times fx[a,bb]).  Channels
-// pass through LDS in tiles of 16; the next tile's q and k are loaded into
-// registers while the current one is multiplied.
+// pass through LDS in tiles of 16; the q and k of the next two tiles are in
+// flight in registers while the current one is multiplied.
 // acc[bb][i] holds row 16a + 4 (lane / 16) + i, column 16bb + lane % 16.
 template <typename E, int DK>
 __device__ __forceinline__ void decayed_mp(const E* q, const E* k, int64_t t0, int n, int32_t Hs, int h,
@@ -324,31 +324,42 @@ __device__ __forceinline__ void decayed_mp(const E* q, const E* k, int64_t t0, i
 #pragma unroll
     for (int bb = 0; bb < kTiles; ++bb) accM[bb] = accP[bb] = f32x4{0.f, 0.f, 0.f, 0.f};
     // raw values in flight (converted when staged, so that nothing waits for
-    // the loads before the products); rows past the end load the last row
-    E rq[R], rk[R];
-    auto fetch = [&](int k0) {
+    // the loads before the products), two tiles ahead in three buffers; rows
+    // past the end load the last row
+    constexpr int NKT = DK / KT;
+    E rq[3][R], rk[3][R];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int idx = tid + r * kBwdThreads;
-            const int64_t o = ((t0 + min(idx / KT, n - 1)) * Hs + h) * DK + k0 + idx % KT;
-            rq[r] = q[o];
-            rk[r] = k[o];
+            const int64_t o = ((t0 + min(idx / KT, n - 1)) * Hs + h) * DK + kt * KT + idx % KT;
+            rq[kt][r] = q[o];
+            rk[kt][r] = k[o];
         }
-    };
-    fetch(0);
-    for (int k0 = 0; k0 < DK; k0 += KT) {
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) {
+        const int k0 = kt * KT, b = kt % 3;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int idx = tid + r * kBwdThreads, t = idx / KT, c = k0 + idx % KT, j = (idx % KT) * SA + t;
-            const float b = sB[t * DK + c], rm = sB[tile_mid_row(t / 16) * DK + c];
-            const float er = capped_exp<E>(b - rm), eir = capped_exp<E>(rm - b);
-            const float qv = t < n ? Elt<E>::to(rq[r]) : 0.f, kv = t < n ? Elt<E>::to(rk[r]) : 0.f;
+            const float bt = sB[t * DK + c], rm = sB[tile_mid_row(t / 16) * DK + c];
+            const float er = capped_exp<E>(bt - rm), eir = capped_exp<E>(rm - bt);
+            const float qv = t < n ? Elt<E>::to(rq[b][r]) : 0.f, kv = t < n ? Elt<E>::to(rk[b][r]) : 0.f;
             tKr[j] = kv * er;
             tQr[j] = qv * er;
             tKi[j] = kv * eir;
         }
         lds_barrier();
-        if (k0 + KT < DK) fetch(k0 + KT);
+        if (kt + 2 < NKT) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int idx = tid + r * kBwdThreads;
+                const int64_t o = ((t0 + min(idx / KT, n - 1)) * Hs + h) * DK + k0 + 2 * KT + idx % KT;
+                rq[(kt + 2) % 3][r] = q[o];
+                rk[(kt + 2) % 3][r] = k[o];
+            }
+        }
 #pragma unroll
         for (int ks = 0; ks < KT; ks += 4) {
             const int kr = ks + lg, c = k0 + kr;
@@ -493,39 +504,94 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
             }
     }
     __syncthreads();
-    // T = (I + A)^{-1}: column j by forward substitution, one thread per
-    // column, the column in registers.  With T[i][j] = 0 above the diagonal
-    // the sums need no per-lane bounds: T[t][j] = -sum_{i<t} A[t][i] T[i][j]
-    // for t != j, and 1 on the diagonal.  A[t][i] is the same for every lane
-    // (broadcast LDS reads, independent of T); four partial sums shorten the
-    // chain of dependent additions (term i goes to sum i % 4 below the last
-    // whole group of four, to sum 0 after it).  A row is read in groups of 16
-    // values, each group's reads together ahead of its products (a scheduling
-    // barrier keeps them apart): left to itself the compiler waited for every
-    // read in turn, about 900 LDS round trips on this one wave.
-    if (tid < C) {
-        const int j = tid;
-        float Tc[C];
-#pragma clang loop unroll(full)
-        for (int t = 0; t < C; ++t) {
-            float s[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma clang loop unroll(full)
-            for (int i0 = 0; i0 < t; i0 += 16) {
-                float r[16];
+    // T = (I + A)^{-1} by 16 x 16 blocks.  The four diagonal blocks by
+    // forward substitution (one column per thread of wave 0, sixteen rows);
+    // the blocks below the diagonal on the fp32 matrix cores in two levels,
+    // with T_a, T_b the inverses of the leading and trailing halves (the
+    // inverse of [[M_a, 0], [A_ba, M_b]] is [[T_a, 0], [-T_b A_ba T_a, T_b]]):
+    //   level 1  T10 = -T11 A10 T00 (wave 0),  T32 = -T33 A32 T22 (wave 1);
+    //   level 2  Z = A_ba T_a:  Z20 = A20 T00 + A21 T10,  Z21 = A21 T11,
+    //            Z30 = A30 T00 + A31 T10,  Z31 = A31 T11  (waves 0-3),
+    //            then T20 = -T22 Z20,  T21 = -T22 Z21,
+    //            T30 = -(T32 Z20 + T33 Z30),  T31 = -(T32 Z21 + T33 Z31).
+    // The blocks above the diagonal are zero.  (One column per thread over
+    // all 64 rows had taken about 2,000 dependent steps on one wave.)
+    {
+        static_assert(C == 64, "four 16-row blocks");
+        const int wv = tid / 64, lg = (tid % 64) / 16, lr = tid % 16;
+        if (tid < 64) {
+            const int blk = tid >> 4, jc = tid & 15, b0 = 16 * blk;
+            float x[16];
 #pragma unroll
-                for (int jj = 0; jj < 16; ++jj)
-                    if (i0 + jj < t) r[jj] = sA[t][i0 + jj];
-                __builtin_amdgcn_sched_barrier(0);
+            for (int t = 0; t < 16; ++t) {
+                float acc = 0.f;
 #pragma unroll
-                for (int jj = 0; jj < 16; ++jj) {
-                    const int i = i0 + jj;
-                    if (i < t) s[i < (t & ~3) ? (i & 3) : 0] += r[jj] * Tc[i];
-                }
+                for (int i = 0; i < t; ++i) acc -= sA[b0 + t][b0 + i] * x[i];
+                x[t] = (t < jc) ? 0.f : ((t == jc) ? 1.f : acc);
             }
-            Tc[t] = t == j ? 1.f : -((s[0] + s[1]) + (s[2] + s[3]));
-        }
 #pragma unroll
-        for (int t = 0; t < C; ++t) sT[t][j] = Tc[t];
+            for (int t = 0; t < 16; ++t) sT[b0 + t][b0 + jc] = x[t];
+        }
+        // the six blocks above the diagonal: (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+        for (int idx = tid; idx < 6 * 256; idx += kBwdThreads) {
+            const int pz = idx / 256, e = idx % 256;
+            const int bi = pz < 3 ? 0 : (pz < 5 ? 1 : 2), bj = pz < 3 ? pz + 1 : (pz < 5 ? pz - 1 : 3);
+            sT[16 * bi + e / 16][16 * bj + e % 16] = 0.f;
+        }
+        __syncthreads();
+        // X += A[bi][m] T[m][bj]: instruction s takes k = 4 lg + s of the block
+        auto mul_AT = [&](int bi, int m, int bj, f32x4 X) {
+            float av[4], bv[4];
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+                av[s4] = sA[16 * bi + lr][16 * m + 4 * lg + s4];
+                bv[s4] = sT[16 * m + 4 * lg + s4][16 * bj + lr];
+            }
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) X = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s4], bv[s4], X, 0, 0, 0);
+            return X;
+        };
+        // Y += T[bi][m] X, X in accumulator layout (which is the B operand of
+        // this product: row 4 lg + s, column lr)
+        auto mul_TX = [&](int bi, int m, f32x4 X, f32x4 Y) {
+            float tv[4];
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) tv[s4] = sT[16 * bi + lr][16 * m + 4 * lg + s4];
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tv[s4], X[s4], Y, 0, 0, 0);
+            return Y;
+        };
+        auto put_block = [&](int bi, int bj, f32x4 Y) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lds_put(&sT[16 * bi + 4 * lg + i][16 * bj + lr], -Y[i]);
+        };
+        const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+        if (wv < 2) {  // level 1: block (i0 + 1, i0), i0 = 0 or 2
+            const int i0 = 2 * wv;
+            put_block(i0 + 1, i0, mul_TX(i0 + 1, i0 + 1, mul_AT(i0 + 1, i0, i0, z4), z4));
+        }
+        __syncthreads();
+        constexpr int LDZ = 33;  // [32][LDZ]: rows of block rows 2 and 3, columns of block columns 0 and 1
+        float* sZ = lds;
+        static_assert(32 * LDZ <= kGemmLds, "Z fits in the block products' staging");
+        const int zi = 2 + (wv >> 1), zj = wv & 1;  // block (zi, zj) of level 2, one per wave
+        {
+            f32x4 Z = z4;
+            for (int m = zj; m < 2; ++m) Z = mul_AT(zi, m, zj, Z);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lds_put(&sZ[(16 * (zi - 2) + 4 * lg + i) * LDZ + 16 * zj + lr], Z[i]);
+        }
+        __syncthreads();
+        {
+            f32x4 Y = z4;
+            for (int m = 2; m <= zi; ++m) {
+                f32x4 Zm;  // Z[m][zj] in accumulator layout
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Zm[i] = sZ[(16 * (m - 2) + 4 * lg + i) * LDZ + 16 * zj + lr];
+                Y = mul_TX(zi, m, Zm, Y);
+            }
+            put_block(zi, zj, Y);
+        }
     }
     __syncthreads();
     for (int idx = tid; idx < C * C; idx += kBwdThreads) {
