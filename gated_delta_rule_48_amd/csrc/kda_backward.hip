@@ -996,7 +996,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
     __shared__ float sColKd[4 * DK];  // sum_t dKd[t][c] Kd[t][c], per wave and column
     // phases 1 and 5 stage five and seven operand tiles at once; phases 2-4 use gemm64's two
     constexpr int kLdsFloats = PH == 0   ? 16 * (3 * (C + 4) + 2 * (DK + 4))
-                               : PH == 2 ? 16 * (4 * (C + 4) + 3 * (DK + 4))
+                               : PH == 2 ? (16 * 3 * (DK + 4) > C * (DK + 1) ? 16 * 3 * (DK + 4) : C * (DK + 1))
                                          : kGemmLds;
     __shared__ __align__(16) float lds[kLdsFloats];
     const int64_t slot = blockIdx.x;
@@ -1247,6 +1247,29 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
 
     if constexpr (PH == 2) {
     __shared__ float sTf[(kTfRows - kTfLocalRow0) * DK];  // tile decay factors and references fs, fe, b_m, f1, f2
+    // dA and dP of the chunk, read as column blocks and as row blocks by the
+    // pass below: loaded once, all at the start
+    __shared__ float sdA[C][C + 1], sdP[C][C + 1];
+    {
+        constexpr int NA = C * C / 4 / kBwdThreads;
+        f32x4 ra[NA], rp[NA];
+        const f32x4* a4 = reinterpret_cast<const f32x4*>(w.dA + oCC) + tid;
+        const f32x4* p4 = reinterpret_cast<const f32x4*>(w.dP + oCC) + tid;
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+            ra[i] = a4[i * kBwdThreads];
+            rp[i] = p4[i * kBwdThreads];
+        }
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+            const int e = 4 * (tid + i * kBwdThreads), t = e / C, c = e % C;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                sdA[t][c + j] = ra[i][j];
+                sdP[t][c + j] = rp[i][j];
+            }
+        }
+    }
     // db = the gate's gradient per row before its reverse prefix sum, [C][DK + 1],
     // in the operand tiles' LDS once the pass over the chunk rows is done
     float* sDb = lds;
@@ -1281,8 +1304,6 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
     // to its own tile's end (fe) or start (fs) and then on to the other
     // tile's middle (f1, f2), factors <= 1 one after another.
     {
-        const float* dA = w.dA + oCC;
-        const float* dP = w.dP + oCC;
         const float* Bm = w.B + oCK;
         // One pass over the chunk-row index in tiles of 16, all three results
         // in registers: dKr and dQr take dA's and dP's column blocks against
@@ -1290,14 +1311,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
         // against Kr's and Qr's rows.  Kr, Qr and Ki are formed from q, k
         // and b as their rows are staged (the same values prep multiplied),
         // nothing is parked.
-        constexpr int KT = 16, SA = C + 4, SB = DK + 4, NT = DK / 16;
-        constexpr int RA = C * KT / kBwdThreads, RB = DK * KT / kBwdThreads;
-        static_assert(KT * (4 * SA + 3 * SB) <= kLdsFloats, "phase-5 tiles fit");
-        float* tAc = lds;            // [kk][t] = dA[t][k0 + kk]
-        float* tPc = tAc + KT * SA;  // [kk][t] = dP[t][k0 + kk]
-        float* tAr = tPc + KT * SA;  // [kk][t] = beta[k0 + kk] dA[k0 + kk][t]
-        float* tPr = tAr + KT * SA;  // [kk][t] = dP[k0 + kk][t]
-        float* tKi = tPr + KT * SA;  // [kk][c] = Ki[k0 + kk][c]
+        constexpr int KT = 16, SB = DK + 4, NT = DK / 16;
+        constexpr int RB = DK * KT / kBwdThreads;
+        static_assert(KT * 3 * SB <= kLdsFloats, "phase-5 tiles fit");
+        float* tKi = lds;            // [kk][c] = Ki[k0 + kk][c]
         float* tKr = tKi + KT * SB;
         float* tQr = tKr + KT * SB;
         const int wv = __builtin_amdgcn_readfirstlane(tid / 64), lg = (tid % 64) / 16, lr = tid % 16;
@@ -1309,7 +1326,6 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
         // when staged (rows past the end load the last row)
         using E2 = typename std::conditional<std::is_same<E, float>::value, float2, uint32_t>::type;
         constexpr int RB2 = RB / 2, DK2 = DK / 2;
-        float rAc[RA], rPc[RA], rAr[RA], rPr[RA];
         float2 rb[RB2];
         E2 rq[RB2], rk[RB2];
         auto lo_hi = [](E2 x, float& lo, float& hi) {
@@ -1323,16 +1339,6 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
         };
         auto fetch = [&](int k0) {
 #pragma unroll
-            for (int r = 0; r < RA; ++r) {
-                const int idx = tid + r * kBwdThreads;
-                const int m = idx / KT, kc = k0 + idx % KT;  // column blocks: 16 per row
-                rAc[r] = dA[(size_t)m * C + kc];
-                rPc[r] = m == kc ? 0.f : dP[(size_t)m * C + kc];  // diagonal: see the epilogue
-                const int kr = k0 + idx / C, t = idx % C;    // row blocks: whole rows
-                rAr[r] = sbeta[kr] * dA[(size_t)kr * C + t];
-                rPr[r] = kr == t ? 0.f : dP[(size_t)kr * C + t];
-            }
-#pragma unroll
             for (int r = 0; r < RB2; ++r) {
                 const int idx = tid + r * kBwdThreads;
                 const int t = k0 + idx / DK2, c = 2 * (idx % DK2);
@@ -1344,15 +1350,6 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
         };
         fetch(0);
         for (int k0 = 0; k0 < C; k0 += KT) {
-#pragma unroll
-            for (int r = 0; r < RA; ++r) {
-                const int idx = tid + r * kBwdThreads;
-                const int m = idx / KT, kk = idx % KT;
-                tAc[kk * SA + m] = rAc[r];
-                tPc[kk * SA + m] = rPc[r];
-                tAr[(idx / C) * SA + idx % C] = rAr[r];
-                tPr[(idx / C) * SA + idx % C] = rPr[r];
-            }
             // Kr = k e^{b - r}, Qr = q e^{b - r}, Ki = k e^{r - b}, r the b
             // of the middle row of this row tile
             const float* rmid = tf_row(kTfBm + k0 / KT);
@@ -1383,8 +1380,12 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
             const float* fv = tf_row(kt < wv ? kTfF1 + pair_of(wv, kt) : kTfF2 + pair_of(kt > wv ? kt : 1, kt > wv ? wv : 0));
 #pragma unroll
             for (int ks = 0; ks < KT; ks += 4) {
-                const int kr = ks + lg, ar = kr * SA + 16 * wv + lr;
-                const float a_Ac = tAc[ar], a_Pc = tPc[ar], a_Ar = tAr[ar], a_Pr = tPr[ar];
+                // dA and dP as column blocks (row 16 wv + lr, column k0 + kr)
+                // and as row blocks (row k0 + kr, column 16 wv + lr); P's
+                // diagonal enters dq and dk in the epilogue instead
+                const int kr = ks + lg, m = 16 * wv + lr, kc = k0 + kr;
+                const float a_Ac = sdA[m][kc], a_Pc = m == kc ? 0.f : sdP[m][kc];
+                const float a_Ar = sbeta[kc] * sdA[kc][m], a_Pr = kc == m ? 0.f : sdP[kc][m];
 #pragma unroll
                 for (int j = 0; j < NT; ++j) {
                     const int br = kr * SB + 16 * j + lr;
@@ -1450,7 +1451,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
                 rk[b] = k[o0 + c];
                 rq[b] = q[o0 + c];
             }
-            const float dPd = w.dP[oCC + (size_t)t * C + t];
+            const float dPd = sdP[t][t];
             const float bt = sbeta[t];
             float oq[NB], ok[NB];
 #pragma unroll
