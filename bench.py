@@ -154,8 +154,9 @@ def cpu_baseline(d, prefix_tokens):
                       threads=threads)
     dt = time.perf_counter() - t0
     return {"value": T / dt, "unit": "tokens/s", "cores": threads, "cpu_model": cpu_model(), "kind": "oracle",
-            "sample": f"first {T} tokens of the 32K x 32-head prefill workload (all heads; the whole "
-                      f"workload when {T} = 32768), fp64 sequential recurrence, {dt:.2f} s"}
+            "sample": (f"the whole 32K x 32-head prefill workload ({T} tokens, all heads)" if T >= 32768 else
+                       f"the first {T} tokens of the 32K x 32-head prefill workload, all heads")
+                      + f": fp64 sequential recurrence, {dt:.2f} s on {threads} threads"}
 
 
 def time_backward(kda, torch, hip, x, d, T, H, dk, dv, stream, steps=5, warmup=2):
