@@ -41,8 +41,9 @@
 //
 // All arithmetic is fp32; every matrix product runs on the fp32 matrix cores
 // (v_mfma_f32_16x16x4f32).  Every intermediate of a chunk is kept in the
-// workspace, except Qr, Kr and Ki: the two launches that multiply them form
-// them again from q, k and b as they stage them.  The two walks run one workgroup per (sequence,
+// workspace, except Qr, Kr and Ki (the two launches that multiply them form
+// them again from q, k and b as they stage them) and dXu (used only inside
+// the middle local launch).  The two walks run one workgroup per (sequence,
 // head, 16-column slice) with register tiles and the next chunk's operands in
 // flight; every product of the per-chunk kernels runs as a 64 x N block
 // product tiled through LDS with 4 x N/16 register tiles.
@@ -1296,13 +1297,13 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
     __syncthreads();
 
     // phase 5: dKr = diag(beta) dA Ki, dKi = (diag(beta) dA)^T Kr + dP^T Qr,
-    // dQr = dP Ki; then dq, dk and db (kept in dW's slot), dbeta, dv.
-    // Tile by tile: row-side results (dKr, dQr) of row tile a are referred to
-    // m(a), column-side ones (dKi) of column tile bb to m(bb), i.e. every
-    // result of a row is referred to the middle row of its own tile, like the
-    // stored operands.  Between two tiles the stored operand is first taken
-    // to its own tile's end (fe) or start (fs) and then on to the other
-    // tile's middle (f1, f2), factors <= 1 one after another.
+    // dQr = dP Ki; then dq, dk, db (in LDS) and dbeta (dv comes from the
+    // middle launch).  Tile by tile: row-side results (dKr, dQr) of row tile
+    // a are referred to m(a), column-side ones (dKi) of column tile bb to
+    // m(bb), i.e. every result of a row is referred to the middle row of its
+    // own tile, like the decayed operands.  Between two tiles the operand is
+    // first taken to its own tile's end (fe) or start (fs) and then on to the
+    // other tile's middle (f1, f2), factors <= 1 one after another.
     {
         const float* Bm = w.B + oCK;
         // One pass over the chunk-row index in tiles of 16, all three results
