@@ -699,6 +699,33 @@ __device__ __forceinline__ f32x4 mfma_tile(f32x4 acc, FA a, FB b, int lg) {
     return acc + odd;
 }
 
+// mfma_tile for two row tiles that share the B operand: both tiles' A values
+// and the common B values are read first, then the instructions of the two
+// tiles interleave (four independent accumulations).  Each tile's result is
+// computed exactly as mfma_tile computes it.
+template <int K, typename FA0, typename FA1, typename FB>
+__device__ __forceinline__ void mfma_tile2(f32x4& acc0, f32x4& acc1, FA0 a0, FA1 a1, FB b, int lg) {
+    static_assert(K % 8 == 0, "two accumulators");
+    float av0[K / 4], av1[K / 4], bv[K / 4];
+#pragma unroll
+    for (int s = 0; s < K / 4; ++s) {
+        av0[s] = a0(4 * s + lg);
+        av1[s] = a1(4 * s + lg);
+        bv[s] = b(4 * s + lg);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 odd0 = {0.f, 0.f, 0.f, 0.f}, odd1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < K / 4; s += 2) {
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(av0[s], bv[s], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(av1[s], bv[s], acc1, 0, 0, 0);
+        odd0 = __builtin_amdgcn_mfma_f32_16x16x4f32(av0[s + 1], bv[s + 1], odd0, 0, 0, 0);
+        odd1 = __builtin_amdgcn_mfma_f32_16x16x4f32(av1[s + 1], bv[s + 1], odd1, 0, 0, 0);
+    }
+    acc0 = acc0 + odd0;
+    acc1 = acc1 + odd1;
+}
+
 // The (sequence, head) pair and 16-column slice of a walk workgroup.  Blocks
 // are dispatched to the eight XCDs in turn (block b to XCD b mod 8); when the
 // pairs fill whole rounds of eight, the NS slices of a pair are all placed on
@@ -800,15 +827,28 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
         // U as 16-byte stores from its LDS copy: one per thread
         *reinterpret_cast<f32x4*>(w.U + oCV + (size_t)(tid / 4) * DV + sl * 16 + 4 * (tid % 4)) =
             *reinterpret_cast<const f32x4*>(sU + 4 * tid);
-        // S <- Diag(Gn) S + Kd^T U (this wave's TPW tiles of rows)
+        // S <- Diag(Gn) S + Kd^T U (this wave's TPW tiles of rows; with two
+        // tiles both are computed together, sharing U)
+        if constexpr (TPW == 2) {
+            const int m0 = 16 * (wv * TPW), m1 = m0 + 16;
+            f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+            mfma_tile2<C>(a0, a1, [&](int k) { return sKd[k * SK + m0 + lr]; },
+                          [&](int k) { return sKd[k * SK + m1 + lr]; }, [&](int k) { return sU[k * 16 + lr]; }, lg);
 #pragma unroll
-        for (int tt = 0; tt < TPW; ++tt) {
-            const int m0 = 16 * (wv * TPW + tt);
-            const f32x4 a = mfma_tile<C>(f32x4{0.f, 0.f, 0.f, 0.f},
-                                         [&](int k) { return sKd[k * SK + m0 + lr]; },
-                                         [&](int k) { return sU[k * 16 + lr]; }, lg);
+            for (int i = 0; i < 4; ++i) {
+                S[i] = gn[i] * S[i] + a0[i];
+                S[4 + i] = gn[4 + i] * S[4 + i] + a1[i];
+            }
+        } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) S[4 * tt + i] = gn[4 * tt + i] * S[4 * tt + i] + a[i];
+            for (int tt = 0; tt < TPW; ++tt) {
+                const int m0 = 16 * (wv * TPW + tt);
+                const f32x4 a = mfma_tile<C>(f32x4{0.f, 0.f, 0.f, 0.f},
+                                             [&](int k) { return sKd[k * SK + m0 + lr]; },
+                                             [&](int k) { return sU[k * 16 + lr]; }, lg);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[4 * tt + i] = gn[4 * tt + i] * S[4 * tt + i] + a[i];
+            }
         }
         fetch_gu(min(ch + 2, c1 - 1), gn, up);
         lds_barrier();
@@ -952,16 +992,31 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
         *reinterpret_cast<f32x4*>(w.dU + oCV + (size_t)(tid / 4) * DV + sl * 16 + 4 * (tid % 4)) =
             *reinterpret_cast<const f32x4*>(sdU + 4 * tid);
         fetch_near(max(ch - 1, c0));
-        // dS = Diag(Gn) dS_next + QG^T dO - W^T dU (this wave's TPW tiles of rows)
+        // dS = Diag(Gn) dS_next + QG^T dO - W^T dU (this wave's TPW tiles of
+        // rows; with two tiles both are computed together, sharing dO and dU)
+        if constexpr (TPW == 2) {
+            const int m0 = 16 * (wv * TPW), m1 = m0 + 16;
+            f32x4 a0 = zero, a1 = zero;
+            mfma_tile2<C>(a0, a1, [&](int k) { return sQG[k * SK + m0 + lr]; },
+                          [&](int k) { return sQG[k * SK + m1 + lr]; }, [&](int k) { return dOc[k * 16 + lr]; }, lg);
+            mfma_tile2<C>(a0, a1, [&](int k) { return sW[k * SK + m0 + lr]; },
+                          [&](int k) { return sW[k * SK + m1 + lr]; }, [&](int k) { return sdU[k * 16 + lr]; }, lg);
 #pragma unroll
-        for (int tt = 0; tt < TPW; ++tt) {
-            const int m0 = 16 * (wv * TPW + tt);
-            f32x4 a = mfma_tile<C>(zero, [&](int k) { return sQG[k * SK + m0 + lr]; },
-                                   [&](int k) { return dOc[k * 16 + lr]; }, lg);
-            a = mfma_tile<C>(a, [&](int k) { return sW[k * SK + m0 + lr]; },
-                             [&](int k) { return sdU[k * 16 + lr]; }, lg);
+            for (int i = 0; i < 4; ++i) {
+                dS[i] = gn[i] * dS[i] + a0[i];
+                dS[4 + i] = gn[4 + i] * dS[4 + i] + a1[i];
+            }
+        } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dS[4 * tt + i] = gn[4 * tt + i] * dS[4 * tt + i] + a[i];
+            for (int tt = 0; tt < TPW; ++tt) {
+                const int m0 = 16 * (wv * TPW + tt);
+                f32x4 a = mfma_tile<C>(zero, [&](int k) { return sQG[k * SK + m0 + lr]; },
+                                       [&](int k) { return dOc[k * 16 + lr]; }, lg);
+                a = mfma_tile<C>(a, [&](int k) { return sW[k * SK + m0 + lr]; },
+                                 [&](int k) { return sdU[k * 16 + lr]; }, lg);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dS[4 * tt + i] = gn[4 * tt + i] * dS[4 * tt + i] + a[i];
+            }
         }
         __builtin_amdgcn_sched_barrier(0);  // the staging below stays after the products
         // sP and sKd were last read before the second barrier, the other dO
