@@ -160,7 +160,7 @@ size_t kda_chunk_bwd_workspace_size(int64_t T_total, int32_t N, int32_t H, int32
                                     kda_dtype dt, kda_gate gk) {
     if (check_common(H, d_k, d_v, dt, gk) != KDA_OK) return 0;
     if (N <= 0 || T_total < 0 || T_total > INT32_MAX) return 0;
-    return kda::bwd_workspace_bytes(T_total, N, H, d_k, d_v);
+    return kda::bwd_workspace_bytes(T_total, N, H, d_k, d_v, dt == KDA_BF16);
 }
 
 kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
@@ -183,7 +183,7 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
         (cu_seqlens && !aligned(cu_seqlens, 4)))
         return KDA_ERR_INVALID_ARG;
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERR_WORKSPACE;
-    if (kda::bwd_head_group(T_total, N, H, d_k, d_v, workspace_bytes) < 1) return KDA_ERR_WORKSPACE;
+    if (kda::bwd_head_group(T_total, N, H, d_k, d_v, dt == KDA_BF16, workspace_bytes) < 1) return KDA_ERR_WORKSPACE;
 
     kda::BwdArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;

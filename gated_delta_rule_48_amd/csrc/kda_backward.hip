@@ -58,7 +58,8 @@ namespace {
 constexpr int kBwdThreads = 256;
 constexpr int C = kChunk;
 
-// Per-(chunk, head) arrays, fp32; slot = chunk * H + head, where H counts the
+// Per-(chunk, head) arrays, fp32 except the walks' operands QG, Kd, W and P,
+// which are kept in the input type; slot = chunk * H + head, where H counts the
 // heads of the group being processed.  Token and state tensors are indexed
 // with the full head count Hs (their row stride); the host offsets their
 // pointers to the group's first head.
@@ -381,6 +382,36 @@ __device__ __forceinline__ void decayed_mp(const E* q, const E* k, int64_t t0, i
     }
 }
 
+// Four stored operand values as loaded (fp32, or four bf16 in 8 bytes) and
+// their widening to fp32.
+template <typename ST> struct Op4;
+template <> struct Op4<float> {
+    typedef f32x4 T;
+    __device__ __forceinline__ static f32x4 widen(T w) { return w; }
+    __device__ __forceinline__ static T neg(T w) { return -w; }
+};
+template <> struct Op4<bf16_t> {
+    typedef uint2 T;
+    __device__ __forceinline__ static f32x4 widen(T w) {
+        return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+                     __uint_as_float(w.y & 0xffff0000u)};
+    }
+    __device__ __forceinline__ static T neg(T w) { return uint2{w.x ^ 0x80008000u, w.y ^ 0x80008000u}; }
+};
+
+// Four consecutive operand values stored in the walks' storage type (the
+// arrays are laid out for fp32; a bf16 array uses the first half of its slot
+// region, element i at (bf16*)base + i).
+template <typename ST>
+__device__ __forceinline__ void store_op4(float* base, size_t i, f32x4 v) {
+    if constexpr (std::is_same<ST, float>::value) {
+        *reinterpret_cast<f32x4*>(base + i) = v;
+    } else {
+        *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(base) + i) =
+            uint2{f32x2_to_bf16x2(v[0], v[1]), f32x2_to_bf16x2(v[2], v[3])};
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Per (chunk, head): prefix sums, decayed operands, M, P, T = (I + A)^{-1},
 // W and U'.
@@ -483,9 +514,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
         }
         const size_t i = oCK + idx;
         *reinterpret_cast<f32x4*>(w.B + i) = b4;
-        *reinterpret_cast<f32x4*>(w.QG + i) = oQG;
+        store_op4<E>(w.QG, i, oQG);
         *reinterpret_cast<f32x4*>(w.KG + i) = oKG;
-        *reinterpret_cast<f32x4*>(w.Kd + i) = oKd;
+        store_op4<E>(w.Kd, i, oKd);
     }
     __syncthreads();
     // M = strict_tril(K K^T with decay) and P = tril(Q K^T with decay), by
@@ -500,7 +531,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
                 const int t = Acc<C>::row(a), i = Acc<C>::col(b);
                 const float mv = (i < t && t < n) ? am[b][a] : 0.f;
                 w.M[oCC + (size_t)t * C + i] = mv;
-                w.P[oCC + (size_t)t * C + i] = (i <= t && t < n) ? ap[b][a] : 0.f;
+                reinterpret_cast<E*>(w.P)[oCC + (size_t)t * C + i] = Elt<E>::from((i <= t && t < n) ? ap[b][a] : 0.f);
                 lds_put(&sA[t][i], sbeta[t] * mv);
             }
     }
@@ -610,7 +641,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
         for (int a = 0; a < 4; ++a)
 #pragma unroll
             for (int b = 0; b < DK / 16; ++b)
-                w.W[oCK + (size_t)Acc<DK>::row(a) * DK + Acc<DK>::col(b)] = aw.t[b][a];
+                reinterpret_cast<E*>(w.W)[oCK + (size_t)Acc<DK>::row(a) * DK + Acc<DK>::col(b)] = Elt<E>::from(aw.t[b][a]);
         Acc<DV> au;
         au.zero();
         // beta_i is zero past the chunk's end, so the rows there (which re-read
@@ -642,18 +673,18 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
 template <int WIDTH>
 constexpr int block_regs() { return C * WIDTH / 4 / kBwdThreads; }
 
-template <int WIDTH>
-__device__ __forceinline__ void block_load(f32x4 (&r)[block_regs<WIDTH>()], const float* src) {
-    const f32x4* s4 = reinterpret_cast<const f32x4*>(src) + threadIdx.x;
+template <int WIDTH, typename ST>
+__device__ __forceinline__ void block_load(typename Op4<ST>::T (&r)[block_regs<WIDTH>()], const ST* src) {
+    const typename Op4<ST>::T* s4 = reinterpret_cast<const typename Op4<ST>::T*>(src) + threadIdx.x;
 #pragma unroll
     for (int i = 0; i < block_regs<WIDTH>(); ++i) r[i] = s4[i * kBwdThreads];
 }
 
 // block_load with the loads issued in index order wherever it is inlined, so
 // that a wait for one register of r is computed alike on every path.
-template <int WIDTH>
-__device__ __forceinline__ void block_load_ordered(f32x4 (&r)[block_regs<WIDTH>()], const float* src) {
-    const f32x4* s4 = reinterpret_cast<const f32x4*>(src) + threadIdx.x;
+template <int WIDTH, typename ST>
+__device__ __forceinline__ void block_load_ordered(typename Op4<ST>::T (&r)[block_regs<WIDTH>()], const ST* src) {
+    const typename Op4<ST>::T* s4 = reinterpret_cast<const typename Op4<ST>::T*>(src) + threadIdx.x;
 #pragma unroll
     for (int i = 0; i < block_regs<WIDTH>(); ++i) {
         r[i] = s4[i * kBwdThreads];
@@ -661,12 +692,12 @@ __device__ __forceinline__ void block_load_ordered(f32x4 (&r)[block_regs<WIDTH>(
     }
 }
 
-template <int WIDTH>
-__device__ __forceinline__ void block_store(const f32x4 (&r)[block_regs<WIDTH>()], float* dst, int stride) {
+template <int WIDTH, typename ST>
+__device__ __forceinline__ void block_store(const typename Op4<ST>::T (&r)[block_regs<WIDTH>()], float* dst, int stride) {
 #pragma unroll
     for (int i = 0; i < block_regs<WIDTH>(); ++i) {
         const int idx = threadIdx.x + i * kBwdThreads;
-        *reinterpret_cast<f32x4*>(dst + (idx / (WIDTH / 4)) * stride + 4 * (idx % (WIDTH / 4))) = r[i];
+        *reinterpret_cast<f32x4*>(dst + (idx / (WIDTH / 4)) * stride + 4 * (idx % (WIDTH / 4))) = Op4<ST>::widen(r[i]);
     }
 }
 
@@ -756,7 +787,7 @@ struct StateWalkLds {
 
 // One workgroup of four waves per CU at most (LDS), so a wave may use the
 // whole register file: the next two chunks' operands are held in registers.
-template <int DK, int DV>
+template <typename E, int DK, int DV>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_state_walk_kernel(int32_t H, int32_t Hs, const float* __restrict__ S0,
                                                                      BwdWs w) {
     using L = StateWalkLds<DK, DV>;
@@ -788,12 +819,13 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
     // chunk the fetches re-read that chunk (unused), so that every path
     // issues the same loads and the compiler's waits stay exact.
     constexpr int NR = block_regs<DK>();
-    f32x4 rWa[NR], rKa[NR], rWb[NR], rKb[NR];
+    using OT = typename Op4<E>::T;  // W and Kd as stored (in the input type)
+    OT rWa[NR], rKa[NR], rWb[NR], rKb[NR];
     float gna[RS], upa[4], gnb[RS], upb[4];
-    auto fetch_wk = [&](int ch, f32x4 (&rW)[NR], f32x4 (&rK)[NR]) {
+    auto fetch_wk = [&](int ch, OT (&rW)[NR], OT (&rK)[NR]) {
         const size_t slot = (size_t)ch * H + h;
-        block_load_ordered<DK>(rW, w.W + slot * C * DK);
-        block_load_ordered<DK>(rK, w.Kd + slot * C * DK);
+        block_load_ordered<DK, E>(rW, reinterpret_cast<const E*>(w.W) + slot * C * DK);
+        block_load_ordered<DK, E>(rK, reinterpret_cast<const E*>(w.Kd) + slot * C * DK);
     };
     auto fetch_gu = [&](int ch, float (&gn)[RS], float (&up)[4]) {
         const size_t slot = (size_t)ch * H + h;
@@ -802,11 +834,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
 #pragma unroll
         for (int i = 0; i < 4; ++i) up[i] = w.Up[slot * C * DV + (size_t)(t0 + i) * DV + col];
     };
-    auto step = [&](int ch, f32x4 (&rW)[NR], f32x4 (&rK)[NR], float (&gn)[RS], float (&up)[4]) {
+    auto step = [&](int ch, OT (&rW)[NR], OT (&rK)[NR], float (&gn)[RS], float (&up)[4]) {
         const size_t slot = (size_t)ch * H + h;
         const size_t oCV = slot * C * DV, oKV = slot * DK * DV;
-        block_store<DK>(rW, sW, SK);
-        block_store<DK>(rK, sKd, SK);
+        block_store<DK, E>(rW, sW, SK);
+        block_store<DK, E>(rK, sKd, SK);
 #pragma unroll
         for (int i = 0; i < RS; ++i) sS[srow(i) * 16 + lr] = S[i];
         lds_barrier();
@@ -932,14 +964,15 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
         for (int i = 0; i < 4; ++i) dst[(t0 + i) * 16 + lr] = t0 + i < n ? Elt<E>::to(r[i]) : 0.f;
     };
     constexpr int NP = block_regs<C>(), NK = block_regs<DK>();
-    f32x4 rP[NP], rK[NK], rQ[NK], rW[NK];
+    using OT = typename Op4<E>::T;  // P, Kd, QG and W as stored (in the input type)
+    OT rP[NP], rK[NK], rQ[NK], rW[NK];
     E rO[4];
     float gn[RS], gnn[RS];
     auto fetch_far = [&](int ch) {  // P, Kd, dO: staged at the end of the step that fetches them
         const size_t slot = (size_t)ch * H + h;
         load_dO(ch, rO);
-        block_load_ordered<C>(rP, w.P + slot * C * C);
-        block_load_ordered<DK>(rK, w.Kd + slot * C * DK);
+        block_load_ordered<C, E>(rP, reinterpret_cast<const E*>(w.P) + slot * C * C);
+        block_load_ordered<DK, E>(rK, reinterpret_cast<const E*>(w.Kd) + slot * C * DK);
         asm volatile("" ::: "memory");
     };
     auto fetch_near = [&](int ch) {  // Gn, QG, W: used at the end of this step and in the next one
@@ -947,14 +980,14 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
 #pragma unroll
         for (int i = 0; i < RS; ++i) gnn[i] = w.Gn[slot * DK + srow(i)];
         asm volatile("" ::: "memory");
-        block_load_ordered<DK>(rQ, w.QG + slot * C * DK);
-        block_load_ordered<DK>(rW, w.W + slot * C * DK);
+        block_load_ordered<DK, E>(rQ, reinterpret_cast<const E*>(w.QG) + slot * C * DK);
+        block_load_ordered<DK, E>(rW, reinterpret_cast<const E*>(w.W) + slot * C * DK);
     };
     int buf = 0;
     fetch_far(c1 - 1);
     fetch_near(c1 - 1);
-    block_store<C>(rP, sP, SC);
-    block_store<DK>(rK, sKd, SK);
+    block_store<C, E>(rP, sP, SC);
+    block_store<DK, E>(rK, sKd, SK);
     stage_dO(c1 - 1, rO, sdO);
 #pragma unroll
     for (int i = 0; i < RS; ++i) gn[i] = gnn[i];
@@ -984,10 +1017,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
         for (int i = 0; i < 4; ++i) sdU[(t0 + i) * 16 + lr] = du[i];
         // no work that waits for the loads in flight is scheduled into the products
         __builtin_amdgcn_sched_barrier(0);
-        block_store<DK>(rQ, sQG, SK);
+        block_store<DK, E>(rQ, sQG, SK);
 #pragma unroll
-        for (int i = 0; i < NK; ++i) rW[i] = -rW[i];
-        block_store<DK>(rW, sW, SK);  // sW holds -W
+        for (int i = 0; i < NK; ++i) rW[i] = Op4<E>::neg(rW[i]);
+        block_store<DK, E>(rW, sW, SK);  // sW holds -W
         lds_barrier();
         *reinterpret_cast<f32x4*>(w.dU + oCV + (size_t)(tid / 4) * DV + sl * 16 + 4 * (tid % 4)) =
             *reinterpret_cast<const f32x4*>(sdU + 4 * tid);
@@ -1021,8 +1054,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
         __builtin_amdgcn_sched_barrier(0);  // the staging below stays after the products
         // sP and sKd were last read before the second barrier, the other dO
         // buffer a step ago; the next step's first barrier publishes these
-        block_store<C>(rP, sP, SC);
-        block_store<DK>(rK, sKd, SK);
+        block_store<C, E>(rP, sP, SC);
+        block_store<DK, E>(rK, sKd, SK);
         stage_dO(max(ch - 1, c0), rO, sdO + (buf ^ 1) * C * 16);
 #pragma unroll
         for (int i = 0; i < RS; ++i) gn[i] = gnn[i];
@@ -1595,25 +1628,30 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
 inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdSizes {
-    size_t head, ck, cv, cc, c, k, kv, total;
+    size_t head, ck, ckw, cv, cc, ccw, c, k, kv, total;
 };
 
-BwdSizes bwd_sizes(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv) {
+// The walks' operands (QG, Kd, W: [C][DK]; P: [C][C]) are kept in the input
+// type (bf16 for bf16 inputs), every other array in fp32.
+BwdSizes bwd_sizes(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, bool bf16) {
     const size_t slots = (size_t)max_chunks_for(T, N) * H;
+    const size_t ew = bf16 ? 2 : 4;
     BwdSizes s;
     s.head = 256 + 2 * al256((size_t)(N + 1) * 4) + al256((size_t)max_chunks_for(T, N) * sizeof(int2));
     s.ck = al256(slots * C * dk * 4);
+    s.ckw = al256(slots * C * dk * ew);
     s.cv = al256(slots * C * dv * 4);
     s.cc = al256(slots * C * C * 4);
+    s.ccw = al256(slots * C * C * ew);
     s.c = al256(slots * C * 4);
     s.k = al256(slots * dk * 4);
     s.kv = al256(slots * dk * dv * 4);
-    s.total = s.head + 9 * s.ck + 3 * s.cv + 5 * s.cc + s.c + 2 * s.k + 2 * s.kv;
+    s.total = s.head + 6 * s.ck + 3 * s.ckw + 3 * s.cv + 4 * s.cc + s.ccw + s.c + 2 * s.k + 2 * s.kv;
     return s;
 }
 
-BwdWs carve_bwd(void* base, int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv) {
-    const BwdSizes s = bwd_sizes(T, N, H, dk, dv);
+BwdWs carve_bwd(void* base, int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, bool bf16) {
+    const BwdSizes s = bwd_sizes(T, N, H, dk, dv, bf16);
     char* p = static_cast<char*>(base);
     BwdWs w;
     w.header = reinterpret_cast<WsHeader*>(p); p += 256;
@@ -1621,12 +1659,15 @@ BwdWs carve_bwd(void* base, int64_t T, int32_t N, int32_t H, int32_t dk, int32_t
     w.chunk_off = reinterpret_cast<int32_t*>(p); p += al256((size_t)(N + 1) * 4);
     w.chunk_tab = reinterpret_cast<int2*>(p); p += al256((size_t)max_chunks_for(T, N) * sizeof(int2));
     auto take = [&](size_t bytes) { float* f = reinterpret_cast<float*>(p); p += bytes; return f; };
-    float** ck[] = {&w.B, &w.QG, &w.KG, &w.Kd, &w.W, &w.dW, &w.dQG, &w.dKd, &w.dXw};
+    float** ck[] = {&w.B, &w.KG, &w.dW, &w.dQG, &w.dKd, &w.dXw};
     for (float** f : ck) *f = take(s.ck);
+    float** ckw[] = {&w.QG, &w.Kd, &w.W};
+    for (float** f : ckw) *f = take(s.ckw);
     float** cv[] = {&w.Up, &w.U, &w.dU};
     for (float** f : cv) *f = take(s.cv);
-    float** cc[] = {&w.M, &w.P, &w.T, &w.dP, &w.dA};
+    float** cc[] = {&w.M, &w.T, &w.dP, &w.dA};
     for (float** f : cc) *f = take(s.cc);
+    w.P = take(s.ccw);
     w.dBr = take(s.c);
     w.Gn = take(s.k);
     w.dGn = take(s.k);
@@ -1653,7 +1694,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, int32_t Hs, const BwdWs& w, hipStream_
                            w);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
-        auto sw = bwd_state_walk_kernel<DK, DV>;
+        auto sw = bwd_state_walk_kernel<E, DK, DV>;
         constexpr size_t sw_lds = StateWalkLds<DK, DV>::bytes;
         if ((e = lds_attr(reinterpret_cast<const void*>(sw), sw_lds)) != hipSuccess) return e;
         hipLaunchKernelGGL(sw, dim3(walks), dim3(kBwdThreads), sw_lds, stream, a.H, Hs, a.S0, w);
@@ -1705,21 +1746,21 @@ P* at(P* p, size_t elems, size_t esz) {
 
 }  // namespace
 
-size_t bwd_workspace_bytes(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv) {
-    return bwd_sizes(T, N, H, dk, dv).total;
+size_t bwd_workspace_bytes(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, bool bf16) {
+    return bwd_sizes(T, N, H, dk, dv, bf16).total;
 }
 
-int32_t bwd_head_group(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, size_t workspace_bytes) {
+int32_t bwd_head_group(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, bool bf16, size_t workspace_bytes) {
     int32_t g = H;
-    while (g > 0 && bwd_sizes(T, N, g, dk, dv).total > workspace_bytes) --g;
+    while (g > 0 && bwd_sizes(T, N, g, dk, dv, bf16).total > workspace_bytes) --g;
     return g;
 }
 
 hipError_t launch_chunk_bwd(const BwdArgs& a, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     // heads are independent: process them in the largest groups whose
     // intermediates fit the workspace, one group after another on the stream
-    const int32_t G = bwd_head_group(a.T, a.N, a.H, a.dk_, a.dv_, workspace_bytes);
-    const BwdWs w = carve_bwd(workspace, a.T, a.N, G, a.dk_, a.dv_);
+    const int32_t G = bwd_head_group(a.T, a.N, a.H, a.dk_, a.dv_, a.bf16, workspace_bytes);
+    const BwdWs w = carve_bwd(workspace, a.T, a.N, G, a.dk_, a.dv_, a.bf16);
     hipError_t e = launch_chunk_map(a.cu_seqlens, a.N, a.T, w.header, w.cu, w.chunk_off, w.chunk_tab, nullptr, 0,
                                     stream);
     if (e != hipSuccess) return e;

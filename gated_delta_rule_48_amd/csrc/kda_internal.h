@@ -117,9 +117,9 @@ struct BwdArgs {
     bool bf16, head_gate;
 };
 
-size_t bwd_workspace_bytes(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv);
+size_t bwd_workspace_bytes(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, bool bf16);
 // The largest number of heads whose intermediates fit in workspace_bytes (0: not even one).
-int32_t bwd_head_group(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, size_t workspace_bytes);
+int32_t bwd_head_group(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, bool bf16, size_t workspace_bytes);
 hipError_t launch_chunk_bwd(const BwdArgs& a, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 }  // namespace kda
