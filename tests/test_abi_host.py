@@ -200,6 +200,12 @@ def test_chunk_bwd_rejects_bad_arguments(lib):
     assert sz(128, 1, 2, 64, 64, 0, 0) > 0
     assert sz(128, 1, 2, 64, 80, 0, 0) == 0
     assert sz(256, 1, 2, 64, 64, 0, 0) > sz(128, 1, 2, 64, 64, 0, 0)
+    # bf16 inputs keep the operands of the sequential passes in bf16:
+    # less workspace than fp32 inputs, and a bf16-sized workspace is too small
+    # for an fp32 call of one head
+    bf, f32 = sz(4096, 1, 1, 128, 128, 0, 0), sz(4096, 1, 1, 128, 128, 1, 0)
+    assert 0 < bf < f32
+    assert call(T=4096, H=1, dk=128, dv=128, dt=1, wsb=bf) == WORKSPACE
 
 
 def test_prepare_inputs_rejects_bad_arguments(lib):
