@@ -40,7 +40,10 @@
 //        for a per-head gate).
 //
 // All arithmetic is fp32; every matrix product runs on the fp32 matrix cores
-// (v_mfma_f32_16x16x4f32).  Every intermediate of a chunk is kept in the
+// (v_mfma_f32_16x16x4f32), except the two walks for bf16 inputs, which run on
+// the bf16 matrix cores with fp32 accumulation (their operands are stored in
+// bf16; the fp32 state enters as two bf16 parts, see the bf16 walks below).
+// Every intermediate of a chunk is kept in the
 // workspace, except Qr, Kr and Ki (the two launches that multiply them form
 // them again from q, k and b as they stage them) and dXu (used only inside
 // the middle local launch).  The two walks run one workgroup per (sequence,
@@ -58,18 +61,23 @@ namespace {
 constexpr int kBwdThreads = 256;
 constexpr int C = kChunk;
 
-// Per-(chunk, head) arrays, fp32 except the walks' operands QG, Kd, W and P,
-// which are kept in the input type; slot = chunk * H + head, where H counts the
-// heads of the group being processed.  Token and state tensors are indexed
-// with the full head count Hs (their row stride); the host offsets their
-// pointers to the group's first head.
+// Per-(chunk, head) arrays, fp32 except the walks' operands, which are kept
+// in the input type; slot = chunk * H + head, where H counts the heads of the
+// group being processed.  Token and state tensors are indexed with the full
+// head count Hs (their row stride); the host offsets their pointers to the
+// group's first head.
+//
+// The walks' operands.  fp32 inputs: QG, Kd, W [C][DK] and P [C][C],
+// row-major.  bf16 inputs: the A operands of the walks' products in fragment
+// order (frag_at), QG^T, Kd, W^T and P^T for the reverse walk, W (in Wr) and
+// Kd^T (in KdT) for the state walk; Wr and KdT are empty for fp32 inputs.
 struct BwdWs {
     WsHeader* header;
     int32_t* cu;
     int32_t* chunk_off;
     int2* chunk_tab;
     // [C][DK]
-    float *B, *QG, *KG, *Kd, *W, *dW, *dQG, *dKd, *dXw;
+    float *B, *QG, *KG, *Kd, *W, *dW, *dQG, *dKd, *dXw, *Wr, *KdT;
     // [C][DV]
     float *Up, *U, *dU;
     // [C]: dbeta's row sums of dA * M and dXu * V
@@ -85,6 +93,18 @@ struct BwdWs {
 template <typename E>
 __device__ __forceinline__ float ld(const E* p, int64_t i) {
     return Elt<E>::load(p + i);
+}
+
+// Fragment order of an R x K matrix-core A operand (bf16, R rows, K the
+// length of the contraction, a multiple of 32): blocks of 16 rows by 32 k
+// (1 KB), block (r / 16, k / 32) at index (r / 16) (K / 32) + k / 32; inside
+// it, lane 16 ((k % 32) / 8) + r % 16 holds k % 8 = 0..7 in 16 contiguous
+// bytes (the A fragment of v_mfma_f32_16x16x32_bf16, which is also the B
+// fragment of the transposed matrix).  A wave reads one block with one
+// coalesced 16-byte load per lane.
+template <int K>
+__host__ __device__ constexpr int frag_at(int r, int k) {
+    return (((r >> 4) * (K / 32) + (k >> 5)) * 64 + 16 * ((k & 31) >> 3) + (r & 15)) * 8 + (k & 7);
 }
 
 // ---------------------------------------------------------------------------
@@ -452,15 +472,17 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
     }
     asm volatile("" ::: "memory");  // the gate's loads go out before those of q and k
     // q and k of this thread's elements of the decayed-operand pass below,
-    // four consecutive channels per load, issued next so that they arrive
-    // while the gate is staged and summed (rows past the end re-read the
-    // last row); waiting for the gate does not wait for them
+    // issued next so that they arrive while the gate is staged and summed
+    // (rows past the end re-read the last row); waiting for the gate does not
+    // wait for them.  The thread takes four consecutive channels qc.. of NQ
+    // consecutive rows qt0.., one load per row.
     using QK4 = typename std::conditional<std::is_same<E, float>::value, f32x4, uint2>::type;
     constexpr int NQ = C * DK / (4 * kBwdThreads);
+    const int qc = 4 * (tid % (DK / 4)), qt0 = NQ * (tid / (DK / 4));
     QK4 rq4[NQ], rk4[NQ];
 #pragma unroll
     for (int it = 0; it < NQ; ++it) {
-        const int idx = 4 * tid + it * 4 * kBwdThreads, t = idx / DK, c = idx % DK;
+        const int t = qt0 + it, c = qc;
         const int64_t o = ((t0 + min(t, n - 1)) * Hs + h) * DK + c;
         rq4[it] = *reinterpret_cast<const QK4*>(q + o);
         rk4[it] = *reinterpret_cast<const QK4*>(k + o);
@@ -495,12 +517,17 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
     // the prefix sums and the decayed operands the later launches read (QG,
     // KG, Kd; the tile-referred Kr, Qr, Ki are formed again from q, k and b
     // wherever they are used).  Four consecutive channels per thread, so each
-    // array is written with 16-byte stores.
+    // row-major array is written with 16-byte stores; for bf16 inputs the
+    // walks' fragment-ordered QG^T and Kd^T take the thread's NQ consecutive
+    // rows of one channel in one store.
+    constexpr bool kFrag = std::is_same<E, bf16_t>::value;
+    uint32_t pq[4][NQ / 2], pk[4][NQ / 2];  // bf16 pairs of QG and Kd over rows (kFrag)
+    f32x4 evQ, evK;                         // the even row's values, until its pair is packed
+    const f32x4 bl4 = *reinterpret_cast<const f32x4*>(sB + (n - 1) * DK + qc);
 #pragma unroll
     for (int it = 0; it < NQ; ++it) {
-        const int idx = 4 * tid + it * 4 * kBwdThreads, t = idx / DK, c = idx % DK;
+        const int t = qt0 + it, c = qc, idx = t * DK + c;
         const f32x4 b4 = *reinterpret_cast<const f32x4*>(sB + idx);
-        const f32x4 bl4 = *reinterpret_cast<const f32x4*>(sB + (n - 1) * DK + c);
         f32x4 oQG, oKG, oKd;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -514,9 +541,42 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
         }
         const size_t i = oCK + idx;
         *reinterpret_cast<f32x4*>(w.B + i) = b4;
-        store_op4<E>(w.QG, i, oQG);
         *reinterpret_cast<f32x4*>(w.KG + i) = oKG;
-        store_op4<E>(w.Kd, i, oKd);
+        if constexpr (kFrag) {
+            // Kd as the reverse walk's A operand (rows t, k = channel)
+            *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(w.Kd) + oCK + frag_at<DK>(t, c)) =
+                uint2{f32x2_to_bf16x2(oKd[0], oKd[1]), f32x2_to_bf16x2(oKd[2], oKd[3])};
+            if (it % 2 == 0) {
+                evQ = oQG;
+                evK = oKd;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    pq[j][it / 2] = f32x2_to_bf16x2(evQ[j], oQG[j]);
+                    pk[j][it / 2] = f32x2_to_bf16x2(evK[j], oKd[j]);
+                }
+            }
+        } else {
+            store_op4<E>(w.QG, i, oQG);
+            store_op4<E>(w.Kd, i, oKd);
+        }
+    }
+    if constexpr (kFrag) {
+        // QG^T (reverse walk) and Kd^T (state walk) as A operands: rows =
+        // channels, k = the thread's NQ consecutive rows (NQ | 8)
+        static_assert(NQ == 4 || NQ == 8, "one store per channel");
+        using PK = typename std::conditional<NQ == 8, uint4, uint2>::type;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const size_t o = oCK + frag_at<C>(qc + j, qt0);
+            if constexpr (NQ == 8) {
+                *reinterpret_cast<PK*>(reinterpret_cast<bf16_t*>(w.QG) + o) = PK{pq[j][0], pq[j][1], pq[j][2], pq[j][3]};
+                *reinterpret_cast<PK*>(reinterpret_cast<bf16_t*>(w.KdT) + o) = PK{pk[j][0], pk[j][1], pk[j][2], pk[j][3]};
+            } else {
+                *reinterpret_cast<PK*>(reinterpret_cast<bf16_t*>(w.QG) + o) = PK{pq[j][0], pq[j][1]};
+                *reinterpret_cast<PK*>(reinterpret_cast<bf16_t*>(w.KdT) + o) = PK{pk[j][0], pk[j][1]};
+            }
+        }
     }
     __syncthreads();
     // M = strict_tril(K K^T with decay) and P = tril(Q K^T with decay), by
@@ -531,9 +591,22 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
                 const int t = Acc<C>::row(a), i = Acc<C>::col(b);
                 const float mv = (i < t && t < n) ? am[b][a] : 0.f;
                 w.M[oCC + (size_t)t * C + i] = mv;
-                reinterpret_cast<E*>(w.P)[oCC + (size_t)t * C + i] = Elt<E>::from((i <= t && t < n) ? ap[b][a] : 0.f);
+                if constexpr (!kFrag) w.P[oCC + (size_t)t * C + i] = (i <= t && t < n) ? ap[b][a] : 0.f;
                 lds_put(&sA[t][i], sbeta[t] * mv);
             }
+        if constexpr (kFrag) {
+            // P^T as the reverse walk's A operand (rows i, k = t): the lane's
+            // four consecutive rows t are four consecutive elements
+#pragma unroll
+            for (int b = 0; b < C / 16; ++b) {
+                const int t = Acc<C>::row(0), i = Acc<C>::col(b);
+                float pv[4];
+#pragma unroll
+                for (int a = 0; a < 4; ++a) pv[a] = (i <= t + a && t + a < n) ? ap[b][a] : 0.f;
+                *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(w.P) + oCC + frag_at<C>(i, t)) =
+                    uint2{f32x2_to_bf16x2(pv[0], pv[1]), f32x2_to_bf16x2(pv[2], pv[3])};
+            }
+        }
     }
     __syncthreads();
     // T = (I + A)^{-1} by 16 x 16 blocks.  The four diagonal blocks by
@@ -637,11 +710,29 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
         aw.zero();
         gemm64<DK, C, true, true>(aw, [&](int t, int i) { return sT[t][i]; },
                                   [&](int i, int c) { return sbeta[i] * KG[(size_t)i * DK + c]; }, lds);
+        if constexpr (kFrag) {
+            // W^T for the reverse walk (rows = channels, k = t: the lane's four
+            // rows t are consecutive elements) and W for the state walk (rows
+            // t, k = channel: one element each)
+            bf16_t* WT = reinterpret_cast<bf16_t*>(w.W) + oCK;
+            bf16_t* Wr = reinterpret_cast<bf16_t*>(w.Wr) + oCK;
+            const int t = Acc<DK>::row(0);
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+            for (int b = 0; b < DK / 16; ++b) {
+                const int c = Acc<DK>::col(b);
+                const f32x4 x = aw.t[b];
+                *reinterpret_cast<uint2*>(WT + frag_at<C>(c, t)) =
+                    uint2{f32x2_to_bf16x2(x[0], x[1]), f32x2_to_bf16x2(x[2], x[3])};
 #pragma unroll
-            for (int b = 0; b < DK / 16; ++b)
-                reinterpret_cast<E*>(w.W)[oCK + (size_t)Acc<DK>::row(a) * DK + Acc<DK>::col(b)] = Elt<E>::from(aw.t[b][a]);
+                for (int a = 0; a < 4; ++a) Wr[frag_at<DK>(t + a, c)] = f32_to_bf16(x[a]);
+            }
+        } else {
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < DK / 16; ++b)
+                    w.W[oCK + (size_t)Acc<DK>::row(a) * DK + Acc<DK>::col(b)] = aw.t[b][a];
+        }
         Acc<DV> au;
         au.zero();
         // beta_i is zero past the chunk's end, so the rows there (which re-read
@@ -1060,6 +1151,358 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
 #pragma unroll
         for (int i = 0; i < RS; ++i) gn[i] = gnn[i];
         buf ^= 1;
+    }
+    if (dS0) {
+#pragma unroll
+        for (int i = 0; i < RS; ++i) dS0[(((size_t)seq * Hs + h) * DK + srow(i)) * DV + col] = dS[i];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The two walks for bf16 inputs, on the bf16 matrix cores
+// (v_mfma_f32_16x16x32_bf16).  Their operands were rounded to bf16 when prep
+// stored them, in fragment order (frag_at), so each wave loads the fragments
+// of its own tiles straight into registers, one chunk ahead, and no operand
+// passes through LDS.  The fp32 state (S, or dS) and U (or dU) enter a product
+// as two bf16 parts, x = hi + lo with hi = bf16(x) and lo = bf16(x - hi),
+// which carry about 16 significant bits; dO is bf16 already.  LDS holds only
+// what the waves exchange: those parts and dO, transposed (16 rows, one per
+// column of the slice) as the products' B fragments, and fp32 copies of the
+// state and of U (dU) for the 16-byte stores of the saved values.
+// Same work item per workgroup and the same results in the workspace as the
+// fp32 walks above.
+
+// x = hi + lo for four values, each part as four packed bf16
+__device__ __forceinline__ void split4(f32x4 x, uint2& hi, uint2& lo) {
+    const uint32_t h01 = f32x2_to_bf16x2(x[0], x[1]), h23 = f32x2_to_bf16x2(x[2], x[3]);
+    hi = uint2{h01, h23};
+    lo = uint2{f32x2_to_bf16x2(x[0] - __uint_as_float(h01 << 16), x[1] - __uint_as_float(h01 & 0xffff0000u)),
+               f32x2_to_bf16x2(x[2] - __uint_as_float(h23 << 16), x[3] - __uint_as_float(h23 & 0xffff0000u))};
+}
+
+// fragment f of a fragment-ordered operand (one coalesced 16-byte load per lane)
+__device__ __forceinline__ Frag<bf16_t> load_frag(const bf16_t* base, int f, int lane) {
+    Frag<bf16_t> r;
+    r.v = *reinterpret_cast<const u16x8*>(base + f * 512 + lane * 8);
+    return r;
+}
+
+// LDS of the bf16 walks, in floats: fp32 copies [rows][16], then the bf16
+// transposed parts [16][rows + 8] (the pad spreads a fragment read's rows
+// over the banks)
+template <int DK>
+struct WalkLdsB {
+    static constexpr int SK = DK + 8, SC = C + 8;  // bf16 row strides
+    static constexpr int X = 0, Y = X + DK * 16, Xh = Y + C * 16, Xl = Xh + 8 * SK, Yh = Xl + 8 * SK,
+                         Yl = Yh + 8 * SC, O = Yl + 8 * SC, floats = O + 8 * SC;
+};
+
+// Forward state walk (bf16 inputs): saves S and U = U' - W S of every chunk,
+// then S <- Diag(Gn) S + Kd^T U.
+template <int DK>
+struct StateOpsB {
+    Frag<bf16_t> w[DK / 32];          // W: the wave's 16 rows t, k over the channels
+    float up[4];                      // U' of the lane's rows t0 .. t0 + 3 in column col
+    Frag<bf16_t> kt[DK / 64 * C / 32];  // Kd^T: the wave's channel tiles, k over the rows
+    f32x4 gn[DK / 64];                // Gn of the lane's rows of S
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_state_walk_bf16_kernel(
+    int32_t H, int32_t Hs, const float* __restrict__ S0, BwdWs w) {
+    using L = WalkLdsB<DK>;
+    constexpr int NS = DV / 16, SK = L::SK, SC = L::SC, TPW = DK / 64, RS = 4 * TPW, KBD = DK / 32, KBC = C / 32;
+    __shared__ __align__(16) float smem[L::floats];
+    float* sS = smem + L::X;                                // [DK][16]
+    float* sU = smem + L::Y;                                // [C][16]
+    bf16_t* sSh = reinterpret_cast<bf16_t*>(smem + L::Xh);  // [16][SK]: S^T, both parts
+    bf16_t* sSl = reinterpret_cast<bf16_t*>(smem + L::Xl);
+    bf16_t* sUh = reinterpret_cast<bf16_t*>(smem + L::Yh);  // [16][SC]: U^T, both parts
+    bf16_t* sUl = reinterpret_cast<bf16_t*>(smem + L::Yl);
+    int sl, nh;
+    walk_item(NS, sl, nh);
+    const int h = nh % H;
+    const int seq = nh / H;
+    if (w.header->bad_seqlens) return;
+    const int tid = threadIdx.x, wv = tid / 64, lane = tid % 64, lg = lane / 16, lr = lane % 16;
+    const int col = sl * 16 + lr;
+    const int t0 = 16 * wv + 4 * lg;  // this lane's rows of U
+    const int c0 = w.chunk_off[seq], c1 = w.chunk_off[seq + 1];
+    // this lane's rows of S (16 (wv TPW + tt) + 4 lg + i) stay in registers
+    float S[RS];
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            S[4 * tt + i] =
+                S0 ? S0[(((size_t)seq * Hs + h) * DK + 16 * (wv * TPW + tt) + 4 * lg + i) * DV + col] : 0.f;
+    if (c0 >= c1) return;
+    // Loads in the order of use; past the sequence's last chunk the fetches
+    // re-read that chunk (unused), so that every path issues the same loads.
+    auto fetch = [&](int ch, StateOpsB<DK>& X) {
+        const size_t slot = (size_t)ch * H + h;
+        const bf16_t* Wr = reinterpret_cast<const bf16_t*>(w.Wr) + slot * C * DK;
+        const bf16_t* KT = reinterpret_cast<const bf16_t*>(w.KdT) + slot * C * DK;
+#pragma unroll
+        for (int kb = 0; kb < KBD; ++kb) X.w[kb] = load_frag(Wr, wv * KBD + kb, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) X.up[i] = w.Up[slot * C * DV + (size_t)(t0 + i) * DV + col];
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+            for (int kb = 0; kb < KBC; ++kb) X.kt[tt * KBC + kb] = load_frag(KT, (wv * TPW + tt) * KBC + kb, lane);
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt)
+            X.gn[tt] = *reinterpret_cast<const f32x4*>(w.Gn + slot * DK + 16 * (wv * TPW + tt) + 4 * lg);
+    };
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    // X holds chunk ch; the next chunk's operands are fetched into Y first,
+    // so they are in flight during the whole step
+    auto step = [&](int ch, StateOpsB<DK>& X, StateOpsB<DK>& Y) {
+        const size_t slot = (size_t)ch * H + h;
+        const size_t oCV = slot * C * DV, oKV = slot * DK * DV;
+        fetch(min(ch + 1, c1 - 1), Y);
+        // S: the fp32 copy for the saved state, the two parts for the product
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt) {
+            const int r0 = 16 * (wv * TPW + tt) + 4 * lg;
+            const f32x4 x = {S[4 * tt], S[4 * tt + 1], S[4 * tt + 2], S[4 * tt + 3]};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sS[(r0 + i) * 16 + lr] = x[i];
+            uint2 hi, lo;
+            split4(x, hi, lo);
+            *reinterpret_cast<uint2*>(sSh + lr * SK + r0) = hi;
+            *reinterpret_cast<uint2*>(sSl + lr * SK + r0) = lo;
+        }
+        lds_barrier();
+        // the saved S as 16-byte stores from its fp32 copy (four lanes per row)
+#pragma unroll
+        for (int i = tid; i < DK * 4; i += kBwdThreads)
+            *reinterpret_cast<f32x4*>(w.S + oKV + (size_t)(i / 4) * DV + sl * 16 + 4 * (i % 4)) =
+                *reinterpret_cast<const f32x4*>(sS + 4 * i);
+        // U = U' - W S (this wave's 16 rows)
+        Frag<bf16_t> bh[KBD], bl[KBD];
+#pragma unroll
+        for (int kb = 0; kb < KBD; ++kb) {
+            bh[kb] = ld_frag(sSh + lr * SK + 32 * kb + 8 * lg);
+            bl[kb] = ld_frag(sSl + lr * SK + 32 * kb + 8 * lg);
+        }
+        f32x4 wh = zero, wl = zero;
+#pragma unroll
+        for (int kb = 0; kb < KBD; ++kb) {
+            wh = mma(X.w[kb], bh[kb], wh);
+            wl = mma(X.w[kb], bl[kb], wl);
+        }
+        f32x4 u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) u[i] = X.up[i] - (wh[i] + wl[i]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sU[(t0 + i) * 16 + lr] = u[i];
+        {
+            uint2 hi, lo;
+            split4(u, hi, lo);
+            *reinterpret_cast<uint2*>(sUh + lr * SC + t0) = hi;
+            *reinterpret_cast<uint2*>(sUl + lr * SC + t0) = lo;
+        }
+        lds_barrier();
+        // U as 16-byte stores from its fp32 copy: one per thread
+        *reinterpret_cast<f32x4*>(w.U + oCV + (size_t)(tid / 4) * DV + sl * 16 + 4 * (tid % 4)) =
+            *reinterpret_cast<const f32x4*>(sU + 4 * tid);
+        // S <- Diag(Gn) S + Kd^T U (this wave's TPW tiles of rows)
+        Frag<bf16_t> uh[KBC], ul[KBC];
+#pragma unroll
+        for (int kb = 0; kb < KBC; ++kb) {
+            uh[kb] = ld_frag(sUh + lr * SC + 32 * kb + 8 * lg);
+            ul[kb] = ld_frag(sUl + lr * SC + 32 * kb + 8 * lg);
+        }
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt) {
+            f32x4 ah = zero, al = zero;
+#pragma unroll
+            for (int kb = 0; kb < KBC; ++kb) {
+                ah = mma(X.kt[tt * KBC + kb], uh[kb], ah);
+                al = mma(X.kt[tt * KBC + kb], ul[kb], al);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[4 * tt + i] = X.gn[tt][i] * S[4 * tt + i] + (ah[i] + al[i]);
+        }
+    };
+    StateOpsB<DK> A, B;
+    fetch(c0, A);
+    // whole rounds of two steps (A, then B), then the chunk left (in A)
+    int ch = c0;
+    for (; ch + 1 < c1; ch += 2) {
+        step(ch, A, B);
+        step(ch + 1, B, A);
+    }
+    if (ch < c1) step(ch, A, B);
+}
+
+// Reverse state walk (bf16 inputs): saves dS_next and dU = P^T dO + Kd dS_next
+// of every chunk, then dS = Diag(Gn) dS_next + QG^T dO - W^T dU; dS0 at the end.
+template <int DK>
+struct RevOpsB {
+    uint2 o;                            // dO: row tid / 4, columns 4 (tid % 4) .. + 3 of the slice
+    Frag<bf16_t> pt[C / 32];            // P^T: the wave's 16 rows, k over the chunk's rows
+    Frag<bf16_t> kd[DK / 32];           // Kd: the wave's 16 rows t, k over the channels
+    Frag<bf16_t> qt[DK / 64 * C / 32];  // QG^T: the wave's channel tiles, k over the rows
+    Frag<bf16_t> wt[DK / 64 * C / 32];  // W^T: likewise
+    f32x4 gn[DK / 64];                  // Gn of the lane's rows of dS
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dstate_walk_bf16_kernel(
+    int32_t H, int32_t Hs, const bf16_t* __restrict__ dO, const float* __restrict__ dST, float* __restrict__ dS0,
+    BwdWs w) {
+    using L = WalkLdsB<DK>;
+    constexpr int NS = DV / 16, SK = L::SK, SC = L::SC, TPW = DK / 64, RS = 4 * TPW, KBD = DK / 32, KBC = C / 32;
+    __shared__ __align__(16) float smem[L::floats];
+    float* sdS = smem + L::X;                               // [DK][16]
+    float* sdU = smem + L::Y;                               // [C][16]
+    bf16_t* sDh = reinterpret_cast<bf16_t*>(smem + L::Xh);  // [16][SK]: dS_next^T, both parts
+    bf16_t* sDl = reinterpret_cast<bf16_t*>(smem + L::Xl);
+    bf16_t* sUh = reinterpret_cast<bf16_t*>(smem + L::Yh);  // [16][SC]: dU^T, both parts
+    bf16_t* sUl = reinterpret_cast<bf16_t*>(smem + L::Yl);
+    bf16_t* sO = reinterpret_cast<bf16_t*>(smem + L::O);    // [16][SC]: dO^T
+    int sl, nh;
+    walk_item(NS, sl, nh);
+    const int h = nh % H;
+    const int seq = nh / H;
+    if (w.header->bad_seqlens) return;
+    const int tid = threadIdx.x, wv = tid / 64, lane = tid % 64, lg = lane / 16, lr = lane % 16;
+    const int col = sl * 16 + lr;
+    const int t0 = 16 * wv + 4 * lg;  // this lane's rows of dU (and of dO it loads)
+    const int c0 = w.chunk_off[seq], c1 = w.chunk_off[seq + 1];
+    auto srow = [&](int i) { return 16 * (wv * TPW + i / 4) + 4 * lg + i % 4; };  // rows of dS
+    float dS[RS];
+#pragma unroll
+    for (int i = 0; i < RS; ++i) dS[i] = dST ? dST[(((size_t)seq * Hs + h) * DK + srow(i)) * DV + col] : 0.f;
+    if (c0 < c1) {
+        const int tok0 = w.cu[seq], tok1 = w.cu[seq + 1];
+        // rows past a chunk's end re-read its last row and are zeroed when staged
+        auto rows_of = [&](int ch) { return min(C, tok1 - (tok0 + (ch - c0) * C)); };
+        auto fetch = [&](int ch, RevOpsB<DK>& X) {
+            const size_t slot = (size_t)ch * H + h;
+            const int first = tok0 + (ch - c0) * C, n = rows_of(ch);
+            X.o = *reinterpret_cast<const uint2*>(dO + (((int64_t)first + min(tid / 4, n - 1)) * Hs + h) * DV + sl * 16 +
+                                                  4 * (tid % 4));
+            const bf16_t* P = reinterpret_cast<const bf16_t*>(w.P) + slot * C * C;
+            const bf16_t* Kd = reinterpret_cast<const bf16_t*>(w.Kd) + slot * C * DK;
+            const bf16_t* QT = reinterpret_cast<const bf16_t*>(w.QG) + slot * C * DK;
+            const bf16_t* WT = reinterpret_cast<const bf16_t*>(w.W) + slot * C * DK;
+#pragma unroll
+            for (int kb = 0; kb < KBC; ++kb) X.pt[kb] = load_frag(P, wv * KBC + kb, lane);
+#pragma unroll
+            for (int kb = 0; kb < KBD; ++kb) X.kd[kb] = load_frag(Kd, wv * KBD + kb, lane);
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+                for (int kb = 0; kb < KBC; ++kb) X.qt[tt * KBC + kb] = load_frag(QT, (wv * TPW + tt) * KBC + kb, lane);
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+                for (int kb = 0; kb < KBC; ++kb) X.wt[tt * KBC + kb] = load_frag(WT, (wv * TPW + tt) * KBC + kb, lane);
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt)
+                X.gn[tt] = *reinterpret_cast<const f32x4*>(w.Gn + slot * DK + 16 * (wv * TPW + tt) + 4 * lg);
+        };
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        // Every LDS array is written before the step's first barrier or
+        // between its two, and read between the two or after the second; so
+        // one copy of each suffices.
+        // X holds chunk ch; the previous chunk's operands are fetched into Y
+        // first, so they are in flight during the whole step
+        auto step = [&](int ch, RevOpsB<DK>& X, RevOpsB<DK>& Y) {
+            const size_t slot = (size_t)ch * H + h;
+            const size_t oCV = slot * C * DV, oKV = slot * DK * DV;
+            fetch(max(ch - 1, c0), Y);
+            {
+                // dO transposed, zero past the chunk's end
+                const int t = tid / 4, c = 4 * (tid % 4);
+                const uint2 o = t < rows_of(ch) ? X.o : uint2{0u, 0u};
+                sO[(c + 0) * SC + t] = (bf16_t)(o.x & 0xffffu);
+                sO[(c + 1) * SC + t] = (bf16_t)(o.x >> 16);
+                sO[(c + 2) * SC + t] = (bf16_t)(o.y & 0xffffu);
+                sO[(c + 3) * SC + t] = (bf16_t)(o.y >> 16);
+            }
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt) {
+                const int r0 = 16 * (wv * TPW + tt) + 4 * lg;
+                const f32x4 x = {dS[4 * tt], dS[4 * tt + 1], dS[4 * tt + 2], dS[4 * tt + 3]};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sdS[(r0 + i) * 16 + lr] = x[i];
+                uint2 hi, lo;
+                split4(x, hi, lo);
+                *reinterpret_cast<uint2*>(sDh + lr * SK + r0) = hi;
+                *reinterpret_cast<uint2*>(sDl + lr * SK + r0) = lo;
+            }
+            lds_barrier();
+            // the saved dS_next as 16-byte stores from its fp32 copy (four lanes per row)
+#pragma unroll
+            for (int i = tid; i < DK * 4; i += kBwdThreads)
+                *reinterpret_cast<f32x4*>(w.dSn + oKV + (size_t)(i / 4) * DV + sl * 16 + 4 * (i % 4)) =
+                    *reinterpret_cast<const f32x4*>(sdS + 4 * i);
+            // dU = P^T dO + Kd dS_next (this wave's 16 rows)
+            Frag<bf16_t> of[KBC], dh[KBD], dl[KBD];
+#pragma unroll
+            for (int kb = 0; kb < KBC; ++kb) of[kb] = ld_frag(sO + lr * SC + 32 * kb + 8 * lg);
+#pragma unroll
+            for (int kb = 0; kb < KBD; ++kb) {
+                dh[kb] = ld_frag(sDh + lr * SK + 32 * kb + 8 * lg);
+                dl[kb] = ld_frag(sDl + lr * SK + 32 * kb + 8 * lg);
+            }
+            f32x4 uo = zero, uh = zero, ul = zero;
+#pragma unroll
+            for (int kb = 0; kb < KBC; ++kb) uo = mma(X.pt[kb], of[kb], uo);
+#pragma unroll
+            for (int kb = 0; kb < KBD; ++kb) {
+                uh = mma(X.kd[kb], dh[kb], uh);
+                ul = mma(X.kd[kb], dl[kb], ul);
+            }
+            f32x4 du;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) du[i] = uo[i] + (uh[i] + ul[i]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sdU[(t0 + i) * 16 + lr] = du[i];
+            {
+                uint2 hi, lo;
+                split4(du, hi, lo);
+                *reinterpret_cast<uint2*>(sUh + lr * SC + t0) = hi;
+                *reinterpret_cast<uint2*>(sUl + lr * SC + t0) = lo;
+            }
+            lds_barrier();
+            // dU as 16-byte stores from its fp32 copy: one per thread
+            *reinterpret_cast<f32x4*>(w.dU + oCV + (size_t)(tid / 4) * DV + sl * 16 + 4 * (tid % 4)) =
+                *reinterpret_cast<const f32x4*>(sdU + 4 * tid);
+            // dS = Diag(Gn) dS_next + QG^T dO - W^T dU (this wave's TPW tiles of rows)
+            Frag<bf16_t> eh[KBC], el[KBC];
+#pragma unroll
+            for (int kb = 0; kb < KBC; ++kb) {
+                eh[kb] = ld_frag(sUh + lr * SC + 32 * kb + 8 * lg);
+                el[kb] = ld_frag(sUl + lr * SC + 32 * kb + 8 * lg);
+            }
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt) {
+                f32x4 aq = zero, ah = zero, al = zero;
+#pragma unroll
+                for (int kb = 0; kb < KBC; ++kb) {
+                    aq = mma(X.qt[tt * KBC + kb], of[kb], aq);
+                    ah = mma(X.wt[tt * KBC + kb], eh[kb], ah);
+                    al = mma(X.wt[tt * KBC + kb], el[kb], al);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dS[4 * tt + i] = X.gn[tt][i] * dS[4 * tt + i] + (aq[i] - (ah[i] + al[i]));
+            }
+        };
+        RevOpsB<DK> A, B;
+        fetch(c1 - 1, A);
+        // whole rounds of two steps (A, then B), then the chunk left (in A)
+        int ch = c1 - 1;
+        for (; ch - 1 >= c0; ch -= 2) {
+            step(ch, A, B);
+            step(ch - 1, B, A);
+        }
+        if (ch >= c0) step(ch, A, B);
     }
     if (dS0) {
 #pragma unroll
@@ -1628,11 +2071,12 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
 inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdSizes {
-    size_t head, ck, ckw, cv, cc, ccw, c, k, kv, total;
+    size_t head, ck, ckw, ckb, cv, cc, ccw, c, k, kv, total;
 };
 
-// The walks' operands (QG, Kd, W: [C][DK]; P: [C][C]) are kept in the input
-// type (bf16 for bf16 inputs), every other array in fp32.
+// The walks' operands (QG, Kd, W: C x DK; P: C x C) are kept in the input
+// type (bf16 for bf16 inputs), every other array in fp32; bf16 inputs keep W
+// and Kd twice (Wr, KdT: one layout per walk).
 BwdSizes bwd_sizes(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, bool bf16) {
     const size_t slots = (size_t)max_chunks_for(T, N) * H;
     const size_t ew = bf16 ? 2 : 4;
@@ -1640,13 +2084,14 @@ BwdSizes bwd_sizes(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, bool
     s.head = 256 + 2 * al256((size_t)(N + 1) * 4) + al256((size_t)max_chunks_for(T, N) * sizeof(int2));
     s.ck = al256(slots * C * dk * 4);
     s.ckw = al256(slots * C * dk * ew);
+    s.ckb = bf16 ? s.ckw : 0;
     s.cv = al256(slots * C * dv * 4);
     s.cc = al256(slots * C * C * 4);
     s.ccw = al256(slots * C * C * ew);
     s.c = al256(slots * C * 4);
     s.k = al256(slots * dk * 4);
     s.kv = al256(slots * dk * dv * 4);
-    s.total = s.head + 6 * s.ck + 3 * s.ckw + 3 * s.cv + 4 * s.cc + s.ccw + s.c + 2 * s.k + 2 * s.kv;
+    s.total = s.head + 6 * s.ck + 3 * s.ckw + 2 * s.ckb + 3 * s.cv + 4 * s.cc + s.ccw + s.c + 2 * s.k + 2 * s.kv;
     return s;
 }
 
@@ -1663,6 +2108,8 @@ BwdWs carve_bwd(void* base, int64_t T, int32_t N, int32_t H, int32_t dk, int32_t
     for (float** f : ck) *f = take(s.ck);
     float** ckw[] = {&w.QG, &w.Kd, &w.W};
     for (float** f : ckw) *f = take(s.ckw);
+    float** ckb[] = {&w.Wr, &w.KdT};
+    for (float** f : ckb) *f = s.ckb ? take(s.ckb) : nullptr;
     float** cv[] = {&w.Up, &w.U, &w.dU};
     for (float** f : cv) *f = take(s.cv);
     float** cc[] = {&w.M, &w.T, &w.dP, &w.dA};
@@ -1694,17 +2141,27 @@ hipError_t launch_bwd_t(const BwdArgs& a, int32_t Hs, const BwdWs& w, hipStream_
                            w);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
-        auto sw = bwd_state_walk_kernel<E, DK, DV>;
-        constexpr size_t sw_lds = StateWalkLds<DK, DV>::bytes;
-        if ((e = lds_attr(reinterpret_cast<const void*>(sw), sw_lds)) != hipSuccess) return e;
-        hipLaunchKernelGGL(sw, dim3(walks), dim3(kBwdThreads), sw_lds, stream, a.H, Hs, a.S0, w);
+        if constexpr (std::is_same<E, bf16_t>::value) {
+            hipLaunchKernelGGL((bwd_state_walk_bf16_kernel<DK, DV>), dim3(walks), dim3(kBwdThreads), 0, stream, a.H,
+                               Hs, a.S0, w);
+        } else {
+            auto sw = bwd_state_walk_kernel<E, DK, DV>;
+            constexpr size_t sw_lds = StateWalkLds<DK, DV>::bytes;
+            if ((e = lds_attr(reinterpret_cast<const void*>(sw), sw_lds)) != hipSuccess) return e;
+            hipLaunchKernelGGL(sw, dim3(walks), dim3(kBwdThreads), sw_lds, stream, a.H, Hs, a.S0, w);
+        }
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    auto dw = bwd_dstate_walk_kernel<E, DK, DV>;
-    constexpr size_t dw_lds = DStateWalkLds<DK, DV>::bytes;
-    if ((e = lds_attr(reinterpret_cast<const void*>(dw), dw_lds)) != hipSuccess) return e;
-    hipLaunchKernelGGL(dw, dim3(walks), dim3(kBwdThreads), dw_lds, stream, a.H, Hs, (const E*)a.dO, a.dS_T, a.dS0,
-                       w);
+    if constexpr (std::is_same<E, bf16_t>::value) {
+        hipLaunchKernelGGL((bwd_dstate_walk_bf16_kernel<DK, DV>), dim3(walks), dim3(kBwdThreads), 0, stream, a.H, Hs,
+                           (const bf16_t*)a.dO, a.dS_T, a.dS0, w);
+    } else {
+        auto dw = bwd_dstate_walk_kernel<E, DK, DV>;
+        constexpr size_t dw_lds = DStateWalkLds<DK, DV>::bytes;
+        if ((e = lds_attr(reinterpret_cast<const void*>(dw), dw_lds)) != hipSuccess) return e;
+        hipLaunchKernelGGL(dw, dim3(walks), dim3(kBwdThreads), dw_lds, stream, a.H, Hs, (const E*)a.dO, a.dS_T,
+                           a.dS0, w);
+    }
     e = hipGetLastError();
     if (e != hipSuccess || a.T == 0) return e;
     hipLaunchKernelGGL((bwd_local_kernel<E, DK, DV, HG, 0>), dim3(slots), dim3(kBwdThreads), 0, stream,

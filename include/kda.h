@@ -312,11 +312,12 @@ kda_status kda_recurrent_step_raw(const void *q_raw, const void *k_raw,
 
 /*
  * Bytes of device workspace kda_chunk_bwd needs to process all H heads at
- * once (0 if the sizes are invalid or unsupported).  About 540 KB per (chunk,
- * head) at d_k = d_v = 128 for KDA_BF16 (590 KB for KDA_F32): the chunk's
- * intermediates are kept, in fp32 except the four operands of the two
- * sequential passes over the chunks, which are kept in type dt.  The value
- * for H = 1 is the least kda_chunk_bwd accepts.
+ * once (0 if the sizes are invalid or unsupported).  About 570 KB per (chunk,
+ * head) at d_k = d_v = 128 for KDA_BF16 (593 KB for KDA_F32): the chunk's
+ * intermediates are kept, in fp32 except the operands of the two sequential
+ * passes over the chunks, which are kept in type dt (for KDA_BF16 in the
+ * matrix cores' fragment order, two of them in two layouts).  The value for
+ * H = 1 is the least kda_chunk_bwd accepts.
  */
 size_t kda_chunk_bwd_workspace_size(int64_t T_total, int32_t N, int32_t H,
                                     int32_t d_k, int32_t d_v, kda_dtype dt,
@@ -357,7 +358,10 @@ size_t kda_chunk_bwd_workspace_size(int64_t T_total, int32_t N, int32_t H,
  * Alignment: every pointer to its element size.  Errors as for
  * kda_chunk_fwd.  Numerics: all arithmetic in fp32, gradients rounded once
  * to dt; the operands of the two sequential passes over the chunks (QG, Kd,
- * W and the intra-chunk P) are rounded to dt as well.  Domain: the forward's.  Every decayed operand is referred to the
+ * W and the intra-chunk P) are rounded to dt as well.  For KDA_BF16 those two
+ * passes multiply on the bf16 matrix cores with fp32 accumulation, the fp32
+ * state and its cotangent entering each product as a sum of two bf16 parts
+ * (about 16 significant bits).  Domain: the forward's.  Every decayed operand is referred to the
  * middle row of its own 16-token tile and the decay between tiles is rebuilt
  * from factors <= 1, so the gradients are exact (up to rounding) while the
  * decay accumulated over any eight consecutive tokens stays above e^-80 (e.g.
