@@ -1526,8 +1526,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
     __shared__ float sbl[DK];
     __shared__ float sRowKG[C];       // sum_c dXw[t][c] KG[t][c], per row
     __shared__ float sColKd[4 * DK];  // sum_t dKd[t][c] Kd[t][c], per wave and column
-    // phases 1 and 5 stage five and seven operand tiles at once; phases 2-4 use gemm64's two
-    constexpr int kLdsFloats = PH == 0   ? 16 * (3 * (C + 4) + 2 * (DK + 4))
+    // phases 1 and 5 stage five and seven operand tiles at once (phase 1 for
+    // bf16 inputs: the two bf16 parts of S, dS_next and U for 32 value
+    // columns, rows padded to 40); phases 2-4 use gemm64's two
+    constexpr bool kBf = std::is_same<E, bf16_t>::value;
+    constexpr int kLdsFloats = PH == 0   ? (kBf ? (4 * DK + 2 * C) * 20 : 16 * (3 * (C + 4) + 2 * (DK + 4)))
                                : PH == 2 ? (16 * 3 * (DK + 4) > C * (DK + 1) ? 16 * 3 * (DK + 4) : C * (DK + 1))
                                          : kGemmLds;
     __shared__ __align__(16) float lds[kLdsFloats];
@@ -1567,7 +1570,126 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
             }
     };
 
-    if constexpr (PH == 0) {
+    if constexpr (PH == 0 && kBf) {
+    // phase 1 for bf16 inputs, on the bf16 matrix cores: dW = -dU S^T,
+    // dQG = dO S^T, dKd = U dS_next^T, dP = tril(dO U^T) and dGn[c] = sum_x
+    // S[c][x] dS_next[c][x].  Every product contracts over the value index x,
+    // which is contiguous in every operand, so a fragment (frag_at) is eight
+    // consecutive x of one row.  Per block of 32 x, S, dS_next and U (the B
+    // sides, all their rows) are staged in LDS as two bf16 parts,
+    // x = hi + lo; the wave's rows of dU and dO (the A sides) are loaded into
+    // registers, dU split likewise and dO exact; U as an A side is read from
+    // its staged parts.  A product of two split operands is hi hi + hi lo +
+    // lo hi (the dropped lo lo is below 2^-16 of it); one with dO is dO hi +
+    // dO lo.  dGn is summed in fp32 from the values as loaded.
+    {
+        constexpr int XB = 32, SP = XB + 8, NT = DK / 16;
+        bf16_t* sSh = reinterpret_cast<bf16_t*>(lds);  // [DK][SP]
+        bf16_t* sSl = sSh + DK * SP;
+        bf16_t* sDh = sSl + DK * SP;                   // dS_next, [DK][SP]
+        bf16_t* sDl = sDh + DK * SP;
+        bf16_t* sUh = sDl + DK * SP;                   // [C][SP]
+        bf16_t* sUl = sUh + C * SP;
+        static_assert((4 * DK + 2 * C) * SP <= 2 * kLdsFloats, "phase-1 parts fit");
+        const int wv = tid / 64, lg = (tid % 64) / 16, lr = tid % 16;
+        const int ta = 16 * wv + lr;  // the lane's row of the A sides
+        // staging shares: rows cs of S and dS_next (TS threads a row, XS
+        // values each), rows cu of U (TU threads a row, XU values each)
+        constexpr int TS = kBwdThreads / DK, XS = XB / TS, TU = kBwdThreads / C, XU = XB / TU;
+        const int cs = tid / TS, xs = XS * (tid % TS), cu = tid / TU, xu = XU * (tid % TU);
+        Acc<DK> aW, aQ, aK;
+        Acc<C> aP;
+        aW.zero();
+        aQ.zero();
+        aK.zero();
+        aP.zero();
+        f32x4 rS[XS / 4], rD[XS / 4], rU[XU / 4], rdU[2];
+        uint4 rdO;
+        auto fetch = [&](int x0) {
+#pragma unroll
+            for (int i = 0; i < XS / 4; ++i) {
+                rS[i] = *reinterpret_cast<const f32x4*>(Sm + (size_t)cs * DV + x0 + xs + 4 * i);
+                rD[i] = *reinterpret_cast<const f32x4*>(dSn + (size_t)cs * DV + x0 + xs + 4 * i);
+            }
+#pragma unroll
+            for (int i = 0; i < XU / 4; ++i)
+                rU[i] = *reinterpret_cast<const f32x4*>(Um + (size_t)cu * DV + x0 + xu + 4 * i);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                rdU[i] = *reinterpret_cast<const f32x4*>(dUm + (size_t)ta * DV + x0 + 8 * lg + 4 * i);
+            rdO = *reinterpret_cast<const uint4*>(dO + ((t0 + min(ta, n - 1)) * Hs + h) * DV + x0 + 8 * lg);
+        };
+        auto put2 = [&](bf16_t* hi, bf16_t* lo, int at, f32x4 v) {
+            uint2 ph, pl;
+            split4(v, ph, pl);
+            *reinterpret_cast<uint2*>(hi + at) = ph;
+            *reinterpret_cast<uint2*>(lo + at) = pl;
+        };
+        float gn = 0.f;
+        fetch(0);
+        for (int x0 = 0; x0 < DV; x0 += XB) {
+#pragma unroll
+            for (int i = 0; i < XS / 4; ++i) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) gn += rS[i][j] * rD[i][j];
+                put2(sSh, sSl, cs * SP + xs + 4 * i, rS[i]);
+                put2(sDh, sDl, cs * SP + xs + 4 * i, rD[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < XU / 4; ++i) put2(sUh, sUl, cu * SP + xu + 4 * i, rU[i]);
+            // the A sides of this block: dU in two parts, dO (zero past the chunk's end)
+            Frag<bf16_t> dUh, dUl, dOf;
+            {
+                uint2 h0, l0, h1, l1;
+                split4(rdU[0], h0, l0);
+                split4(rdU[1], h1, l1);
+                dUh.v = __builtin_bit_cast(u16x8, uint4{h0.x, h0.y, h1.x, h1.y});
+                dUl.v = __builtin_bit_cast(u16x8, uint4{l0.x, l0.y, l1.x, l1.y});
+                dOf.v = __builtin_bit_cast(u16x8, ta < n ? rdO : uint4{0u, 0u, 0u, 0u});
+            }
+            lds_barrier();
+            if (x0 + XB < DV) fetch(x0 + XB);
+            const Frag<bf16_t> uhA = ld_frag(sUh + ta * SP + 8 * lg), ulA = ld_frag(sUl + ta * SP + 8 * lg);
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                const int at = (16 * j + lr) * SP + 8 * lg;
+                const Frag<bf16_t> sh = ld_frag(sSh + at), sl = ld_frag(sSl + at);
+                const Frag<bf16_t> dh = ld_frag(sDh + at), dl = ld_frag(sDl + at);
+                aW.t[j] = mma(dUh, sh, aW.t[j]);
+                aQ.t[j] = mma(dOf, sh, aQ.t[j]);
+                aK.t[j] = mma(uhA, dh, aK.t[j]);
+                aW.t[j] = mma(dUh, sl, aW.t[j]);
+                aQ.t[j] = mma(dOf, sl, aQ.t[j]);
+                aK.t[j] = mma(uhA, dl, aK.t[j]);
+                aW.t[j] = mma(dUl, sh, aW.t[j]);
+                aK.t[j] = mma(ulA, dh, aK.t[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < C / 16; ++j) {
+                const int at = (16 * j + lr) * SP + 8 * lg;
+                aP.t[j] = mma(dOf, ld_frag(sUh + at), aP.t[j]);
+                aP.t[j] = mma(dOf, ld_frag(sUl + at), aP.t[j]);
+            }
+            lds_barrier();
+        }
+        // the TS threads of a row of S hold partial sums of dGn
+#pragma unroll
+        for (int o = 1; o < TS; o <<= 1) gn += __shfl_xor(gn, o);
+        put(aW, w.dW + oCK, DK, -1.f);
+        put(aQ, w.dQG + oCK, DK, 1.f);
+        put(aK, w.dKd + oCK, DK, 1.f);
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < C / 16; ++b) {
+                const int t = Acc<C>::row(a), i = Acc<C>::col(b);
+                w.dP[oCC + (size_t)t * C + i] = (i <= t && t < n) ? aP.t[b][a] : 0.f;
+            }
+        if (tid % TS == 0) w.dGn[oK + cs] = gn;
+    }
+    }  // PH == 0, bf16
+
+    if constexpr (PH == 0 && !kBf) {
     // phase 1 as one pass over the value index x in tiles of 16: dW = -dU S^T,
     // dQG = dO S^T, dKd = U dS_next^T, dP = tril(dO U^T) and dGn[c] = sum_x
     // S[c][x] dS_next[c][x].  Each operand tile is read from memory once and
