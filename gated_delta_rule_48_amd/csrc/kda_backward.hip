@@ -1172,6 +1172,12 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
 // Same work item per workgroup and the same results in the workspace as the
 // fp32 walks above.
 
+// Eight bytes to LDS as one store that is never paired with another
+// (lds_put; matrix-core results reach LDS only this way)
+__device__ __forceinline__ void lds_put8(bf16_t* p, uint2 v) {
+    lds_put(reinterpret_cast<unsigned long long*>(p), (static_cast<unsigned long long>(v.y) << 32) | v.x);
+}
+
 // x = hi + lo for four values, each part as four packed bf16
 __device__ __forceinline__ void split4(f32x4 x, uint2& hi, uint2& lo) {
     const uint32_t h01 = f32x2_to_bf16x2(x[0], x[1]), h23 = f32x2_to_bf16x2(x[2], x[3]);
@@ -1268,11 +1274,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
             const int r0 = 16 * (wv * TPW + tt) + 4 * lg;
             const f32x4 x = {S[4 * tt], S[4 * tt + 1], S[4 * tt + 2], S[4 * tt + 3]};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sS[(r0 + i) * 16 + lr] = x[i];
+            for (int i = 0; i < 4; ++i) lds_put(&sS[(r0 + i) * 16 + lr], x[i]);
             uint2 hi, lo;
             split4(x, hi, lo);
-            *reinterpret_cast<uint2*>(sSh + lr * SK + r0) = hi;
-            *reinterpret_cast<uint2*>(sSl + lr * SK + r0) = lo;
+            lds_put8(sSh + lr * SK + r0, hi);
+            lds_put8(sSl + lr * SK + r0, lo);
         }
         lds_barrier();
         // the saved S as 16-byte stores from its fp32 copy (four lanes per row)
@@ -1297,12 +1303,12 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
 #pragma unroll
         for (int i = 0; i < 4; ++i) u[i] = X.up[i] - (wh[i] + wl[i]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sU[(t0 + i) * 16 + lr] = u[i];
+        for (int i = 0; i < 4; ++i) lds_put(&sU[(t0 + i) * 16 + lr], u[i]);
         {
             uint2 hi, lo;
             split4(u, hi, lo);
-            *reinterpret_cast<uint2*>(sUh + lr * SC + t0) = hi;
-            *reinterpret_cast<uint2*>(sUl + lr * SC + t0) = lo;
+            lds_put8(sUh + lr * SC + t0, hi);
+            lds_put8(sUl + lr * SC + t0, lo);
         }
         lds_barrier();
         // U as 16-byte stores from its fp32 copy: one per thread
@@ -1430,11 +1436,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
                 const int r0 = 16 * (wv * TPW + tt) + 4 * lg;
                 const f32x4 x = {dS[4 * tt], dS[4 * tt + 1], dS[4 * tt + 2], dS[4 * tt + 3]};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sdS[(r0 + i) * 16 + lr] = x[i];
+                for (int i = 0; i < 4; ++i) lds_put(&sdS[(r0 + i) * 16 + lr], x[i]);
                 uint2 hi, lo;
                 split4(x, hi, lo);
-                *reinterpret_cast<uint2*>(sDh + lr * SK + r0) = hi;
-                *reinterpret_cast<uint2*>(sDl + lr * SK + r0) = lo;
+                lds_put8(sDh + lr * SK + r0, hi);
+                lds_put8(sDl + lr * SK + r0, lo);
             }
             lds_barrier();
             // the saved dS_next as 16-byte stores from its fp32 copy (four lanes per row)
@@ -1463,12 +1469,12 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
 #pragma unroll
             for (int i = 0; i < 4; ++i) du[i] = uo[i] + (uh[i] + ul[i]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sdU[(t0 + i) * 16 + lr] = du[i];
+            for (int i = 0; i < 4; ++i) lds_put(&sdU[(t0 + i) * 16 + lr], du[i]);
             {
                 uint2 hi, lo;
                 split4(du, hi, lo);
-                *reinterpret_cast<uint2*>(sUh + lr * SC + t0) = hi;
-                *reinterpret_cast<uint2*>(sUl + lr * SC + t0) = lo;
+                lds_put8(sUh + lr * SC + t0, hi);
+                lds_put8(sUl + lr * SC + t0, lo);
             }
             lds_barrier();
             // dU as 16-byte stores from its fp32 copy: one per thread
