@@ -2035,7 +2035,14 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
             // e(kt), then to m(wv).  Column side: nothing for kt < wv; for
             // kt > wv, Kr and Qr go to s(kt), then to m(wv).
             const int kt = k0 / KT;
-            const bool row_side = kt <= wv, col_side = kt >= wv;
+            const bool below = kt < wv, above = kt > wv;
+            // No branch inside the loop (tested there, every column tile had
+            // been a branch of its own around a few reads and instructions):
+            // both sides' instructions run for every tile pair, and the side
+            // that does not apply multiplies exact zeros, since dA and dP are
+            // zero above the diagonal (row side, kt > wv) and their
+            // transposes below it (column side, kt < wv); its right operand
+            // is then left unscaled, finite.
             const float* fu = tf_row(kt < wv ? kTfFe + kt : kTfFs + kt);
             const float* fv = tf_row(kt < wv ? kTfF1 + pair_of(wv, kt) : kTfF2 + pair_of(kt > wv ? kt : 1, kt > wv ? wv : 0));
 #pragma unroll
@@ -2049,22 +2056,14 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(PH 
 #pragma unroll
                 for (int j = 0; j < NT; ++j) {
                     const int br = kr * SB + 16 * j + lr;
-                    float bKi = tKi[br], bKr = tKr[br], bQr = tQr[br];
-                    if (kt < wv) {
-                        bKi = (bKi * fu[16 * j + lr]) * fv[16 * j + lr];
-                    } else if (kt > wv) {
-                        const float u = fu[16 * j + lr], x = fv[16 * j + lr];
-                        bKr = (bKr * u) * x;
-                        bQr = (bQr * u) * x;
-                    }
-                    if (row_side) {
-                        aKr.t[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_Ac, bKi, aKr.t[j], 0, 0, 0);
-                        aQr.t[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_Pc, bKi, aQr.t[j], 0, 0, 0);
-                    }
-                    if (col_side) {
-                        acc.t[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_Ar, bKr, acc.t[j], 0, 0, 0);
-                        acc.t[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_Pr, bQr, acc.t[j], 0, 0, 0);
-                    }
+                    const float bKi = tKi[br], bKr = tKr[br], bQr = tQr[br];
+                    const float u = fu[16 * j + lr], x = fv[16 * j + lr];
+                    const float sKi = below ? (bKi * u) * x : bKi;
+                    const float sKr = above ? (bKr * u) * x : bKr, sQr = above ? (bQr * u) * x : bQr;
+                    aKr.t[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_Ac, sKi, aKr.t[j], 0, 0, 0);
+                    aQr.t[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_Pc, sKi, aQr.t[j], 0, 0, 0);
+                    acc.t[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_Ar, sKr, acc.t[j], 0, 0, 0);
+                    acc.t[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_Pr, sQr, acc.t[j], 0, 0, 0);
                 }
             }
             lds_barrier();
