@@ -40,16 +40,17 @@
 //        for a per-head gate).
 //
 // All arithmetic is fp32; every matrix product runs on the fp32 matrix cores
-// (v_mfma_f32_16x16x4f32), except the two walks for bf16 inputs, which run on
-// the bf16 matrix cores with fp32 accumulation (their operands are stored in
-// bf16; the fp32 state enters as two bf16 parts, see the bf16 walks below).
-// Every intermediate of a chunk is kept in the
-// workspace, except Qr, Kr and Ki (the two launches that multiply them form
-// them again from q, k and b as they stage them) and dXu (used only inside
-// the middle local launch).  The two walks run one workgroup per (sequence,
-// head, 16-column slice) with register tiles and the next chunk's operands in
-// flight; every product of the per-chunk kernels runs as a 64 x N block
-// product tiled through LDS with 4 x N/16 register tiles.
+// (v_mfma_f32_16x16x4f32), except, for bf16 inputs, those of the two walks and
+// of the first local launch, which run on the bf16 matrix cores with fp32
+// accumulation (the walks' operands are stored in bf16; an fp32 operand enters
+// as two bf16 parts, see the bf16 walks below).  Every intermediate of a chunk
+// is kept in the workspace, except Qr, Kr and Ki (the two launches that
+// multiply them form them again from q, k and b as they stage them) and dXu
+// (used only inside the middle local launch).  The two walks run one
+// workgroup per (sequence, head, 16-column slice) with register tiles and the
+// next chunk's operands in flight; the other products of the per-chunk
+// kernels run as 64 x N block products tiled through LDS with 4 x N/16
+// register tiles.
 #include "kda_internal.h"
 
 #include <type_traits>

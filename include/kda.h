@@ -359,9 +359,10 @@ size_t kda_chunk_bwd_workspace_size(int64_t T_total, int32_t N, int32_t H,
  * kda_chunk_fwd.  Numerics: all arithmetic in fp32, gradients rounded once
  * to dt; the operands of the two sequential passes over the chunks (QG, Kd,
  * W and the intra-chunk P) are rounded to dt as well.  For KDA_BF16 those two
- * passes multiply on the bf16 matrix cores with fp32 accumulation, the fp32
- * state and its cotangent entering each product as a sum of two bf16 parts
- * (about 16 significant bits).  Domain: the forward's.  Every decayed operand is referred to the
+ * passes, and the per-chunk products with the saved states (dW, dQG, dKd, dP),
+ * multiply on the bf16 matrix cores with fp32 accumulation, every fp32 operand
+ * entering as a sum of two bf16 parts (about 16 significant bits).  Domain:
+ * the forward's.  Every decayed operand is referred to the
  * middle row of its own 16-token tile and the decay between tiles is rebuilt
  * from factors <= 1, so the gradients are exact (up to rounding) while the
  * decay accumulated over any eight consecutive tokens stays above e^-80 (e.g.
